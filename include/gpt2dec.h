@@ -1,0 +1,143 @@
+/*
+ * gpt2dec.h -- C ABI of the MI355X (gfx950) batch-1 GPT-2 decode library.
+ *
+ * One call of gpt2_step runs the one-token forward pass that the "model.fir"
+ * page (gpt2-125m model file) describes node by node: token + positional
+ * embedding, per layer LayerNorm -> QKV linear + bias -> attn_decode (append
+ * this position's K/V, causal softmax over positions 0..position, weighted sum
+ * of values) -> attention linear + bias + residual -> LayerNorm -> fc linear +
+ * bias -> gelu_new -> projection linear + bias + residual, then the final
+ * LayerNorm and the output head tied to wte, with greedy choice = argmax
+ * ("Let's make GPT-2 in assembly", Step 7).  Weights arrive in the Hugging Face
+ * checkpoint layout (Conv1D matrices as [input][output], as both pages note)
+ * and are re-laid out once at load, output-major, as the gpt2.s README
+ * ("Inner Workings") and the blog's Step 1 do.
+ *
+ * Conventions for every entry point:
+ *  - All pointers are HOST pointers unless stated otherwise; the caller owns
+ *    them and they are only read (or written, for outputs) during the call.
+ *  - The library owns all device memory and the context.  Work runs on the
+ *    context's HIP stream (library-created, or the caller's via
+ *    gpt2_set_stream); every call that returns host data synchronizes it.
+ *  - Return value 0 = success, or one of the negative GPT2_E_* codes below.
+ *    Arguments are validated before any device work, so a rejected call
+ *    changes nothing.  After GPT2_E_DEVICE the context is poisoned: every
+ *    later call except gpt2_last_error/gpt2_free returns GPT2_E_STATE.
+ *  - A context must not be used by two threads at once.
+ */
+#ifndef GPT2DEC_H
+#define GPT2DEC_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* exported from libgpt2dec.so (built with hidden default visibility) */
+#if defined(__GNUC__) || defined(__clang__)
+#define GPT2DEC_API __attribute__((visibility("default")))
+#else
+#define GPT2DEC_API
+#endif
+
+#define GPT2_OK 0
+#define GPT2_E_INVAL (-1)   /* bad argument or unsupported configuration        */
+#define GPT2_E_NOMEM (-2)   /* host or device allocation failed                 */
+#define GPT2_E_DEVICE (-3)  /* HIP error, no GPU, or a device-side wait timeout */
+#define GPT2_E_STATE (-4)   /* context poisoned by an earlier device error      */
+
+/* Storage of the 48 block matrices (and, for fp16, the output head).  fp32 is
+ * the model file's f32 linears ("--fir-f32"); fp16 is the gpt2.s "-h" option
+ * (matrices and head stored fp16, widened to fp32, fp32 products and sums;
+ * embeddings, biases and LayerNorm stay fp32); int4 is the model file's "q4"
+ * linears (grouped asymmetric int4 along the input after transposing to
+ * [output][input]; the tied head stays fp32). */
+typedef enum { GPT2_W_FP32 = 0, GPT2_W_FP16 = 1, GPT2_W_INT4 = 2 } gpt2_wdtype;
+
+typedef struct {
+    int n_layer;      /* L >= 1                                              */
+    int n_embd;       /* E; supported: 768 (head dim 64) and 128 (head dim 32) */
+    int n_head;       /* H; E / H must be the head dim above                  */
+    int n_positions;  /* P >= 1: context length (1024 for GPT-2)              */
+    int vocab_size;   /* V >= 1; V <= 256 * workgroups (65536 at E=768)        */
+    float ln_eps;     /* LayerNorm epsilon (layer_norm_epsilon, 1e-5)         */
+    int wdtype;       /* gpt2_wdtype                                          */
+    int q4_group;     /* int4 group size along the input; must be 32          */
+} gpt2_config;
+
+/* Host fp32 parameters in Hugging Face names and layouts (F = 4E).  The
+ * per-layer members are arrays of L pointers.  Read only during gpt2_load. */
+typedef struct {
+    const float *wte;                       /* [V][E] embedding, also the tied head */
+    const float *wpe;                       /* [P][E]                               */
+    const float *const *ln1_w, *const *ln1_b;             /* [E]                    */
+    const float *const *c_attn_w, *const *c_attn_b;       /* [E][3E], [3E]          */
+    const float *const *attn_proj_w, *const *attn_proj_b; /* [E][E], [E]            */
+    const float *const *ln2_w, *const *ln2_b;             /* [E]                    */
+    const float *const *c_fc_w, *const *c_fc_b;           /* [E][F], [F]            */
+    const float *const *mlp_proj_w, *const *mlp_proj_b;   /* [F][E], [E]            */
+    const float *lnf_w, *lnf_b;                           /* [E]                    */
+} gpt2_weights;
+
+typedef struct gpt2_ctx gpt2_ctx;
+
+/* Validate cfg (the model file's config checks: E = H * head_dim, MLP = 4E;
+ * plus the shapes this build supports), copy the weights to the GPU, re-lay
+ * them out output-major (fp16: round to nearest even; int4: quantise as
+ * above), allocate the KV cache ([L][H][P][head_dim] fp32) and the working
+ * buffers.  On success *out receives the context (filled = 0).
+ * Errors: GPT2_E_INVAL (bad cfg / null pointer), GPT2_E_NOMEM, GPT2_E_DEVICE. */
+GPT2DEC_API int gpt2_load(const gpt2_config *cfg, const gpt2_weights *w, gpt2_ctx **out);
+
+/* Run later work on `hip_stream` (a hipStream_t, e.g. torch's current stream;
+ * NULL = the library's own stream).  The stream must outlive its use. */
+GPT2DEC_API int gpt2_set_stream(gpt2_ctx *c, void *hip_stream);
+
+/* One decode step: token_id at `position` (0 <= position <= filled and
+ * position < P; position < filled rewinds: row `position` of the cache is
+ * overwritten and positions 0..position are read, exactly as the model
+ * file's attn_decode kernel does).  Afterwards filled = position + 1.
+ * logits_out: NULL or host float[V]; argmax_out: NULL or host int (lowest id
+ * among equal maxima).  Errors: GPT2_E_INVAL, GPT2_E_DEVICE, GPT2_E_STATE. */
+GPT2DEC_API int gpt2_step(gpt2_ctx *c, int token_id, int position, float *logits_out, int *argmax_out);
+
+/* Greedy generation chained on the device (one kernel launch, no host round
+ * trip per token): the n_prompt ids are fed at positions filled ..
+ * filled+n_prompt-1, then each argmax is fed back until n_new ids exist.
+ * That is n_prompt + n_new - 1 forward passes; the last pass's argmax is the
+ * n_new-th id and is not fed.  out_ids: host int[n_new].
+ * Requires filled + n_prompt + n_new - 1 <= P.  Afterwards
+ * filled += n_prompt + n_new - 1.  Errors as gpt2_step. */
+GPT2DEC_API int gpt2_generate(gpt2_ctx *c, const int *prompt, int n_prompt, int n_new, int *out_ids);
+
+/* filled = 0.  The cache need not be cleared: reads never pass `position`. */
+GPT2DEC_API int gpt2_reset(gpt2_ctx *c);
+
+/* Release everything; c may be NULL. */
+GPT2DEC_API void gpt2_free(gpt2_ctx *c);
+
+/* Message for the last failing call on c (c == NULL: the last gpt2_load
+ * failure of this thread).  Valid until the next call on c. */
+GPT2DEC_API const char *gpt2_last_error(const gpt2_ctx *c);
+
+/* Number of filled positions (the next appending position). -1 if c is NULL. */
+GPT2DEC_API int gpt2_filled(const gpt2_ctx *c);
+
+/* ---- test hooks (not needed for decoding) ------------------------------ */
+
+/* Effective weights of one matrix as the GPU kernels see them, dequantised by
+ * the same device code the GEMV uses, output-major: which = 0 QKV [3E][E],
+ * 1 attention projection [E][E], 2 fc [F][E], 3 MLP projection [E][F],
+ * 4 output head [V][E] (layer ignored).  out: host float[N*K]. */
+GPT2DEC_API int gpt2_debug_dequant(gpt2_ctx *c, int layer, int which, float *out);
+
+/* Fill every KV-cache entry with `value` (e.g. NaN) so that a read of a row
+ * past the current position would show in the result. */
+GPT2DEC_API int gpt2_debug_fill_kv(gpt2_ctx *c, float value);
+
+/* Launch geometry: workgroups and threads per workgroup of the decode kernel. */
+GPT2DEC_API int gpt2_debug_geometry(const gpt2_ctx *c, int *workgroups, int *threads);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

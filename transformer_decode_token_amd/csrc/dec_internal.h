@@ -1,0 +1,86 @@
+// Internal interface between the host runtime (gpt2dec_host.hip) and the
+// device code (decode_kernel.hip, relayout.hip).  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gpt2dec {
+
+enum { WD_F32 = 0, WD_F16 = 1, WD_Q4 = 2 };
+
+// One weight matrix of every layer, output-major [N][K] per layer, layers
+// back to back.  For int4: `w` holds the nibbles ([N][K/2] bytes, element k in
+// byte k/2, low nibble for even k) and `sz` the (scale, zero) pair of each
+// group of 32 inputs ([N][K/32]).
+struct MatW {
+  const void *w;
+  const float2 *sz;
+};
+
+// Everything the decode kernel reads or writes.  Cross-workgroup activations
+// travel as 64-bit words (payload bits | epoch << 32) written and read with
+// agent-scope atomics; a consumer knows its input is complete when every word
+// carries the epoch of the producing phase.
+struct DecodeArgs {
+  MatW qkv, ap, fc, pr;              // the four block matrices
+  const float *ln1w, *ln1b;          // [L][E]
+  const float *bqkv;                 // [L][3E]
+  const float *bap;                  // [L][E]
+  const float *ln2w, *ln2b;          // [L][E]
+  const float *bfc;                  // [L][F]
+  const float *bpr;                  // [L][E]
+  const float *wte;                  // [V][E] fp32 embedding
+  const void *head;                  // [V][E] output head (fp32 = wte, or fp16 copy)
+  const float *wpe;                  // [P][E]
+  const float *lnfw, *lnfb;          // [E]
+  float *kc, *vc;                    // [L][H][P][D] KV cache
+  uint64_t *qkv_t;                   // [L][3E]        tagged QKV outputs
+  uint64_t *att_t;                   // [L][H][MAXCH][D+2] tagged attention partials
+  uint64_t *xa_t;                    // [L][E]         tagged residual after attention
+  uint64_t *act_t;                   // [L][F]         tagged gelu activations
+  uint64_t *xb_t;                    // [L][E]         tagged residual after the MLP
+  uint64_t *amax_t;                  // [2][G]         tagged per-workgroup argmax (value, index)
+  float *logits;                     // [V]            logits of the last step
+  int *out_ids;                      // greedy ids
+  int *err;                          // [4] flag, workgroup, phase, epoch (device-side wait timeout)
+  const int *feed;                   // [n_feed] ids fed at the first steps
+  int n_feed;
+  int pos0;                          // position of step 0
+  int nsteps;
+  int out_from;                      // step whose argmax is out_ids[0]
+  int L, V, P;
+  float eps;
+  uint32_t epoch0;                   // epochs used: epoch0 + 1 .. epoch0 + nsteps*(5L+1)
+  long long timeout_ticks;           // wall-clock ticks a wait may take before aborting
+};
+
+// Shape instantiations compiled into the library.
+struct ShapeInfo {
+  int E, D, G, threads;
+  size_t lds_bytes;
+  int maxch;                         // maximum attention chunks per head
+};
+bool shape_info(int E, int D, ShapeInfo *out);
+
+// Launch the decode kernel (cooperative: all workgroups are co-resident).
+hipError_t launch_decode(int E, int D, int wd, const DecodeArgs &a, hipStream_t s);
+// Occupancy check: blocks of the decode kernel per CU.
+hipError_t decode_occupancy(int E, int D, int wd, int *blocks_per_cu);
+
+// Load-time re-layout (relayout.hip).
+// src: Conv1D [K][N] fp32 (device); dst: [N][K] fp32.
+hipError_t relayout_f32(const float *src, float *dst, int K, int N, hipStream_t s);
+// src: Conv1D [K][N] fp32; dst: [N][K] fp16, round to nearest even.
+hipError_t relayout_f16(const float *src, void *dst, int K, int N, hipStream_t s);
+// src: Conv1D [K][N] fp32; tmp: [N][K] fp32 scratch; nib: [N][K/2]; sz: [N][K/32].
+hipError_t relayout_q4(const float *src, float *tmp, uint8_t *nib, float2 *sz, int K, int N,
+                       hipStream_t s);
+// Row-major [R][C] fp32 -> fp16 (no transpose), round to nearest even.
+hipError_t convert_f16(const float *src, void *dst, size_t n, hipStream_t s);
+// Dequantise an output-major matrix [N][K] of type wd into float (the GEMV's own chunk decode).
+hipError_t debug_dequant(int wd, const MatW &m, size_t layer_offset_elems, int N, int K, float *dst,
+                         hipStream_t s);
+hipError_t fill_f32(float *dst, size_t n, float v, hipStream_t s);
+
+}  // namespace gpt2dec

@@ -1,0 +1,518 @@
+// gpt2dec_host.hip -- host runtime behind the C ABI in include/gpt2dec.h.
+//
+// Owns the device memory of one model (re-laid-out weights, KV cache, tagged
+// activation words), validates every call before touching the device, and
+// drives the decode kernel: one cooperative launch per gpt2_step (one token)
+// or per gpt2_generate (the whole greedy run chained on the device).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/gpt2dec.h"
+#include "dec_internal.h"
+
+using namespace gpt2dec;
+
+namespace {
+thread_local std::string g_load_error;
+
+size_t wd_bytes(int wd, size_t elems) {
+  if (wd == WD_F32) return elems * 4;
+  if (wd == WD_F16) return elems * 2;
+  return elems / 2;
+}
+}  // namespace
+
+struct gpt2_ctx {
+  gpt2_config cfg{};
+  int L = 0, E = 0, H = 0, D = 0, F = 0, P = 0, V = 0, wd = 0;
+  ShapeInfo si{};
+  int device = 0;
+  hipStream_t own_stream = nullptr, stream = nullptr;
+  std::vector<void *> dev_allocs;
+  std::vector<void *> host_allocs;
+  DecodeArgs base{};
+  int *feed_d = nullptr, *ids_d = nullptr, *err_d = nullptr;
+  int *feed_h = nullptr, *ids_h = nullptr, *err_h = nullptr;
+  float *logits_h = nullptr;
+  uint64_t *tag_bufs[6] = {};
+  size_t tag_sizes[6] = {};
+  uint32_t epoch = 0;
+  int filled = 0;
+  bool poisoned = false;
+  long long timeout_ticks = 0;
+  std::string err;
+
+  int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    err = buf;
+    return code;
+  }
+  int device_fail(hipError_t e, const char *what) {
+    poisoned = true;
+    return fail(GPT2_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+  }
+  template <typename T>
+  T *dalloc(size_t bytes) {
+    static const bool inject = getenv("GPT2DEC_FAIL_ALLOC") && atoi(getenv("GPT2DEC_FAIL_ALLOC")) != 0;
+    if (inject) return nullptr;
+    void *p = nullptr;
+    if (hipMalloc(&p, bytes ? bytes : 4) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    dev_allocs.push_back(p);
+    return static_cast<T *>(p);
+  }
+  template <typename T>
+  T *halloc(size_t bytes) {
+    void *p = nullptr;
+    if (hipHostMalloc(&p, bytes ? bytes : 4, hipHostMallocDefault) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    host_allocs.push_back(p);
+    return static_cast<T *>(p);
+  }
+  ~gpt2_ctx() {
+    if (stream) (void)hipStreamSynchronize(stream);
+    for (void *p : dev_allocs) (void)hipFree(p);
+    for (void *p : host_allocs) (void)hipHostFree(p);
+    if (own_stream) (void)hipStreamDestroy(own_stream);
+  }
+};
+
+namespace {
+
+bool bad_ptr_list(const float *const *a, int n) {
+  if (!a) return true;
+  for (int i = 0; i < n; i++)
+    if (!a[i]) return true;
+  return false;
+}
+
+int validate_config(const gpt2_config *c, ShapeInfo *si, std::string &msg) {
+  char buf[256];
+  if (c->n_layer < 1 || c->n_embd < 1 || c->n_head < 1 || c->n_positions < 1 || c->vocab_size < 1) {
+    msg = "sizes must be positive";
+    return GPT2_E_INVAL;
+  }
+  if (c->n_embd % c->n_head != 0) {
+    msg = "n_embd must equal n_head * head_dim";
+    return GPT2_E_INVAL;
+  }
+  if (!(c->ln_eps > 0.0f) || !std::isfinite(c->ln_eps)) {
+    msg = "ln_eps must be positive and finite";
+    return GPT2_E_INVAL;
+  }
+  if (c->wdtype < GPT2_W_FP32 || c->wdtype > GPT2_W_INT4) {
+    msg = "unknown weight dtype";
+    return GPT2_E_INVAL;
+  }
+  const int D = c->n_embd / c->n_head;
+  if (!shape_info(c->n_embd, D, si)) {
+    snprintf(buf, sizeof buf, "unsupported shape n_embd=%d head_dim=%d (built: 768/64, 128/32)", c->n_embd, D);
+    msg = buf;
+    return GPT2_E_INVAL;
+  }
+  if (c->wdtype == GPT2_W_INT4 && c->q4_group != 32) {
+    msg = "int4 weights need q4_group = 32";
+    return GPT2_E_INVAL;
+  }
+  if (c->n_positions > 64 * si->maxch) {
+    snprintf(buf, sizeof buf, "n_positions %d above the supported %d", c->n_positions, 64 * si->maxch);
+    msg = buf;
+    return GPT2_E_INVAL;
+  }
+  if (c->vocab_size > 256 * si->G) {
+    snprintf(buf, sizeof buf, "vocab_size %d above the supported %d", c->vocab_size, 256 * si->G);
+    msg = buf;
+    return GPT2_E_INVAL;
+  }
+  return GPT2_OK;
+}
+
+// Launch `nsteps` forward passes; see gpt2_step / gpt2_generate.
+int run(gpt2_ctx *c, const int *feed, int n_feed, int pos0, int nsteps, int out_from, int n_out, int *ids_out,
+        float *logits_out) {
+  hipError_t e = hipSetDevice(c->device);
+  if (e != hipSuccess) return c->device_fail(e, "hipSetDevice");
+  const uint64_t used = (uint64_t)nsteps * (uint64_t)(5 * c->L + 1);
+  if ((uint64_t)c->epoch + used >= 0xffffff00ull) {
+    // epochs would wrap: clear every tagged word (tag 0 is never expected) and restart
+    for (int i = 0; i < 6; i++) {
+      e = hipMemsetAsync(c->tag_bufs[i], 0, c->tag_sizes[i], c->stream);
+      if (e != hipSuccess) return c->device_fail(e, "hipMemsetAsync");
+    }
+    c->epoch = 0;
+  }
+  memcpy(c->feed_h, feed, sizeof(int) * (size_t)n_feed);
+  e = hipMemcpyAsync(c->feed_d, c->feed_h, sizeof(int) * (size_t)n_feed, hipMemcpyHostToDevice, c->stream);
+  if (e == hipSuccess) e = hipMemsetAsync(c->err_d, 0, 4 * sizeof(int), c->stream);
+  if (e != hipSuccess) return c->device_fail(e, "staging inputs");
+  DecodeArgs a = c->base;
+  a.feed = c->feed_d;
+  a.n_feed = n_feed;
+  a.pos0 = pos0;
+  a.nsteps = nsteps;
+  a.out_from = out_from;
+  a.epoch0 = c->epoch;
+  a.timeout_ticks = c->timeout_ticks;
+  e = launch_decode(c->E, c->D, c->wd, a, c->stream);
+  c->epoch += (uint32_t)used;
+  if (e != hipSuccess) return c->device_fail(e, "decode launch");
+  e = hipMemcpyAsync(c->ids_h, c->ids_d, sizeof(int) * (size_t)n_out, hipMemcpyDeviceToHost, c->stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(c->err_h, c->err_d, 4 * sizeof(int), hipMemcpyDeviceToHost, c->stream);
+  if (e == hipSuccess && logits_out)
+    e = hipMemcpyAsync(c->logits_h, c->base.logits, sizeof(float) * (size_t)c->V, hipMemcpyDeviceToHost,
+                       c->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) return c->device_fail(e, "decode run");
+  if (c->err_h[0] != 0) {
+    c->poisoned = true;
+    return c->fail(GPT2_E_DEVICE, "device wait timed out (workgroup %d, producer phase %d)", c->err_h[1],
+                   c->err_h[2]);
+  }
+  memcpy(ids_out, c->ids_h, sizeof(int) * (size_t)n_out);
+  if (logits_out) memcpy(logits_out, c->logits_h, sizeof(float) * (size_t)c->V);
+  return GPT2_OK;
+}
+
+int load_impl(gpt2_ctx *c, const gpt2_config *cfg, const gpt2_weights *w) {
+  c->cfg = *cfg;
+  c->L = cfg->n_layer;
+  c->E = cfg->n_embd;
+  c->H = cfg->n_head;
+  c->D = c->E / c->H;
+  c->F = 4 * c->E;
+  c->P = cfg->n_positions;
+  c->V = cfg->vocab_size;
+  c->wd = cfg->wdtype;
+  const int L = c->L, E = c->E, F = c->F, P = c->P, V = c->V, H = c->H, D = c->D, G = c->si.G;
+  hipError_t e = hipGetDevice(&c->device);
+  if (e != hipSuccess) return c->device_fail(e, "hipGetDevice");
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, c->device);
+  if (e != hipSuccess) return c->device_fail(e, "hipGetDeviceProperties");
+  int blocks = 0;
+  e = decode_occupancy(E, D, c->wd, &blocks);
+  if (e != hipSuccess) return c->device_fail(e, "decode kernel occupancy");
+  if (blocks < 1 || (long)blocks * prop.multiProcessorCount < G)
+    return c->fail(GPT2_E_DEVICE, "device cannot hold %d co-resident workgroups (%d CUs x %d)", G,
+                   prop.multiProcessorCount, blocks);
+  int clock_khz = 0;
+  if (hipDeviceGetAttribute(&clock_khz, hipDeviceAttributeWallClockRate, c->device) != hipSuccess || clock_khz <= 0)
+    clock_khz = 100000;
+  double timeout_ms = 2000.0;
+  if (const char *t = getenv("GPT2DEC_TIMEOUT_MS")) timeout_ms = atof(t);
+  c->timeout_ticks = (long long)(timeout_ms * clock_khz);
+  e = hipStreamCreateWithFlags(&c->own_stream, hipStreamNonBlocking);
+  if (e != hipSuccess) return c->device_fail(e, "hipStreamCreate");
+  c->stream = c->own_stream;
+  hipStream_t s = c->stream;
+
+  // ---- device buffers
+  const size_t nq = (size_t)3 * E * E, na = (size_t)E * E, nf = (size_t)F * E, np = (size_t)E * F;
+  void *mq = c->dalloc<void>(wd_bytes(c->wd, nq * L));
+  void *ma = c->dalloc<void>(wd_bytes(c->wd, na * L));
+  void *mf = c->dalloc<void>(wd_bytes(c->wd, nf * L));
+  void *mp = c->dalloc<void>(wd_bytes(c->wd, np * L));
+  float2 *sq = nullptr, *sa = nullptr, *sf = nullptr, *sp = nullptr;
+  if (c->wd == WD_Q4) {
+    sq = c->dalloc<float2>(nq * L / 32 * sizeof(float2));
+    sa = c->dalloc<float2>(na * L / 32 * sizeof(float2));
+    sf = c->dalloc<float2>(nf * L / 32 * sizeof(float2));
+    sp = c->dalloc<float2>(np * L / 32 * sizeof(float2));
+    if (!sq || !sa || !sf || !sp) return c->fail(GPT2_E_NOMEM, "device allocation failed");
+  }
+  float *stage = c->dalloc<float>(nf * sizeof(float));
+  float *tmp = c->wd == WD_Q4 ? c->dalloc<float>(nf * sizeof(float)) : nullptr;
+  float *ln1w = c->dalloc<float>((size_t)L * E * 4), *ln1b = c->dalloc<float>((size_t)L * E * 4);
+  float *ln2w = c->dalloc<float>((size_t)L * E * 4), *ln2b = c->dalloc<float>((size_t)L * E * 4);
+  float *bqkv = c->dalloc<float>((size_t)L * 3 * E * 4), *bap = c->dalloc<float>((size_t)L * E * 4);
+  float *bfc = c->dalloc<float>((size_t)L * F * 4), *bpr = c->dalloc<float>((size_t)L * E * 4);
+  float *lnfw = c->dalloc<float>((size_t)E * 4), *lnfb = c->dalloc<float>((size_t)E * 4);
+  float *wte = c->dalloc<float>((size_t)V * E * 4), *wpe = c->dalloc<float>((size_t)P * E * 4);
+  void *head16 = c->wd == WD_F16 ? c->dalloc<void>((size_t)V * E * 2) : nullptr;
+  const size_t kv = (size_t)L * H * P * D;
+  float *kc = c->dalloc<float>(kv * 4), *vc = c->dalloc<float>(kv * 4);
+  c->tag_sizes[0] = (size_t)L * 3 * E * 8;
+  c->tag_sizes[1] = (size_t)L * H * c->si.maxch * (D + 2) * 8;
+  c->tag_sizes[2] = (size_t)L * E * 8;
+  c->tag_sizes[3] = (size_t)L * F * 8;
+  c->tag_sizes[4] = (size_t)L * E * 8;
+  c->tag_sizes[5] = (size_t)2 * G * 8;
+  for (int i = 0; i < 6; i++) c->tag_bufs[i] = c->dalloc<uint64_t>(c->tag_sizes[i]);
+  float *logits = c->dalloc<float>((size_t)V * 4);
+  c->ids_d = c->dalloc<int>((size_t)P * 4);
+  c->feed_d = c->dalloc<int>((size_t)P * 4);
+  c->err_d = c->dalloc<int>(4 * 4);
+  c->feed_h = c->halloc<int>((size_t)P * 4);
+  c->ids_h = c->halloc<int>((size_t)P * 4);
+  c->err_h = c->halloc<int>(4 * 4);
+  c->logits_h = c->halloc<float>((size_t)V * 4);
+  if (!mq || !ma || !mf || !mp || !stage || (c->wd == WD_Q4 && !tmp) || !ln1w || !ln1b || !ln2w || !ln2b ||
+      !bqkv || !bap || !bfc || !bpr || !lnfw || !lnfb || !wte || !wpe || (c->wd == WD_F16 && !head16) || !kc ||
+      !vc || !logits || !c->ids_d || !c->feed_d || !c->err_d || !c->feed_h || !c->ids_h || !c->err_h ||
+      !c->logits_h)
+    return c->fail(GPT2_E_NOMEM, "allocation failed");
+  for (int i = 0; i < 6; i++)
+    if (!c->tag_bufs[i]) return c->fail(GPT2_E_NOMEM, "allocation failed");
+
+  // ---- small parameters
+  auto up = [&](float *dst, const float *src, size_t n) {
+    return hipMemcpyAsync(dst, src, n * sizeof(float), hipMemcpyHostToDevice, s);
+  };
+  for (int l = 0; l < L && e == hipSuccess; l++) {
+    e = up(ln1w + (size_t)l * E, w->ln1_w[l], E);
+    if (e == hipSuccess) e = up(ln1b + (size_t)l * E, w->ln1_b[l], E);
+    if (e == hipSuccess) e = up(ln2w + (size_t)l * E, w->ln2_w[l], E);
+    if (e == hipSuccess) e = up(ln2b + (size_t)l * E, w->ln2_b[l], E);
+    if (e == hipSuccess) e = up(bqkv + (size_t)l * 3 * E, w->c_attn_b[l], 3 * (size_t)E);
+    if (e == hipSuccess) e = up(bap + (size_t)l * E, w->attn_proj_b[l], E);
+    if (e == hipSuccess) e = up(bfc + (size_t)l * F, w->c_fc_b[l], F);
+    if (e == hipSuccess) e = up(bpr + (size_t)l * E, w->mlp_proj_b[l], E);
+  }
+  if (e == hipSuccess) e = up(lnfw, w->lnf_w, E);
+  if (e == hipSuccess) e = up(lnfb, w->lnf_b, E);
+  if (e == hipSuccess) e = up(wte, w->wte, (size_t)V * E);
+  if (e == hipSuccess) e = up(wpe, w->wpe, (size_t)P * E);
+  if (e == hipSuccess && head16) e = convert_f16(wte, head16, (size_t)V * E, s);
+  if (e != hipSuccess) return c->device_fail(e, "uploading parameters");
+
+  // ---- block matrices: Conv1D [K][N] -> output-major [N][K]
+  struct M {
+    const float *const *src;
+    void *dst;
+    float2 *sz;
+    int K, N;
+  } mats[4] = {{w->c_attn_w, mq, sq, E, 3 * E},
+               {w->attn_proj_w, ma, sa, E, E},
+               {w->c_fc_w, mf, sf, E, F},
+               {w->mlp_proj_w, mp, sp, F, E}};
+  for (int m = 0; m < 4; m++) {
+    const size_t n = (size_t)mats[m].K * mats[m].N;
+    for (int l = 0; l < L; l++) {
+      e = up(stage, mats[m].src[l], n);
+      if (e != hipSuccess) break;
+      if (c->wd == WD_F32) {
+        e = relayout_f32(stage, static_cast<float *>(mats[m].dst) + (size_t)l * n, mats[m].K, mats[m].N, s);
+      } else if (c->wd == WD_F16) {
+        e = relayout_f16(stage, static_cast<uint16_t *>(mats[m].dst) + (size_t)l * n, mats[m].K, mats[m].N, s);
+      } else {
+        e = relayout_q4(stage, tmp, static_cast<uint8_t *>(mats[m].dst) + (size_t)l * n / 2,
+                        mats[m].sz + (size_t)l * n / 32, mats[m].K, mats[m].N, s);
+      }
+      if (e != hipSuccess) break;
+      // the staging buffer is reused by the next upload: keep the order explicit
+      e = hipStreamSynchronize(s);
+      if (e != hipSuccess) break;
+    }
+    if (e != hipSuccess) return c->device_fail(e, "weight re-layout");
+  }
+  for (int i = 0; i < 6 && e == hipSuccess; i++) e = hipMemsetAsync(c->tag_bufs[i], 0, c->tag_sizes[i], s);
+  if (e == hipSuccess) e = hipMemsetAsync(kc, 0, kv * 4, s);
+  if (e == hipSuccess) e = hipMemsetAsync(vc, 0, kv * 4, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return c->device_fail(e, "initialising buffers");
+
+  DecodeArgs &a = c->base;
+  a.qkv = MatW{mq, sq};
+  a.ap = MatW{ma, sa};
+  a.fc = MatW{mf, sf};
+  a.pr = MatW{mp, sp};
+  a.ln1w = ln1w; a.ln1b = ln1b; a.bqkv = bqkv; a.bap = bap;
+  a.ln2w = ln2w; a.ln2b = ln2b; a.bfc = bfc; a.bpr = bpr;
+  a.wte = wte;
+  a.head = head16 ? head16 : static_cast<const void *>(wte);
+  a.wpe = wpe;
+  a.lnfw = lnfw; a.lnfb = lnfb;
+  a.kc = kc; a.vc = vc;
+  a.qkv_t = c->tag_bufs[0];
+  a.att_t = c->tag_bufs[1];
+  a.xa_t = c->tag_bufs[2];
+  a.act_t = c->tag_bufs[3];
+  a.xb_t = c->tag_bufs[4];
+  a.amax_t = c->tag_bufs[5];
+  a.logits = logits;
+  a.out_ids = c->ids_d;
+  a.err = c->err_d;
+  a.L = L; a.V = V; a.P = P;
+  a.eps = cfg->ln_eps;
+  return GPT2_OK;
+}
+
+bool usable(gpt2_ctx *c, int *rc) {
+  if (!c) { *rc = GPT2_E_INVAL; return false; }
+  if (c->poisoned) {
+    *rc = GPT2_E_STATE;
+    c->err = "context poisoned by an earlier device error";
+    return false;
+  }
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gpt2_load(const gpt2_config *cfg, const gpt2_weights *w, gpt2_ctx **out) {
+  g_load_error.clear();
+  if (!out) { g_load_error = "out is NULL"; return GPT2_E_INVAL; }
+  *out = nullptr;
+  if (!cfg || !w) { g_load_error = "cfg or weights is NULL"; return GPT2_E_INVAL; }
+  ShapeInfo si{};
+  std::string msg;
+  int rc = validate_config(cfg, &si, msg);
+  if (rc != GPT2_OK) { g_load_error = msg; return rc; }
+  const int L = cfg->n_layer;
+  if (!w->wte || !w->wpe || !w->lnf_w || !w->lnf_b || bad_ptr_list(w->ln1_w, L) || bad_ptr_list(w->ln1_b, L) ||
+      bad_ptr_list(w->c_attn_w, L) || bad_ptr_list(w->c_attn_b, L) || bad_ptr_list(w->attn_proj_w, L) ||
+      bad_ptr_list(w->attn_proj_b, L) || bad_ptr_list(w->ln2_w, L) || bad_ptr_list(w->ln2_b, L) ||
+      bad_ptr_list(w->c_fc_w, L) || bad_ptr_list(w->c_fc_b, L) || bad_ptr_list(w->mlp_proj_w, L) ||
+      bad_ptr_list(w->mlp_proj_b, L)) {
+    g_load_error = "a weight pointer is NULL";
+    return GPT2_E_INVAL;
+  }
+  int ndev = 0;
+  hipError_t e = hipGetDeviceCount(&ndev);
+  if (e != hipSuccess || ndev < 1) {
+    (void)hipGetLastError();
+    g_load_error = "no HIP device available";
+    return GPT2_E_DEVICE;
+  }
+  gpt2_ctx *c = new (std::nothrow) gpt2_ctx();
+  if (!c) { g_load_error = "out of host memory"; return GPT2_E_NOMEM; }
+  c->si = si;
+  rc = load_impl(c, cfg, w);
+  if (rc != GPT2_OK) {
+    g_load_error = c->err;
+    delete c;
+    return rc;
+  }
+  *out = c;
+  return GPT2_OK;
+}
+
+int gpt2_set_stream(gpt2_ctx *c, void *hip_stream) {
+  int rc;
+  if (!usable(c, &rc)) return rc;
+  c->stream = hip_stream ? static_cast<hipStream_t>(hip_stream) : c->own_stream;
+  return GPT2_OK;
+}
+
+int gpt2_step(gpt2_ctx *c, int token_id, int position, float *logits_out, int *argmax_out) {
+  int rc;
+  if (!usable(c, &rc)) return rc;
+  if (token_id < 0 || token_id >= c->V)
+    return c->fail(GPT2_E_INVAL, "token_id %d outside [0, %d)", token_id, c->V);
+  if (position < 0 || position >= c->P)
+    return c->fail(GPT2_E_INVAL, "position %d outside [0, %d)", position, c->P);
+  if (position > c->filled)
+    return c->fail(GPT2_E_INVAL, "position %d beyond the %d filled positions", position, c->filled);
+  int id = -1;
+  rc = run(c, &token_id, 1, position, 1, 0, 1, &id, logits_out);
+  if (rc != GPT2_OK) return rc;
+  c->filled = position + 1;
+  if (argmax_out) *argmax_out = id;
+  return GPT2_OK;
+}
+
+int gpt2_generate(gpt2_ctx *c, const int *prompt, int n_prompt, int n_new, int *out_ids) {
+  int rc;
+  if (!usable(c, &rc)) return rc;
+  if (!prompt || !out_ids) return c->fail(GPT2_E_INVAL, "prompt or out_ids is NULL");
+  if (n_prompt < 1 || n_new < 1) return c->fail(GPT2_E_INVAL, "n_prompt and n_new must be >= 1");
+  const long long steps = (long long)n_prompt + n_new - 1;
+  if ((long long)c->filled + steps > c->P)
+    return c->fail(GPT2_E_INVAL, "%lld steps from position %d exceed n_positions %d", steps, c->filled, c->P);
+  for (int i = 0; i < n_prompt; i++)
+    if (prompt[i] < 0 || prompt[i] >= c->V)
+      return c->fail(GPT2_E_INVAL, "prompt[%d] = %d outside [0, %d)", i, prompt[i], c->V);
+  rc = run(c, prompt, n_prompt, c->filled, (int)steps, n_prompt - 1, n_new, out_ids, nullptr);
+  if (rc != GPT2_OK) return rc;
+  c->filled += (int)steps;
+  return GPT2_OK;
+}
+
+int gpt2_reset(gpt2_ctx *c) {
+  int rc;
+  if (!usable(c, &rc)) return rc;
+  c->filled = 0;
+  return GPT2_OK;
+}
+
+void gpt2_free(gpt2_ctx *c) { delete c; }
+
+const char *gpt2_last_error(const gpt2_ctx *c) {
+  if (!c) return g_load_error.c_str();
+  return c->err.c_str();
+}
+
+int gpt2_filled(const gpt2_ctx *c) { return c ? c->filled : -1; }
+
+int gpt2_debug_dequant(gpt2_ctx *c, int layer, int which, float *out) {
+  int rc;
+  if (!usable(c, &rc)) return rc;
+  if (!out) return c->fail(GPT2_E_INVAL, "out is NULL");
+  MatW m{};
+  int N = 0, K = 0, wd = c->wd;
+  size_t lofs = 0;
+  const int E = c->E, F = c->F;
+  switch (which) {
+  case 0: m = c->base.qkv; N = 3 * E; K = E; break;
+  case 1: m = c->base.ap; N = E; K = E; break;
+  case 2: m = c->base.fc; N = F; K = E; break;
+  case 3: m = c->base.pr; N = E; K = F; break;
+  case 4:
+    m = MatW{c->base.head, nullptr};
+    N = c->V; K = E;
+    wd = (c->wd == WD_F16) ? WD_F16 : WD_F32;
+    break;
+  default: return c->fail(GPT2_E_INVAL, "which must be 0..4");
+  }
+  if (which != 4) {
+    if (layer < 0 || layer >= c->L) return c->fail(GPT2_E_INVAL, "layer %d outside [0, %d)", layer, c->L);
+    lofs = (size_t)layer * N * K;
+  }
+  float *d = nullptr;
+  hipError_t e = hipMalloc(&d, (size_t)N * K * 4);
+  if (e != hipSuccess) { (void)hipGetLastError(); return c->fail(GPT2_E_NOMEM, "device allocation failed"); }
+  e = debug_dequant(wd, m, lofs, N, K, d, c->stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(out, d, (size_t)N * K * 4, hipMemcpyDeviceToHost, c->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+  (void)hipFree(d);
+  if (e != hipSuccess) return c->device_fail(e, "debug dequant");
+  return GPT2_OK;
+}
+
+int gpt2_debug_fill_kv(gpt2_ctx *c, float value) {
+  int rc;
+  if (!usable(c, &rc)) return rc;
+  const size_t kv = (size_t)c->L * c->H * c->P * c->D;
+  hipError_t e = fill_f32(c->base.kc, kv, value, c->stream);
+  if (e == hipSuccess) e = fill_f32(c->base.vc, kv, value, c->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) return c->device_fail(e, "fill kv");
+  return GPT2_OK;
+}
+
+int gpt2_debug_geometry(const gpt2_ctx *c, int *workgroups, int *threads) {
+  if (!c) return GPT2_E_INVAL;
+  if (workgroups) *workgroups = c->si.G;
+  if (threads) *threads = c->si.threads;
+  return GPT2_OK;
+}
+
+}  // extern "C"
