@@ -1,0 +1,191 @@
+"""Benchmark: batch-1 GPT-2 124M greedy decode on one MI355X.
+
+One bench step = one whole greedy run of the workload (default: the fp32 124M
+model, 10 prompt ids + 60 greedy ids = 69 one-token forward passes, chained on
+the device by gpt2_generate).  `value` is forward passes (decoded tokens) per
+second over the timed steps, with weights and prompt already resident on the
+GPU.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--config 2..5] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+
+
+def bytes_per_step(cfg, p):
+    """Algorithmic bytes of one forward pass at position p: every weight once
+    (block matrices in their storage type, the head, biases and LayerNorm
+    parameters, the two embedding rows) plus the K and V rows 0..p read by
+    attention."""
+    E, F, V, L = cfg.n_embd, 4 * cfg.n_embd, cfg.vocab, cfg.n_layer
+    elems = L * (3 * E * E + E * E + F * E + E * F)
+    if cfg.wdtype == "fp32":
+        mats = elems * 4
+        head = V * E * 4
+    elif cfg.wdtype == "fp16":
+        mats = elems * 2
+        head = V * E * 2
+    else:
+        mats = elems // 2 + elems // 32 * 8
+        head = V * E * 4
+    small = (L * (2 * E + 3 * E + E + 2 * E + F + E) + 2 * E) * 4 + 2 * E * 4
+    kv = L * 2 * E * 4 * (p + 1)
+    return mats + head + small + kv
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("decode_kernel.hip", "dec_internal.h"):
+        with open(os.path.join(ROOT, "transformer_decode_token_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(cfg_key):
+    """HBM bytes per launch measured with rocprofv3 counters for this exact
+    kernel source (profiles/decode_traffic.json), else None."""
+    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    e = d.get(str(cfg_key))
+    if not e or e.get("kernel_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, seconds=15.0):
+    """The oracle, single-threaded, on the GPU host: greedy decode of the same
+    workload from position 0 for about `seconds`."""
+    import synth
+    from oracle import Oracle
+    model = synth.make_model(cfg)
+    orc = Oracle(model)
+    prompt = synth.make_prompt(cfg)
+    toks = list(int(t) for t in prompt)
+    t0 = time.perf_counter()
+    n = 0
+    while n < cfg.n_steps and (time.perf_counter() - t0) < seconds:
+        am, _ = orc.step(toks[n], n, want_logits=False)
+        if n + 1 >= len(toks):
+            toks.append(am)
+        n += 1
+    dt = time.perf_counter() - t0
+    orc.close()
+    return {"value": round(n / dt, 3), "unit": "tok/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} forward passes (positions 0..{n - 1}) of the same greedy run, "
+                      f"{dt:.1f} s, one thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sync-steps", type=int, default=30,
+                    help="gpt2_step calls timed for the synchronous per-token rate")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (batch-1 decode of one sequence does "
+              "not shard usefully); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import transformer_decode_token_amd as g2
+
+    cfg = synth.CONFIGS[args.config]
+    print(f"[bench] config {cfg.key} {cfg.name}: generating weights", file=sys.stderr, flush=True)
+    model = synth.make_model(cfg)
+    prompt = synth.make_prompt(cfg)
+    torch.cuda.init()
+    ctx = g2.gpt2_load(cfg.n_layer, cfg.n_embd, cfg.n_head, cfg.n_positions, cfg.vocab, model.t,
+                       wdtype=cfg.wdtype, ln_eps=cfg.ln_eps, q4_group=cfg.q4_group)
+    stream = torch.cuda.current_stream()
+    g2.gpt2_set_stream(ctx, stream.cuda_stream)
+    print("[bench] loaded; warming up", file=sys.stderr, flush=True)
+
+    def run():
+        g2.gpt2_reset(ctx)
+        return g2.gpt2_generate(ctx, prompt, cfg.n_new)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        g2.gpt2_reset(ctx)
+        starts[i].record(stream)
+        g2.gpt2_generate(ctx, prompt, cfg.n_new)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_launch = float(np.mean(launch_ms))
+    ms_per_step = wall * 1e3 / args.steps
+    tok_per_s = cfg.n_steps * args.steps / wall
+
+    # synchronous one-token calls (host round trip per token)
+    g2.gpt2_reset(ctx)
+    torch.cuda.synchronize()
+    ts = time.perf_counter()
+    ns = min(args.sync_steps, cfg.n_steps)
+    for pos in range(ns):
+        g2.gpt2_step(ctx, int(prompt[pos % len(prompt)]), pos, want_logits=False)
+    sync_tok_s = ns / (time.perf_counter() - ts)
+
+    alg_bytes = sum(bytes_per_step(cfg, p) for p in range(cfg.n_steps))
+    achieved = alg_bytes / (ms_launch * 1e-3) / 1e9
+    traffic = load_traffic(cfg.key)
+    out = {
+        "metric": "batch-1 decode tok/s GPT-2 124M fp32/fp16/int4; achieved HBM GB/s vs peak",
+        "value": round(tok_per_s, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"fp32": "f32", "fp16": "f16 weights, f32 math", "int4": "u4 weights, f32 math"}[cfg.wdtype],
+        "data": "synthetic (seeded random weights of the GPT-2 124M shape; seeded prompt ids)",
+        "config": {"workload": f"{cfg.name}: {cfg.n_prompt} prompt ids + {cfg.n_new} greedy ids = "
+                               f"{cfg.n_steps} one-token forward passes, batch 1",
+                   "n_layer": cfg.n_layer, "n_embd": cfg.n_embd, "n_head": cfg.n_head,
+                   "vocab": cfg.vocab, "weights": cfg.wdtype, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "decode_kernel_ms_per_launch": round(ms_launch, 4),
+        "us_per_token": round(ms_launch * 1e3 / cfg.n_steps, 2),
+        "algorithmic_bytes_per_launch": alg_bytes,
+        "generated_tok_per_s": round(cfg.n_new * args.steps / wall, 2),
+        "sync_step_tok_per_s": round(sync_tok_s, 1),
+    }
+    ctx.close()
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

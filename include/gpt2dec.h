@@ -134,6 +134,16 @@ GPT2DEC_API int gpt2_debug_dequant(gpt2_ctx *c, int layer, int which, float *out
  * past the current position would show in the result. */
 GPT2DEC_API int gpt2_debug_fill_kv(gpt2_ctx *c, float value);
 
+/* Timeline of the decode kernel (profiling aid).  With out == NULL: from now
+ * on record the first `steps` steps of every run (0 = stop recording).  With
+ * out != NULL: copy the last run's record, then apply `steps` as above.
+ * Layout: [steps][5L+1 phases][workgroups][4] int64 device wall-clock ticks
+ * (inputs ready, first and second workgroup barrier passed, outputs
+ * published; 0 where a workgroup had no such event), phases
+ * per layer l: 5l QKV, 5l+1 attention, 5l+2 attention projection, 5l+3 fc,
+ * 5l+4 MLP projection; phase 5L is the output head. */
+GPT2DEC_API int gpt2_debug_trace(gpt2_ctx *c, int steps, long long *out);
+
 /* Launch geometry: workgroups and threads per workgroup of the decode kernel. */
 GPT2DEC_API int gpt2_debug_geometry(const gpt2_ctx *c, int *workgroups, int *threads);
 

@@ -22,7 +22,7 @@ ERROR_NAMES = {GPT2_E_INVAL: "GPT2_E_INVAL", GPT2_E_NOMEM: "GPT2_E_NOMEM",
 # the symbols include/gpt2dec.h declares
 ABI_FUNCTIONS = ("gpt2_load", "gpt2_set_stream", "gpt2_step", "gpt2_generate", "gpt2_reset",
                  "gpt2_free", "gpt2_last_error", "gpt2_filled", "gpt2_debug_dequant",
-                 "gpt2_debug_fill_kv", "gpt2_debug_geometry")
+                 "gpt2_debug_fill_kv", "gpt2_debug_geometry", "gpt2_debug_trace")
 
 
 class Gpt2Error(RuntimeError):
@@ -71,6 +71,7 @@ def lib():
         L.gpt2_debug_dequant.argtypes = [C.c_void_p, C.c_int, C.c_int, C.c_void_p]
         L.gpt2_debug_fill_kv.argtypes = [C.c_void_p, C.c_float]
         L.gpt2_debug_geometry.argtypes = [C.c_void_p, C.POINTER(C.c_int), C.POINTER(C.c_int)]
+        L.gpt2_debug_trace.argtypes = [C.c_void_p, C.c_int, C.c_void_p]
         _lib = L
     return _lib
 
@@ -190,3 +191,15 @@ def gpt2_debug_geometry(ctx):
     g, t = C.c_int(), C.c_int()
     _check(lib().gpt2_debug_geometry(ctx.handle, C.byref(g), C.byref(t)), ctx.handle)
     return g.value, t.value
+
+
+def gpt2_debug_trace(ctx, steps, fetch_steps=None):
+    """Start recording `steps` steps per run; if fetch_steps is given, first return
+    the previous run's record as int64 [fetch_steps][5L+1][G][4]."""
+    out = None
+    if fetch_steps:
+        g, _ = gpt2_debug_geometry(ctx)
+        out = np.zeros((fetch_steps, 5 * ctx.cfg.n_layer + 1, g, 4), np.int64)
+    _check(lib().gpt2_debug_trace(ctx.handle, int(steps), out.ctypes.data if out is not None else None),
+           ctx.handle)
+    return out

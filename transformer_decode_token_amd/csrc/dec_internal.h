@@ -36,7 +36,8 @@ struct DecodeArgs {
   const float *lnfw, *lnfb;          // [E]
   float *kc, *vc;                    // [L][H][P][D] KV cache
   uint64_t *qkv_t;                   // [L][3E]        tagged QKV outputs
-  uint64_t *att_t;                   // [L][H][MAXCH][D+2] tagged attention partials
+  uint64_t *att_t;                   // [L][H][MAXCH][D+2] tagged attention chunk partials
+  uint64_t *attn_t;                  // [L][E]         tagged merged attention output
   uint64_t *xa_t;                    // [L][E]         tagged residual after attention
   uint64_t *act_t;                   // [L][F]         tagged gelu activations
   uint64_t *xb_t;                    // [L][E]         tagged residual after the MLP
@@ -53,6 +54,8 @@ struct DecodeArgs {
   float eps;
   uint32_t epoch0;                   // epochs used: epoch0 + 1 .. epoch0 + nsteps*(5L+1)
   long long timeout_ticks;           // wall-clock ticks a wait may take before aborting
+  long long *trace;                  // optional: [trace_steps][5L+1][G][2] wall-clock stamps
+  int trace_steps;                   //   (inputs ready, outputs published) per phase
 };
 
 // Shape instantiations compiled into the library.

@@ -3,23 +3,26 @@
 // One cooperative launch runs `nsteps` whole forward passes (one token each).
 // The per-token work follows the node order of the gpt2-125m "model.fir" file:
 // embedding add, then per layer
-//   A: LayerNorm 1 + QKV linear + bias          (K/V of this position kept for attention)
-//   B: attn_decode over positions 0..position   (split over position chunks)
-//   C: chunk merge + attention linear + bias + residual
+//   A: LayerNorm 1 + QKV linear + bias
+//   B: attn_decode: this position's K/V are appended, causal softmax over
+//      positions 0..position, weighted sum of values (split in position chunks
+//      of at most 64; the first chunk of a head merges the others)
+//   C: attention linear + bias + residual
 //   D: LayerNorm 2 + fc linear + bias + gelu_new
 //   E: projection linear + bias + residual
 // and finally H: final LayerNorm + tied output head + argmax.
 //
-// Work split.  Every workgroup owns RAP consecutive rows of each E-output
-// matrix (3*RAP of QKV, 4*RAP of fc), so the 256 workgroups of the 124M shape
-// each stream an equal 1/256 of every matrix, and a contiguous 1/256 of the
-// head.  A workgroup is one control wave plus NCW compute waves:
-//   * compute waves hold the workgroup's weight slices of a whole layer in
-//     registers and re-issue the loads for the next layer as soon as a slice
-//     has been used, so the HBM stream runs a full layer ahead of the
-//     dependency chain;
+// Work split.  Every workgroup owns RAP consecutive output rows of each
+// E-output matrix (3*RAP of QKV, 4*RAP of fc), so the 256 workgroups of the
+// 124M shape each stream an equal 1/256 of every matrix, and a contiguous
+// 1/256 of the head.  Inside a workgroup each output row is owned by a segment
+// of LPR lanes (16 or 64), so a row's dot product ends in one short DPP
+// reduction and all rows reduce at once.  A workgroup is one control wave plus
+// NCW compute waves:
+//   * compute waves stream the workgroup's weight slices through two register
+//     buffers, requesting each slice one phase before it is used;
 //   * the control wave waits for the inputs of each phase, normalises them
-//     into LDS, and publishes the phase's outputs.
+//     into LDS, runs the attention chunk, and publishes the phase's outputs.
 // Batch 1 makes every linear a matrix-vector product (0.5 flop per fp32 byte),
 // so there is no MFMA here: the kernel is bound by weight bytes and by the
 // latency of the 5L+1 dependent phases of a token.
@@ -38,10 +41,10 @@
 namespace gpt2dec {
 namespace {
 
-constexpr int CHMIN = 16;      // positions per attention chunk before a head is split further
-constexpr int PSTRIDE = 256;   // LDS stride of per-wave partial sums (>= rows per workgroup)
+constexpr int CHMIN = 64;      // positions per attention chunk before a head is split
+constexpr int PSTRIDE = 256;   // LDS room for row results (>= rows per workgroup)
 
-template <int E_, int D_, int NCW_, int RAP_, int MAXCH_>
+template <int E_, int D_, int NCW_, int RAP_, int MAXCH_, int LPRH_>
 struct Shape {
   static constexpr int E = E_, D = D_, H = E_ / D_, F = 4 * E_;
   static constexpr int NCW = NCW_;        // compute waves
@@ -50,43 +53,40 @@ struct Shape {
   static constexpr int RAP = RAP_;        // rows of an E-output matrix per workgroup
   static constexpr int G = E_ / RAP_;     // workgroups
   static constexpr int MAXCH = MAXCH_;    // attention chunks per head at most
-  static_assert(E_ % D_ == 0 && E_ % 64 == 0, "shape");
+  static constexpr int LPRH = LPRH_;      // lanes per head row
+  static_assert(E_ % D_ == 0 && E_ % 64 == 0 && D_ <= 64 && 64 % (D_ / 4) == 0, "shape");
   static_assert(H * MAXCH <= G, "one attention chunk per workgroup at most");
   // LDS layout (floats)
   static constexpr int L_XS = 0;                         // [F] phase input vector
-  static constexpr int L_PART = L_XS + F;                // [NCW][PSTRIDE] partial row sums
-  static constexpr int L_Q = L_PART + NCW * PSTRIDE;     // [D] query of the attention item
+  static constexpr int L_PART = L_XS + F;                // [PSTRIDE] row results
+  static constexpr int L_Q = L_PART + PSTRIDE;           // [D] query of the attention item
   static constexpr int L_KP = L_Q + D;                   // [D] key of this position
   static constexpr int L_VP = L_KP + D;                  // [D] value of this position
   static constexpr int L_SC = L_VP + D;                  // [64] chunk scores / weights
-  static constexpr int L_SLOT = L_SC + 64;               // [D+2] chunk output (o, m, l)
-  static constexpr int L_FLAG = L_SLOT + D + 2;          // [4] control flags
+  static constexpr int L_FLAG = L_SC + 64;               // [4] control flags
   static constexpr int L_TOTAL = L_FLAG + 4;
 };
 
 // 124M shape: 256 workgroups x (3 compute + 1 control) waves.
-using ShapeS = Shape<768, 64, 3, 3, 16>;
+using ShapeS = Shape<768, 64, 3, 3, 16, 16>;
 // tiny shape: 32 workgroups x (2 compute + 1 control) waves.
-using ShapeT = Shape<128, 32, 2, 4, 8>;
+using ShapeT = Shape<128, 32, 2, 4, 8, 8>;
 
-// Rows of length K split in 4-element chunks over the NL compute lanes: either
-// a row spans whole passes of all lanes (ROWWIDE, PPR passes per row) or one
-// pass covers RPP rows of KC lanes each.
-template <class S, int K>
-struct RowGeo {
-  static constexpr int KC = K / 4;
-  static constexpr bool ROWWIDE = (KC % S::NL) == 0;
-  static_assert(ROWWIDE || (S::NL % KC == 0 && KC <= 64), "unsupported row geometry");
-  static constexpr int PPR = ROWWIDE ? KC / S::NL : 1;
-  static constexpr int RPP = ROWWIDE ? 1 : S::NL / KC;
-};
+constexpr int lpr_for(int R, int KC, int NL) {
+  int l = 64;
+  while (l > 1 && (R * l > NL || KC % l != 0)) l >>= 1;
+  return l;
+}
 
-// Geometry of one workgroup slice: R rows of length K.
+// Geometry of one workgroup slice: R rows of length K in 4-element chunks.
+// Lane l < R*LPR owns row l/LPR and the chunks (l%LPR) + LPR*i, i < NPASS.
 template <class S, int R, int K>
-struct Geo : RowGeo<S, K> {
-  static constexpr int NCH = R * RowGeo<S, K>::KC;
-  static_assert(NCH % S::NL == 0, "slice must split evenly over compute lanes");
-  static constexpr int NPASS = NCH / S::NL;
+struct Geo {
+  static constexpr int KC = K / 4;
+  static constexpr int LPR = lpr_for(R, KC, S::NL);
+  static constexpr int NPASS = KC / LPR;
+  static constexpr int ACTIVE = R * LPR;
+  static_assert(ACTIVE <= S::NL && KC % LPR == 0 && LPR >= 4, "row geometry");
 };
 
 // ---- weight chunks: 4 consecutive inputs of one output row ----------------
@@ -97,16 +97,26 @@ template <> struct Chunk<WD_Q4> { uint32_t q; float2 sz; };
 
 // gc: chunk index inside the layer's [N][K] matrix (= row*K/4 + k/4);
 // lofs: element offset of the layer (= layer*N*K).
+// Weights are read once per token: non-temporal loads keep them from
+// displacing the small, reused data (LayerNorm parameters, biases,
+// activations) in the caches.
+typedef float g2_v4f __attribute__((ext_vector_type(4)));
+typedef float g2_v2f __attribute__((ext_vector_type(2)));
+typedef unsigned int g2_v2u __attribute__((ext_vector_type(2)));
+
 template <int WD>
 __device__ __forceinline__ Chunk<WD> ld_chunk(const MatW &m, size_t lofs, size_t gc) {
   Chunk<WD> c;
   if constexpr (WD == WD_F32) {
-    c.v = reinterpret_cast<const float4 *>(m.w)[lofs / 4 + gc];
+    const g2_v4f v = __builtin_nontemporal_load(reinterpret_cast<const g2_v4f *>(m.w) + lofs / 4 + gc);
+    c.v = make_float4(v.x, v.y, v.z, v.w);
   } else if constexpr (WD == WD_F16) {
-    c.v = reinterpret_cast<const uint2 *>(m.w)[lofs / 4 + gc];
+    const g2_v2u v = __builtin_nontemporal_load(reinterpret_cast<const g2_v2u *>(m.w) + lofs / 4 + gc);
+    c.v = make_uint2(v.x, v.y);
   } else {
-    c.q = reinterpret_cast<const uint16_t *>(m.w)[lofs / 4 + gc];
-    c.sz = m.sz[lofs / 32 + gc / 8];
+    c.q = __builtin_nontemporal_load(reinterpret_cast<const unsigned short *>(m.w) + lofs / 4 + gc);
+    const g2_v2f z = __builtin_nontemporal_load(reinterpret_cast<const g2_v2f *>(m.sz) + lofs / 32 + gc / 8);
+    c.sz = make_float2(z.x, z.y);
   }
   return c;
 }
@@ -140,18 +150,63 @@ __device__ __forceinline__ float dot4(float4 w, float4 x, float acc) {
   return acc;
 }
 
-// Butterfly reductions: every lane of the group ends with the same bits.
-template <int W>
-__device__ __forceinline__ float seg_sum(float a) {
-#pragma unroll
-  for (int m = W / 2; m >= 1; m >>= 1) a += __shfl_xor(a, m, 64);
-  return a;
+// ---- DPP reductions ----------------------------------------------------------
+// Inclusive scans with row_shr 1,2,4,8 (within 16-lane rows), then
+// row_bcast:15 / row_bcast:31 across rows: the total of each W-lane segment
+// ends in the segment's last lane.  Lanes whose DPP source is out of range,
+// or whose row is masked off, take the identity.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_or(float v, float ident) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(ident), __float_as_int(v), CTRL, ROWMASK,
+                                                    0xF, false));
 }
-__device__ __forceinline__ float wave_sum(float a) { return seg_sum<64>(a); }
-__device__ __forceinline__ float wave_max(float a) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m, 64));
-  return a;
+template <int W>
+__device__ __forceinline__ float seg_sum_last(float v) {
+  static_assert(W == 4 || W == 8 || W == 16 || W == 32 || W == 64, "segment");
+  v += dpp_or<0x111, 0xF>(v, 0.f);
+  v += dpp_or<0x112, 0xF>(v, 0.f);
+  if constexpr (W >= 8) v += dpp_or<0x114, 0xF>(v, 0.f);
+  if constexpr (W >= 16) v += dpp_or<0x118, 0xF>(v, 0.f);
+  if constexpr (W >= 32) v += dpp_or<0x142, 0xA>(v, 0.f);
+  if constexpr (W >= 64) v += dpp_or<0x143, 0xC>(v, 0.f);
+  return v;
+}
+// Whole-wave sum / max, the same bits in every lane.
+__device__ __forceinline__ float wave_sum_all(float v) {
+  const float t = seg_sum_last<64>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), 63));
+}
+__device__ __forceinline__ float wave_max_all(float v) {
+  const float ninf = -INFINITY;
+  v = fmaxf(v, dpp_or<0x111, 0xF>(v, ninf));
+  v = fmaxf(v, dpp_or<0x112, 0xF>(v, ninf));
+  v = fmaxf(v, dpp_or<0x114, 0xF>(v, ninf));
+  v = fmaxf(v, dpp_or<0x118, 0xF>(v, ninf));
+  v = fmaxf(v, dpp_or<0x142, 0xA>(v, ninf));
+  v = fmaxf(v, dpp_or<0x143, 0xC>(v, ninf));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32_all(uint32_t v) {
+  auto step = [](uint32_t x, uint32_t y) { return x < y ? x : y; };
+#define G2_MIN_STEP(CTRL, ROWMASK) \
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp((int)0xffffffffu, (int)v, CTRL, ROWMASK, 0xF, false))
+  G2_MIN_STEP(0x111, 0xF);
+  G2_MIN_STEP(0x112, 0xF);
+  G2_MIN_STEP(0x114, 0xF);
+  G2_MIN_STEP(0x118, 0xF);
+  G2_MIN_STEP(0x142, 0xA);
+  G2_MIN_STEP(0x143, 0xC);
+#undef G2_MIN_STEP
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Greedy pick over the wave: the largest value, and the lowest index among
+// the lanes that hold it (each lane passes its own best value and index).
+__device__ __forceinline__ uint32_t wave_argmax(float v, uint32_t idx, float *best = nullptr) {
+  const float m = wave_max_all(v);
+  if (best) *best = m;
+  return wave_min_u32_all(v == m ? idx : 0xffffffffu);
 }
 
 __device__ __forceinline__ void wg_barrier() {
@@ -174,6 +229,8 @@ __device__ __forceinline__ void tst_u(uint64_t *p, uint32_t v, uint32_t ep) {
 __device__ __forceinline__ void st_agent(float *p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ bool tag_is(uint64_t x, uint32_t ep) { return (uint32_t)(x >> 32) == ep; }
+__device__ __forceinline__ float payload(uint64_t x) { return __uint_as_float((uint32_t)x); }
 
 // Bounded waiting: a wait that outlives the time limit, or sees another
 // workgroup's abort, sets the error word and makes the caller stop.
@@ -181,6 +238,10 @@ struct Waiter {
   const DecodeArgs *a;
   long long t0;
   int phase;
+  __device__ void start(int ph) {
+    t0 = (long long)wall_clock64();
+    phase = ph;
+  }
   __device__ bool expired() {
     if (__hip_atomic_load(a->err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return true;
     if ((long long)wall_clock64() - t0 > a->timeout_ticks) {
@@ -204,8 +265,8 @@ __device__ bool poll_vec(const uint64_t *src, uint32_t ep, float (&v)[PER], int 
 #pragma unroll
     for (int j = 0; j < PER; j++) {
       const uint64_t x = tld(src + lane + 64 * j);
-      v[j] = __uint_as_float((uint32_t)x);
-      ok &= ((uint32_t)(x >> 32) == ep);
+      v[j] = payload(x);
+      ok &= tag_is(x, ep);
     }
     if (__all(ok)) return true;
     if (wt.expired()) return false;
@@ -224,14 +285,14 @@ __device__ __forceinline__ void layernorm_to_lds(const float (&x)[E / 64], const
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < PER; j++) s += x[j];
-  const float mean = wave_sum(s) * (1.0f / (float)E);
+  const float mean = wave_sum_all(s) * (1.0f / (float)E);
   float q = 0.f;
 #pragma unroll
   for (int j = 0; j < PER; j++) {
     const float d = x[j] - mean;
     q = __builtin_fmaf(d, d, q);
   }
-  const float var = wave_sum(q) * (1.0f / (float)E);
+  const float var = wave_sum_all(q) * (1.0f / (float)E);
   const float r = 1.0f / sqrtf(var + eps);
 #pragma unroll
   for (int j = 0; j < PER; j++) dst[lane + 64 * j] = __builtin_fmaf((x[j] - mean) * r, g[j], b[j]);
@@ -257,208 +318,126 @@ __device__ __forceinline__ void att_chunks(int p, int &nch, int &ch) {
   ch = (n + nch - 1) / nch;
 }
 
-template <class S>
+// Optional timeline of one workgroup's control wave (lane 0): inputs ready, first and
+// second workgroup barrier passed, outputs published.
+__device__ __forceinline__ void stamp(const DecodeArgs &a, int step, int ph, int which, int G) {
+  if (a.trace && step < a.trace_steps)
+    a.trace[(((size_t)step * (5 * a.L + 1) + ph) * G + blockIdx.x) * 4 + which] = (long long)wall_clock64();
+}
+
 __device__ __forceinline__ uint32_t epoch_of(const DecodeArgs &a, int step, int ph) {
   return a.epoch0 + (uint32_t)step * (uint32_t)(5 * a.L + 1) + (uint32_t)ph + 1u;
 }
 
 // ---- compute waves ---------------------------------------------------------
-template <class S, int R, int K, int WD, int NP>
-__device__ __forceinline__ void load_slice(Chunk<WD> (&w)[NP], const MatW &m, int layer, int lane) {
+template <class S, int R, int K, int WD, int NB>
+__device__ __forceinline__ void load_slice(Chunk<WD> (&w)[NB], const MatW &m, int layer, int lane) {
   using Gm = Geo<S, R, K>;
-  static_assert(NP == Gm::NPASS, "register slice size");
+  static_assert(Gm::NPASS <= NB, "register buffer too small");
+  // Lanes past the slice re-read the last row (same addresses as its own
+  // lanes in the same wave; their results are discarded).  Keeping every load
+  // unconditional lets the compiler count outstanding loads exactly.
+  const int r = min(lane / Gm::LPR, R - 1);
   const size_t lofs = (size_t)layer * (size_t)(R * S::G) * K;
-  const size_t c0 = (size_t)blockIdx.x * Gm::NCH + lane;
+  const size_t c0 = ((size_t)blockIdx.x * R + r) * Gm::KC + (lane % Gm::LPR);
 #pragma unroll
-  for (int i = 0; i < Gm::NPASS; i++) w[i] = ld_chunk<WD>(m, lofs, c0 + (size_t)i * S::NL);
+  for (int i = 0; i < Gm::NPASS; i++) w[i] = ld_chunk<WD>(m, lofs, c0 + (size_t)i * Gm::LPR);
 }
 
-template <class S, int R, int K, int WD, int NP>
-__device__ __forceinline__ void slice_dot(const Chunk<WD> (&w)[NP], const float *xs, float *part, int lane) {
+// Row results of the slice into part[0..R).
+template <class S, int R, int K, int WD, int NB>
+__device__ __forceinline__ void slice_dot(const Chunk<WD> (&w)[NB], const float *xs, float *part, int lane) {
   using Gm = Geo<S, R, K>;
-  static_assert(NP == Gm::NPASS, "register slice size");
-  if constexpr (Gm::ROWWIDE) {
-    const int wave = lane >> 6;
+  static_assert(Gm::NPASS <= NB, "register buffer too small");
+  const int q = lane % Gm::LPR;
+  float a = 0.f;
 #pragma unroll
-    for (int r = 0; r < R; r++) {
-      float a = 0.f;
-#pragma unroll
-      for (int j = 0; j < Gm::PPR; j++) {
-        const float4 x = reinterpret_cast<const float4 *>(xs)[j * S::NL + lane];
-        a = dot4(deq<WD>(w[r * Gm::PPR + j]), x, a);
-      }
-      a = wave_sum(a);
-      if ((lane & 63) == 0) part[wave * PSTRIDE + r] = a;
-    }
-  } else {
-    const int kc = lane % Gm::KC;
-    const float4 x = reinterpret_cast<const float4 *>(xs)[kc];
-#pragma unroll
-    for (int i = 0; i < Gm::NPASS; i++) {
-      float a = dot4(deq<WD>(w[i]), x, 0.f);
-      a = seg_sum<Gm::KC>(a);
-      if (kc == 0) part[i * Gm::RPP + lane / Gm::KC] = a;
-    }
-  }
+  for (int i = 0; i < Gm::NPASS; i++)
+    a = dot4(deq<WD>(w[i]), reinterpret_cast<const float4 *>(xs)[i * Gm::LPR + q], a);
+  a = seg_sum_last<Gm::LPR>(a);
+  if (lane < Gm::ACTIVE && q == Gm::LPR - 1) part[lane / Gm::LPR] = a;
 }
 
-// Row total from the partials (read by the control wave).
-template <class S, int K>
-__device__ __forceinline__ float row_total(const float *part, int r) {
-  using Gm = RowGeo<S, K>;
-  if constexpr (Gm::ROWWIDE) {
-    float t = part[r];
-#pragma unroll
-    for (int w = 1; w < S::NCW; w++) t += part[w * PSTRIDE + r];
-    return t;
-  } else {
-    return part[r];
-  }
-}
-
-// One attention chunk (head h, positions t0..t1-1) on the control wave.  Scores and
-// softmax weights follow the attn_decode kernel (q.k * 1/sqrt(D), subtract the
-// maximum, exp); the chunk leaves (o = sum e_t v_t, m = max, l = sum e_t) for
-// the merge.
-template <class S>
-__device__ void attention_chunk(const DecodeArgs &a, float *lds, int l, int h, int p, int t0, int t1,
-                                int lane) {
-  constexpr int D = S::D, D4 = D / 4, RPL = 64 / D4;
-  const float *K = a.kc + ((size_t)(l * S::H + h) * a.P) * D;
-  const float *V = a.vc + ((size_t)(l * S::H + h) * a.P) * D;
-  const float scale = 1.0f / sqrtf((float)D);
-  const float4 q4 = reinterpret_cast<const float4 *>(lds + S::L_Q)[lane % D4];
-  const int n = t1 - t0;
-  const bool last = (t1 == p + 1);      // this chunk ends at the current position
-  const int tg = last ? p : t1;         // rows t0..tg-1 come from the cache
-  // (global and LDS reads stay in separate statements so that neither turns
-  // into a generic-address load)
-  for (int it = 0; it * RPL < tg - t0; it++) {
-    const int t = t0 + it * RPL + lane / D4;
-    float4 k4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (t < tg) k4 = reinterpret_cast<const float4 *>(K + (size_t)t * D)[lane % D4];
-    float s = dot4(k4, q4, 0.f);
-    s = seg_sum<D4>(s) * scale;
-    if ((lane % D4) == 0 && t < tg) lds[S::L_SC + (t - t0)] = s;
-  }
-  if (last) {
-    const float4 k4 = reinterpret_cast<const float4 *>(lds + S::L_KP)[lane % D4];
-    float s = dot4(k4, q4, 0.f);
-    s = seg_sum<D4>(s) * scale;
-    if (lane == 0) lds[S::L_SC + (p - t0)] = s;
-  }
-  const float s = lane < n ? lds[S::L_SC + lane] : -INFINITY;
-  const float m = wave_max(s);
-  const float e = lane < n ? expf(s - m) : 0.f;
-  const float lsum = wave_sum(e);
-  lds[S::L_SC + lane] = e;
-  // o[d] = sum_t e_t * v_t[d] in ascending t; lanes cover d (and, for D < 64,
-  // alternate rows)
-  constexpr int RG = 64 / D;
-  const int d = lane % D, g = lane / D;
-  float o = 0.f;
-  for (int t = t0 + g; t < tg; t += RG) o = __builtin_fmaf(lds[S::L_SC + (t - t0)], V[(size_t)t * D + d], o);
-  if (last && ((p - t0) % RG) == g) o = __builtin_fmaf(lds[S::L_SC + (p - t0)], lds[S::L_VP + d], o);
-#pragma unroll
-  for (int m2 = 32; m2 >= D; m2 >>= 1) o += __shfl_xor(o, m2, 64);
-  if (lane < D) lds[S::L_SLOT + lane] = o;
-  if (lane == 0) {
-    lds[S::L_SLOT + D] = m;
-    lds[S::L_SLOT + D + 1] = lsum;
-  }
-}
-
+// Compute waves.  Two register buffers alternate: when a phase's inputs are
+// ready, the slice of the next phase is requested into the other buffer and
+// the current slice (requested one phase earlier) is consumed, so every slice
+// streams in while the previous phase computes, publishes and waits.
 template <class S, int WD>
 __device__ void compute_main(const DecodeArgs &a, float *lds, int lane) {
   constexpr int E = S::E, F = S::F, RAP = S::RAP;
-  Chunk<WD> wq[Geo<S, 3 * RAP, E>::NPASS];
-  Chunk<WD> wa[Geo<S, RAP, E>::NPASS];
-  Chunk<WD> wf[Geo<S, 4 * RAP, E>::NPASS];
-  Chunk<WD> wp[Geo<S, RAP, F>::NPASS];
-  load_slice<S, 3 * RAP, E, WD>(wq, a.qkv, 0, lane);
-  load_slice<S, RAP, E, WD>(wa, a.ap, 0, lane);
-  load_slice<S, 4 * RAP, E, WD>(wf, a.fc, 0, lane);
-  load_slice<S, RAP, F, WD>(wp, a.pr, 0, lane);
-  // plain LDS accesses: the barrier's memory clobber orders them
+  constexpr int NB = Geo<S, 3 * RAP, E>::NPASS > Geo<S, RAP, F>::NPASS ? Geo<S, 3 * RAP, E>::NPASS
+                                                                      : Geo<S, RAP, F>::NPASS;
+  static_assert(Geo<S, 4 * RAP, E>::NPASS <= NB && Geo<S, RAP, E>::NPASS <= NB, "buffer size");
   const int *flag = reinterpret_cast<const int *>(lds + S::L_FLAG);
   float *part = lds + S::L_PART;
   const float *xs = lds + S::L_XS;
+  Chunk<WD> b0[NB], b1[NB];
+  load_slice<S, 3 * RAP, E, WD>(b0, a.qkv, 0, lane);
   for (int step = 0; step < a.nsteps; step++) {
     for (int l = 0; l < a.L; l++) {
-      const int ln = (l + 1 == a.L) ? 0 : l + 1;
-      // A: QKV
+      // A: QKV (b0); request the attention projection into b1
       wg_barrier();
       if (flag[0]) return;
-      slice_dot<S, 3 * RAP, E, WD>(wq, xs, part, lane);
+      load_slice<S, RAP, E, WD>(b1, a.ap, l, lane);
+      slice_dot<S, 3 * RAP, E, WD>(b0, xs, part, lane);
       wg_barrier();
-      load_slice<S, 3 * RAP, E, WD>(wq, a.qkv, ln, lane);
       // B: attention runs on the control wave alone
-      // C: attention projection
+      // C: attention projection (b1); request fc into b0
       wg_barrier();
       if (flag[0]) return;
-      slice_dot<S, RAP, E, WD>(wa, xs, part, lane);
+      load_slice<S, 4 * RAP, E, WD>(b0, a.fc, l, lane);
+      slice_dot<S, RAP, E, WD>(b1, xs, part, lane);
       wg_barrier();
-      load_slice<S, RAP, E, WD>(wa, a.ap, ln, lane);
-      // D: fc
-      wg_barrier();
-      if (flag[0]) return;
-      slice_dot<S, 4 * RAP, E, WD>(wf, xs, part, lane);
-      wg_barrier();
-      load_slice<S, 4 * RAP, E, WD>(wf, a.fc, ln, lane);
-      // E: MLP projection
+      // D: fc (b0); request the MLP projection into b1
       wg_barrier();
       if (flag[0]) return;
-      slice_dot<S, RAP, F, WD>(wp, xs, part, lane);
+      load_slice<S, RAP, F, WD>(b1, a.pr, l, lane);
+      slice_dot<S, 4 * RAP, E, WD>(b0, xs, part, lane);
       wg_barrier();
-      load_slice<S, RAP, F, WD>(wp, a.pr, ln, lane);
+      // E: MLP projection (b1); request the next layer's QKV into b0
+      wg_barrier();
+      if (flag[0]) return;
+      load_slice<S, 3 * RAP, E, WD>(b0, a.qkv, (l + 1 < a.L) ? l + 1 : 0, lane);
+      slice_dot<S, RAP, F, WD>(b1, xs, part, lane);
+      wg_barrier();
     }
-    // H: output head over this workgroup's vocabulary rows
+    // H: output head over this workgroup's vocabulary rows, RB rows per batch,
+    // two batches in flight
     wg_barrier();
     if (flag[0]) return;
     {
-      using Gm = RowGeo<S, E>;
-      constexpr int KC = Gm::KC;
+      constexpr int KC = E / 4, LPR = S::LPRH, NPH = KC / LPR, RB = S::NL / LPR;
+      static_assert(KC % LPR == 0 && S::NL % LPR == 0, "head geometry");
+      constexpr int HWD = (WD == WD_F16) ? WD_F16 : WD_F32;
+      const MatW hm{a.head, nullptr};
       const int hr0 = (int)(((long long)blockIdx.x * a.V) / S::G);
       const int hr1 = (int)(((long long)(blockIdx.x + 1) * a.V) / S::G);
       const int nr = hr1 - hr0;
-      const MatW hm{a.head, nullptr};
-      constexpr int HWD = (WD == WD_F16) ? WD_F16 : WD_F32;
-      if constexpr (Gm::ROWWIDE) {
-        constexpr int PPR = Gm::PPR;
-        constexpr int NB = 8;
-        const int wave = lane >> 6;
-        float4 xv[PPR];
+      const int q = lane % LPR, rl = lane / LPR;
+      float4 xv[NPH];
 #pragma unroll
-        for (int j = 0; j < PPR; j++) xv[j] = reinterpret_cast<const float4 *>(xs)[j * S::NL + lane];
-        for (int r0 = 0; r0 < nr; r0 += NB) {
-          Chunk<HWD> hc[NB][PPR];
+      for (int i = 0; i < NPH; i++) xv[i] = reinterpret_cast<const float4 *>(xs)[i * LPR + q];
+      Chunk<HWD> h0[NPH], h1[NPH];
+      auto fetch = [&](Chunk<HWD>(&b)[NPH], int r0) {
+        const int r = min(r0 + rl, nr - 1);
+        const size_t c0 = (size_t)(hr0 + r) * KC + q;
 #pragma unroll
-          for (int b = 0; b < NB; b++) {
-            const int r = min(r0 + b, nr - 1);
+        for (int i = 0; i < NPH; i++) b[i] = ld_chunk<HWD>(hm, 0, c0 + (size_t)i * LPR);
+      };
+      auto consume = [&](const Chunk<HWD>(&b)[NPH], int r0) {
+        float acc = 0.f;
 #pragma unroll
-            for (int j = 0; j < PPR; j++)
-              hc[b][j] = ld_chunk<HWD>(hm, 0, (size_t)(hr0 + r) * KC + j * S::NL + lane);
-          }
-#pragma unroll
-          for (int b = 0; b < NB; b++) {
-            float acc = 0.f;
-#pragma unroll
-            for (int j = 0; j < PPR; j++) acc = dot4(deq<HWD>(hc[b][j]), xv[j], acc);
-            acc = wave_sum(acc);
-            if ((lane & 63) == 0 && r0 + b < nr) part[wave * PSTRIDE + r0 + b] = acc;
-          }
-        }
-      } else {
-        constexpr int RPP = Gm::RPP;
-        const int kc = lane % KC;
-        const float4 x = reinterpret_cast<const float4 *>(xs)[kc];
-        for (int r0 = 0; r0 < nr; r0 += RPP) {
-          const int r = r0 + lane / KC;
-          const int rr = min(r, nr - 1);
-          const Chunk<HWD> hc = ld_chunk<HWD>(hm, 0, (size_t)(hr0 + rr) * KC + kc);
-          float acc = dot4(deq<HWD>(hc), x, 0.f);
-          acc = seg_sum<KC>(acc);
-          if (kc == 0 && r < nr) part[r] = acc;
+        for (int i = 0; i < NPH; i++) acc = dot4(deq<HWD>(b[i]), xv[i], acc);
+        acc = seg_sum_last<LPR>(acc);
+        if (q == LPR - 1 && r0 + rl < nr) part[r0 + rl] = acc;
+      };
+      if (nr > 0) {
+        fetch(h0, 0);
+        for (int r0 = 0; r0 < nr; r0 += 2 * RB) {
+          if (r0 + RB < nr) fetch(h1, r0 + RB);
+          consume(h0, r0);
+          if (r0 + 2 * RB < nr) fetch(h0, r0 + 2 * RB);
+          if (r0 + RB < nr) consume(h1, r0 + RB);
         }
       }
     }
@@ -467,17 +446,149 @@ __device__ void compute_main(const DecodeArgs &a, float *lds, int lane) {
 }
 
 // ---- control wave ----------------------------------------------------------
+template <class S>
+__device__ __forceinline__ bool reduce_argmax(const DecodeArgs &a, uint32_t ep, int lane, Waiter &wt,
+                                              uint32_t &out_idx) {
+  constexpr int G = S::G;
+  float bv = -INFINITY;
+  uint32_t bi = 0xffffffffu;
+  while (true) {
+    bool ok = true;
+    float v = -INFINITY;
+    uint32_t idx = 0xffffffffu;
+    for (int g0 = lane; g0 < G; g0 += 64) {
+      const uint64_t xv = tld(a.amax_t + g0), xi = tld(a.amax_t + G + g0);
+      ok &= tag_is(xv, ep) && tag_is(xi, ep);
+      const float cv = payload(xv);
+      const uint32_t ci = (uint32_t)xi;
+      if (cv > v || (cv == v && ci < idx)) { v = cv; idx = ci; }
+    }
+    if (__all(ok)) { bv = v; bi = idx; break; }
+    if (wt.expired()) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  out_idx = wave_argmax(bv, bi);
+  return true;
+}
+
+// One attention chunk of head h over positions t0..t1-1 on the control wave,
+// following the attn_decode kernel: scores q.k * (1/sqrt(D)), subtract the
+// maximum, exp; the chunk's (o = sum e_t v_t, m = max, l = sum e_t).  Row p
+// (the current position) comes from LDS, the others from the cache.  Lane
+// (g, d4) handles rows t0 + g + RPL*it and dimensions 4*d4..4*d4+3.
+template <class S>
+struct AttChunk {
+  static constexpr int D = S::D, D4 = D / 4, RPL = 64 / D4, IT = 64 / RPL;
+  float4 k[IT], v[IT];
+  __device__ void fetch(const DecodeArgs &a, int l, int h, int t0, int tg, int lane) {
+    const float *K = a.kc + ((size_t)(l * S::H + h) * a.P) * D;
+    const float *V = a.vc + ((size_t)(l * S::H + h) * a.P) * D;
+    const int g = lane / D4, d4 = lane % D4;
+#pragma unroll
+    for (int it = 0; it < IT; it++) {
+      const int t = t0 + g + RPL * it;
+      k[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+      v[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (t < tg) {
+        k[it] = reinterpret_cast<const float4 *>(K + (size_t)t * D)[d4];
+        v[it] = reinterpret_cast<const float4 *>(V + (size_t)t * D)[d4];
+      }
+    }
+  }
+  // m, lsum in all lanes; o (dims 4*d4..4*d4+3) summed over all rows in lanes of group 0
+  __device__ void run(float *lds, int p, int t0, int t1, int tg, int lane, float &m, float &lsum, float4 &o) {
+    const int g = lane / D4, d4 = lane % D4;
+    const float scale = 1.0f / sqrtf((float)D);
+    const float4 q4 = reinterpret_cast<const float4 *>(lds + S::L_Q)[d4];
+    const int n = t1 - t0;
+#pragma unroll
+    for (int it = 0; it < IT; it++) {
+      const int t = t0 + g + RPL * it;
+      const float s = seg_sum_last<D4>(dot4(k[it], q4, 0.f)) * scale;
+      if (d4 == D4 - 1 && t < tg) lds[S::L_SC + (t - t0)] = s;
+    }
+    if (tg < t1) {  // this position
+      const float4 kp = reinterpret_cast<const float4 *>(lds + S::L_KP)[d4];
+      const float s = seg_sum_last<D4>(dot4(kp, q4, 0.f)) * scale;
+      if (lane == D4 - 1) lds[S::L_SC + (p - t0)] = s;
+    }
+    const float s = lane < n ? lds[S::L_SC + lane] : -INFINITY;
+    m = wave_max_all(s);
+    const float e = lane < n ? expf(s - m) : 0.f;
+    lsum = wave_sum_all(e);
+    lds[S::L_SC + lane] = e;
+    o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int it = 0; it < IT; it++) {
+      const int t = t0 + g + RPL * it;
+      if (t < tg) {
+        const float wt = lds[S::L_SC + (t - t0)];
+        o.x = __builtin_fmaf(wt, v[it].x, o.x);
+        o.y = __builtin_fmaf(wt, v[it].y, o.y);
+        o.z = __builtin_fmaf(wt, v[it].z, o.z);
+        o.w = __builtin_fmaf(wt, v[it].w, o.w);
+      }
+    }
+    if (tg < t1 && ((p - t0) % RPL) == g) {
+      const float wt = lds[S::L_SC + (p - t0)];
+      const float4 vp = reinterpret_cast<const float4 *>(lds + S::L_VP)[d4];
+      o.x = __builtin_fmaf(wt, vp.x, o.x);
+      o.y = __builtin_fmaf(wt, vp.y, o.y);
+      o.z = __builtin_fmaf(wt, vp.z, o.z);
+      o.w = __builtin_fmaf(wt, vp.w, o.w);
+    }
+    // sum the RPL row groups in group order through LDS (the phase-input
+    // area is free while the attention chunk runs); lanes of group 0 end
+    // with the chunk's o
+    float4 *scr = reinterpret_cast<float4 *>(lds + S::L_XS);
+    scr[lane] = o;
+    if (g == 0) {
+      float4 t = scr[d4];
+#pragma unroll
+      for (int gg = 1; gg < RPL; gg++) {
+        const float4 u = scr[gg * D4 + d4];
+        t.x += u.x;
+        t.y += u.y;
+        t.z += u.z;
+        t.w += u.w;
+      }
+      o = t;
+    }
+  }
+};
+
 template <class S, int WD>
 __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
   constexpr int E = S::E, F = S::F, D = S::D, H = S::H, RAP = S::RAP, G = S::G;
-  constexpr int PE = E / 64, PF = F / 64;
+  constexpr int PE = E / 64, PF = F / 64, D4 = D / 4;
   const int w = blockIdx.x;
   int *flag = reinterpret_cast<int *>(lds + S::L_FLAG);
   float *xs = lds + S::L_XS;
   const float *part = lds + S::L_PART;
-  float res = 0.f;   // residual stream value of row w*RAP + lane (lanes < RAP)
+  float res = 0.f;  // residual stream value of row w*RAP + lane (lanes < RAP)
   int tok = 0;
   Waiter wt{&a, 0, 0};
+  // Parameters of a phase are requested one or two phases ahead, before an
+  // earlier wait, so their latency hides behind it:
+  //   A(l): ln1, QKV bias   <- requested before D(l-1)'s wait (or H's)
+  //   C(l): attn-proj bias  <- before A(l)'s wait
+  //   D(l): ln2, fc bias    <- before A(l)'s wait
+  //   E(l): MLP-proj bias   <- before C(l)'s wait
+  //   H   : ln_f            <- before D(L-1)'s wait
+  float g1[PE], b1[PE], g2[PE], b2[PE], gf[PE], bf[PE];
+  float bq = 0.f, ba = 0.f, bfc = 0.f, bp = 0.f;
+  auto fetch_ln = [&](float (&g)[PE], float (&b)[PE], const float *gs, const float *bs) {
+#pragma unroll
+    for (int j = 0; j < PE; j++) {
+      g[j] = gs[lane + 64 * j];
+      b[j] = bs[lane + 64 * j];
+    }
+  };
+  auto fetch_a = [&](int l) {
+    fetch_ln(g1, b1, a.ln1w + l * E, a.ln1b + l * E);
+    bq = lane < 3 * RAP ? a.bqkv[l * 3 * E + w * 3 * RAP + lane] : 0.f;
+  };
+  fetch_a(0);
   auto abort_all = [&]() {
     if (lane == 0) flag[0] = 1;
     wg_barrier();
@@ -485,51 +596,33 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
   for (int step = 0; step < a.nsteps; step++) {
     const int p = a.pos0 + step;
     // token of this step: fed, or the argmax of the previous step
-    if (step < a.n_feed) {
-      tok = a.feed[step];
-    }
+    if (step < a.n_feed) tok = a.feed[step];
     if (step > 0) {
-      const uint32_t ep = epoch_of<S>(a, step - 1, 5 * a.L);
-      wt.t0 = wall_clock64();
-      wt.phase = 5 * a.L;
-      float bv = -INFINITY;
-      uint32_t bi = 0xffffffffu;
-      while (true) {
-        bool ok = true;
-        float v = -INFINITY;
-        uint32_t idx = 0xffffffffu;
-        for (int g0 = lane; g0 < G; g0 += 64) {
-          const uint64_t xv = tld(a.amax_t + g0), xi = tld(a.amax_t + G + g0);
-          ok &= ((uint32_t)(xv >> 32) == ep) && ((uint32_t)(xi >> 32) == ep);
-          const float cv = __uint_as_float((uint32_t)xv);
-          const uint32_t ci = (uint32_t)xi;
-          if (cv > v || (cv == v && ci < idx)) { v = cv; idx = ci; }
-        }
-        if (__all(ok)) { bv = v; bi = idx; break; }
-        if (wt.expired()) { abort_all(); return; }
-        __builtin_amdgcn_s_sleep(1);
-      }
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {
-        const float ov = __shfl_xor(bv, m, 64);
-        const uint32_t oi = (uint32_t)__shfl_xor((int)bi, m, 64);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-      }
+      uint32_t bi = 0;
+      wt.start(5 * a.L);
+      if (!reduce_argmax<S>(a, epoch_of(a, step - 1, 5 * a.L), lane, wt, bi)) { abort_all(); return; }
       if (w == 0 && lane == 0 && step - 1 >= a.out_from) a.out_ids[step - 1 - a.out_from] = (int)bi;
       // (an all-NaN head cannot name a row; keep the index in range)
       if (step >= a.n_feed) tok = bi < (uint32_t)a.V ? (int)bi : 0;
     }
+    int nch, ch;
+    att_chunks<S>(p, nch, ch);
+    const bool has_item = w < H * nch;
+    const int ih = has_item ? w / nch : 0, ic = has_item ? w % nch : 0;
+    const int it0 = ic * ch, it1 = min(it0 + ch, p + 1);
+    const bool ilast = (it1 == p + 1);
+    const int itg = ilast ? p : it1;  // cache rows it0..itg-1
     for (int l = 0; l < a.L; l++) {
-      const uint32_t epA = epoch_of<S>(a, step, 5 * l + 0), epB = epA + 1, epC = epA + 2,
-                     epD = epA + 3, epE = epA + 4;
+      const uint32_t epA = epoch_of(a, step, 5 * l + 0), epB = epA + 1, epC = epA + 2, epD = epA + 3,
+                     epE = epA + 4;
       // ---------------- A: LayerNorm 1 + QKV
       {
-        float x[PE], g[PE], b[PE];
-#pragma unroll
-        for (int j = 0; j < PE; j++) {
-          g[j] = a.ln1w[l * E + lane + 64 * j];
-          b[j] = a.ln1b[l * E + lane + 64 * j];
-        }
+        constexpr int R = 3 * RAP;
+        // requests for C and D
+        ba = lane < RAP ? a.bap[l * E + w * RAP + lane] : 0.f;
+        fetch_ln(g2, b2, a.ln2w + l * E, a.ln2b + l * E);
+        bfc = lane < 4 * RAP ? a.bfc[l * F + w * 4 * RAP + lane] : 0.f;
+        float x[PE];
         if (l == 0) {
 #pragma unroll
           for (int j = 0; j < PE; j++)
@@ -539,237 +632,230 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
             res = a.wte[(size_t)tok * E + o] + a.wpe[(size_t)p * E + o];
           }
         } else {
-          wt.t0 = wall_clock64();
-          wt.phase = 5 * (l - 1) + 4;
+          wt.start(5 * (l - 1) + 4);
           if (!poll_vec<PE>(a.xb_t + (size_t)(l - 1) * E, epA - 1, x, lane, wt)) { abort_all(); return; }
         }
-        layernorm_to_lds<E>(x, g, b, a.eps, xs, lane);
+        layernorm_to_lds<E>(x, g1, b1, a.eps, xs, lane);
+        if (lane == 0) stamp(a, step, 5 * l + 0, 0, G);
         if (lane == 0) flag[0] = 0;
         wg_barrier();
+        if (lane == 0) stamp(a, step, 5 * l + 0, 1, G);
         wg_barrier();
-        constexpr int R = 3 * RAP;
-        if (lane < R) {
-          const int o = w * R + lane;
-          const float y = row_total<S, E>(part, lane) + a.bqkv[l * 3 * E + o];
-          tst(a.qkv_t + (size_t)l * 3 * E + o, y, epA);
-        }
+        if (lane == 0) stamp(a, step, 5 * l + 0, 2, G);
+        if (lane < R) tst(a.qkv_t + (size_t)l * 3 * E + w * R + lane, part[lane] + bq, epA);
+        if (lane == 0) stamp(a, step, 5 * l + 0, 3, G);
       }
-      // ---------------- B: attention chunk
-      {
-        int nch, ch;
-        att_chunks<S>(p, nch, ch);
-        const int item = w;
-        const bool has = item < H * nch;
-        int h = 0, c = 0, t0 = 0, t1 = 0;
-        if (has) {
-          h = item / nch;
-          c = item % nch;
-          t0 = c * ch;
-          t1 = min(t0 + ch, p + 1);
-          const bool last = (t1 == p + 1);
-          wt.t0 = wall_clock64();
-          wt.phase = 5 * l + 0;
-          const uint64_t *qk = a.qkv_t + (size_t)l * 3 * E + h * D + (lane % D);
-          while (true) {
-            const uint64_t xq = tld(qk);
-            uint64_t xk = ((uint64_t)epA << 32), xv = ((uint64_t)epA << 32);
-            if (last) {
-              xk = tld(qk + E);
-              xv = tld(qk + 2 * E);
-            }
-            const bool ok = ((uint32_t)(xq >> 32) == epA) && ((uint32_t)(xk >> 32) == epA) &&
-                            ((uint32_t)(xv >> 32) == epA);
-            if (__all(ok)) {
-              if (lane < D) {
-                lds[S::L_Q + lane] = __uint_as_float((uint32_t)xq);
-                lds[S::L_KP + lane] = __uint_as_float((uint32_t)xk);
-                lds[S::L_VP + lane] = __uint_as_float((uint32_t)xv);
-                if (last) {
-                  const size_t row = ((size_t)(l * H + h) * a.P + p) * D + lane;
-                  st_agent(a.kc + row, __uint_as_float((uint32_t)xk));
-                  st_agent(a.vc + row, __uint_as_float((uint32_t)xv));
-                }
+      // ---------------- B: attention chunk (control wave only)
+      if (has_item) {
+        AttChunk<S> at;
+        at.fetch(a, l, ih, it0, itg, lane);  // cache rows: written at earlier steps
+        wt.start(5 * l + 0);
+        const uint64_t *qk = a.qkv_t + (size_t)l * 3 * E + ih * D + (lane % D);
+        while (true) {
+          const uint64_t xq = tld(qk);
+          uint64_t xk = (uint64_t)epA << 32, xv = (uint64_t)epA << 32;
+          if (ilast) {
+            xk = tld(qk + E);
+            xv = tld(qk + 2 * E);
+          }
+          if (__all(tag_is(xq, epA) && tag_is(xk, epA) && tag_is(xv, epA))) {
+            if (lane < D) {
+              lds[S::L_Q + lane] = payload(xq);
+              lds[S::L_KP + lane] = payload(xk);
+              lds[S::L_VP + lane] = payload(xv);
+              if (ilast) {
+                const size_t row = ((size_t)(l * H + ih) * a.P + p) * D + lane;
+                st_agent(a.kc + row, payload(xk));
+                st_agent(a.vc + row, payload(xv));
               }
-              break;
             }
-            if (wt.expired()) { abort_all(); return; }
-            __builtin_amdgcn_s_sleep(1);
+            break;
           }
+          if (wt.expired()) { abort_all(); return; }
+          __builtin_amdgcn_s_sleep(1);
         }
-        if (has) {
-          attention_chunk<S>(a, lds, l, h, p, t0, t1, lane);
-          // cache row stores complete before the chunk result is published
-          __builtin_amdgcn_s_waitcnt(0);
-          uint64_t *dst = a.att_t + ((size_t)(l * H + h) * S::MAXCH + c) * (D + 2);
-          if (lane < D) tst(dst + lane, lds[S::L_SLOT + lane], epB);
+        if (lane == 0) stamp(a, step, 5 * l + 1, 0, G);
+        float m, lsum;
+        float4 o;
+        at.run(lds, p, it0, it1, itg, lane, m, lsum, o);
+        // cache-row stores complete before anything of this step is published
+        __builtin_amdgcn_s_waitcnt(0);
+        const int g = lane / D4, d4 = lane % D4;
+        if (nch == 1) {
+          if (g == 0) {
+            uint64_t *dst = a.attn_t + (size_t)l * E + ih * D + 4 * d4;
+            tst(dst + 0, o.x / lsum, epB);
+            tst(dst + 1, o.y / lsum, epB);
+            tst(dst + 2, o.z / lsum, epB);
+            tst(dst + 3, o.w / lsum, epB);
+          }
+        } else if (ic > 0) {
+          uint64_t *dst = a.att_t + ((size_t)(l * H + ih) * S::MAXCH + ic) * (D + 2);
+          if (g == 0) {
+            tst(dst + 4 * d4 + 0, o.x, epB);
+            tst(dst + 4 * d4 + 1, o.y, epB);
+            tst(dst + 4 * d4 + 2, o.z, epB);
+            tst(dst + 4 * d4 + 3, o.w, epB);
+          }
           if (lane == 0) {
-            tst(dst + D, lds[S::L_SLOT + D], epB);
-            tst(dst + D + 1, lds[S::L_SLOT + D + 1], epB);
+            tst(dst + D, m, epB);
+            tst(dst + D + 1, lsum, epB);
           }
-        }
-      }
-      // ---------------- C: merge chunks, attention projection + residual
-      {
-        int nch, ch;
-        att_chunks<S>(p, nch, ch);
-        wt.t0 = wall_clock64();
-        wt.phase = 5 * l + 1;
-        const int d = lane % D;
-        for (int h = 0; h < H; h++) {
-          const uint64_t *src = a.att_t + ((size_t)(l * H + h) * S::MAXCH) * (D + 2);
+        } else {
+          // chunk 0 merges the head: max over chunks, then rescaled sums in chunk order
+          const uint64_t *src = a.att_t + ((size_t)(l * H + ih) * S::MAXCH) * (D + 2);
+          float mc[S::MAXCH], lc[S::MAXCH];
+          float4 oc[S::MAXCH];
+          wt.start(5 * l + 1);
           while (true) {
             bool ok = true;
-            float mc[S::MAXCH], lc[S::MAXCH], oc[S::MAXCH];
 #pragma unroll
-            for (int c = 0; c < S::MAXCH; c++) {
+            for (int c = 1; c < S::MAXCH; c++) {
               if (c < nch) {
-                const uint64_t *s = src + (size_t)c * (D + 2);
-                const uint64_t xo = tld(s + d), xm = tld(s + D), xl = tld(s + D + 1);
-                ok &= ((uint32_t)(xo >> 32) == epB) && ((uint32_t)(xm >> 32) == epB) &&
-                      ((uint32_t)(xl >> 32) == epB);
-                oc[c] = __uint_as_float((uint32_t)xo);
-                mc[c] = __uint_as_float((uint32_t)xm);
-                lc[c] = __uint_as_float((uint32_t)xl);
+                const uint64_t *s2 = src + (size_t)c * (D + 2);
+                const uint64_t x0 = tld(s2 + 4 * d4 + 0), x1 = tld(s2 + 4 * d4 + 1), x2 = tld(s2 + 4 * d4 + 2),
+                               x3 = tld(s2 + 4 * d4 + 3), xm = tld(s2 + D), xl = tld(s2 + D + 1);
+                ok &= tag_is(x0, epB) && tag_is(x1, epB) && tag_is(x2, epB) && tag_is(x3, epB) &&
+                      tag_is(xm, epB) && tag_is(xl, epB);
+                oc[c] = make_float4(payload(x0), payload(x1), payload(x2), payload(x3));
+                mc[c] = payload(xm);
+                lc[c] = payload(xl);
               }
             }
-            if (__all(ok)) {
-              float M = mc[0];
-#pragma unroll
-              for (int c = 1; c < S::MAXCH; c++)
-                if (c < nch) M = fmaxf(M, mc[c]);
-              float Ls = 0.f, O = 0.f;
-#pragma unroll
-              for (int c = 0; c < S::MAXCH; c++) {
-                if (c < nch) {
-                  const float f = expf(mc[c] - M);
-                  Ls = __builtin_fmaf(lc[c], f, Ls);
-                  O = __builtin_fmaf(oc[c], f, O);
-                }
-              }
-              if (lane < D) xs[h * D + d] = O / Ls;
-              break;
-            }
+            if (__all(ok)) break;
             if (wt.expired()) { abort_all(); return; }
             __builtin_amdgcn_s_sleep(1);
           }
+          mc[0] = m;
+          lc[0] = lsum;
+          oc[0] = o;
+          float M = mc[0];
+#pragma unroll
+          for (int c = 1; c < S::MAXCH; c++)
+            if (c < nch) M = fmaxf(M, mc[c]);
+          float Ls = 0.f;
+          float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+          for (int c = 0; c < S::MAXCH; c++) {
+            if (c < nch) {
+              const float f = expf(mc[c] - M);
+              Ls = __builtin_fmaf(lc[c], f, Ls);
+              O.x = __builtin_fmaf(oc[c].x, f, O.x);
+              O.y = __builtin_fmaf(oc[c].y, f, O.y);
+              O.z = __builtin_fmaf(oc[c].z, f, O.z);
+              O.w = __builtin_fmaf(oc[c].w, f, O.w);
+            }
+          }
+          if (g == 0) {
+            uint64_t *dst = a.attn_t + (size_t)l * E + ih * D + 4 * d4;
+            tst(dst + 0, O.x / Ls, epB);
+            tst(dst + 1, O.y / Ls, epB);
+            tst(dst + 2, O.z / Ls, epB);
+            tst(dst + 3, O.w / Ls, epB);
+          }
         }
+        if (lane == 0) stamp(a, step, 5 * l + 1, 3, G);
+      }
+      // ---------------- C: attention projection + residual
+      {
+        bp = lane < RAP ? a.bpr[l * E + w * RAP + lane] : 0.f;  // request for E
+        float x[PE];
+        wt.start(5 * l + 1);
+        if (!poll_vec<PE>(a.attn_t + (size_t)l * E, epB, x, lane, wt)) { abort_all(); return; }
+#pragma unroll
+        for (int j = 0; j < PE; j++) xs[lane + 64 * j] = x[j];
+        if (lane == 0) stamp(a, step, 5 * l + 2, 0, G);
         if (lane == 0) flag[0] = 0;
         wg_barrier();
+        if (lane == 0) stamp(a, step, 5 * l + 2, 1, G);
         wg_barrier();
+        if (lane == 0) stamp(a, step, 5 * l + 2, 2, G);
         if (lane < RAP) {
           const int o = w * RAP + lane;
-          const float mix = row_total<S, E>(part, lane) + a.bap[l * E + o];
+          const float mix = part[lane] + ba;
           res = res + mix;
           tst(a.xa_t + (size_t)l * E + o, res, epC);
         }
+        if (lane == 0) stamp(a, step, 5 * l + 2, 3, G);
       }
       // ---------------- D: LayerNorm 2 + fc + gelu_new
       {
-        float x[PE], g[PE], b[PE];
-#pragma unroll
-        for (int j = 0; j < PE; j++) {
-          g[j] = a.ln2w[l * E + lane + 64 * j];
-          b[j] = a.ln2b[l * E + lane + 64 * j];
-        }
-        wt.t0 = wall_clock64();
-        wt.phase = 5 * l + 2;
+        constexpr int R = 4 * RAP;
+        // requests for the next A (or for the head after the last layer)
+        if (l + 1 < a.L) fetch_a(l + 1);
+        else fetch_ln(gf, bf, a.lnfw, a.lnfb);
+        float x[PE];
+        wt.start(5 * l + 2);
         if (!poll_vec<PE>(a.xa_t + (size_t)l * E, epC, x, lane, wt)) { abort_all(); return; }
-        layernorm_to_lds<E>(x, g, b, a.eps, xs, lane);
+        layernorm_to_lds<E>(x, g2, b2, a.eps, xs, lane);
+        if (lane == 0) stamp(a, step, 5 * l + 3, 0, G);
         if (lane == 0) flag[0] = 0;
         wg_barrier();
+        if (lane == 0) stamp(a, step, 5 * l + 3, 1, G);
         wg_barrier();
-        constexpr int R = 4 * RAP;
-        if (lane < R) {
-          const int o = w * R + lane;
-          const float f = row_total<S, E>(part, lane) + a.bfc[l * F + o];
-          tst(a.act_t + (size_t)l * F + o, gelu_new(f), epD);
-        }
+        if (lane == 0) stamp(a, step, 5 * l + 3, 2, G);
+        if (lane < R) tst(a.act_t + (size_t)l * F + w * R + lane, gelu_new(part[lane] + bfc), epD);
+        if (lane == 0) stamp(a, step, 5 * l + 3, 3, G);
       }
       // ---------------- E: MLP projection + residual
       {
         float x[PF];
-        wt.t0 = wall_clock64();
-        wt.phase = 5 * l + 3;
+        wt.start(5 * l + 3);
         if (!poll_vec<PF>(a.act_t + (size_t)l * F, epD, x, lane, wt)) { abort_all(); return; }
 #pragma unroll
         for (int j = 0; j < PF; j++) xs[lane + 64 * j] = x[j];
+        if (lane == 0) stamp(a, step, 5 * l + 4, 0, G);
         if (lane == 0) flag[0] = 0;
         wg_barrier();
+        if (lane == 0) stamp(a, step, 5 * l + 4, 1, G);
         wg_barrier();
+        if (lane == 0) stamp(a, step, 5 * l + 4, 2, G);
         if (lane < RAP) {
           const int o = w * RAP + lane;
-          const float mix = row_total<S, F>(part, lane) + a.bpr[l * E + o];
+          const float mix = part[lane] + bp;
           res = res + mix;
           tst(a.xb_t + (size_t)l * E + o, res, epE);
         }
+        if (lane == 0) stamp(a, step, 5 * l + 4, 3, G);
       }
     }
     // ---------------- H: final LayerNorm + head + local argmax
     {
-      const uint32_t epH = epoch_of<S>(a, step, 5 * a.L);
-      float x[PE], g[PE], b[PE];
-#pragma unroll
-      for (int j = 0; j < PE; j++) {
-        g[j] = a.lnfw[lane + 64 * j];
-        b[j] = a.lnfb[lane + 64 * j];
-      }
-      wt.t0 = wall_clock64();
-      wt.phase = 5 * a.L - 1;
+      const uint32_t epH = epoch_of(a, step, 5 * a.L);
+      fetch_a(0);  // request for the next step's first layer
+      float x[PE];
+      wt.start(5 * a.L - 1);
       if (!poll_vec<PE>(a.xb_t + (size_t)(a.L - 1) * E, epH - 1, x, lane, wt)) { abort_all(); return; }
-      layernorm_to_lds<E>(x, g, b, a.eps, xs, lane);
+      layernorm_to_lds<E>(x, gf, bf, a.eps, xs, lane);
+      if (lane == 0) stamp(a, step, 5 * a.L, 0, G);
       if (lane == 0) flag[0] = 0;
       wg_barrier();
+      if (lane == 0) stamp(a, step, 5 * a.L, 1, G);
       wg_barrier();
+      if (lane == 0) stamp(a, step, 5 * a.L, 2, G);
       const int hr0 = (int)(((long long)w * a.V) / G);
       const int hr1 = (int)(((long long)(w + 1) * a.V) / G);
       const int nr = hr1 - hr0;
       float bv = -INFINITY;
       uint32_t bi = 0xffffffffu;
       for (int r = lane; r < nr; r += 64) {
-        const float v = row_total<S, E>(part, r);
+        const float v = part[r];
         a.logits[hr0 + r] = v;
         if (v > bv || (v == bv && (uint32_t)(hr0 + r) < bi)) { bv = v; bi = (uint32_t)(hr0 + r); }
       }
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {
-        const float ov = __shfl_xor(bv, m, 64);
-        const uint32_t oi = (uint32_t)__shfl_xor((int)bi, m, 64);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-      }
+      bi = wave_argmax(bv, bi, &bv);
       if (lane == 0) {
         tst(a.amax_t + w, bv, epH);
         tst_u(a.amax_t + G + w, bi, epH);
       }
+      if (lane == 0) stamp(a, step, 5 * a.L, 3, G);
     }
   }
   // the last step's greedy id
   if (w == 0) {
-    const uint32_t ep = epoch_of<S>(a, a.nsteps - 1, 5 * a.L);
-    wt.t0 = wall_clock64();
-    wt.phase = 5 * a.L;
-    float bv = -INFINITY;
-    uint32_t bi = 0xffffffffu;
-    while (true) {
-      bool ok = true;
-      float v = -INFINITY;
-      uint32_t idx = 0xffffffffu;
-      for (int g0 = lane; g0 < G; g0 += 64) {
-        const uint64_t xv = tld(a.amax_t + g0), xi = tld(a.amax_t + G + g0);
-        ok &= ((uint32_t)(xv >> 32) == ep) && ((uint32_t)(xi >> 32) == ep);
-        const float cv = __uint_as_float((uint32_t)xv);
-        const uint32_t ci = (uint32_t)xi;
-        if (cv > v || (cv == v && ci < idx)) { v = cv; idx = ci; }
-      }
-      if (__all(ok)) { bv = v; bi = idx; break; }
-      if (wt.expired()) return;
-      __builtin_amdgcn_s_sleep(1);
-    }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const float ov = __shfl_xor(bv, m, 64);
-      const uint32_t oi = (uint32_t)__shfl_xor((int)bi, m, 64);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
+    uint32_t bi = 0;
+    wt.start(5 * a.L);
+    if (!reduce_argmax<S>(a, epoch_of(a, a.nsteps - 1, 5 * a.L), lane, wt, bi)) return;
     if (lane == 0 && a.nsteps - 1 >= a.out_from) a.out_ids[a.nsteps - 1 - a.out_from] = (int)bi;
   }
 }
@@ -782,12 +868,9 @@ __global__ void __launch_bounds__(S::NT, 1) decode_kernel(DecodeArgs a) {
   else compute_main<S, WD>(a, lds, tid);
 }
 
-template <class S>
-constexpr size_t lds_bytes() {
-  // the layout needs S::L_TOTAL floats; ask for more than half of the CU's
-  // 160 KB so that exactly one workgroup lands on each CU
-  return 96 * 1024;
-}
+// The layout needs S::L_TOTAL floats; ask for more than half of the CU's
+// 160 KB so that exactly one workgroup lands on each CU.
+constexpr size_t kLdsBytes = 96 * 1024;
 
 template <class S>
 const void *kernel_for(int wd) {
@@ -801,21 +884,21 @@ const void *kernel_for(int wd) {
 
 template <class S>
 hipError_t launch_t(int wd, const DecodeArgs &a, hipStream_t s) {
-  static_assert(S::L_TOTAL * sizeof(float) <= 96 * 1024, "LDS layout too large");
+  static_assert(S::L_TOTAL * sizeof(float) <= kLdsBytes, "LDS layout too large");
   const void *k = kernel_for<S>(wd);
   if (!k) return hipErrorInvalidValue;
   DecodeArgs copy = a;
   void *args[] = {&copy};
-  return hipLaunchCooperativeKernel(k, dim3(S::G), dim3(S::NT), args, lds_bytes<S>(), s);
+  return hipLaunchCooperativeKernel(k, dim3(S::G), dim3(S::NT), args, kLdsBytes, s);
 }
 
 template <class S>
 hipError_t occupancy_t(int wd, int *blocks) {
   const void *k = kernel_for<S>(wd);
   if (!k) return hipErrorInvalidValue;
-  hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes<S>());
+  hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
   if (e != hipSuccess) return e;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k, S::NT, lds_bytes<S>());
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k, S::NT, kLdsBytes);
 }
 
 template <class S>
@@ -824,7 +907,7 @@ void info_t(ShapeInfo *o) {
   o->D = S::D;
   o->G = S::G;
   o->threads = S::NT;
-  o->lds_bytes = lds_bytes<S>();
+  o->lds_bytes = kLdsBytes;
   o->maxch = S::MAXCH;
 }
 

@@ -41,12 +41,14 @@ struct gpt2_ctx {
   int *feed_d = nullptr, *ids_d = nullptr, *err_d = nullptr;
   int *feed_h = nullptr, *ids_h = nullptr, *err_h = nullptr;
   float *logits_h = nullptr;
-  uint64_t *tag_bufs[6] = {};
-  size_t tag_sizes[6] = {};
+  uint64_t *tag_bufs[7] = {};
+  size_t tag_sizes[7] = {};
   uint32_t epoch = 0;
   int filled = 0;
   bool poisoned = false;
   long long timeout_ticks = 0;
+  long long *trace_d = nullptr;   // per-phase timeline of the last run (debug)
+  int trace_steps = 0;
   std::string err;
 
   int fail(int code, const char *fmt, ...) {
@@ -86,6 +88,7 @@ struct gpt2_ctx {
   }
   ~gpt2_ctx() {
     if (stream) (void)hipStreamSynchronize(stream);
+    if (trace_d) (void)hipFree(trace_d);
     for (void *p : dev_allocs) (void)hipFree(p);
     for (void *p : host_allocs) (void)hipHostFree(p);
     if (own_stream) (void)hipStreamDestroy(own_stream);
@@ -150,7 +153,7 @@ int run(gpt2_ctx *c, const int *feed, int n_feed, int pos0, int nsteps, int out_
   const uint64_t used = (uint64_t)nsteps * (uint64_t)(5 * c->L + 1);
   if ((uint64_t)c->epoch + used >= 0xffffff00ull) {
     // epochs would wrap: clear every tagged word (tag 0 is never expected) and restart
-    for (int i = 0; i < 6; i++) {
+    for (int i = 0; i < 7; i++) {
       e = hipMemsetAsync(c->tag_bufs[i], 0, c->tag_sizes[i], c->stream);
       if (e != hipSuccess) return c->device_fail(e, "hipMemsetAsync");
     }
@@ -168,6 +171,12 @@ int run(gpt2_ctx *c, const int *feed, int n_feed, int pos0, int nsteps, int out_
   a.out_from = out_from;
   a.epoch0 = c->epoch;
   a.timeout_ticks = c->timeout_ticks;
+  a.trace = c->trace_d;
+  a.trace_steps = c->trace_d ? c->trace_steps : 0;
+  if (c->trace_d) {
+    e = hipMemsetAsync(c->trace_d, 0, (size_t)c->trace_steps * (5 * c->L + 1) * c->si.G * 4 * 8, c->stream);
+    if (e != hipSuccess) return c->device_fail(e, "trace reset");
+  }
   e = launch_decode(c->E, c->D, c->wd, a, c->stream);
   c->epoch += (uint32_t)used;
   if (e != hipSuccess) return c->device_fail(e, "decode launch");
@@ -253,7 +262,8 @@ int load_impl(gpt2_ctx *c, const gpt2_config *cfg, const gpt2_weights *w) {
   c->tag_sizes[3] = (size_t)L * F * 8;
   c->tag_sizes[4] = (size_t)L * E * 8;
   c->tag_sizes[5] = (size_t)2 * G * 8;
-  for (int i = 0; i < 6; i++) c->tag_bufs[i] = c->dalloc<uint64_t>(c->tag_sizes[i]);
+  c->tag_sizes[6] = (size_t)L * E * 8;
+  for (int i = 0; i < 7; i++) c->tag_bufs[i] = c->dalloc<uint64_t>(c->tag_sizes[i]);
   float *logits = c->dalloc<float>((size_t)V * 4);
   c->ids_d = c->dalloc<int>((size_t)P * 4);
   c->feed_d = c->dalloc<int>((size_t)P * 4);
@@ -267,7 +277,7 @@ int load_impl(gpt2_ctx *c, const gpt2_config *cfg, const gpt2_weights *w) {
       !vc || !logits || !c->ids_d || !c->feed_d || !c->err_d || !c->feed_h || !c->ids_h || !c->err_h ||
       !c->logits_h)
     return c->fail(GPT2_E_NOMEM, "allocation failed");
-  for (int i = 0; i < 6; i++)
+  for (int i = 0; i < 7; i++)
     if (!c->tag_bufs[i]) return c->fail(GPT2_E_NOMEM, "allocation failed");
 
   // ---- small parameters
@@ -321,7 +331,7 @@ int load_impl(gpt2_ctx *c, const gpt2_config *cfg, const gpt2_weights *w) {
     }
     if (e != hipSuccess) return c->device_fail(e, "weight re-layout");
   }
-  for (int i = 0; i < 6 && e == hipSuccess; i++) e = hipMemsetAsync(c->tag_bufs[i], 0, c->tag_sizes[i], s);
+  for (int i = 0; i < 7 && e == hipSuccess; i++) e = hipMemsetAsync(c->tag_bufs[i], 0, c->tag_sizes[i], s);
   if (e == hipSuccess) e = hipMemsetAsync(kc, 0, kv * 4, s);
   if (e == hipSuccess) e = hipMemsetAsync(vc, 0, kv * 4, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
@@ -345,6 +355,7 @@ int load_impl(gpt2_ctx *c, const gpt2_config *cfg, const gpt2_weights *w) {
   a.act_t = c->tag_bufs[3];
   a.xb_t = c->tag_bufs[4];
   a.amax_t = c->tag_bufs[5];
+  a.attn_t = c->tag_bufs[6];
   a.logits = logits;
   a.out_ids = c->ids_d;
   a.err = c->err_d;
@@ -505,6 +516,36 @@ int gpt2_debug_fill_kv(gpt2_ctx *c, float value) {
   if (e == hipSuccess) e = fill_f32(c->base.vc, kv, value, c->stream);
   if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
   if (e != hipSuccess) return c->device_fail(e, "fill kv");
+  return GPT2_OK;
+}
+
+int gpt2_debug_trace(gpt2_ctx *c, int steps, long long *out) {
+  int rc;
+  if (!usable(c, &rc)) return rc;
+  if (steps < 0) return c->fail(GPT2_E_INVAL, "steps must be >= 0");
+  const size_t n = (size_t)c->trace_steps * (5 * c->L + 1) * c->si.G * 4;
+  if (out && c->trace_d) {
+    hipError_t e = hipMemcpyAsync(out, c->trace_d, n * 8, hipMemcpyDeviceToHost, c->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    if (e != hipSuccess) return c->device_fail(e, "trace copy");
+  }
+  if (steps != c->trace_steps) {
+    if (c->trace_d) {
+      (void)hipStreamSynchronize(c->stream);
+      (void)hipFree(c->trace_d);
+      c->trace_d = nullptr;
+    }
+    c->trace_steps = 0;
+    if (steps > 0) {
+      const size_t m = (size_t)steps * (5 * c->L + 1) * c->si.G * 4;
+      if (hipMalloc(&c->trace_d, m * 8) != hipSuccess) {
+        (void)hipGetLastError();
+        c->trace_d = nullptr;
+        return c->fail(GPT2_E_NOMEM, "trace allocation failed");
+      }
+      c->trace_steps = steps;
+    }
+  }
   return GPT2_OK;
 }
 
