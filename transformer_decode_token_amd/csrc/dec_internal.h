@@ -35,13 +35,13 @@ struct DecodeArgs {
   const float *wpe;                  // [P][E]
   const float *lnfw, *lnfb;          // [E]
   float *kc, *vc;                    // [L][H][P][D] KV cache
-  uint64_t *qkv_t;                   // [L][3E]        tagged QKV outputs
+  uint64_t *qkv_t;                   // [L][8][3E]     tagged QKV outputs (8 copies)
   uint64_t *att_t;                   // [L][H][MAXCH][D+2] tagged attention chunk partials
-  uint64_t *attn_t;                  // [L][E]         tagged merged attention output
-  uint64_t *xa_t;                    // [L][E]         tagged residual after attention
-  uint64_t *act_t;                   // [L][F]         tagged gelu activations
-  uint64_t *xb_t;                    // [L][E]         tagged residual after the MLP
-  uint64_t *amax_t;                  // [2][G]         tagged per-workgroup argmax (value, index)
+  uint64_t *attn_t;                  // [L][8][E]      tagged merged attention output
+  uint64_t *xa_t;                    // [L][8][E]      tagged residual after attention
+  uint64_t *act_t;                   // [L][8][F]      tagged gelu activations
+  uint64_t *xb_t;                    // [L][8][E]      tagged residual after the MLP
+  uint64_t *amax_t;                  // [8][2][G]      tagged per-workgroup argmax (value, index)
   float *logits;                     // [V]            logits of the last step
   int *out_ids;                      // greedy ids
   int *err;                          // [4] flag, workgroup, phase, epoch (device-side wait timeout)

@@ -41,6 +41,10 @@
 namespace gpt2dec {
 namespace {
 
+#ifndef G2_HEAD_NT
+#define G2_HEAD_NT 0
+#endif
+constexpr bool HEAD_NT = G2_HEAD_NT != 0;  // head rows: temporal loads (may stay in the memory-side cache)
 constexpr int CHMIN = 64;      // positions per attention chunk before a head is split
 constexpr int PSTRIDE = 256;   // LDS room for row results (>= rows per workgroup)
 
@@ -104,15 +108,23 @@ typedef float g2_v4f __attribute__((ext_vector_type(4)));
 typedef float g2_v2f __attribute__((ext_vector_type(2)));
 typedef unsigned int g2_v2u __attribute__((ext_vector_type(2)));
 
-template <int WD>
+template <int WD, bool NT = true>
 __device__ __forceinline__ Chunk<WD> ld_chunk(const MatW &m, size_t lofs, size_t gc) {
   Chunk<WD> c;
   if constexpr (WD == WD_F32) {
-    const g2_v4f v = __builtin_nontemporal_load(reinterpret_cast<const g2_v4f *>(m.w) + lofs / 4 + gc);
-    c.v = make_float4(v.x, v.y, v.z, v.w);
+    if constexpr (NT) {
+      const g2_v4f v = __builtin_nontemporal_load(reinterpret_cast<const g2_v4f *>(m.w) + lofs / 4 + gc);
+      c.v = make_float4(v.x, v.y, v.z, v.w);
+    } else {
+      c.v = reinterpret_cast<const float4 *>(m.w)[lofs / 4 + gc];
+    }
   } else if constexpr (WD == WD_F16) {
-    const g2_v2u v = __builtin_nontemporal_load(reinterpret_cast<const g2_v2u *>(m.w) + lofs / 4 + gc);
-    c.v = make_uint2(v.x, v.y);
+    if constexpr (NT) {
+      const g2_v2u v = __builtin_nontemporal_load(reinterpret_cast<const g2_v2u *>(m.w) + lofs / 4 + gc);
+      c.v = make_uint2(v.x, v.y);
+    } else {
+      c.v = reinterpret_cast<const uint2 *>(m.w)[lofs / 4 + gc];
+    }
   } else {
     c.q = __builtin_nontemporal_load(reinterpret_cast<const unsigned short *>(m.w) + lofs / 4 + gc);
     const g2_v2f z = __builtin_nontemporal_load(reinterpret_cast<const g2_v2f *>(m.sz) + lofs / 32 + gc / 8);
@@ -230,6 +242,15 @@ __device__ __forceinline__ void st_agent(float *p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ bool tag_is(uint64_t x, uint32_t ep) { return (uint32_t)(x >> 32) == ep; }
+// Every published vector exists in NCOPY copies, one per XCD (workgroup w is
+// taken to run on XCD w % 8): a producer writes all copies, a consumer polls
+// the copy of its own XCD, which spreads the polling over 8x the lines.
+constexpr int NCOPY = 8;
+__device__ __forceinline__ int my_copy() { return (int)(blockIdx.x % NCOPY); }
+__device__ __forceinline__ void tst_all(uint64_t *base, size_t stride, size_t idx, float v, uint32_t ep) {
+#pragma unroll
+  for (int c = 0; c < NCOPY; c++) tst(base + c * stride + idx, v, ep);
+}
 __device__ __forceinline__ float payload(uint64_t x) { return __uint_as_float((uint32_t)x); }
 
 // Bounded waiting: a wait that outlives the time limit, or sees another
@@ -422,7 +443,7 @@ __device__ void compute_main(const DecodeArgs &a, float *lds, int lane) {
         const int r = min(r0 + rl, nr - 1);
         const size_t c0 = (size_t)(hr0 + r) * KC + q;
 #pragma unroll
-        for (int i = 0; i < NPH; i++) b[i] = ld_chunk<HWD>(hm, 0, c0 + (size_t)i * LPR);
+        for (int i = 0; i < NPH; i++) b[i] = ld_chunk<HWD, HEAD_NT>(hm, 0, c0 + (size_t)i * LPR);
       };
       auto consume = [&](const Chunk<HWD>(&b)[NPH], int r0) {
         float acc = 0.f;
@@ -457,7 +478,8 @@ __device__ __forceinline__ bool reduce_argmax(const DecodeArgs &a, uint32_t ep, 
     float v = -INFINITY;
     uint32_t idx = 0xffffffffu;
     for (int g0 = lane; g0 < G; g0 += 64) {
-      const uint64_t xv = tld(a.amax_t + g0), xi = tld(a.amax_t + G + g0);
+      const uint64_t *am = a.amax_t + (size_t)my_copy() * 2 * G;
+      const uint64_t xv = tld(am + g0), xi = tld(am + G + g0);
       ok &= tag_is(xv, ep) && tag_is(xi, ep);
       const float cv = payload(xv);
       const uint32_t ci = (uint32_t)xi;
@@ -633,7 +655,10 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
           }
         } else {
           wt.start(5 * (l - 1) + 4);
-          if (!poll_vec<PE>(a.xb_t + (size_t)(l - 1) * E, epA - 1, x, lane, wt)) { abort_all(); return; }
+          if (!poll_vec<PE>(a.xb_t + ((size_t)(l - 1) * NCOPY + my_copy()) * E, epA - 1, x, lane, wt)) {
+            abort_all();
+            return;
+          }
         }
         layernorm_to_lds<E>(x, g1, b1, a.eps, xs, lane);
         if (lane == 0) stamp(a, step, 5 * l + 0, 0, G);
@@ -642,7 +667,7 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
         if (lane == 0) stamp(a, step, 5 * l + 0, 1, G);
         wg_barrier();
         if (lane == 0) stamp(a, step, 5 * l + 0, 2, G);
-        if (lane < R) tst(a.qkv_t + (size_t)l * 3 * E + w * R + lane, part[lane] + bq, epA);
+        if (lane < R) tst_all(a.qkv_t + (size_t)l * NCOPY * 3 * E, 3 * E, w * R + lane, part[lane] + bq, epA);
         if (lane == 0) stamp(a, step, 5 * l + 0, 3, G);
       }
       // ---------------- B: attention chunk (control wave only)
@@ -650,7 +675,7 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
         AttChunk<S> at;
         at.fetch(a, l, ih, it0, itg, lane);  // cache rows: written at earlier steps
         wt.start(5 * l + 0);
-        const uint64_t *qk = a.qkv_t + (size_t)l * 3 * E + ih * D + (lane % D);
+        const uint64_t *qk = a.qkv_t + ((size_t)l * NCOPY + my_copy()) * 3 * E + ih * D + (lane % D);
         while (true) {
           const uint64_t xq = tld(qk);
           uint64_t xk = (uint64_t)epA << 32, xv = (uint64_t)epA << 32;
@@ -683,11 +708,12 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
         const int g = lane / D4, d4 = lane % D4;
         if (nch == 1) {
           if (g == 0) {
-            uint64_t *dst = a.attn_t + (size_t)l * E + ih * D + 4 * d4;
-            tst(dst + 0, o.x / lsum, epB);
-            tst(dst + 1, o.y / lsum, epB);
-            tst(dst + 2, o.z / lsum, epB);
-            tst(dst + 3, o.w / lsum, epB);
+            uint64_t *dst = a.attn_t + (size_t)l * NCOPY * E;
+            const size_t ix = ih * D + 4 * d4;
+            tst_all(dst, E, ix + 0, o.x / lsum, epB);
+            tst_all(dst, E, ix + 1, o.y / lsum, epB);
+            tst_all(dst, E, ix + 2, o.z / lsum, epB);
+            tst_all(dst, E, ix + 3, o.w / lsum, epB);
           }
         } else if (ic > 0) {
           uint64_t *dst = a.att_t + ((size_t)(l * H + ih) * S::MAXCH + ic) * (D + 2);
@@ -747,11 +773,12 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
             }
           }
           if (g == 0) {
-            uint64_t *dst = a.attn_t + (size_t)l * E + ih * D + 4 * d4;
-            tst(dst + 0, O.x / Ls, epB);
-            tst(dst + 1, O.y / Ls, epB);
-            tst(dst + 2, O.z / Ls, epB);
-            tst(dst + 3, O.w / Ls, epB);
+            uint64_t *dst = a.attn_t + (size_t)l * NCOPY * E;
+            const size_t ix = ih * D + 4 * d4;
+            tst_all(dst, E, ix + 0, O.x / Ls, epB);
+            tst_all(dst, E, ix + 1, O.y / Ls, epB);
+            tst_all(dst, E, ix + 2, O.z / Ls, epB);
+            tst_all(dst, E, ix + 3, O.w / Ls, epB);
           }
         }
         if (lane == 0) stamp(a, step, 5 * l + 1, 3, G);
@@ -761,7 +788,7 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
         bp = lane < RAP ? a.bpr[l * E + w * RAP + lane] : 0.f;  // request for E
         float x[PE];
         wt.start(5 * l + 1);
-        if (!poll_vec<PE>(a.attn_t + (size_t)l * E, epB, x, lane, wt)) { abort_all(); return; }
+        if (!poll_vec<PE>(a.attn_t + ((size_t)l * NCOPY + my_copy()) * E, epB, x, lane, wt)) { abort_all(); return; }
 #pragma unroll
         for (int j = 0; j < PE; j++) xs[lane + 64 * j] = x[j];
         if (lane == 0) stamp(a, step, 5 * l + 2, 0, G);
@@ -774,7 +801,7 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
           const int o = w * RAP + lane;
           const float mix = part[lane] + ba;
           res = res + mix;
-          tst(a.xa_t + (size_t)l * E + o, res, epC);
+          tst_all(a.xa_t + (size_t)l * NCOPY * E, E, o, res, epC);
         }
         if (lane == 0) stamp(a, step, 5 * l + 2, 3, G);
       }
@@ -786,7 +813,7 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
         else fetch_ln(gf, bf, a.lnfw, a.lnfb);
         float x[PE];
         wt.start(5 * l + 2);
-        if (!poll_vec<PE>(a.xa_t + (size_t)l * E, epC, x, lane, wt)) { abort_all(); return; }
+        if (!poll_vec<PE>(a.xa_t + ((size_t)l * NCOPY + my_copy()) * E, epC, x, lane, wt)) { abort_all(); return; }
         layernorm_to_lds<E>(x, g2, b2, a.eps, xs, lane);
         if (lane == 0) stamp(a, step, 5 * l + 3, 0, G);
         if (lane == 0) flag[0] = 0;
@@ -794,14 +821,14 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
         if (lane == 0) stamp(a, step, 5 * l + 3, 1, G);
         wg_barrier();
         if (lane == 0) stamp(a, step, 5 * l + 3, 2, G);
-        if (lane < R) tst(a.act_t + (size_t)l * F + w * R + lane, gelu_new(part[lane] + bfc), epD);
+        if (lane < R) tst_all(a.act_t + (size_t)l * NCOPY * F, F, w * R + lane, gelu_new(part[lane] + bfc), epD);
         if (lane == 0) stamp(a, step, 5 * l + 3, 3, G);
       }
       // ---------------- E: MLP projection + residual
       {
         float x[PF];
         wt.start(5 * l + 3);
-        if (!poll_vec<PF>(a.act_t + (size_t)l * F, epD, x, lane, wt)) { abort_all(); return; }
+        if (!poll_vec<PF>(a.act_t + ((size_t)l * NCOPY + my_copy()) * F, epD, x, lane, wt)) { abort_all(); return; }
 #pragma unroll
         for (int j = 0; j < PF; j++) xs[lane + 64 * j] = x[j];
         if (lane == 0) stamp(a, step, 5 * l + 4, 0, G);
@@ -814,7 +841,7 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
           const int o = w * RAP + lane;
           const float mix = part[lane] + bp;
           res = res + mix;
-          tst(a.xb_t + (size_t)l * E + o, res, epE);
+          tst_all(a.xb_t + (size_t)l * NCOPY * E, E, o, res, epE);
         }
         if (lane == 0) stamp(a, step, 5 * l + 4, 3, G);
       }
@@ -825,7 +852,10 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
       fetch_a(0);  // request for the next step's first layer
       float x[PE];
       wt.start(5 * a.L - 1);
-      if (!poll_vec<PE>(a.xb_t + (size_t)(a.L - 1) * E, epH - 1, x, lane, wt)) { abort_all(); return; }
+      if (!poll_vec<PE>(a.xb_t + ((size_t)(a.L - 1) * NCOPY + my_copy()) * E, epH - 1, x, lane, wt)) {
+        abort_all();
+        return;
+      }
       layernorm_to_lds<E>(x, gf, bf, a.eps, xs, lane);
       if (lane == 0) stamp(a, step, 5 * a.L, 0, G);
       if (lane == 0) flag[0] = 0;
@@ -845,8 +875,11 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
       }
       bi = wave_argmax(bv, bi, &bv);
       if (lane == 0) {
-        tst(a.amax_t + w, bv, epH);
-        tst_u(a.amax_t + G + w, bi, epH);
+        #pragma unroll
+        for (int c = 0; c < NCOPY; c++) {
+          tst(a.amax_t + (size_t)c * 2 * G + w, bv, epH);
+          tst_u(a.amax_t + (size_t)c * 2 * G + G + w, bi, epH);
+        }
       }
       if (lane == 0) stamp(a, step, 5 * a.L, 3, G);
     }

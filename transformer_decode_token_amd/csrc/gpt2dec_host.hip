@@ -256,13 +256,15 @@ int load_impl(gpt2_ctx *c, const gpt2_config *cfg, const gpt2_weights *w) {
   void *head16 = c->wd == WD_F16 ? c->dalloc<void>((size_t)V * E * 2) : nullptr;
   const size_t kv = (size_t)L * H * P * D;
   float *kc = c->dalloc<float>(kv * 4), *vc = c->dalloc<float>(kv * 4);
-  c->tag_sizes[0] = (size_t)L * 3 * E * 8;
+  // published vectors exist in 8 copies (one per XCD); chunk partials have one reader
+  const size_t NC = 8;
+  c->tag_sizes[0] = NC * L * 3 * E * 8;
   c->tag_sizes[1] = (size_t)L * H * c->si.maxch * (D + 2) * 8;
-  c->tag_sizes[2] = (size_t)L * E * 8;
-  c->tag_sizes[3] = (size_t)L * F * 8;
-  c->tag_sizes[4] = (size_t)L * E * 8;
-  c->tag_sizes[5] = (size_t)2 * G * 8;
-  c->tag_sizes[6] = (size_t)L * E * 8;
+  c->tag_sizes[2] = NC * L * E * 8;
+  c->tag_sizes[3] = NC * L * F * 8;
+  c->tag_sizes[4] = NC * L * E * 8;
+  c->tag_sizes[5] = NC * 2 * G * 8;
+  c->tag_sizes[6] = NC * L * E * 8;
   for (int i = 0; i < 7; i++) c->tag_bufs[i] = c->dalloc<uint64_t>(c->tag_sizes[i]);
   float *logits = c->dalloc<float>((size_t)V * 4);
   c->ids_d = c->dalloc<int>((size_t)P * 4);
