@@ -12,17 +12,20 @@
 //   E: projection linear + bias + residual
 // and finally H: final LayerNorm + tied output head + argmax.
 //
-// Work split.  Every workgroup owns RAP consecutive output rows of each
-// E-output matrix (3*RAP of QKV, 4*RAP of fc), so the 256 workgroups of the
-// 124M shape each stream an equal 1/256 of every matrix, and a contiguous
-// 1/256 of the head.  Inside a workgroup each output row is owned by a segment
-// of LPR lanes (16 or 64), so a row's dot product ends in one short DPP
-// reduction and all rows reduce at once.  A workgroup is one control wave plus
-// NCW compute waves:
-//   * compute waves stream the workgroup's weight slices through two register
-//     buffers, requesting each slice one phase before it is used;
-//   * the control wave waits for the inputs of each phase, normalises them
-//     into LDS, runs the attention chunk, and publishes the phase's outputs.
+// Work split.  The workgroups form four disjoint sets, one per block matrix
+// (QKV, attention projection, fc, MLP projection); a workgroup owns an equal
+// share of consecutive output rows of its set's matrix in every layer, and
+// all workgroups share the output head by contiguous vocabulary rows.  Inside
+// a workgroup an output row belongs to a segment of LPR lanes, so a row's dot
+// product ends in one short DPP reduction.  A workgroup is one control wave
+// plus NCW compute waves:
+//   * the compute waves hold the workgroup's slice of one layer in registers
+//     and request the next layer's slice as soon as the phase is done, so the
+//     weights stream in during the other sets' phases;
+//   * the control wave waits for the inputs of its phase, normalises them
+//     into LDS, runs an attention chunk when it has one, and publishes.
+// Each phase's inputs therefore come from, and go to, a few dozen workgroups
+// rather than all of them, which shortens every hand-over.
 // Batch 1 makes every linear a matrix-vector product (0.5 flop per fp32 byte),
 // so there is no MFMA here: the kernel is bound by weight bytes and by the
 // latency of the 5L+1 dependent phases of a token.
@@ -48,17 +51,22 @@ constexpr bool HEAD_NT = G2_HEAD_NT != 0;  // head rows: temporal loads (may sta
 constexpr int CHMIN = 64;      // positions per attention chunk before a head is split
 constexpr int PSTRIDE = 256;   // LDS room for row results (>= rows per workgroup)
 
-template <int E_, int D_, int NCW_, int RAP_, int MAXCH_, int LPRH_>
+template <int E_, int D_, int NCW_, int MAXCH_, int LPRH_, int LPR_, int NQ_, int NA_, int NF_, int NM_>
 struct Shape {
   static constexpr int E = E_, D = D_, H = E_ / D_, F = 4 * E_;
   static constexpr int NCW = NCW_;        // compute waves
   static constexpr int NL = 64 * NCW_;    // compute lanes
   static constexpr int NT = NL + 64;      // threads: compute waves + control wave
-  static constexpr int RAP = RAP_;        // rows of an E-output matrix per workgroup
-  static constexpr int G = E_ / RAP_;     // workgroups
   static constexpr int MAXCH = MAXCH_;    // attention chunks per head at most
   static constexpr int LPRH = LPRH_;      // lanes per head row
+  static constexpr int LPR = LPR_;        // lanes per row of a block matrix
+  // Workgroup sets, one per block matrix, over consecutive blockIdx ranges in
+  // this order: QKV, attention projection, fc, MLP projection.
+  static constexpr int NQ = NQ_, NA = NA_, NF = NF_, NM = NM_;
+  static constexpr int G = NQ_ + NA_ + NF_ + NM_;  // workgroups
   static_assert(E_ % D_ == 0 && E_ % 64 == 0 && D_ <= 64 && 64 % (D_ / 4) == 0, "shape");
+  static_assert((3 * E_) % NQ_ == 0 && E_ % NA_ == 0 && (4 * E_) % NF_ == 0 && E_ % NM_ == 0,
+                "equal row shares");
   static_assert(H * MAXCH <= G, "one attention chunk per workgroup at most");
   // LDS layout (floats)
   static constexpr int L_XS = 0;                         // [F] phase input vector
@@ -71,26 +79,42 @@ struct Shape {
   static constexpr int L_TOTAL = L_FLAG + 4;
 };
 
-// 124M shape: 256 workgroups x (3 compute + 1 control) waves.
-using ShapeS = Shape<768, 64, 3, 3, 16, 16>;
-// tiny shape: 32 workgroups x (2 compute + 1 control) waves.
-using ShapeT = Shape<128, 32, 2, 4, 8, 8>;
+// 124M shape: 256 workgroups x (3 compute + 1 control) waves in sets of 64
+// (QKV, 36 rows each), 32 (attention projection, 24 rows), 96 (fc, 32 rows)
+// and 64 (MLP projection, 12 rows); each set streams an equal share of its
+// matrix, so every workgroup reads 74 to 147 KB of fp32 weights per layer.
+using ShapeS = Shape<768, 64, 3, 16, 16, 16, 64, 32, 96, 64>;
+// tiny shape: 32 workgroups x (2 compute + 1 control) waves, sets 8/4/16/4.
+using ShapeT = Shape<128, 32, 2, 8, 8, 8, 8, 4, 16, 4>;
 
-constexpr int lpr_for(int R, int KC, int NL) {
-  int l = 64;
-  while (l > 1 && (R * l > NL || KC % l != 0)) l >>= 1;
-  return l;
+// The workgroup sets.  Set SET owns the R consecutive rows rank*R.. of its
+// [ROWS][K] matrix for every layer.  Inside the workgroup, LPR lanes share a
+// row (chunks lane%LPR + LPR*i, i < CPR), RP = NL/LPR rows are covered per
+// pass and NP passes cover the R rows, so each lane holds NB = NP*CPR weight
+// chunks and reuses each of its CPR input chunks NP times.
+enum { SET_Q = 0, SET_A = 1, SET_F = 2, SET_M = 3 };
+// Lanes per row: the shape's default, doubled (up to 64) while a lane would
+// need more than 12 input chunks, so that a dot product reads at most 12
+// chunks of the input vector from LDS.
+constexpr int lpr_for(int KC, int lpr) {
+  while (KC / lpr > 12 && lpr < 64) lpr *= 2;
+  return lpr;
 }
-
-// Geometry of one workgroup slice: R rows of length K in 4-element chunks.
-// Lane l < R*LPR owns row l/LPR and the chunks (l%LPR) + LPR*i, i < NPASS.
-template <class S, int R, int K>
-struct Geo {
+template <class S, int SET>
+struct Set {
+  static constexpr int FIRST = SET == SET_Q ? 0 : SET == SET_A ? S::NQ : SET == SET_F ? S::NQ + S::NA
+                                                                                      : S::NQ + S::NA + S::NF;
+  static constexpr int N = SET == SET_Q ? S::NQ : SET == SET_A ? S::NA : SET == SET_F ? S::NF : S::NM;
+  static constexpr int ROWS = SET == SET_Q ? 3 * S::E : SET == SET_F ? S::F : S::E;
+  static constexpr int K = SET == SET_M ? S::F : S::E;
+  static constexpr int R = ROWS / N;
   static constexpr int KC = K / 4;
-  static constexpr int LPR = lpr_for(R, KC, S::NL);
-  static constexpr int NPASS = KC / LPR;
-  static constexpr int ACTIVE = R * LPR;
-  static_assert(ACTIVE <= S::NL && KC % LPR == 0 && LPR >= 4, "row geometry");
+  static constexpr int LPR = lpr_for(KC, S::LPR);
+  static constexpr int RP = S::NL / LPR;
+  static constexpr int NP = (R + RP - 1) / RP;
+  static constexpr int CPR = KC / LPR;
+  static constexpr int NB = NP * CPR;
+  static_assert(KC % LPR == 0 && S::NL % LPR == 0 && R <= 64 && R <= PSTRIDE, "slice geometry");
 };
 
 // ---- weight chunks: 4 consecutive inputs of one output row ----------------
@@ -182,6 +206,18 @@ __device__ __forceinline__ float seg_sum_last(float v) {
   if constexpr (W >= 32) v += dpp_or<0x142, 0xA>(v, 0.f);
   if constexpr (W >= 64) v += dpp_or<0x143, 0xC>(v, 0.f);
   return v;
+}
+// The last lane's value of each W-lane segment, in every lane of the segment
+// (16-lane rows: one DPP row broadcast; otherwise a lane permute).
+template <int W>
+__device__ __forceinline__ float seg_bcast_last(float v, int lane) {
+  if constexpr (W == 16) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x15F, 0xF, 0xF, false));
+  } else if constexpr (W == 64) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  } else {
+    return __shfl(v, lane | (W - 1));
+  }
 }
 // Whole-wave sum / max, the same bits in every lane.
 __device__ __forceinline__ float wave_sum_all(float v) {
@@ -278,16 +314,28 @@ struct Waiter {
   }
 };
 
-// Poll PER*64 tagged floats (element lane + 64*j) into v until all carry ep.
+// A lane's share of a polled vector: element vidx(lane, j) for j < PER, in
+// pairs of neighbours, so that one 16-byte load brings two tagged words.
+__device__ __forceinline__ int vidx(int lane, int j) { return 128 * (j >> 1) + 2 * lane + (j & 1); }
+
+// Poll the PER*64 tagged floats at src (lane share as vidx) into v until all
+// carry ep.  Each 8-byte half of a 16-byte load is one word written by one
+// atomic store, so a half is either the old word or the new one; the loads
+// use device scope (sc1) like the atomic loads elsewhere.
+constexpr int AUX_SC1 = 16;
 template <int PER>
 __device__ bool poll_vec(const uint64_t *src, uint32_t ep, float (&v)[PER], int lane, Waiter &wt) {
+  static_assert(PER % 2 == 0, "words are polled in pairs");
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint64_t *>(src), (short)0, PER * 64 * 8,
+                                                    0x00020000);
   while (true) {
     bool ok = true;
 #pragma unroll
-    for (int j = 0; j < PER; j++) {
-      const uint64_t x = tld(src + lane + 64 * j);
-      v[j] = payload(x);
-      ok &= tag_is(x, ep);
+    for (int j = 0; j < PER; j += 2) {
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, vidx(lane, j) * 8, 0, AUX_SC1);
+      v[j] = __uint_as_float(x[0]);
+      v[j + 1] = __uint_as_float(x[2]);
+      ok &= (x[1] == ep) && (x[3] == ep);
     }
     if (__all(ok)) return true;
     if (wt.expired()) return false;
@@ -295,7 +343,7 @@ __device__ bool poll_vec(const uint64_t *src, uint32_t ep, float (&v)[PER], int 
   }
 }
 
-// LayerNorm of E values held lane-strided (element lane + 64*j) into LDS,
+// LayerNorm of E values held as a lane share (element vidx(lane, j)) into LDS,
 // following the model file's layernorm kernel: mean, biased variance,
 // ((x - mean) * rsqrt(var + eps)) * gamma + beta.
 template <int E>
@@ -316,7 +364,7 @@ __device__ __forceinline__ void layernorm_to_lds(const float (&x)[E / 64], const
   const float var = wave_sum_all(q) * (1.0f / (float)E);
   const float r = 1.0f / sqrtf(var + eps);
 #pragma unroll
-  for (int j = 0; j < PER; j++) dst[lane + 64 * j] = __builtin_fmaf((x[j] - mean) * r, g[j], b[j]);
+  for (int j = 0; j < PER; j++) dst[vidx(lane, j)] = __builtin_fmaf((x[j] - mean) * r, g[j], b[j]);
 }
 
 __device__ __forceinline__ float gelu_new(float f) {
@@ -351,119 +399,139 @@ __device__ __forceinline__ uint32_t epoch_of(const DecodeArgs &a, int step, int 
 }
 
 // ---- compute waves ---------------------------------------------------------
-template <class S, int R, int K, int WD, int NB>
-__device__ __forceinline__ void load_slice(Chunk<WD> (&w)[NB], const MatW &m, int layer, int lane) {
-  using Gm = Geo<S, R, K>;
-  static_assert(Gm::NPASS <= NB, "register buffer too small");
-  // Lanes past the slice re-read the last row (same addresses as its own
-  // lanes in the same wave; their results are discarded).  Keeping every load
-  // unconditional lets the compiler count outstanding loads exactly.
-  const int r = min(lane / Gm::LPR, R - 1);
-  const size_t lofs = (size_t)layer * (size_t)(R * S::G) * K;
-  const size_t c0 = ((size_t)blockIdx.x * R + r) * Gm::KC + (lane % Gm::LPR);
+// Request this workgroup's slice of one layer of its set's matrix.  Lanes of a
+// pass past the slice re-read its last row (same addresses as other lanes of
+// the wave, results discarded), so every load is unconditional.
+template <class ST, int WD>
+__device__ __forceinline__ void load_set(Chunk<WD> (&b)[ST::NB], const MatW &m, int layer, int rank, int lane) {
+  const size_t lofs = (size_t)layer * ST::ROWS * ST::K;
+  const int q = lane % ST::LPR;
 #pragma unroll
-  for (int i = 0; i < Gm::NPASS; i++) w[i] = ld_chunk<WD>(m, lofs, c0 + (size_t)i * Gm::LPR);
+  for (int t = 0; t < ST::NP; t++) {
+    const int r = min(t * ST::RP + lane / ST::LPR, ST::R - 1);
+    const size_t c0 = ((size_t)rank * ST::R + r) * ST::KC + q;
+#pragma unroll
+    for (int i = 0; i < ST::CPR; i++) b[t * ST::CPR + i] = ld_chunk<WD>(m, lofs, c0 + (size_t)i * ST::LPR);
+  }
 }
 
-// Row results of the slice into part[0..R).
-template <class S, int R, int K, int WD, int NB>
-__device__ __forceinline__ void slice_dot(const Chunk<WD> (&w)[NB], const float *xs, float *part, int lane) {
-  using Gm = Geo<S, R, K>;
-  static_assert(Gm::NPASS <= NB, "register buffer too small");
-  const int q = lane % Gm::LPR;
-  float a = 0.f;
+// Row results of the slice (input vector in LDS) into part[0..R): each lane
+// sums its chunks in order, then a DPP reduction over the row's LPR lanes.
+template <class ST, int WD>
+__device__ __forceinline__ void dot_set(const Chunk<WD> (&b)[ST::NB], const float *xs, float *part, int lane) {
+  const int q = lane % ST::LPR;
+  // all input chunks first: one burst of LDS reads instead of one round trip per chunk
+  float4 xv[ST::CPR];
 #pragma unroll
-  for (int i = 0; i < Gm::NPASS; i++)
-    a = dot4(deq<WD>(w[i]), reinterpret_cast<const float4 *>(xs)[i * Gm::LPR + q], a);
-  a = seg_sum_last<Gm::LPR>(a);
-  if (lane < Gm::ACTIVE && q == Gm::LPR - 1) part[lane / Gm::LPR] = a;
+  for (int i = 0; i < ST::CPR; i++) xv[i] = reinterpret_cast<const float4 *>(xs)[i * ST::LPR + q];
+  float acc[ST::NP];
+#pragma unroll
+  for (int t = 0; t < ST::NP; t++) acc[t] = 0.f;
+#pragma unroll
+  for (int i = 0; i < ST::CPR; i++) {
+#pragma unroll
+    for (int t = 0; t < ST::NP; t++) acc[t] = dot4(deq<WD>(b[t * ST::CPR + i]), xv[i], acc[t]);
+  }
+#pragma unroll
+  for (int t = 0; t < ST::NP; t++) {
+    const float v = seg_sum_last<ST::LPR>(acc[t]);
+    const int r = t * ST::RP + lane / ST::LPR;
+    if (q == ST::LPR - 1 && r < ST::R) part[r] = v;
+  }
 }
 
-// Compute waves.  Two register buffers alternate: when a phase's inputs are
-// ready, the slice of the next phase is requested into the other buffer and
-// the current slice (requested one phase earlier) is consumed, so every slice
-// streams in while the previous phase computes, publishes and waits.
+// Output head over this workgroup's contiguous vocabulary rows, RB rows per
+// batch, two batches in flight; the first two are requested before the final
+// LayerNorm is ready.  Batches past the last row re-read that row, which
+// keeps every load unconditional.  False when the control wave aborted.
 template <class S, int WD>
-__device__ void compute_main(const DecodeArgs &a, float *lds, int lane) {
-  constexpr int E = S::E, F = S::F, RAP = S::RAP;
-  constexpr int NB = Geo<S, 3 * RAP, E>::NPASS > Geo<S, RAP, F>::NPASS ? Geo<S, 3 * RAP, E>::NPASS
-                                                                      : Geo<S, RAP, F>::NPASS;
-  static_assert(Geo<S, 4 * RAP, E>::NPASS <= NB && Geo<S, RAP, E>::NPASS <= NB, "buffer size");
+__device__ bool head_rows(const DecodeArgs &a, float *lds, int lane) {
+  constexpr int KC = S::E / 4, LPR = S::LPRH, NPH = KC / LPR, RB = S::NL / LPR;
+  static_assert(KC % LPR == 0 && S::NL % LPR == 0, "head geometry");
+  constexpr int HWD = (WD == WD_F16) ? WD_F16 : WD_F32;
   const int *flag = reinterpret_cast<const int *>(lds + S::L_FLAG);
   float *part = lds + S::L_PART;
   const float *xs = lds + S::L_XS;
-  Chunk<WD> b0[NB], b1[NB];
-  load_slice<S, 3 * RAP, E, WD>(b0, a.qkv, 0, lane);
-  for (int step = 0; step < a.nsteps; step++) {
-    for (int l = 0; l < a.L; l++) {
-      // A: QKV (b0); request the attention projection into b1
-      wg_barrier();
-      if (flag[0]) return;
-      load_slice<S, RAP, E, WD>(b1, a.ap, l, lane);
-      slice_dot<S, 3 * RAP, E, WD>(b0, xs, part, lane);
-      wg_barrier();
-      // B: attention runs on the control wave alone
-      // C: attention projection (b1); request fc into b0
-      wg_barrier();
-      if (flag[0]) return;
-      load_slice<S, 4 * RAP, E, WD>(b0, a.fc, l, lane);
-      slice_dot<S, RAP, E, WD>(b1, xs, part, lane);
-      wg_barrier();
-      // D: fc (b0); request the MLP projection into b1
-      wg_barrier();
-      if (flag[0]) return;
-      load_slice<S, RAP, F, WD>(b1, a.pr, l, lane);
-      slice_dot<S, 4 * RAP, E, WD>(b0, xs, part, lane);
-      wg_barrier();
-      // E: MLP projection (b1); request the next layer's QKV into b0
-      wg_barrier();
-      if (flag[0]) return;
-      load_slice<S, 3 * RAP, E, WD>(b0, a.qkv, (l + 1 < a.L) ? l + 1 : 0, lane);
-      slice_dot<S, RAP, F, WD>(b1, xs, part, lane);
-      wg_barrier();
-    }
-    // H: output head over this workgroup's vocabulary rows, RB rows per batch,
-    // two batches in flight
-    wg_barrier();
-    if (flag[0]) return;
-    {
-      constexpr int KC = E / 4, LPR = S::LPRH, NPH = KC / LPR, RB = S::NL / LPR;
-      static_assert(KC % LPR == 0 && S::NL % LPR == 0, "head geometry");
-      constexpr int HWD = (WD == WD_F16) ? WD_F16 : WD_F32;
-      const MatW hm{a.head, nullptr};
-      const int hr0 = (int)(((long long)blockIdx.x * a.V) / S::G);
-      const int hr1 = (int)(((long long)(blockIdx.x + 1) * a.V) / S::G);
-      const int nr = hr1 - hr0;
-      const int q = lane % LPR, rl = lane / LPR;
-      float4 xv[NPH];
+  const MatW hm{a.head, nullptr};
+  const int hr0 = (int)(((long long)blockIdx.x * a.V) / S::G);
+  const int hr1 = (int)(((long long)(blockIdx.x + 1) * a.V) / S::G);
+  const int nr = hr1 - hr0;
+  const int q = lane % LPR, rl = lane / LPR;
+  Chunk<HWD> h0[NPH], h1[NPH];
+  auto fetch = [&](Chunk<HWD>(&b)[NPH], int r0) {
+    const int r = min(r0 + rl, nr - 1);
+    const size_t c0 = (size_t)(hr0 + r) * KC + q;
 #pragma unroll
-      for (int i = 0; i < NPH; i++) xv[i] = reinterpret_cast<const float4 *>(xs)[i * LPR + q];
-      Chunk<HWD> h0[NPH], h1[NPH];
-      auto fetch = [&](Chunk<HWD>(&b)[NPH], int r0) {
-        const int r = min(r0 + rl, nr - 1);
-        const size_t c0 = (size_t)(hr0 + r) * KC + q;
-#pragma unroll
-        for (int i = 0; i < NPH; i++) b[i] = ld_chunk<HWD, HEAD_NT>(hm, 0, c0 + (size_t)i * LPR);
-      };
-      auto consume = [&](const Chunk<HWD>(&b)[NPH], int r0) {
-        float acc = 0.f;
-#pragma unroll
-        for (int i = 0; i < NPH; i++) acc = dot4(deq<HWD>(b[i]), xv[i], acc);
-        acc = seg_sum_last<LPR>(acc);
-        if (q == LPR - 1 && r0 + rl < nr) part[r0 + rl] = acc;
-      };
-      if (nr > 0) {
-        fetch(h0, 0);
-        for (int r0 = 0; r0 < nr; r0 += 2 * RB) {
-          if (r0 + RB < nr) fetch(h1, r0 + RB);
-          consume(h0, r0);
-          if (r0 + 2 * RB < nr) fetch(h0, r0 + 2 * RB);
-          if (r0 + RB < nr) consume(h1, r0 + RB);
-        }
-      }
-    }
-    wg_barrier();
+    for (int i = 0; i < NPH; i++) b[i] = ld_chunk<HWD, HEAD_NT>(hm, 0, c0 + (size_t)i * LPR);
+  };
+  if (nr > 0) {
+    fetch(h0, 0);
+    fetch(h1, RB);
   }
+  wg_barrier();
+  if (flag[0]) return false;
+  float4 xv[NPH];
+#pragma unroll
+  for (int i = 0; i < NPH; i++) xv[i] = reinterpret_cast<const float4 *>(xs)[i * LPR + q];
+  auto consume = [&](const Chunk<HWD>(&b)[NPH], int r0) {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < NPH; i++) acc = dot4(deq<HWD>(b[i]), xv[i], acc);
+    acc = seg_sum_last<LPR>(acc);
+    if (q == LPR - 1 && r0 + rl < nr) part[r0 + rl] = acc;
+  };
+  if (nr > 0) {
+    for (int r0 = 0; r0 < nr; r0 += 2 * RB) {
+      consume(h0, r0);
+      fetch(h0, r0 + 2 * RB);
+      consume(h1, r0 + RB);
+      fetch(h1, r0 + 3 * RB);
+    }
+  }
+  wg_barrier();
+  return true;
+}
+
+// Compute waves of a workgroup of set SET.  Its slice of a layer sits in
+// registers from one layer to the next: right after the phase has consumed
+// it (and the control wave has issued the phase's stores, third barrier), the
+// next layer's slice is requested into the same registers, and has a whole
+// layer to arrive.  Sets whose phase comes late in the layer request the next
+// step's first slice only after the output head, whose loads it would delay.
+template <class S, int WD, int SET>
+__device__ void compute_set(const DecodeArgs &a, const MatW &m, float *lds, int lane) {
+  using ST = Set<S, SET>;
+  constexpr bool LATE = (SET == SET_F || SET == SET_M);
+  const int *flag = reinterpret_cast<const int *>(lds + S::L_FLAG);
+  float *part = lds + S::L_PART;
+  const float *xs = lds + S::L_XS;
+  const int rank = (int)blockIdx.x - ST::FIRST;
+  Chunk<WD> b[ST::NB];
+  load_set<ST, WD>(b, m, 0, rank, lane);
+  for (int step = 0; step < a.nsteps; step++) {
+    const bool more = step + 1 < a.nsteps;
+    for (int l = 0; l < a.L; l++) {
+      wg_barrier();
+      if (flag[0]) return;
+      dot_set<ST, WD>(b, xs, part, lane);
+      wg_barrier();
+      wg_barrier();
+      if (l + 1 < a.L) load_set<ST, WD>(b, m, l + 1, rank, lane);
+      else if (more && !LATE) load_set<ST, WD>(b, m, 0, rank, lane);
+    }
+    if (!head_rows<S, WD>(a, lds, lane)) return;
+    wg_barrier();  // the control wave has issued the logits and its argmax
+    if (more && LATE) load_set<ST, WD>(b, m, 0, rank, lane);
+  }
+}
+
+template <class S, int WD>
+__device__ void compute_main(const DecodeArgs &a, float *lds, int lane) {
+  const int w = (int)blockIdx.x;
+  if (w < Set<S, SET_A>::FIRST) compute_set<S, WD, SET_Q>(a, a.qkv, lds, lane);
+  else if (w < Set<S, SET_F>::FIRST) compute_set<S, WD, SET_A>(a, a.ap, lds, lane);
+  else if (w < Set<S, SET_M>::FIRST) compute_set<S, WD, SET_F>(a, a.fc, lds, lane);
+  else compute_set<S, WD, SET_M>(a, a.pr, lds, lane);
 }
 
 // ---- control wave ----------------------------------------------------------
@@ -517,109 +585,144 @@ struct AttChunk {
       }
     }
   }
-  // m, lsum in all lanes; o (dims 4*d4..4*d4+3) summed over all rows in lanes of group 0
-  __device__ void run(float *lds, int p, int t0, int t1, int tg, int lane, float &m, float &lsum, float4 &o) {
+  // The chunk's m, lsum and o (dims 4*d4..4*d4+3, summed over all its rows)
+  // in every lane.  A row's score is reduced over its D4-lane segment and
+  // broadcast back to the segment, so scores, weights and the weighted sum
+  // stay in registers; the RPL row groups are combined with xor shuffles.
+  __device__ void run(const float *lds, int p, int t0, int t1, int tg, int lane, float &m, float &lsum,
+                      float4 &o) {
     const int g = lane / D4, d4 = lane % D4;
     const float scale = 1.0f / sqrtf((float)D);
     const float4 q4 = reinterpret_cast<const float4 *>(lds + S::L_Q)[d4];
-    const int n = t1 - t0;
+    const bool has_p = tg < t1;  // this position closes the chunk
+    float s[IT];
 #pragma unroll
-    for (int it = 0; it < IT; it++) {
-      const int t = t0 + g + RPL * it;
-      const float s = seg_sum_last<D4>(dot4(k[it], q4, 0.f)) * scale;
-      if (d4 == D4 - 1 && t < tg) lds[S::L_SC + (t - t0)] = s;
-    }
-    if (tg < t1) {  // this position
+    for (int it = 0; it < IT; it++) s[it] = seg_sum_last<D4>(dot4(k[it], q4, 0.f));
+    float sp = -INFINITY;
+    float4 vp = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (has_p) {
       const float4 kp = reinterpret_cast<const float4 *>(lds + S::L_KP)[d4];
-      const float s = seg_sum_last<D4>(dot4(kp, q4, 0.f)) * scale;
-      if (lane == D4 - 1) lds[S::L_SC + (p - t0)] = s;
+      vp = reinterpret_cast<const float4 *>(lds + S::L_VP)[d4];
+      sp = seg_bcast_last<D4>(seg_sum_last<D4>(dot4(kp, q4, 0.f)), lane) * scale;
     }
-    const float s = lane < n ? lds[S::L_SC + lane] : -INFINITY;
-    m = wave_max_all(s);
-    const float e = lane < n ? expf(s - m) : 0.f;
-    lsum = wave_sum_all(e);
-    lds[S::L_SC + lane] = e;
-    o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int it = 0; it < IT; it++) s[it] = seg_bcast_last<D4>(s[it], lane) * scale;
+    float mx = sp;
+#pragma unroll
+    for (int it = 0; it < IT; it++)
+      if (t0 + g + RPL * it < tg) mx = fmaxf(mx, s[it]);
+    m = wave_max_all(mx);
+    float lp = 0.f;
+    float4 oo = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int it = 0; it < IT; it++) {
-      const int t = t0 + g + RPL * it;
-      if (t < tg) {
-        const float wt = lds[S::L_SC + (t - t0)];
-        o.x = __builtin_fmaf(wt, v[it].x, o.x);
-        o.y = __builtin_fmaf(wt, v[it].y, o.y);
-        o.z = __builtin_fmaf(wt, v[it].z, o.z);
-        o.w = __builtin_fmaf(wt, v[it].w, o.w);
+      if (t0 + g + RPL * it < tg) {
+        const float e = expf(s[it] - m);
+        lp += e;
+        oo.x = __builtin_fmaf(e, v[it].x, oo.x);
+        oo.y = __builtin_fmaf(e, v[it].y, oo.y);
+        oo.z = __builtin_fmaf(e, v[it].z, oo.z);
+        oo.w = __builtin_fmaf(e, v[it].w, oo.w);
       }
     }
-    if (tg < t1 && ((p - t0) % RPL) == g) {
-      const float wt = lds[S::L_SC + (p - t0)];
-      const float4 vp = reinterpret_cast<const float4 *>(lds + S::L_VP)[d4];
-      o.x = __builtin_fmaf(wt, vp.x, o.x);
-      o.y = __builtin_fmaf(wt, vp.y, o.y);
-      o.z = __builtin_fmaf(wt, vp.z, o.z);
-      o.w = __builtin_fmaf(wt, vp.w, o.w);
+    const float ep = has_p ? expf(sp - m) : 0.f;
+    if (has_p && ((p - t0) % RPL) == g) {
+      oo.x = __builtin_fmaf(ep, vp.x, oo.x);
+      oo.y = __builtin_fmaf(ep, vp.y, oo.y);
+      oo.z = __builtin_fmaf(ep, vp.z, oo.z);
+      oo.w = __builtin_fmaf(ep, vp.w, oo.w);
     }
-    // sum the RPL row groups in group order through LDS (the phase-input
-    // area is free while the attention chunk runs); lanes of group 0 end
-    // with the chunk's o
-    float4 *scr = reinterpret_cast<float4 *>(lds + S::L_XS);
-    scr[lane] = o;
-    if (g == 0) {
-      float4 t = scr[d4];
+    // one lane per row group holds the group's sum of weights
+    lsum = wave_sum_all(d4 == 0 ? lp : 0.f) + ep;
 #pragma unroll
-      for (int gg = 1; gg < RPL; gg++) {
-        const float4 u = scr[gg * D4 + d4];
-        t.x += u.x;
-        t.y += u.y;
-        t.z += u.z;
-        t.w += u.w;
-      }
-      o = t;
+    for (int sh = D4; sh < 64; sh <<= 1) {
+      oo.x += __shfl_xor(oo.x, sh);
+      oo.y += __shfl_xor(oo.y, sh);
+      oo.z += __shfl_xor(oo.z, sh);
+      oo.w += __shfl_xor(oo.w, sh);
     }
+    o = oo;
   }
 };
 
+// One tagged word per lane (lanes < n) until it carries ep; v is its payload.
+__device__ bool poll_rows(const uint64_t *src, int n, uint32_t ep, float &v, int lane, Waiter &wt) {
+  while (true) {
+    bool ok = true;
+    if (lane < n) {
+      const uint64_t x = tld(src + lane);
+      v = payload(x);
+      ok = tag_is(x, ep);
+    }
+    if (__all(ok)) return true;
+    if (wt.expired()) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// Control wave.  Per layer it runs the phase of its workgroup's set, and the
+// attention chunk if one is assigned to this workgroup:
+//   set Q: A  LayerNorm 1 of the residual stream, QKV rows + bias
+//   any  : B  one attention chunk (items go to the workgroups after set Q)
+//   set A: C  attention projection rows + bias + residual
+//   set F: D  LayerNorm 2, fc rows + bias, gelu_new
+//   set M: E  MLP projection rows + bias + residual
+// and with all workgroups H, the final LayerNorm and the output head.  The
+// residual rows a set adds come back from the published vectors (the values
+// written are the values read), so no workgroup carries state across phases.
 template <class S, int WD>
 __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
-  constexpr int E = S::E, F = S::F, D = S::D, H = S::H, RAP = S::RAP, G = S::G;
+  constexpr int E = S::E, F = S::F, D = S::D, H = S::H, G = S::G;
   constexpr int PE = E / 64, PF = F / 64, D4 = D / 4;
+  using SQ = Set<S, SET_Q>;
+  using SA = Set<S, SET_A>;
+  using SF = Set<S, SET_F>;
+  using SM = Set<S, SET_M>;
   const int w = blockIdx.x;
+  const int set = w < SA::FIRST ? SET_Q : w < SF::FIRST ? SET_A : w < SM::FIRST ? SET_F : SET_M;
+  const int rank = w - (set == SET_Q ? 0 : set == SET_A ? SA::FIRST : set == SET_F ? SF::FIRST : SM::FIRST);
   int *flag = reinterpret_cast<int *>(lds + S::L_FLAG);
   float *xs = lds + S::L_XS;
   const float *part = lds + S::L_PART;
-  float res = 0.f;  // residual stream value of row w*RAP + lane (lanes < RAP)
   int tok = 0;
   Waiter wt{&a, 0, 0};
-  // Parameters of a phase are requested one or two phases ahead, before an
-  // earlier wait, so their latency hides behind it:
-  //   A(l): ln1, QKV bias   <- requested before D(l-1)'s wait (or H's)
-  //   C(l): attn-proj bias  <- before A(l)'s wait
-  //   D(l): ln2, fc bias    <- before A(l)'s wait
-  //   E(l): MLP-proj bias   <- before C(l)'s wait
-  //   H   : ln_f            <- before D(L-1)'s wait
-  float g1[PE], b1[PE], g2[PE], b2[PE], gf[PE], bf[PE];
-  float bq = 0.f, ba = 0.f, bfc = 0.f, bp = 0.f;
-  auto fetch_ln = [&](float (&g)[PE], float (&b)[PE], const float *gs, const float *bs) {
+  // Parameters of the set's next phase are requested right after its phase,
+  // a whole layer before use: the LayerNorm of the phase (sets Q, F) and the
+  // bias of row rank*R + lane.  The final LayerNorm is read once.
+  float g[PE], bt[PE], gf[PE], bf[PE];
+  float bias = 0.f;
+  auto fetch_ln = [&](float (&gg)[PE], float (&bb)[PE], const float *gs, const float *bs) {
 #pragma unroll
     for (int j = 0; j < PE; j++) {
-      g[j] = gs[lane + 64 * j];
-      b[j] = bs[lane + 64 * j];
+      gg[j] = gs[vidx(lane, j)];
+      bb[j] = bs[vidx(lane, j)];
     }
   };
-  auto fetch_a = [&](int l) {
-    fetch_ln(g1, b1, a.ln1w + l * E, a.ln1b + l * E);
-    bq = lane < 3 * RAP ? a.bqkv[l * 3 * E + w * 3 * RAP + lane] : 0.f;
+  auto fetch_params = [&](int l) {
+    if (set == SET_Q) {
+      fetch_ln(g, bt, a.ln1w + l * E, a.ln1b + l * E);
+      bias = lane < SQ::R ? a.bqkv[l * 3 * E + rank * SQ::R + lane] : 0.f;
+    } else if (set == SET_A) {
+      bias = lane < SA::R ? a.bap[l * E + rank * SA::R + lane] : 0.f;
+    } else if (set == SET_F) {
+      fetch_ln(g, bt, a.ln2w + l * E, a.ln2b + l * E);
+      bias = lane < SF::R ? a.bfc[l * F + rank * SF::R + lane] : 0.f;
+    } else {
+      bias = lane < SM::R ? a.bpr[l * E + rank * SM::R + lane] : 0.f;
+    }
   };
-  fetch_a(0);
+  fetch_ln(gf, bf, a.lnfw, a.lnfb);
+  fetch_params(0);
   auto abort_all = [&]() {
     if (lane == 0) flag[0] = 1;
     wg_barrier();
   };
+  const bool needs_tok = (set == SET_Q || set == SET_A);
   for (int step = 0; step < a.nsteps; step++) {
     const int p = a.pos0 + step;
     // token of this step: fed, or the argmax of the previous step
     if (step < a.n_feed) tok = a.feed[step];
-    if (step > 0) {
+    if (step > 0 && needs_tok) {
       uint32_t bi = 0;
       wt.start(5 * a.L);
       if (!reduce_argmax<S>(a, epoch_of(a, step - 1, 5 * a.L), lane, wt, bi)) { abort_all(); return; }
@@ -629,30 +732,23 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
     }
     int nch, ch;
     att_chunks<S>(p, nch, ch);
-    const bool has_item = w < H * nch;
-    const int ih = has_item ? w / nch : 0, ic = has_item ? w % nch : 0;
+    const int item = (w + G - S::NQ) % G;
+    const bool has_item = item < H * nch;
+    const int ih = has_item ? item / nch : 0, ic = has_item ? item % nch : 0;
     const int it0 = ic * ch, it1 = min(it0 + ch, p + 1);
     const bool ilast = (it1 == p + 1);
     const int itg = ilast ? p : it1;  // cache rows it0..itg-1
     for (int l = 0; l < a.L; l++) {
       const uint32_t epA = epoch_of(a, step, 5 * l + 0), epB = epA + 1, epC = epA + 2, epD = epA + 3,
                      epE = epA + 4;
-      // ---------------- A: LayerNorm 1 + QKV
-      {
-        constexpr int R = 3 * RAP;
-        // requests for C and D
-        ba = lane < RAP ? a.bap[l * E + w * RAP + lane] : 0.f;
-        fetch_ln(g2, b2, a.ln2w + l * E, a.ln2b + l * E);
-        bfc = lane < 4 * RAP ? a.bfc[l * F + w * 4 * RAP + lane] : 0.f;
+      const int lnext = l + 1 < a.L ? l + 1 : 0;
+      // ---------------- A: LayerNorm 1 + QKV (set Q)
+      if (set == SET_Q) {
         float x[PE];
         if (l == 0) {
 #pragma unroll
           for (int j = 0; j < PE; j++)
-            x[j] = a.wte[(size_t)tok * E + lane + 64 * j] + a.wpe[(size_t)p * E + lane + 64 * j];
-          if (lane < RAP) {
-            const int o = w * RAP + lane;
-            res = a.wte[(size_t)tok * E + o] + a.wpe[(size_t)p * E + o];
-          }
+            x[j] = a.wte[(size_t)tok * E + vidx(lane, j)] + a.wpe[(size_t)p * E + vidx(lane, j)];
         } else {
           wt.start(5 * (l - 1) + 4);
           if (!poll_vec<PE>(a.xb_t + ((size_t)(l - 1) * NCOPY + my_copy()) * E, epA - 1, x, lane, wt)) {
@@ -660,15 +756,18 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
             return;
           }
         }
-        layernorm_to_lds<E>(x, g1, b1, a.eps, xs, lane);
+        layernorm_to_lds<E>(x, g, bt, a.eps, xs, lane);
         if (lane == 0) stamp(a, step, 5 * l + 0, 0, G);
         if (lane == 0) flag[0] = 0;
         wg_barrier();
         if (lane == 0) stamp(a, step, 5 * l + 0, 1, G);
         wg_barrier();
         if (lane == 0) stamp(a, step, 5 * l + 0, 2, G);
-        if (lane < R) tst_all(a.qkv_t + (size_t)l * NCOPY * 3 * E, 3 * E, w * R + lane, part[lane] + bq, epA);
+        if (lane < SQ::R)
+          tst_all(a.qkv_t + (size_t)l * NCOPY * 3 * E, 3 * E, rank * SQ::R + lane, part[lane] + bias, epA);
         if (lane == 0) stamp(a, step, 5 * l + 0, 3, G);
+        wg_barrier();  // stores issued: the compute waves may request the next slice
+        fetch_params(lnext);
       }
       // ---------------- B: attention chunk (control wave only)
       if (has_item) {
@@ -703,17 +802,21 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
         float m, lsum;
         float4 o;
         at.run(lds, p, it0, it1, itg, lane, m, lsum, o);
-        // cache-row stores complete before anything of this step is published
-        __builtin_amdgcn_s_waitcnt(0);
+        // The cache-row stores need no wait here: the next poll of this wave
+        // (its own set's phase, or the output head) waits for all of its
+        // outstanding memory operations, stores included, before this
+        // workgroup publishes again, and every reader of row p runs at a
+        // later step, after that publish.
         const int g = lane / D4, d4 = lane % D4;
         if (nch == 1) {
-          if (g == 0) {
-            uint64_t *dst = a.attn_t + (size_t)l * NCOPY * E;
-            const size_t ix = ih * D + 4 * d4;
-            tst_all(dst, E, ix + 0, o.x / lsum, epB);
-            tst_all(dst, E, ix + 1, o.y / lsum, epB);
-            tst_all(dst, E, ix + 2, o.z / lsum, epB);
-            tst_all(dst, E, ix + 3, o.w / lsum, epB);
+          // every lane holds the head's output; row group g writes the copies c = g mod RPL
+          uint64_t *dst = a.attn_t + (size_t)l * NCOPY * E + ih * D + 4 * d4;
+          const float4 r = make_float4(o.x / lsum, o.y / lsum, o.z / lsum, o.w / lsum);
+          for (int c = g; c < NCOPY; c += AttChunk<S>::RPL) {
+            tst(dst + (size_t)c * E + 0, r.x, epB);
+            tst(dst + (size_t)c * E + 1, r.y, epB);
+            tst(dst + (size_t)c * E + 2, r.z, epB);
+            tst(dst + (size_t)c * E + 3, r.w, epB);
           }
         } else if (ic > 0) {
           uint64_t *dst = a.att_t + ((size_t)(l * H + ih) * S::MAXCH + ic) * (D + 2);
@@ -772,84 +875,101 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
               O.w = __builtin_fmaf(oc[c].w, f, O.w);
             }
           }
-          if (g == 0) {
-            uint64_t *dst = a.attn_t + (size_t)l * NCOPY * E;
-            const size_t ix = ih * D + 4 * d4;
-            tst_all(dst, E, ix + 0, O.x / Ls, epB);
-            tst_all(dst, E, ix + 1, O.y / Ls, epB);
-            tst_all(dst, E, ix + 2, O.z / Ls, epB);
-            tst_all(dst, E, ix + 3, O.w / Ls, epB);
+          uint64_t *dst = a.attn_t + (size_t)l * NCOPY * E + ih * D + 4 * d4;
+          const float4 r = make_float4(O.x / Ls, O.y / Ls, O.z / Ls, O.w / Ls);
+          for (int c = g; c < NCOPY; c += AttChunk<S>::RPL) {
+            tst(dst + (size_t)c * E + 0, r.x, epB);
+            tst(dst + (size_t)c * E + 1, r.y, epB);
+            tst(dst + (size_t)c * E + 2, r.z, epB);
+            tst(dst + (size_t)c * E + 3, r.w, epB);
           }
         }
         if (lane == 0) stamp(a, step, 5 * l + 1, 3, G);
       }
-      // ---------------- C: attention projection + residual
-      {
-        bp = lane < RAP ? a.bpr[l * E + w * RAP + lane] : 0.f;  // request for E
+      // ---------------- C: attention projection + residual (set A)
+      if (set == SET_A) {
+        float xr = 0.f;  // residual stream row rank*R + lane
+        if (l == 0) {
+          if (lane < SA::R) {
+            const int o = rank * SA::R + lane;
+            xr = a.wte[(size_t)tok * E + o] + a.wpe[(size_t)p * E + o];
+          }
+        } else {
+          wt.start(5 * (l - 1) + 4);
+          if (!poll_rows(a.xb_t + ((size_t)(l - 1) * NCOPY + my_copy()) * E + rank * SA::R, SA::R, epA - 1, xr,
+                         lane, wt)) {
+            abort_all();
+            return;
+          }
+        }
         float x[PE];
         wt.start(5 * l + 1);
         if (!poll_vec<PE>(a.attn_t + ((size_t)l * NCOPY + my_copy()) * E, epB, x, lane, wt)) { abort_all(); return; }
 #pragma unroll
-        for (int j = 0; j < PE; j++) xs[lane + 64 * j] = x[j];
+        for (int j = 0; j < PE; j++) xs[vidx(lane, j)] = x[j];
         if (lane == 0) stamp(a, step, 5 * l + 2, 0, G);
         if (lane == 0) flag[0] = 0;
         wg_barrier();
         if (lane == 0) stamp(a, step, 5 * l + 2, 1, G);
         wg_barrier();
         if (lane == 0) stamp(a, step, 5 * l + 2, 2, G);
-        if (lane < RAP) {
-          const int o = w * RAP + lane;
-          const float mix = part[lane] + ba;
-          res = res + mix;
-          tst_all(a.xa_t + (size_t)l * NCOPY * E, E, o, res, epC);
+        if (lane < SA::R) {
+          const float mix = part[lane] + bias;
+          tst_all(a.xa_t + (size_t)l * NCOPY * E, E, rank * SA::R + lane, xr + mix, epC);
         }
         if (lane == 0) stamp(a, step, 5 * l + 2, 3, G);
+        wg_barrier();  // stores issued: the compute waves may request the next slice
+        fetch_params(lnext);
       }
-      // ---------------- D: LayerNorm 2 + fc + gelu_new
-      {
-        constexpr int R = 4 * RAP;
-        // requests for the next A (or for the head after the last layer)
-        if (l + 1 < a.L) fetch_a(l + 1);
-        else fetch_ln(gf, bf, a.lnfw, a.lnfb);
+      // ---------------- D: LayerNorm 2 + fc + gelu_new (set F)
+      if (set == SET_F) {
         float x[PE];
         wt.start(5 * l + 2);
         if (!poll_vec<PE>(a.xa_t + ((size_t)l * NCOPY + my_copy()) * E, epC, x, lane, wt)) { abort_all(); return; }
-        layernorm_to_lds<E>(x, g2, b2, a.eps, xs, lane);
+        layernorm_to_lds<E>(x, g, bt, a.eps, xs, lane);
         if (lane == 0) stamp(a, step, 5 * l + 3, 0, G);
         if (lane == 0) flag[0] = 0;
         wg_barrier();
         if (lane == 0) stamp(a, step, 5 * l + 3, 1, G);
         wg_barrier();
         if (lane == 0) stamp(a, step, 5 * l + 3, 2, G);
-        if (lane < R) tst_all(a.act_t + (size_t)l * NCOPY * F, F, w * R + lane, gelu_new(part[lane] + bfc), epD);
+        if (lane < SF::R)
+          tst_all(a.act_t + (size_t)l * NCOPY * F, F, rank * SF::R + lane, gelu_new(part[lane] + bias), epD);
         if (lane == 0) stamp(a, step, 5 * l + 3, 3, G);
+        wg_barrier();  // stores issued: the compute waves may request the next slice
+        fetch_params(lnext);
       }
-      // ---------------- E: MLP projection + residual
-      {
+      // ---------------- E: MLP projection + residual (set M)
+      if (set == SET_M) {
+        float xr = 0.f;
+        wt.start(5 * l + 2);
+        if (!poll_rows(a.xa_t + ((size_t)l * NCOPY + my_copy()) * E + rank * SM::R, SM::R, epC, xr, lane, wt)) {
+          abort_all();
+          return;
+        }
         float x[PF];
         wt.start(5 * l + 3);
         if (!poll_vec<PF>(a.act_t + ((size_t)l * NCOPY + my_copy()) * F, epD, x, lane, wt)) { abort_all(); return; }
 #pragma unroll
-        for (int j = 0; j < PF; j++) xs[lane + 64 * j] = x[j];
+        for (int j = 0; j < PF; j++) xs[vidx(lane, j)] = x[j];
         if (lane == 0) stamp(a, step, 5 * l + 4, 0, G);
         if (lane == 0) flag[0] = 0;
         wg_barrier();
         if (lane == 0) stamp(a, step, 5 * l + 4, 1, G);
         wg_barrier();
         if (lane == 0) stamp(a, step, 5 * l + 4, 2, G);
-        if (lane < RAP) {
-          const int o = w * RAP + lane;
-          const float mix = part[lane] + bp;
-          res = res + mix;
-          tst_all(a.xb_t + (size_t)l * NCOPY * E, E, o, res, epE);
+        if (lane < SM::R) {
+          const float mix = part[lane] + bias;
+          tst_all(a.xb_t + (size_t)l * NCOPY * E, E, rank * SM::R + lane, xr + mix, epE);
         }
         if (lane == 0) stamp(a, step, 5 * l + 4, 3, G);
+        wg_barrier();  // stores issued: the compute waves may request the next slice
+        fetch_params(lnext);
       }
     }
     // ---------------- H: final LayerNorm + head + local argmax
     {
       const uint32_t epH = epoch_of(a, step, 5 * a.L);
-      fetch_a(0);  // request for the next step's first layer
       float x[PE];
       wt.start(5 * a.L - 1);
       if (!poll_vec<PE>(a.xb_t + ((size_t)(a.L - 1) * NCOPY + my_copy()) * E, epH - 1, x, lane, wt)) {
@@ -882,6 +1002,7 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
         }
       }
       if (lane == 0) stamp(a, step, 5 * a.L, 3, G);
+      wg_barrier();  // stores issued: the compute waves may request the next slices
     }
   }
   // the last step's greedy id
