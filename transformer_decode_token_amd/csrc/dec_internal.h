@@ -54,8 +54,9 @@ struct DecodeArgs {
   float eps;
   uint32_t epoch0;                   // epochs used: epoch0 + 1 .. epoch0 + nsteps*(5L+1)
   long long timeout_ticks;           // wall-clock ticks a wait may take before aborting
-  long long *trace;                  // optional: [trace_steps][5L+1][G][2] wall-clock stamps
-  int trace_steps;                   //   (inputs ready, outputs published) per phase
+  long long *trace;                  // optional: [trace_steps][5L+1][G][4] wall-clock stamps
+  int trace_steps;                   //   (inputs ready, barrier 1, barrier 2, published) per phase
+  int head_lds_rows;                 // output-head rows a workgroup keeps in LDS (set at launch)
 };
 
 // Shape instantiations compiled into the library.

@@ -39,6 +39,8 @@
 // agent-scope stores one step before any other workgroup reads them.
 #include <hip/hip_fp16.h>
 
+#include <algorithm>
+
 #include "dec_internal.h"
 
 namespace gpt2dec {
@@ -77,6 +79,7 @@ struct Shape {
   static constexpr int L_SC = L_VP + D;                  // [64] chunk scores / weights
   static constexpr int L_FLAG = L_SC + 64;               // [4] control flags
   static constexpr int L_TOTAL = L_FLAG + 4;
+  static constexpr int L_HEAD = (L_TOTAL + 63) & ~63;    // output-head rows kept for the launch
 };
 
 // 124M shape: 256 workgroups x (3 compute + 1 control) waves in sets of 64
@@ -219,6 +222,56 @@ __device__ __forceinline__ float seg_bcast_last(float v, int lane) {
     return __shfl(v, lane | (W - 1));
   }
 }
+// Lane k's value of each W-lane segment, in every lane of the segment.
+template <int W>
+__device__ __forceinline__ float seg_bcast(float v, int k, int lane) {
+  if constexpr (W == 16) {
+    // row_newbcast:k; k is a compile-time constant after unrolling
+    switch (k) {
+#define G2_NB(K) case K: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + K, 0xF, 0xF, false));
+      G2_NB(0) G2_NB(1) G2_NB(2) G2_NB(3) G2_NB(4) G2_NB(5) G2_NB(6) G2_NB(7)
+      G2_NB(8) G2_NB(9) G2_NB(10) G2_NB(11) G2_NB(12) G2_NB(13) G2_NB(14) G2_NB(15)
+#undef G2_NB
+    }
+    return v;
+  } else {
+    return __shfl(v, (lane & ~(W - 1)) | k);
+  }
+}
+
+// Reduce-scatter inside W-lane segments (W = 8 or 16): x[i] holds each
+// lane's part of row i; afterwards lane j of a segment returns the total of
+// row j over the segment's W lanes.  Each step pairs lanes that differ in the
+// bits of one mask (xor 15, 7, 2, 1 via row mirror, half-row mirror and quad
+// permutes): one lane keeps the lower half of its remaining rows, its partner
+// the upper half, and each adds the partner's part of the rows it keeps.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int H, int CTRL>
+__device__ __forceinline__ void rs_step(float (&x)[16], bool upper) {
+#pragma unroll
+  for (int i = 0; i < H; i++) {
+    const float keep = upper ? x[i + H] : x[i];
+    const float send = upper ? x[i] : x[i + H];
+    x[i] = keep + dpp_mov<CTRL>(send);
+  }
+}
+template <int W>
+__device__ __forceinline__ float seg_reduce_scatter(const float (&in)[W], int lane) {
+  static_assert(W == 8 || W == 16, "segment");
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < W; i++) x[i] = in[i];
+  const int j = lane % W;
+  if constexpr (W == 16) rs_step<8, 0x140>(x, (j & 8) != 0);  // row_mirror: lane j <-> 15 - j
+  rs_step<4, 0x141>(x, (j & 4) != 0);                         // row_half_mirror: j <-> j ^ 7
+  rs_step<2, 0x4E>(x, (j & 2) != 0);                          // quad_perm [2,3,0,1]: j <-> j ^ 2
+  rs_step<1, 0xB1>(x, (j & 1) != 0);                          // quad_perm [1,0,3,2]: j <-> j ^ 1
+  return x[0];
+}
+
 // Whole-wave sum / max, the same bits in every lane.
 __device__ __forceinline__ float wave_sum_all(float v) {
   const float t = seg_sum_last<64>(v);
@@ -440,10 +493,35 @@ __device__ __forceinline__ void dot_set(const Chunk<WD> (&b)[ST::NB], const floa
   }
 }
 
+// The first head_lds_rows of this workgroup's output-head rows stay in LDS
+// for the whole launch (the head does not change between steps); they are
+// copied in once, during the first layer of the first step.
+template <class S, int WD>
+__device__ void fill_head_lds(const DecodeArgs &a, float *lds, int lane) {
+  constexpr int KC = S::E / 4, U = 4;
+  constexpr int HWD = (WD == WD_F16) ? WD_F16 : WD_F32;
+  const int hr0 = (int)(((long long)blockIdx.x * a.V) / S::G);
+  const int hr1 = (int)(((long long)(blockIdx.x + 1) * a.V) / S::G);
+  const int n = min(hr1 - hr0, a.head_lds_rows) * KC;
+  if (n <= 0) return;
+  const MatW hm{a.head, nullptr};
+  Chunk<HWD> *dst = reinterpret_cast<Chunk<HWD> *>(lds + S::L_HEAD);
+  for (int i0 = 0; i0 < n; i0 += U * S::NL) {
+    Chunk<HWD> c[U];
+#pragma unroll
+    for (int u = 0; u < U; u++)
+      c[u] = ld_chunk<HWD, HEAD_NT>(hm, 0, (size_t)hr0 * KC + min(i0 + u * S::NL + lane, n - 1));
+#pragma unroll
+    for (int u = 0; u < U; u++)
+      if (i0 + u * S::NL + lane < n) dst[i0 + u * S::NL + lane] = c[u];
+  }
+}
+
 // Output head over this workgroup's contiguous vocabulary rows, RB rows per
-// batch, two batches in flight; the first two are requested before the final
-// LayerNorm is ready.  Batches past the last row re-read that row, which
-// keeps every load unconditional.  False when the control wave aborted.
+// batch: first the rows kept in LDS, then the rest from memory with two
+// batches in flight, the first two requested before the final LayerNorm is
+// ready.  Memory batches past the last row re-read that row, which keeps
+// every load unconditional.  False when the control wave aborted.
 template <class S, int WD>
 __device__ bool head_rows(const DecodeArgs &a, float *lds, int lane) {
   constexpr int KC = S::E / 4, LPR = S::LPRH, NPH = KC / LPR, RB = S::NL / LPR;
@@ -456,15 +534,16 @@ __device__ bool head_rows(const DecodeArgs &a, float *lds, int lane) {
   const int hr0 = (int)(((long long)blockIdx.x * a.V) / S::G);
   const int hr1 = (int)(((long long)(blockIdx.x + 1) * a.V) / S::G);
   const int nr = hr1 - hr0;
+  const int nl = min(nr, a.head_lds_rows), nh = nr - nl, hb = hr0 + nl;
   const int q = lane % LPR, rl = lane / LPR;
   Chunk<HWD> h0[NPH], h1[NPH];
   auto fetch = [&](Chunk<HWD>(&b)[NPH], int r0) {
-    const int r = min(r0 + rl, nr - 1);
-    const size_t c0 = (size_t)(hr0 + r) * KC + q;
+    const int r = min(r0 + rl, nh - 1);
+    const size_t c0 = (size_t)(hb + r) * KC + q;
 #pragma unroll
     for (int i = 0; i < NPH; i++) b[i] = ld_chunk<HWD, HEAD_NT>(hm, 0, c0 + (size_t)i * LPR);
   };
-  if (nr > 0) {
+  if (nh > 0) {
     fetch(h0, 0);
     fetch(h1, RB);
   }
@@ -473,18 +552,26 @@ __device__ bool head_rows(const DecodeArgs &a, float *lds, int lane) {
   float4 xv[NPH];
 #pragma unroll
   for (int i = 0; i < NPH; i++) xv[i] = reinterpret_cast<const float4 *>(xs)[i * LPR + q];
-  auto consume = [&](const Chunk<HWD>(&b)[NPH], int r0) {
+  auto consume = [&](const Chunk<HWD>(&b)[NPH], int r, int lim) {
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < NPH; i++) acc = dot4(deq<HWD>(b[i]), xv[i], acc);
     acc = seg_sum_last<LPR>(acc);
-    if (q == LPR - 1 && r0 + rl < nr) part[r0 + rl] = acc;
+    if (q == LPR - 1 && r < lim) part[r] = acc;
   };
-  if (nr > 0) {
-    for (int r0 = 0; r0 < nr; r0 += 2 * RB) {
-      consume(h0, r0);
+  const Chunk<HWD> *hl = reinterpret_cast<const Chunk<HWD> *>(lds + S::L_HEAD);
+  for (int r0 = 0; r0 < nl; r0 += RB) {
+    const int r = min(r0 + rl, nl - 1);
+    Chunk<HWD> c[NPH];
+#pragma unroll
+    for (int i = 0; i < NPH; i++) c[i] = hl[r * KC + q + LPR * i];
+    consume(c, r0 + rl, nl);
+  }
+  if (nh > 0) {
+    for (int r0 = 0; r0 < nh; r0 += 2 * RB) {
+      consume(h0, nl + r0 + rl, nr);
       fetch(h0, r0 + 2 * RB);
-      consume(h1, r0 + RB);
+      consume(h1, nl + r0 + RB + rl, nr);
       fetch(h1, r0 + 3 * RB);
     }
   }
@@ -518,6 +605,7 @@ __device__ void compute_set(const DecodeArgs &a, const MatW &m, float *lds, int 
       wg_barrier();
       if (l + 1 < a.L) load_set<ST, WD>(b, m, l + 1, rank, lane);
       else if (more && !LATE) load_set<ST, WD>(b, m, 0, rank, lane);
+      if (step == 0 && l == 0) fill_head_lds<S, WD>(a, lds, lane);
     }
     if (!head_rows<S, WD>(a, lds, lane)) return;
     wg_barrier();  // the control wave has issued the logits and its argmax
@@ -586,18 +674,24 @@ struct AttChunk {
     }
   }
   // The chunk's m, lsum and o (dims 4*d4..4*d4+3, summed over all its rows)
-  // in every lane.  A row's score is reduced over its D4-lane segment and
-  // broadcast back to the segment, so scores, weights and the weighted sum
-  // stay in registers; the RPL row groups are combined with xor shuffles.
+  // in every lane.  The IT (= D4) partial scores of a lane are reduced over
+  // its D4-lane segment by a reduce-scatter that leaves lane j of the segment
+  // with the full score of the segment's row it = j, so each lane takes one
+  // exponential; the weights are then broadcast back along the segment for
+  // the weighted sum of values, and the RPL row groups are combined with xor
+  // shuffles.  Everything stays in registers.
   __device__ void run(const float *lds, int p, int t0, int t1, int tg, int lane, float &m, float &lsum,
                       float4 &o) {
+    static_assert(IT == D4, "one row per lane of a segment");
     const int g = lane / D4, d4 = lane % D4;
     const float scale = 1.0f / sqrtf((float)D);
     const float4 q4 = reinterpret_cast<const float4 *>(lds + S::L_Q)[d4];
     const bool has_p = tg < t1;  // this position closes the chunk
-    float s[IT];
+    float x[IT];
 #pragma unroll
-    for (int it = 0; it < IT; it++) s[it] = seg_sum_last<D4>(dot4(k[it], q4, 0.f));
+    for (int it = 0; it < IT; it++) x[it] = dot4(k[it], q4, 0.f);
+    const float s = seg_reduce_scatter<D4>(x, lane) * scale;  // row t0 + g + RPL*d4
+    const bool valid = t0 + g + RPL * d4 < tg;
     float sp = -INFINITY;
     float4 vp = make_float4(0.f, 0.f, 0.f, 0.f);
     if (has_p) {
@@ -605,35 +699,25 @@ struct AttChunk {
       vp = reinterpret_cast<const float4 *>(lds + S::L_VP)[d4];
       sp = seg_bcast_last<D4>(seg_sum_last<D4>(dot4(kp, q4, 0.f)), lane) * scale;
     }
-#pragma unroll
-    for (int it = 0; it < IT; it++) s[it] = seg_bcast_last<D4>(s[it], lane) * scale;
-    float mx = sp;
-#pragma unroll
-    for (int it = 0; it < IT; it++)
-      if (t0 + g + RPL * it < tg) mx = fmaxf(mx, s[it]);
-    m = wave_max_all(mx);
-    float lp = 0.f;
+    m = wave_max_all(valid ? fmaxf(s, sp) : sp);
+    const float e = valid ? expf(s - m) : 0.f;
+    const float ep = has_p ? expf(sp - m) : 0.f;
+    lsum = wave_sum_all(e) + ep;
     float4 oo = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int it = 0; it < IT; it++) {
-      if (t0 + g + RPL * it < tg) {
-        const float e = expf(s[it] - m);
-        lp += e;
-        oo.x = __builtin_fmaf(e, v[it].x, oo.x);
-        oo.y = __builtin_fmaf(e, v[it].y, oo.y);
-        oo.z = __builtin_fmaf(e, v[it].z, oo.z);
-        oo.w = __builtin_fmaf(e, v[it].w, oo.w);
-      }
+      const float w = seg_bcast<D4>(e, it, lane);
+      oo.x = __builtin_fmaf(w, v[it].x, oo.x);
+      oo.y = __builtin_fmaf(w, v[it].y, oo.y);
+      oo.z = __builtin_fmaf(w, v[it].z, oo.z);
+      oo.w = __builtin_fmaf(w, v[it].w, oo.w);
     }
-    const float ep = has_p ? expf(sp - m) : 0.f;
     if (has_p && ((p - t0) % RPL) == g) {
       oo.x = __builtin_fmaf(ep, vp.x, oo.x);
       oo.y = __builtin_fmaf(ep, vp.y, oo.y);
       oo.z = __builtin_fmaf(ep, vp.z, oo.z);
       oo.w = __builtin_fmaf(ep, vp.w, oo.w);
     }
-    // one lane per row group holds the group's sum of weights
-    lsum = wave_sum_all(d4 == 0 ? lp : 0.f) + ep;
 #pragma unroll
     for (int sh = D4; sh < 64; sh <<= 1) {
       oo.x += __shfl_xor(oo.x, sh);
@@ -802,12 +886,14 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
         float m, lsum;
         float4 o;
         at.run(lds, p, it0, it1, itg, lane, m, lsum, o);
+        if (lane == 0) stamp(a, step, 5 * l + 1, 1, G);
         // The cache-row stores need no wait here: the next poll of this wave
         // (its own set's phase, or the output head) waits for all of its
         // outstanding memory operations, stores included, before this
         // workgroup publishes again, and every reader of row p runs at a
         // later step, after that publish.
         const int g = lane / D4, d4 = lane % D4;
+        if (lane == 0) stamp(a, step, 5 * l + 1, 2, G);
         if (nch == 1) {
           // every lane holds the head's output; row group g writes the copies c = g mod RPL
           uint64_t *dst = a.attn_t + (size_t)l * NCOPY * E + ih * D + 4 * d4;
@@ -1022,9 +1108,22 @@ __global__ void __launch_bounds__(S::NT, 1) decode_kernel(DecodeArgs a) {
   else compute_main<S, WD>(a, lds, tid);
 }
 
-// The layout needs S::L_TOTAL floats; ask for more than half of the CU's
-// 160 KB so that exactly one workgroup lands on each CU.
-constexpr size_t kLdsBytes = 96 * 1024;
+// Dynamic LDS: the device's per-workgroup limit, at most 160 KB.  More than
+// half of a CU's LDS puts exactly one workgroup on each CU; what the layout
+// does not need beyond S::L_HEAD holds output-head rows.
+constexpr size_t kLdsMax = 160 * 1024;
+size_t lds_budget() {
+  int dev = 0, m = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&m, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) return 0;
+  return m > 0 ? std::min((size_t)m, kLdsMax) : 0;
+}
+template <class S>
+int head_lds_rows_for(int wd, size_t lds) {
+  const size_t row = (size_t)(S::E / 4) * (wd == WD_F16 ? 8 : 16);
+  const size_t base = (size_t)S::L_HEAD * sizeof(float);
+  return lds > base ? (int)((lds - base) / row) : 0;
+}
 
 template <class S>
 const void *kernel_for(int wd) {
@@ -1038,21 +1137,26 @@ const void *kernel_for(int wd) {
 
 template <class S>
 hipError_t launch_t(int wd, const DecodeArgs &a, hipStream_t s) {
-  static_assert(S::L_TOTAL * sizeof(float) <= kLdsBytes, "LDS layout too large");
+  static_assert(S::L_HEAD * sizeof(float) <= 64 * 1024, "LDS layout too large");
   const void *k = kernel_for<S>(wd);
   if (!k) return hipErrorInvalidValue;
+  const size_t lds = lds_budget();
+  if (lds < (size_t)S::L_HEAD * sizeof(float)) return hipErrorInvalidConfiguration;
   DecodeArgs copy = a;
+  copy.head_lds_rows = head_lds_rows_for<S>(wd, lds);
   void *args[] = {&copy};
-  return hipLaunchCooperativeKernel(k, dim3(S::G), dim3(S::NT), args, kLdsBytes, s);
+  return hipLaunchCooperativeKernel(k, dim3(S::G), dim3(S::NT), args, lds, s);
 }
 
 template <class S>
 hipError_t occupancy_t(int wd, int *blocks) {
   const void *k = kernel_for<S>(wd);
   if (!k) return hipErrorInvalidValue;
-  hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+  const size_t lds = lds_budget();
+  if (lds < (size_t)S::L_HEAD * sizeof(float)) return hipErrorInvalidConfiguration;
+  hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k, S::NT, kLdsBytes);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k, S::NT, lds);
 }
 
 template <class S>
@@ -1061,7 +1165,7 @@ void info_t(ShapeInfo *o) {
   o->D = S::D;
   o->G = S::G;
   o->threads = S::NT;
-  o->lds_bytes = kLdsBytes;
+  o->lds_bytes = kLdsMax;
   o->maxch = S::MAXCH;
 }
 
