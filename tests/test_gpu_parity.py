@@ -178,3 +178,52 @@ def test_invalid_calls_change_nothing():
     orc = Oracle(model)
     am_o, lg_o = orc.step(1, 0)
     compare_step(lg, am, lg_o)
+
+
+def _long_fixture():
+    import json
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "gpt2_124m_fp32_long.json")
+    with open(path) as f:
+        return json.load(f)
+
+
+def test_long_context_against_stored_oracle_run():
+    """The long-context workload at full size (fp32 124M shape, positions 0..1023, up
+    to 16 attention chunks per head): the oracle's greedy run is stored by
+    tests/golden/make_long_context.py.  Teacher-forced on the oracle's tokens, the
+    GPU's argmax equals the oracle's at every step whose top-2 margin exceeds 1e-3,
+    and at the sampled positions the stored logits agree within 1e-4 * max|logit|.
+    Then the device-chained greedy run reproduces the oracle's ids up to the first
+    low-margin step."""
+    from tests.gpu_util import MARGIN, REL_TOL
+    fx = _long_fixture()
+    cfg = synth.CONFIGS[5]
+    assert fx["n_steps"] == cfg.n_steps == 1024
+    model = synth.make_model(cfg)
+    assert [int(t) for t in synth.make_prompt(cfg)] == fx["prompt"]
+    ctx = load_gpu(model)
+    print(f"[parity] long context: {cfg.n_steps} teacher-forced steps", flush=True)
+    worst = 0.0
+    for pos, st in enumerate(fx["steps"]):
+        want = str(pos) in fx["samples"]
+        am, lg = g2.gpt2_step(ctx, st["tok"], pos, want_logits=want)
+        if st["margin"] > MARGIN:
+            assert am == st["argmax"], f"argmax differs at pos {pos}"
+        if want:
+            smp = fx["samples"][str(pos)]
+            got = np.asarray(lg, np.float64)[smp["ids"]]
+            err = np.abs(got - np.asarray(smp["logits"])).max()
+            assert np.all(np.isfinite(got)), f"non-finite logits at pos {pos}"
+            assert err <= REL_TOL * st["maxabs"], f"logit error {err:.3e} at pos {pos}"
+            worst = max(worst, err / st["maxabs"])
+    print(f"[parity] long context: worst sampled relative logit error {worst:.2e}", flush=True)
+    g2.gpt2_reset(ctx)
+    ids = g2.gpt2_generate(ctx, np.asarray(fx["prompt"], np.int32), cfg.n_new)
+    oracle_ids = [st["argmax"] for st in fx["steps"][cfg.n_prompt - 1:]]
+    for k, (a, b) in enumerate(zip(ids, oracle_ids)):
+        if fx["steps"][cfg.n_prompt - 1 + k]["margin"] <= MARGIN:
+            break
+        assert int(a) == b, f"greedy id {k} differs"
+    print(f"[parity] long context: greedy ids agree for the first {k + 1} of {len(oracle_ids)}", flush=True)
+    ctx.close()

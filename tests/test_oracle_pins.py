@@ -341,3 +341,31 @@ def test_q4_group_properties_and_bruteforce(olib):
         chosen = dist[np.arange(32), q]
         assert np.all(chosen <= best + 4 * np.spacing(np.float32(s)))
         del levels
+
+
+def test_long_context_fixture_is_the_oracles_run():
+    """The stored long-context run (tests/golden/gpt2_124m_fp32_long.json, written by
+    tests/golden/make_long_context.py from the oracle alone) is what the current
+    oracle and input generators produce: its prompt, and its first 12 steps."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "gpt2_124m_fp32_long.json")
+    with open(path) as f:
+        fx = json.load(f)
+    cfg = synth.CONFIGS[5]
+    assert fx["n_steps"] == cfg.n_steps and fx["n_prompt"] == cfg.n_prompt
+    assert fx["prompt"] == [int(t) for t in synth.make_prompt(cfg)]
+    orc = Oracle(synth.make_model(cfg))
+    for pos in range(12):
+        st = fx["steps"][pos]
+        am, lg = orc.step(st["tok"], pos)
+        lg = np.asarray(lg, np.float64)
+        assert am == st["argmax"]
+        assert abs(np.abs(lg).max() - st["maxabs"]) <= 1e-12 * st["maxabs"]
+        if str(pos) in fx["samples"]:
+            smp = fx["samples"][str(pos)]
+            assert np.array_equal(lg[smp["ids"]], np.asarray(smp["logits"]))
+    orc.close()
+    # the stored ids follow the greedy rule: each step after the prompt feeds the previous argmax
+    for pos in range(cfg.n_prompt, cfg.n_steps):
+        assert fx["steps"][pos]["tok"] == fx["steps"][pos - 1]["argmax"]
