@@ -518,8 +518,8 @@ __device__ void fill_head_lds(const DecodeArgs &a, float *lds, int lane) {
 }
 
 // Output head over this workgroup's contiguous vocabulary rows, RB rows per
-// batch: first the rows kept in LDS, then the rest from memory with two
-// batches in flight, the first two requested before the final LayerNorm is
+// batch: first the rows kept in LDS, then the rest from memory with three
+// batches in flight, the first three requested before the final LayerNorm is
 // ready.  Memory batches past the last row re-read that row, which keeps
 // every load unconditional.  False when the control wave aborted.
 template <class S, int WD>
@@ -536,7 +536,7 @@ __device__ bool head_rows(const DecodeArgs &a, float *lds, int lane) {
   const int nr = hr1 - hr0;
   const int nl = min(nr, a.head_lds_rows), nh = nr - nl, hb = hr0 + nl;
   const int q = lane % LPR, rl = lane / LPR;
-  Chunk<HWD> h0[NPH], h1[NPH];
+  Chunk<HWD> h0[NPH], h1[NPH], h2[NPH];
   auto fetch = [&](Chunk<HWD>(&b)[NPH], int r0) {
     const int r = min(r0 + rl, nh - 1);
     const size_t c0 = (size_t)(hb + r) * KC + q;
@@ -546,6 +546,7 @@ __device__ bool head_rows(const DecodeArgs &a, float *lds, int lane) {
   if (nh > 0) {
     fetch(h0, 0);
     fetch(h1, RB);
+    fetch(h2, 2 * RB);
   }
   wg_barrier();
   if (flag[0]) return false;
@@ -568,11 +569,13 @@ __device__ bool head_rows(const DecodeArgs &a, float *lds, int lane) {
     consume(c, r0 + rl, nl);
   }
   if (nh > 0) {
-    for (int r0 = 0; r0 < nh; r0 += 2 * RB) {
+    for (int r0 = 0; r0 < nh; r0 += 3 * RB) {
       consume(h0, nl + r0 + rl, nr);
-      fetch(h0, r0 + 2 * RB);
+      fetch(h0, r0 + 3 * RB);
       consume(h1, nl + r0 + RB + rl, nr);
-      fetch(h1, r0 + 3 * RB);
+      fetch(h1, r0 + 4 * RB);
+      consume(h2, nl + r0 + 2 * RB + rl, nr);
+      fetch(h2, r0 + 5 * RB);
     }
   }
   wg_barrier();
