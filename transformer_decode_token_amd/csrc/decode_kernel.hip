@@ -396,6 +396,14 @@ __device__ bool poll_vec(const uint64_t *src, uint32_t ep, float (&v)[PER], int 
   }
 }
 
+// Two tagged words with one 16-byte store at byte offset off of buffer rs;
+// each 8-byte half is one whole word (the consumers poll word pairs).
+__device__ __forceinline__ void tst2(__amdgpu_buffer_rsrc_t rs, uint32_t off, float a, float b, uint32_t ep) {
+  typedef unsigned int g2_v4u __attribute__((ext_vector_type(4)));
+  const g2_v4u v = {__float_as_uint(a), ep, __float_as_uint(b), ep};
+  __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, AUX_SC1);
+}
+
 // LayerNorm of E values held as a lane share (element vidx(lane, j)) into LDS,
 // following the model file's layernorm kernel: mean, biased variance,
 // ((x - mean) * rsqrt(var + eps)) * gamma + beta.
@@ -897,81 +905,89 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
         // later step, after that publish.
         const int g = lane / D4, d4 = lane % D4;
         if (lane == 0) stamp(a, step, 5 * l + 1, 2, G);
-        if (nch == 1) {
-          // every lane holds the head's output; row group g writes the copies c = g mod RPL
-          uint64_t *dst = a.attn_t + (size_t)l * NCOPY * E + ih * D + 4 * d4;
-          const float4 r = make_float4(o.x / lsum, o.y / lsum, o.z / lsum, o.w / lsum);
+        // every lane holds the head's output; row group g writes the copies c = g mod RPL
+        const auto attn_rs = __builtin_amdgcn_make_buffer_rsrc(a.attn_t + (size_t)l * NCOPY * E, (short)0,
+                                                               NCOPY * E * 8, 0x00020000);
+        auto publish_head = [&](const float4 &r) {
           for (int c = g; c < NCOPY; c += AttChunk<S>::RPL) {
-            tst(dst + (size_t)c * E + 0, r.x, epB);
-            tst(dst + (size_t)c * E + 1, r.y, epB);
-            tst(dst + (size_t)c * E + 2, r.z, epB);
-            tst(dst + (size_t)c * E + 3, r.w, epB);
+            const uint32_t off = (uint32_t)((c * E + ih * D + 4 * d4) * 8);
+            tst2(attn_rs, off, r.x, r.y, epB);
+            tst2(attn_rs, off + 16, r.z, r.w, epB);
           }
+        };
+        if (nch == 1) {
+          publish_head(make_float4(o.x / lsum, o.y / lsum, o.z / lsum, o.w / lsum));
         } else if (ic > 0) {
-          uint64_t *dst = a.att_t + ((size_t)(l * H + ih) * S::MAXCH + ic) * (D + 2);
+          // this chunk's (o, m, l) for chunk 0 of the head, as word pairs
+          const auto prs = __builtin_amdgcn_make_buffer_rsrc(
+              a.att_t + ((size_t)(l * H + ih) * S::MAXCH + ic) * (D + 2), (short)0, (D + 2) * 8, 0x00020000);
           if (g == 0) {
-            tst(dst + 4 * d4 + 0, o.x, epB);
-            tst(dst + 4 * d4 + 1, o.y, epB);
-            tst(dst + 4 * d4 + 2, o.z, epB);
-            tst(dst + 4 * d4 + 3, o.w, epB);
+            tst2(prs, (uint32_t)(4 * d4 * 8), o.x, o.y, epB);
+            tst2(prs, (uint32_t)((4 * d4 + 2) * 8), o.z, o.w, epB);
           }
-          if (lane == 0) {
-            tst(dst + D, m, epB);
-            tst(dst + D + 1, lsum, epB);
-          }
+          if (lane == 0) tst2(prs, (uint32_t)(D * 8), m, lsum, epB);
         } else {
-          // chunk 0 merges the head: max over chunks, then rescaled sums in chunk order
-          const uint64_t *src = a.att_t + ((size_t)(l * H + ih) * S::MAXCH) * (D + 2);
-          float mc[S::MAXCH], lc[S::MAXCH];
-          float4 oc[S::MAXCH];
+          // chunk 0 merges the head.  The partials of chunks 1..nch-1 are polled as one
+          // flat array of word pairs spread over the lanes (a fixed number of 16-byte
+          // loads per lane, clamped, so the wait counts stay exact), staged in LDS (the
+          // phase-input area is free while the item runs), and combined: the largest
+          // chunk maximum, one rescale factor per chunk (lane c), then the sums in
+          // chunk order.
+          constexpr int PP = (D + 2) / 2;                       // word pairs per chunk slot
+          constexpr int PPL = ((S::MAXCH - 1) * PP + 63) / 64;  // pair loads per lane
+          constexpr int SP = D + 4;                             // staged slot stride (16-byte aligned)
+          const int npairs = (nch - 1) * PP;
+          const auto mrs = __builtin_amdgcn_make_buffer_rsrc(
+              a.att_t + ((size_t)(l * H + ih) * S::MAXCH + 1) * (D + 2), (short)0, (S::MAXCH - 1) * (D + 2) * 8,
+              0x00020000);
+          float va[PPL], vb[PPL];
           wt.start(5 * l + 1);
           while (true) {
             bool ok = true;
 #pragma unroll
-            for (int c = 1; c < S::MAXCH; c++) {
-              if (c < nch) {
-                const uint64_t *s2 = src + (size_t)c * (D + 2);
-                const uint64_t x0 = tld(s2 + 4 * d4 + 0), x1 = tld(s2 + 4 * d4 + 1), x2 = tld(s2 + 4 * d4 + 2),
-                               x3 = tld(s2 + 4 * d4 + 3), xm = tld(s2 + D), xl = tld(s2 + D + 1);
-                ok &= tag_is(x0, epB) && tag_is(x1, epB) && tag_is(x2, epB) && tag_is(x3, epB) &&
-                      tag_is(xm, epB) && tag_is(xl, epB);
-                oc[c] = make_float4(payload(x0), payload(x1), payload(x2), payload(x3));
-                mc[c] = payload(xm);
-                lc[c] = payload(xl);
-              }
+            for (int k = 0; k < PPL; k++) {
+              const int f = min(lane + 64 * k, npairs - 1);
+              const auto x = __builtin_amdgcn_raw_buffer_load_b128(mrs, (uint32_t)(f * 16), 0, AUX_SC1);
+              va[k] = __uint_as_float(x[0]);
+              vb[k] = __uint_as_float(x[2]);
+              ok &= (lane + 64 * k >= npairs) || (x[1] == epB && x[3] == epB);
             }
             if (__all(ok)) break;
             if (wt.expired()) { abort_all(); return; }
             __builtin_amdgcn_s_sleep(1);
           }
-          mc[0] = m;
-          lc[0] = lsum;
-          oc[0] = o;
-          float M = mc[0];
+          float *scr = lds + S::L_XS;
 #pragma unroll
-          for (int c = 1; c < S::MAXCH; c++)
-            if (c < nch) M = fmaxf(M, mc[c]);
-          float Ls = 0.f;
-          float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-          for (int c = 0; c < S::MAXCH; c++) {
-            if (c < nch) {
-              const float f = expf(mc[c] - M);
-              Ls = __builtin_fmaf(lc[c], f, Ls);
-              O.x = __builtin_fmaf(oc[c].x, f, O.x);
-              O.y = __builtin_fmaf(oc[c].y, f, O.y);
-              O.z = __builtin_fmaf(oc[c].z, f, O.z);
-              O.w = __builtin_fmaf(oc[c].w, f, O.w);
+          for (int k = 0; k < PPL; k++) {
+            const int f = lane + 64 * k;
+            if (f < npairs) {
+              const int w2 = 2 * f, sl = w2 / (D + 2), wi = w2 % (D + 2);
+              scr[sl * SP + wi] = va[k];
+              scr[sl * SP + wi + 1] = vb[k];
             }
           }
-          uint64_t *dst = a.attn_t + (size_t)l * NCOPY * E + ih * D + 4 * d4;
-          const float4 r = make_float4(O.x / Ls, O.y / Ls, O.z / Ls, O.w / Ls);
-          for (int c = g; c < NCOPY; c += AttChunk<S>::RPL) {
-            tst(dst + (size_t)c * E + 0, r.x, epB);
-            tst(dst + (size_t)c * E + 1, r.y, epB);
-            tst(dst + (size_t)c * E + 2, r.z, epB);
-            tst(dst + (size_t)c * E + 3, r.w, epB);
+          float mcl = -INFINITY, lcl = 0.f;  // lane c < nch: chunk c's maximum and sum
+          if (lane == 0) {
+            mcl = m;
+            lcl = lsum;
+          } else if (lane < nch) {
+            mcl = scr[(lane - 1) * SP + D];
+            lcl = scr[(lane - 1) * SP + D + 1];
           }
+          const float M = wave_max_all(mcl);
+          const float fl = lane < nch ? expf(mcl - M) : 0.f;
+          const float Ls = wave_sum_all(lcl * fl);
+          const float f0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fl), 0));
+          float4 O = make_float4(o.x * f0, o.y * f0, o.z * f0, o.w * f0);
+          for (int c = 1; c < nch; c++) {
+            const float fc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fl), c));
+            const float4 oc = reinterpret_cast<const float4 *>(scr + (c - 1) * SP)[d4];
+            O.x = __builtin_fmaf(oc.x, fc, O.x);
+            O.y = __builtin_fmaf(oc.y, fc, O.y);
+            O.z = __builtin_fmaf(oc.z, fc, O.z);
+            O.w = __builtin_fmaf(oc.w, fc, O.w);
+          }
+          publish_head(make_float4(O.x / Ls, O.y / Ls, O.z / Ls, O.w / Ls));
         }
         if (lane == 0) stamp(a, step, 5 * l + 1, 3, G);
       }
