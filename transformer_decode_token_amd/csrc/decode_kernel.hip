@@ -118,6 +118,7 @@ struct Set {
   static constexpr int CPR = KC / LPR;
   static constexpr int NB = NP * CPR;
   static_assert(KC % LPR == 0 && S::NL % LPR == 0 && R <= 64 && R <= PSTRIDE, "slice geometry");
+  static_assert(R % 2 == 0, "rows are published in pairs");
 };
 
 // ---- weight chunks: 4 consecutive inputs of one output row ----------------
@@ -334,12 +335,9 @@ __device__ __forceinline__ bool tag_is(uint64_t x, uint32_t ep) { return (uint32
 // Every published vector exists in NCOPY copies, one per XCD (workgroup w is
 // taken to run on XCD w % 8): a producer writes all copies, a consumer polls
 // the copy of its own XCD, which spreads the polling over 8x the lines.
+// (Producers write the copies with tst_pairs / tst2 below.)
 constexpr int NCOPY = 8;
 __device__ __forceinline__ int my_copy() { return (int)(blockIdx.x % NCOPY); }
-__device__ __forceinline__ void tst_all(uint64_t *base, size_t stride, size_t idx, float v, uint32_t ep) {
-#pragma unroll
-  for (int c = 0; c < NCOPY; c++) tst(base + c * stride + idx, v, ep);
-}
 __device__ __forceinline__ float payload(uint64_t x) { return __uint_as_float((uint32_t)x); }
 
 // Bounded waiting: a wait that outlives the time limit, or sees another
@@ -404,6 +402,23 @@ __device__ __forceinline__ void tst2(__amdgpu_buffer_rsrc_t rs, uint32_t off, fl
   __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, AUX_SC1);
 }
 
+// Publish one value per lane (the lane's row; lanes < R, R even, row parity =
+// lane parity) to all NCOPY copies of a vector of `stride` words, as word
+// pairs: the two lanes of a pair exchange values, the even one writes the
+// pair to the first half of the copies, the odd one to the second half.
+__device__ __forceinline__ void tst_pairs(__amdgpu_buffer_rsrc_t rs, int stride, int row, float v, uint32_t ep,
+                                          int lane) {
+  const float vn = dpp_mov<0xB1>(v);  // quad_perm [1,0,3,2]: the other lane of the pair
+  const bool odd = (lane & 1) != 0;
+  const float lo = odd ? vn : v, hi = odd ? v : vn;
+  const int r0 = row & ~1, c0 = odd ? NCOPY / 2 : 0;
+#pragma unroll
+  for (int k = 0; k < NCOPY / 2; k++) tst2(rs, (uint32_t)(((c0 + k) * stride + r0) * 8), lo, hi, ep);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t copies_rsrc(uint64_t *base, int stride) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, NCOPY * stride * 8, 0x00020000);
+}
+
 // LayerNorm of E values held as a lane share (element vidx(lane, j)) into LDS,
 // following the model file's layernorm kernel: mean, biased variance,
 // ((x - mean) * rsqrt(var + eps)) * gamma + beta.
@@ -412,17 +427,18 @@ __device__ __forceinline__ void layernorm_to_lds(const float (&x)[E / 64], const
                                                  const float (&b)[E / 64], float eps, float *dst,
                                                  int lane) {
   constexpr int PER = E / 64;
-  float s = 0.f;
+  // four independent partial sums per lane (shorter dependency chains)
+  float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int j = 0; j < PER; j++) s += x[j];
-  const float mean = wave_sum_all(s) * (1.0f / (float)E);
-  float q = 0.f;
+  for (int j = 0; j < PER; j++) s4[j % 4] += x[j];
+  const float mean = wave_sum_all((s4[0] + s4[1]) + (s4[2] + s4[3])) * (1.0f / (float)E);
+  float q4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < PER; j++) {
     const float d = x[j] - mean;
-    q = __builtin_fmaf(d, d, q);
+    q4[j % 4] = __builtin_fmaf(d, d, q4[j % 4]);
   }
-  const float var = wave_sum_all(q) * (1.0f / (float)E);
+  const float var = wave_sum_all((q4[0] + q4[1]) + (q4[2] + q4[3])) * (1.0f / (float)E);
   const float r = 1.0f / sqrtf(var + eps);
 #pragma unroll
   for (int j = 0; j < PER; j++) dst[vidx(lane, j)] = __builtin_fmaf((x[j] - mean) * r, g[j], b[j]);
@@ -501,6 +517,46 @@ __device__ __forceinline__ void dot_set(const Chunk<WD> (&b)[ST::NB], const floa
   }
 }
 
+template <class S, int WD>
+struct HeadGeo {
+  static constexpr int KC = S::E / 4, LPR = S::LPRH, NPH = KC / LPR, RB = S::NL / LPR;
+  static constexpr int HWD = (WD == WD_F16) ? WD_F16 : WD_F32;
+  static_assert(KC % LPR == 0 && S::NL % LPR == 0, "head geometry");
+};
+
+// Batches of head rows that the slice registers of a workgroup of set SET
+// hold during the output head: the late sets, when the register chunk type is
+// the head's (not for int4).
+template <class S, int WD, int SET>
+constexpr int head_reg_batches() {
+  using HG = HeadGeo<S, WD>;
+  return (SET != SET_Q && WD == HG::HWD) ? Set<S, SET>::NB / HG::NPH : 0;
+}
+
+// Output-head rows [hr0, hr1) of workgroup w: the rows left after each
+// workgroup's register batches are split evenly, and each workgroup adds the
+// rows its registers hold (capped so that no workgroup exceeds PSTRIDE rows),
+// so every workgroup streams about the same number of rows during the head.
+template <class S, int WD>
+__device__ __forceinline__ void head_range(int V, int w, int &hr0, int &hr1) {
+  constexpr int RB = HeadGeo<S, WD>::RB;
+  const int even = V / S::G;
+  // no workgroup may get more than PSTRIDE rows (the row results live in LDS)
+  const int cap = min(even, max(0, PSTRIDE - even - 1));
+  const int eA = min(head_reg_batches<S, WD, SET_A>() * RB, cap);
+  const int eF = min(head_reg_batches<S, WD, SET_F>() * RB, cap);
+  const int eM = min(head_reg_batches<S, WD, SET_M>() * RB, cap);
+  const int rest = V - S::NA * eA - S::NF * eF - S::NM * eM;
+  auto start = [&](int u) {
+    const int na = min(max(u - Set<S, SET_A>::FIRST, 0), S::NA);
+    const int nf = min(max(u - Set<S, SET_F>::FIRST, 0), S::NF);
+    const int nm = min(max(u - Set<S, SET_M>::FIRST, 0), S::NM);
+    return (int)(((long long)u * rest) / S::G) + na * eA + nf * eF + nm * eM;
+  };
+  hr0 = start(w);
+  hr1 = start(w + 1);
+}
+
 // The first head_lds_rows of this workgroup's output-head rows stay in LDS
 // for the whole launch (the head does not change between steps); they are
 // copied in once, during the first layer of the first step.
@@ -508,8 +564,8 @@ template <class S, int WD>
 __device__ void fill_head_lds(const DecodeArgs &a, float *lds, int lane) {
   constexpr int KC = S::E / 4, U = 4;
   constexpr int HWD = (WD == WD_F16) ? WD_F16 : WD_F32;
-  const int hr0 = (int)(((long long)blockIdx.x * a.V) / S::G);
-  const int hr1 = (int)(((long long)(blockIdx.x + 1) * a.V) / S::G);
+  int hr0, hr1;
+  head_range<S, WD>(a.V, (int)blockIdx.x, hr0, hr1);
   const int n = min(hr1 - hr0, a.head_lds_rows) * KC;
   if (n <= 0) return;
   const MatW hm{a.head, nullptr};
@@ -526,23 +582,49 @@ __device__ void fill_head_lds(const DecodeArgs &a, float *lds, int lane) {
 }
 
 // Output head over this workgroup's contiguous vocabulary rows, RB rows per
-// batch: first the rows kept in LDS, then the rest from memory with three
-// batches in flight, the first three requested before the final LayerNorm is
-// ready.  Memory batches past the last row re-read that row, which keeps
+// batch: first the rows kept in LDS, then the NRB batches requested into the
+// slice registers beforehand (late sets), then the rest from memory with
+// three batches in flight, the first three requested before the final
+// LayerNorm is ready.  Memory batches past the last row re-read that row, which keeps
 // every load unconditional.  False when the control wave aborted.
-template <class S, int WD>
-__device__ bool head_rows(const DecodeArgs &a, float *lds, int lane) {
-  constexpr int KC = S::E / 4, LPR = S::LPRH, NPH = KC / LPR, RB = S::NL / LPR;
-  static_assert(KC % LPR == 0 && S::NL % LPR == 0, "head geometry");
-  constexpr int HWD = (WD == WD_F16) ? WD_F16 : WD_F32;
+// Request the NRB batches of head rows that follow the LDS-resident ones into
+// registers b (a set whose slice registers are idle until after the head).
+template <class S, int WD, int NRB, int NB>
+__device__ __forceinline__ void head_prefetch_regs(const DecodeArgs &a, Chunk<WD> (&b)[NB], int lane) {
+  using HG = HeadGeo<S, WD>;
+  static_assert(NRB * HG::NPH <= NB && (NRB == 0 || WD == HG::HWD), "register batches");
+  if constexpr (NRB > 0) {
+    int hr0, hr1;
+    head_range<S, WD>(a.V, (int)blockIdx.x, hr0, hr1);
+    const int nr = hr1 - hr0, nl = min(nr, a.head_lds_rows);
+    if (nr - nl <= 0) return;
+    const MatW hm{a.head, nullptr};
+    const int q = lane % HG::LPR, rl = lane / HG::LPR;
+#pragma unroll
+    for (int k = 0; k < NRB; k++) {
+      const int r = min(nl + k * HG::RB + rl, nr - 1);
+      const size_t c0 = (size_t)(hr0 + r) * HG::KC + q;
+#pragma unroll
+      for (int i = 0; i < HG::NPH; i++)
+        b[k * HG::NPH + i] = ld_chunk<WD, HEAD_NT>(hm, 0, c0 + (size_t)i * HG::LPR);
+    }
+  }
+}
+
+template <class S, int WD, int NRB, int NB>
+__device__ bool head_rows(const DecodeArgs &a, float *lds, int lane, const Chunk<WD> (&breg)[NB]) {
+  using HG = HeadGeo<S, WD>;
+  constexpr int KC = HG::KC, LPR = HG::LPR, NPH = HG::NPH, RB = HG::RB, HWD = HG::HWD;
   const int *flag = reinterpret_cast<const int *>(lds + S::L_FLAG);
   float *part = lds + S::L_PART;
   const float *xs = lds + S::L_XS;
   const MatW hm{a.head, nullptr};
-  const int hr0 = (int)(((long long)blockIdx.x * a.V) / S::G);
-  const int hr1 = (int)(((long long)(blockIdx.x + 1) * a.V) / S::G);
+  int hr0, hr1;
+  head_range<S, WD>(a.V, (int)blockIdx.x, hr0, hr1);
   const int nr = hr1 - hr0;
-  const int nl = min(nr, a.head_lds_rows), nh = nr - nl, hb = hr0 + nl;
+  const int nl = min(nr, a.head_lds_rows);
+  const int ng = min(nr - nl, NRB * RB);  // rows requested into registers beforehand
+  const int nh = nr - nl - ng, hb = hr0 + nl + ng;
   const int q = lane % LPR, rl = lane / LPR;
   Chunk<HWD> h0[NPH], h1[NPH], h2[NPH];
   auto fetch = [&](Chunk<HWD>(&b)[NPH], int r0) {
@@ -576,13 +658,25 @@ __device__ bool head_rows(const DecodeArgs &a, float *lds, int lane) {
     for (int i = 0; i < NPH; i++) c[i] = hl[r * KC + q + LPR * i];
     consume(c, r0 + rl, nl);
   }
+  if constexpr (NRB > 0) {
+#pragma unroll
+    for (int k = 0; k < NRB; k++) {
+      if (k * RB < ng) {
+        Chunk<HWD> c[NPH];
+#pragma unroll
+        for (int i = 0; i < NPH; i++) c[i] = breg[k * NPH + i];
+        consume(c, nl + k * RB + rl, nl + ng);
+      }
+    }
+  }
   if (nh > 0) {
+    const int nb = nl + ng;
     for (int r0 = 0; r0 < nh; r0 += 3 * RB) {
-      consume(h0, nl + r0 + rl, nr);
+      consume(h0, nb + r0 + rl, nr);
       fetch(h0, r0 + 3 * RB);
-      consume(h1, nl + r0 + RB + rl, nr);
+      consume(h1, nb + r0 + RB + rl, nr);
       fetch(h1, r0 + 4 * RB);
-      consume(h2, nl + r0 + 2 * RB + rl, nr);
+      consume(h2, nb + r0 + 2 * RB + rl, nr);
       fetch(h2, r0 + 5 * RB);
     }
   }
@@ -599,7 +693,10 @@ __device__ bool head_rows(const DecodeArgs &a, float *lds, int lane) {
 template <class S, int WD, int SET>
 __device__ void compute_set(const DecodeArgs &a, const MatW &m, float *lds, int lane) {
   using ST = Set<S, SET>;
-  constexpr bool LATE = (SET == SET_F || SET == SET_M);
+  // sets whose phase is not the first of a layer request the next step's first
+  // slice only after the output head; meanwhile their slice registers hold head rows
+  constexpr bool LATE = SET != SET_Q;
+  constexpr int NRB = head_reg_batches<S, WD, SET>();
   const int *flag = reinterpret_cast<const int *>(lds + S::L_FLAG);
   float *part = lds + S::L_PART;
   const float *xs = lds + S::L_XS;
@@ -616,9 +713,10 @@ __device__ void compute_set(const DecodeArgs &a, const MatW &m, float *lds, int 
       wg_barrier();
       if (l + 1 < a.L) load_set<ST, WD>(b, m, l + 1, rank, lane);
       else if (more && !LATE) load_set<ST, WD>(b, m, 0, rank, lane);
+      else head_prefetch_regs<S, WD, NRB>(a, b, lane);  // idle slice registers take head rows
       if (step == 0 && l == 0) fill_head_lds<S, WD>(a, lds, lane);
     }
-    if (!head_rows<S, WD>(a, lds, lane)) return;
+    if (!head_rows<S, WD, NRB>(a, lds, lane, b)) return;
     wg_barrier();  // the control wave has issued the logits and its argmax
     if (more && LATE) load_set<ST, WD>(b, m, 0, rank, lane);
   }
@@ -859,7 +957,8 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
         wg_barrier();
         if (lane == 0) stamp(a, step, 5 * l + 0, 2, G);
         if (lane < SQ::R)
-          tst_all(a.qkv_t + (size_t)l * NCOPY * 3 * E, 3 * E, rank * SQ::R + lane, part[lane] + bias, epA);
+          tst_pairs(copies_rsrc(a.qkv_t + (size_t)l * NCOPY * 3 * E, 3 * E), 3 * E, rank * SQ::R + lane,
+                    part[lane] + bias, epA, lane);
         if (lane == 0) stamp(a, step, 5 * l + 0, 3, G);
         wg_barrier();  // stores issued: the compute waves may request the next slice
         fetch_params(lnext);
@@ -1020,7 +1119,7 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
         if (lane == 0) stamp(a, step, 5 * l + 2, 2, G);
         if (lane < SA::R) {
           const float mix = part[lane] + bias;
-          tst_all(a.xa_t + (size_t)l * NCOPY * E, E, rank * SA::R + lane, xr + mix, epC);
+          tst_pairs(copies_rsrc(a.xa_t + (size_t)l * NCOPY * E, E), E, rank * SA::R + lane, xr + mix, epC, lane);
         }
         if (lane == 0) stamp(a, step, 5 * l + 2, 3, G);
         wg_barrier();  // stores issued: the compute waves may request the next slice
@@ -1039,7 +1138,8 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
         wg_barrier();
         if (lane == 0) stamp(a, step, 5 * l + 3, 2, G);
         if (lane < SF::R)
-          tst_all(a.act_t + (size_t)l * NCOPY * F, F, rank * SF::R + lane, gelu_new(part[lane] + bias), epD);
+          tst_pairs(copies_rsrc(a.act_t + (size_t)l * NCOPY * F, F), F, rank * SF::R + lane,
+                    gelu_new(part[lane] + bias), epD, lane);
         if (lane == 0) stamp(a, step, 5 * l + 3, 3, G);
         wg_barrier();  // stores issued: the compute waves may request the next slice
         fetch_params(lnext);
@@ -1065,7 +1165,7 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
         if (lane == 0) stamp(a, step, 5 * l + 4, 2, G);
         if (lane < SM::R) {
           const float mix = part[lane] + bias;
-          tst_all(a.xb_t + (size_t)l * NCOPY * E, E, rank * SM::R + lane, xr + mix, epE);
+          tst_pairs(copies_rsrc(a.xb_t + (size_t)l * NCOPY * E, E), E, rank * SM::R + lane, xr + mix, epE, lane);
         }
         if (lane == 0) stamp(a, step, 5 * l + 4, 3, G);
         wg_barrier();  // stores issued: the compute waves may request the next slice
@@ -1088,8 +1188,8 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
       if (lane == 0) stamp(a, step, 5 * a.L, 1, G);
       wg_barrier();
       if (lane == 0) stamp(a, step, 5 * a.L, 2, G);
-      const int hr0 = (int)(((long long)w * a.V) / G);
-      const int hr1 = (int)(((long long)(w + 1) * a.V) / G);
+      int hr0, hr1;
+      head_range<S, WD>(a.V, w, hr0, hr1);
       const int nr = hr1 - hr0;
       float bv = -INFINITY;
       uint32_t bi = 0xffffffffu;
