@@ -83,10 +83,11 @@ struct Shape {
 };
 
 // 124M shape: 256 workgroups x (3 compute + 1 control) waves in sets of 64
-// (QKV, 36 rows each), 32 (attention projection, 24 rows), 96 (fc, 32 rows)
-// and 64 (MLP projection, 12 rows); each set streams an equal share of its
+// (QKV, 36 rows each), 32 (attention projection, 24 rows), 64 (fc, 48 rows)
+// and 96 (MLP projection, 8 rows); each set streams an equal share of its
 // matrix, so every workgroup reads 74 to 147 KB of fp32 weights per layer.
-using ShapeS = Shape<768, 64, 3, 16, 16, 16, 64, 32, 96, 64>;
+// (Set sizes chosen by measurement among the partitions that fit.)
+using ShapeS = Shape<768, 64, 3, 16, 16, 16, 64, 32, 64, 96>;
 // tiny shape: 32 workgroups x (2 compute + 1 control) waves, sets 8/4/16/4.
 using ShapeT = Shape<128, 32, 2, 8, 8, 8, 8, 4, 16, 4>;
 
