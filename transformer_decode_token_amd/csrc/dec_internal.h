@@ -9,6 +9,13 @@ namespace gpt2dec {
 
 enum { WD_F32 = 0, WD_F16 = 1, WD_Q4 = 2 };
 
+// Copies of every published activation vector (one or more per XCD; a
+// consumer polls the copy of its own XCD).
+#ifndef G2_NCOPY
+#define G2_NCOPY 8
+#endif
+constexpr int kTagCopies = G2_NCOPY;
+
 // One weight matrix of every layer, output-major [N][K] per layer, layers
 // back to back.  For int4: `w` holds the nibbles ([N][K/2] bytes, element k in
 // byte k/2, low nibble for even k) and `sz` the (scale, zero) pair of each
@@ -35,13 +42,13 @@ struct DecodeArgs {
   const float *wpe;                  // [P][E]
   const float *lnfw, *lnfb;          // [E]
   float *kc, *vc;                    // [L][H][P][D] KV cache
-  uint64_t *qkv_t;                   // [L][8][3E]     tagged QKV outputs (8 copies)
+  uint64_t *qkv_t;                   // [L][C][3E]     tagged QKV outputs (C = kTagCopies copies)
   uint64_t *att_t;                   // [L][H][MAXCH][D+2] tagged attention chunk partials
-  uint64_t *attn_t;                  // [L][8][E]      tagged merged attention output
-  uint64_t *xa_t;                    // [L][8][E]      tagged residual after attention
-  uint64_t *act_t;                   // [L][8][F]      tagged gelu activations
-  uint64_t *xb_t;                    // [L][8][E]      tagged residual after the MLP
-  uint64_t *amax_t;                  // [8][2][G]      tagged per-workgroup argmax (value, index)
+  uint64_t *attn_t;                  // [L][C][E]      tagged merged attention output
+  uint64_t *xa_t;                    // [L][C][E]      tagged residual after attention
+  uint64_t *act_t;                   // [L][C][F]      tagged gelu activations
+  uint64_t *xb_t;                    // [L][C][E]      tagged residual after the MLP
+  uint64_t *amax_t;                  // [C][2][G]      tagged per-workgroup argmax (value, index)
   float *logits;                     // [V]            logits of the last step
   int *out_ids;                      // greedy ids
   int *err;                          // [4] flag, workgroup, phase, epoch (device-side wait timeout)

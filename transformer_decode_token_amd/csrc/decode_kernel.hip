@@ -333,11 +333,12 @@ __device__ __forceinline__ void st_agent(float *p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ bool tag_is(uint64_t x, uint32_t ep) { return (uint32_t)(x >> 32) == ep; }
-// Every published vector exists in NCOPY copies, one per XCD (workgroup w is
-// taken to run on XCD w % 8): a producer writes all copies, a consumer polls
-// the copy of its own XCD, which spreads the polling over 8x the lines.
-// (Producers write the copies with tst_pairs / tst2 below.)
-constexpr int NCOPY = 8;
+// Every published vector exists in NCOPY copies, a multiple of the 8 XCDs
+// (workgroup w is taken to run on XCD w % 8): a producer writes all copies
+// (with tst_pairs / tst2 below), a consumer polls copy w % NCOPY, which
+// spreads the polling over NCOPY times the lines.
+constexpr int NCOPY = kTagCopies;
+static_assert(NCOPY % 8 == 0, "copies per XCD");
 __device__ __forceinline__ int my_copy() { return (int)(blockIdx.x % NCOPY); }
 __device__ __forceinline__ float payload(uint64_t x) { return __uint_as_float((uint32_t)x); }
 

@@ -256,8 +256,8 @@ int load_impl(gpt2_ctx *c, const gpt2_config *cfg, const gpt2_weights *w) {
   void *head16 = c->wd == WD_F16 ? c->dalloc<void>((size_t)V * E * 2) : nullptr;
   const size_t kv = (size_t)L * H * P * D;
   float *kc = c->dalloc<float>(kv * 4), *vc = c->dalloc<float>(kv * 4);
-  // published vectors exist in 8 copies (one per XCD); chunk partials have one reader
-  const size_t NC = 8;
+  // published vectors exist in kTagCopies copies (per XCD); chunk partials have one reader
+  const size_t NC = kTagCopies;
   c->tag_sizes[0] = NC * L * 3 * E * 8;
   c->tag_sizes[1] = (size_t)L * H * c->si.maxch * (D + 2) * 8;
   c->tag_sizes[2] = NC * L * E * 8;
