@@ -348,12 +348,18 @@ struct Waiter {
   const DecodeArgs *a;
   long long t0;
   int phase;
+  unsigned polls;
   __device__ void start(int ph) {
     t0 = (long long)wall_clock64();
     phase = ph;
+    polls = 0;
   }
   __device__ bool expired() {
-    if (__hip_atomic_load(a->err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return true;
+    // Another workgroup's abort is looked for at every 32nd failed poll only:
+    // the error word is a memory round trip of its own, which would otherwise
+    // double the period of every poll loop.  The clock is read every time.
+    if ((++polls & 31u) == 0 && __hip_atomic_load(a->err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+      return true;
     if ((long long)wall_clock64() - t0 > a->timeout_ticks) {
       int zero = 0;
       if (__hip_atomic_compare_exchange_strong(a->err, &zero, 1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
@@ -880,7 +886,7 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
   float *xs = lds + S::L_XS;
   const float *part = lds + S::L_PART;
   int tok = 0;
-  Waiter wt{&a, 0, 0};
+  Waiter wt{&a, 0, 0, 0u};
   // Parameters of the set's next phase are requested right after its phase,
   // a whole layer before use: the LayerNorm of the phase (sets Q, F) and the
   // bias of row rank*R + lane.  The final LayerNorm is read once.
