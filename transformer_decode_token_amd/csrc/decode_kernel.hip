@@ -472,6 +472,18 @@ __device__ __forceinline__ void att_chunks(int p, int &nch, int &ch) {
   ch = (n + nch - 1) / nch;
 }
 
+// Attention items go to the workgroups after set Q, in blockIdx order: item
+// (head h, chunk c) is h*nch + c.  The item index of workgroup w, and whether
+// it has one at position p.
+template <class S>
+__device__ __forceinline__ int att_item_of(int w) { return (w + S::G - S::NQ) % S::G; }
+template <class S>
+__device__ __forceinline__ bool has_att_item(int p, int w) {
+  int nch, ch;
+  att_chunks<S>(p, nch, ch);
+  return att_item_of<S>(w) < S::H * nch;
+}
+
 // Optional timeline of one workgroup's control wave (lane 0): inputs ready, first and
 // second workgroup barrier passed, outputs published.
 __device__ __forceinline__ void stamp(const DecodeArgs &a, int step, int ph, int which, int G) {
@@ -710,23 +722,42 @@ __device__ void compute_set(const DecodeArgs &a, const MatW &m, float *lds, int 
   const float *xs = lds + S::L_XS;
   const int rank = (int)blockIdx.x - ST::FIRST;
   Chunk<WD> b[ST::NB];
-  load_set<ST, WD>(b, m, 0, rank, lane);
+  // A workgroup of set M whose control wave runs an attention item in a step
+  // requests each layer's slice only after that item (one more barrier): the
+  // slice would otherwise still be streaming in, two phases after its request,
+  // when the item reads its K/V rows and polls q/k/v.
+  auto defers = [&](int step) {
+    return SET == SET_M && step < a.nsteps && has_att_item<S>(a.pos0 + step, (int)blockIdx.x);
+  };
+  bool defer = defers(0);
+  if (!defer) load_set<ST, WD>(b, m, 0, rank, lane);
   for (int step = 0; step < a.nsteps; step++) {
     const bool more = step + 1 < a.nsteps;
+    const bool defer_next = defers(step + 1);
     for (int l = 0; l < a.L; l++) {
+      if (defer) {
+        wg_barrier();  // the control wave has run its attention item
+        if (flag[0]) return;
+        load_set<ST, WD>(b, m, l, rank, lane);
+      }
       wg_barrier();
       if (flag[0]) return;
       dot_set<ST, WD>(b, xs, part, lane);
       wg_barrier();
       wg_barrier();
-      if (l + 1 < a.L) load_set<ST, WD>(b, m, l + 1, rank, lane);
-      else if (more && !LATE) load_set<ST, WD>(b, m, 0, rank, lane);
-      else head_prefetch_regs<S, WD, NRB>(a, b, lane);  // idle slice registers take head rows
+      if (l + 1 < a.L) {
+        if (!defer) load_set<ST, WD>(b, m, l + 1, rank, lane);
+      } else if (more && !LATE) {
+        load_set<ST, WD>(b, m, 0, rank, lane);
+      } else {
+        head_prefetch_regs<S, WD, NRB>(a, b, lane);  // idle slice registers take head rows
+      }
       if (step == 0 && l == 0) fill_head_lds<S, WD>(a, lds, lane);
     }
     if (!head_rows<S, WD, NRB>(a, lds, lane, b)) return;
     wg_barrier();  // the control wave has issued the logits and its argmax
-    if (more && LATE) load_set<ST, WD>(b, m, 0, rank, lane);
+    if (more && LATE && !defer_next) load_set<ST, WD>(b, m, 0, rank, lane);
+    defer = defer_next;
   }
 }
 
@@ -933,7 +964,7 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
     }
     int nch, ch;
     att_chunks<S>(p, nch, ch);
-    const int item = (w + G - S::NQ) % G;
+    const int item = att_item_of<S>(w);
     const bool has_item = item < H * nch;
     const int ih = has_item ? item / nch : 0, ic = has_item ? item % nch : 0;
     const int it0 = ic * ch, it1 = min(it0 + ch, p + 1);
@@ -1097,6 +1128,7 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
           publish_head(make_float4(O.x / Ls, O.y / Ls, O.z / Ls, O.w / Ls));
         }
         if (lane == 0) stamp(a, step, 5 * l + 1, 3, G);
+        if (set == SET_M) wg_barrier();  // the compute waves may now request this layer's slice
       }
       // ---------------- C: attention projection + residual (set A)
       if (set == SET_A) {
