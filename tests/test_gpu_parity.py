@@ -50,7 +50,7 @@ def test_teacher_forced_logits_and_ids(name):
     ctx.close()
 
 
-@pytest.mark.parametrize("name", ["tiny", "tiny-rich", "gpt2-124m-fp32"])
+@pytest.mark.parametrize("name", ["tiny", "tiny-rich", "gpt2-124m-fp32", "gpt2-124m-fp16w", "gpt2-124m-int4w"])
 def test_generate_matches_oracle_greedy(name):
     """Device-chained greedy ids equal the oracle's up to the first step whose
     oracle top-2 margin is at or below 1e-3 (where summation order may decide)."""
@@ -226,4 +226,73 @@ def test_long_context_against_stored_oracle_run():
             break
         assert int(a) == b, f"greedy id {k} differs"
     print(f"[parity] long context: greedy ids agree for the first {k + 1} of {len(oracle_ids)}", flush=True)
+    ctx.close()
+
+
+def _oracle_greedy(orc, fed, pos0, n_new):
+    """Oracle run continuing at position pos0: the ids `fed` at pos0.., then greedy
+    until n_new ids exist.  Returns (ids, margins of the passes that produced them)."""
+    toks = list(fed)
+    ids, margins = [], []
+    n_steps = len(fed) + n_new - 1
+    for k in range(n_steps):
+        am, lg = orc.step(toks[k], pos0 + k)
+        if k >= len(fed) - 1:
+            ids.append(am)
+            margins.append(top2_margin(lg))
+        if k + 1 >= len(toks):
+            toks.append(am)
+    return ids, margins
+
+
+def _assert_ids(got, want, margins, what):
+    assert len(got) == len(want)
+    for j, (a, b) in enumerate(zip(got, want)):
+        if margins[j] <= 1e-3:
+            break
+        assert int(a) == int(b), f"{what}: id {j} differs: gpu {a} oracle {b}"
+
+
+def test_generate_edges():
+    """Device-chained runs at the edges of the call's contract, against the oracle:
+    a one-id prompt with one new id (a single pass), a run that continues after
+    steps already taken (position 3 on), and a run that fills every position
+    (n_positions = 64), after which one more pass is refused and changes nothing."""
+    cfg = CASES["tiny-rich"]
+    model = synth.make_model(cfg)
+    orc = Oracle(model)
+    ctx = load_gpu(model)
+    rng = np.random.default_rng(77)
+    toks = [int(t) for t in rng.integers(0, cfg.vocab, 80)]
+
+    # one pass
+    got = g2.gpt2_generate(ctx, np.array(toks[:1], np.int32), 1)
+    orc.reset()
+    want, mg = _oracle_greedy(orc, toks[:1], 0, 1)
+    _assert_ids(got, want, mg, "single pass")
+    assert g2.gpt2_filled(ctx) == 1
+
+    # continue after three single steps
+    g2.gpt2_reset(ctx)
+    orc.reset()
+    for pos in range(3):
+        g2.gpt2_step(ctx, toks[pos], pos, want_logits=False)
+        orc.step(toks[pos], pos)
+    got = g2.gpt2_generate(ctx, np.array(toks[3:5], np.int32), 6)
+    want, mg = _oracle_greedy(orc, toks[3:5], 3, 6)
+    _assert_ids(got, want, mg, "continued run")
+    assert g2.gpt2_filled(ctx) == 3 + 2 + 6 - 1
+
+    # fill every position, then one pass too many
+    g2.gpt2_reset(ctx)
+    orc.reset()
+    P = cfg.n_positions
+    got = g2.gpt2_generate(ctx, np.array(toks[:8], np.int32), P - 8 + 1)
+    want, mg = _oracle_greedy(orc, toks[:8], 0, P - 8 + 1)
+    _assert_ids(got, want, mg, "full run")
+    assert g2.gpt2_filled(ctx) == P
+    with pytest.raises(g2.Gpt2Error):
+        g2.gpt2_generate(ctx, np.array(toks[:1], np.int32), 1)
+    assert g2.gpt2_filled(ctx) == P
+    orc.close()
     ctx.close()
