@@ -30,13 +30,15 @@
 // so there is no MFMA here: the kernel is bound by weight bytes and by the
 // latency of the 5L+1 dependent phases of a token.
 //
-// Synchronisation.  There is no grid barrier.  Each output element is written
-// as one 64-bit agent-scope atomic word (float bits | epoch << 32), where the
-// epoch numbers the producing phase uniquely within and across launches; a
-// consumer polls the words it needs until all carry the expected epoch.  Per-
-// location atomic coherence is all this needs: no cache write-back/invalidate
-// fences are executed in the loop.  KV-cache rows are written with
-// agent-scope stores one step before any other workgroup reads them.
+// Synchronisation.  There is no grid barrier.  Each output element travels as
+// one 64-bit word (float bits | epoch << 32), written and read with device-
+// scope (sc1) accesses, two words per 16-byte store or load; the epoch numbers
+// the producing phase uniquely within and across launches, and a consumer
+// polls the words it needs until all carry the expected epoch.  Per-word
+// coherence is all this needs: no cache write-back/invalidate fences are
+// executed in the loop.  Every published vector exists in one copy per XCD.
+// KV-cache rows are written with device-scope stores one step before any
+// other workgroup reads them.
 #include <hip/hip_fp16.h>
 
 #include <algorithm>
@@ -46,10 +48,10 @@
 namespace gpt2dec {
 namespace {
 
-#ifndef G2_HEAD_NT
-#define G2_HEAD_NT 0
-#endif
-constexpr bool HEAD_NT = G2_HEAD_NT != 0;  // head rows: temporal loads (may stay in the memory-side cache)
+// Output-head rows are read with temporal loads: between steps they can stay
+// in the memory-side cache, which the non-temporal block-matrix stream does
+// not fill (measured faster than non-temporal head loads).
+constexpr bool HEAD_NT = false;
 constexpr int CHMIN = 64;      // positions per attention chunk before a head is split
 constexpr int PSTRIDE = 256;   // LDS room for row results (>= rows per workgroup)
 
