@@ -64,6 +64,16 @@ struct Shape {
   static constexpr int MAXCH = MAXCH_;    // attention chunks per head at most
   static constexpr int LPRH = LPRH_;      // lanes per head row
   static constexpr int LPR = LPR_;        // lanes per row of a block matrix
+  // Output head, per wave: batches streamed from memory in flight, and at most
+  // this many batches held in idle slice registers (with more than four waves
+  // a wave has 256 registers, not 512).
+  static constexpr int HEAD_BATCHES = NCW_ <= 3 ? 3 : 1;
+  static constexpr int HEAD_REG_BATCHES = NCW_ <= 3 ? 64 : 1;
+  // The MLP activation (the longest polled vector) is polled in this many
+  // equal parts by as many waves at once: the compute waves and the control
+  // wave (each part a whole number of 128-word pair loads), else by the
+  // control wave alone.
+  static constexpr int M_PARTS = (4 * E_) % (128 * (NCW_ + 1)) == 0 ? NCW_ + 1 : 1;
   // Workgroup sets, one per block matrix, over consecutive blockIdx ranges in
   // this order: QKV, attention projection, fc, MLP projection.
   static constexpr int NQ = NQ_, NA = NA_, NF = NF_, NM = NM_;
@@ -79,7 +89,7 @@ struct Shape {
   static constexpr int L_KP = L_Q + D;                   // [D] key of this position
   static constexpr int L_VP = L_KP + D;                  // [D] value of this position
   static constexpr int L_SC = L_VP + D;                  // [64] chunk scores / weights
-  static constexpr int L_FLAG = L_SC + 64;               // [4] control flags
+  static constexpr int L_FLAG = L_SC + 64;               // [4] flags: abort (control), abort (compute)
   static constexpr int L_TOTAL = L_FLAG + 4;
   static constexpr int L_HEAD = (L_TOTAL + 63) & ~63;    // output-head rows kept for the launch
 };
@@ -122,6 +132,7 @@ struct Set {
   static constexpr int NB = NP * CPR;
   static_assert(KC % LPR == 0 && S::NL % LPR == 0 && R <= 64 && R <= PSTRIDE, "slice geometry");
   static_assert(R % 2 == 0, "rows are published in pairs");
+  static_assert(LPR % 8 == 0, "chunk steps are whole int4 groups");
 };
 
 // ---- weight chunks: 4 consecutive inputs of one output row ----------------
@@ -130,38 +141,51 @@ template <> struct Chunk<WD_F32> { float4 v; };
 template <> struct Chunk<WD_F16> { uint2 v; };
 template <> struct Chunk<WD_Q4> { uint32_t q; float2 sz; };
 
-// gc: chunk index inside the layer's [N][K] matrix (= row*K/4 + k/4);
-// lofs: element offset of the layer (= layer*N*K).
-// Weights are read once per token: non-temporal loads keep them from
-// displacing the small, reused data (LayerNorm parameters, biases,
-// activations) in the caches.
-typedef float g2_v4f __attribute__((ext_vector_type(4)));
+// Weight chunks are read with buffer loads: the base of the stream (a
+// layer's slice, or a run of output-head rows) sits in a scalar resource and
+// each lane adds one 32-bit byte offset plus a constant per chunk, so no
+// 64-bit address per chunk is kept in registers.  Weights are read once per
+// token: non-temporal loads keep them from displacing the small, reused data
+// (LayerNorm parameters, biases, activations) in the caches.
 typedef float g2_v2f __attribute__((ext_vector_type(2)));
 typedef unsigned int g2_v2u __attribute__((ext_vector_type(2)));
+typedef unsigned int g2_v4u __attribute__((ext_vector_type(4)));
 
+struct WSrc {
+  __amdgpu_buffer_rsrc_t w, sz;
+};
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const void *p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, 0x7fffffff, 0x00020000);
+}
+// The chunks of m from chunk index c0 on (c0 = row*K/4 + k/4 over the layers'
+// [L][N][K] matrices; for int4 a multiple of 8, a group boundary).
+template <int WD>
+__device__ __forceinline__ WSrc wsrc(const MatW &m, size_t c0) {
+  WSrc s;
+  constexpr size_t CB = WD == WD_F32 ? 16 : WD == WD_F16 ? 8 : 2;  // bytes per chunk
+  s.w = stream_rsrc(static_cast<const char *>(m.w) + c0 * CB);
+  s.sz = s.w;
+  if constexpr (WD == WD_Q4) s.sz = stream_rsrc(m.sz + c0 / 8);
+  return s;
+}
+// Chunk cl + ck of the stream: cl per lane, ck uniform (a multiple of 8; it
+// goes into the scalar offset, so a run of loads shares one lane offset).
 template <int WD, bool NT = true>
-__device__ __forceinline__ Chunk<WD> ld_chunk(const MatW &m, size_t lofs, size_t gc) {
-  Chunk<WD> c;
+__device__ __forceinline__ Chunk<WD> ld_chunk(const WSrc &s, uint32_t cl, uint32_t ck = 0) {
+  constexpr int AUX = NT ? 2 : 0;  // nt
+  Chunk<WD> r;
   if constexpr (WD == WD_F32) {
-    if constexpr (NT) {
-      const g2_v4f v = __builtin_nontemporal_load(reinterpret_cast<const g2_v4f *>(m.w) + lofs / 4 + gc);
-      c.v = make_float4(v.x, v.y, v.z, v.w);
-    } else {
-      c.v = reinterpret_cast<const float4 *>(m.w)[lofs / 4 + gc];
-    }
+    const g2_v4u v = __builtin_amdgcn_raw_buffer_load_b128(s.w, cl * 16u, ck * 16u, AUX);
+    r.v = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
   } else if constexpr (WD == WD_F16) {
-    if constexpr (NT) {
-      const g2_v2u v = __builtin_nontemporal_load(reinterpret_cast<const g2_v2u *>(m.w) + lofs / 4 + gc);
-      c.v = make_uint2(v.x, v.y);
-    } else {
-      c.v = reinterpret_cast<const uint2 *>(m.w)[lofs / 4 + gc];
-    }
+    const g2_v2u v = __builtin_amdgcn_raw_buffer_load_b64(s.w, cl * 8u, ck * 8u, AUX);
+    r.v = make_uint2(v.x, v.y);
   } else {
-    c.q = __builtin_nontemporal_load(reinterpret_cast<const unsigned short *>(m.w) + lofs / 4 + gc);
-    const g2_v2f z = __builtin_nontemporal_load(reinterpret_cast<const g2_v2f *>(m.sz) + lofs / 32 + gc / 8);
-    c.sz = make_float2(z.x, z.y);
+    r.q = __builtin_amdgcn_raw_buffer_load_b16(s.w, cl * 2u, ck * 2u, AUX);
+    const g2_v2u z = __builtin_amdgcn_raw_buffer_load_b64(s.sz, (cl / 8u) * 8u, ck, AUX);
+    r.sz = make_float2(__uint_as_float(z.x), __uint_as_float(z.y));
   }
-  return c;
+  return r;
 }
 
 __device__ __forceinline__ float h2f(uint32_t bits16) {
@@ -503,14 +527,14 @@ __device__ __forceinline__ uint32_t epoch_of(const DecodeArgs &a, int step, int 
 // the wave, results discarded), so every load is unconditional.
 template <class ST, int WD>
 __device__ __forceinline__ void load_set(Chunk<WD> (&b)[ST::NB], const MatW &m, int layer, int rank, int lane) {
-  const size_t lofs = (size_t)layer * ST::ROWS * ST::K;
+  const WSrc src = wsrc<WD>(m, ((size_t)layer * ST::ROWS + (size_t)rank * ST::R) * ST::KC);
   const int q = lane % ST::LPR;
 #pragma unroll
   for (int t = 0; t < ST::NP; t++) {
     const int r = min(t * ST::RP + lane / ST::LPR, ST::R - 1);
-    const size_t c0 = ((size_t)rank * ST::R + r) * ST::KC + q;
+    const uint32_t c0 = (uint32_t)(r * ST::KC + q);
 #pragma unroll
-    for (int i = 0; i < ST::CPR; i++) b[t * ST::CPR + i] = ld_chunk<WD>(m, lofs, c0 + (size_t)i * ST::LPR);
+    for (int i = 0; i < ST::CPR; i++) b[t * ST::CPR + i] = ld_chunk<WD>(src, c0, (uint32_t)(i * ST::LPR));
   }
 }
 
@@ -543,7 +567,7 @@ template <class S, int WD>
 struct HeadGeo {
   static constexpr int KC = S::E / 4, LPR = S::LPRH, NPH = KC / LPR, RB = S::NL / LPR;
   static constexpr int HWD = (WD == WD_F16) ? WD_F16 : WD_F32;
-  static_assert(KC % LPR == 0 && S::NL % LPR == 0, "head geometry");
+  static_assert(KC % LPR == 0 && S::NL % LPR == 0 && LPR % 8 == 0, "head geometry");
 };
 
 // Batches of head rows that the slice registers of a workgroup of set SET
@@ -552,7 +576,8 @@ struct HeadGeo {
 template <class S, int WD, int SET>
 constexpr int head_reg_batches() {
   using HG = HeadGeo<S, WD>;
-  return (SET != SET_Q && WD == HG::HWD) ? Set<S, SET>::NB / HG::NPH : 0;
+  constexpr int n = Set<S, SET>::NB / HG::NPH;
+  return (SET != SET_Q && WD == HG::HWD) ? (n < S::HEAD_REG_BATCHES ? n : S::HEAD_REG_BATCHES) : 0;
 }
 
 // Output-head rows [hr0, hr1) of workgroup w: the rows left after each
@@ -590,13 +615,12 @@ __device__ void fill_head_lds(const DecodeArgs &a, float *lds, int lane) {
   head_range<S, WD>(a.V, (int)blockIdx.x, hr0, hr1);
   const int n = min(hr1 - hr0, a.head_lds_rows) * KC;
   if (n <= 0) return;
-  const MatW hm{a.head, nullptr};
+  const WSrc src = wsrc<HWD>(MatW{a.head, nullptr}, (size_t)hr0 * KC);
   Chunk<HWD> *dst = reinterpret_cast<Chunk<HWD> *>(lds + S::L_HEAD);
   for (int i0 = 0; i0 < n; i0 += U * S::NL) {
     Chunk<HWD> c[U];
 #pragma unroll
-    for (int u = 0; u < U; u++)
-      c[u] = ld_chunk<HWD, HEAD_NT>(hm, 0, (size_t)hr0 * KC + min(i0 + u * S::NL + lane, n - 1));
+    for (int u = 0; u < U; u++) c[u] = ld_chunk<HWD, HEAD_NT>(src, (uint32_t)min(i0 + u * S::NL + lane, n - 1));
 #pragma unroll
     for (int u = 0; u < U; u++)
       if (i0 + u * S::NL + lane < n) dst[i0 + u * S::NL + lane] = c[u];
@@ -620,15 +644,15 @@ __device__ __forceinline__ void head_prefetch_regs(const DecodeArgs &a, Chunk<WD
     head_range<S, WD>(a.V, (int)blockIdx.x, hr0, hr1);
     const int nr = hr1 - hr0, nl = min(nr, a.head_lds_rows);
     if (nr - nl <= 0) return;
-    const MatW hm{a.head, nullptr};
+    const WSrc src = wsrc<WD>(MatW{a.head, nullptr}, (size_t)hr0 * HG::KC);
     const int q = lane % HG::LPR, rl = lane / HG::LPR;
 #pragma unroll
     for (int k = 0; k < NRB; k++) {
       const int r = min(nl + k * HG::RB + rl, nr - 1);
-      const size_t c0 = (size_t)(hr0 + r) * HG::KC + q;
+      const uint32_t c0 = (uint32_t)(r * HG::KC + q);
 #pragma unroll
       for (int i = 0; i < HG::NPH; i++)
-        b[k * HG::NPH + i] = ld_chunk<WD, HEAD_NT>(hm, 0, c0 + (size_t)i * HG::LPR);
+        b[k * HG::NPH + i] = ld_chunk<WD, HEAD_NT>(src, c0, (uint32_t)(i * HG::LPR));
     }
   }
 }
@@ -640,25 +664,25 @@ __device__ bool head_rows(const DecodeArgs &a, float *lds, int lane, const Chunk
   const int *flag = reinterpret_cast<const int *>(lds + S::L_FLAG);
   float *part = lds + S::L_PART;
   const float *xs = lds + S::L_XS;
-  const MatW hm{a.head, nullptr};
   int hr0, hr1;
   head_range<S, WD>(a.V, (int)blockIdx.x, hr0, hr1);
   const int nr = hr1 - hr0;
   const int nl = min(nr, a.head_lds_rows);
   const int ng = min(nr - nl, NRB * RB);  // rows requested into registers beforehand
   const int nh = nr - nl - ng, hb = hr0 + nl + ng;
+  const WSrc src = wsrc<HWD>(MatW{a.head, nullptr}, (size_t)hb * KC);
   const int q = lane % LPR, rl = lane / LPR;
-  Chunk<HWD> h0[NPH], h1[NPH], h2[NPH];
+  constexpr int HB = S::HEAD_BATCHES;  // batches streamed from memory in flight
+  Chunk<HWD> hbuf[HB][NPH];
   auto fetch = [&](Chunk<HWD>(&b)[NPH], int r0) {
     const int r = min(r0 + rl, nh - 1);
-    const size_t c0 = (size_t)(hb + r) * KC + q;
+    const uint32_t c0 = (uint32_t)(r * KC + q);
 #pragma unroll
-    for (int i = 0; i < NPH; i++) b[i] = ld_chunk<HWD, HEAD_NT>(hm, 0, c0 + (size_t)i * LPR);
+    for (int i = 0; i < NPH; i++) b[i] = ld_chunk<HWD, HEAD_NT>(src, c0, (uint32_t)(i * LPR));
   };
   if (nh > 0) {
-    fetch(h0, 0);
-    fetch(h1, RB);
-    fetch(h2, 2 * RB);
+#pragma unroll
+    for (int k = 0; k < HB; k++) fetch(hbuf[k], k * RB);
   }
   wg_barrier();
   if (flag[0]) return false;
@@ -693,17 +717,41 @@ __device__ bool head_rows(const DecodeArgs &a, float *lds, int lane, const Chunk
   }
   if (nh > 0) {
     const int nb = nl + ng;
-    for (int r0 = 0; r0 < nh; r0 += 3 * RB) {
-      consume(h0, nb + r0 + rl, nr);
-      fetch(h0, r0 + 3 * RB);
-      consume(h1, nb + r0 + RB + rl, nr);
-      fetch(h1, r0 + 4 * RB);
-      consume(h2, nb + r0 + 2 * RB + rl, nr);
-      fetch(h2, r0 + 5 * RB);
+    for (int r0 = 0; r0 < nh; r0 += HB * RB) {
+#pragma unroll
+      for (int k = 0; k < HB; k++) {
+        consume(hbuf[k], nb + r0 + k * RB + rl, nr);
+        fetch(hbuf[k], r0 + (HB + k) * RB);
+      }
     }
   }
   wg_barrier();
   return true;
+}
+
+// Compute wave lane/64 (< M_PARTS - 1) of a set-M workgroup polls its part of
+// the MLP activation into the phase input (right after requesting its slice);
+// the control wave polls the last part.  Each wave's poll round is a quarter
+// of the whole vector, so the last part is seen sooner after it lands.  A
+// failed wait raises the compute-side abort flag, which every wave reads
+// after the next barrier.
+template <class S>
+__device__ void poll_act_part(const DecodeArgs &a, int step, int l, float *lds, int lane) {
+  constexpr int PW = S::F / S::M_PARTS, PER = PW / 64;
+  // the wave index is uniform: in a scalar register, the part's buffer
+  // resource is too (a per-lane resource would serialise the loads)
+  const int wv = __builtin_amdgcn_readfirstlane(lane / 64), wl = lane % 64;
+  if (wv >= S::M_PARTS - 1) return;
+  Waiter wt{&a, 0, 0, 0u};
+  wt.start(5 * l + 3);
+  float v[PER];
+  const uint64_t *src = a.act_t + ((size_t)l * NCOPY + my_copy()) * S::F + wv * PW;
+  if (poll_vec<PER>(src, epoch_of(a, step, 5 * l + 3), v, wl, wt)) {
+#pragma unroll
+    for (int j = 0; j < PER; j++) lds[S::L_XS + wv * PW + vidx(wl, j)] = v[j];
+  } else if (wl == 0) {
+    reinterpret_cast<int *>(lds + S::L_FLAG)[1] = 1;
+  }
 }
 
 // Compute waves of a workgroup of set SET.  Its slice of a layer sits in
@@ -742,8 +790,9 @@ __device__ void compute_set(const DecodeArgs &a, const MatW &m, float *lds, int 
         if (flag[0]) return;
         load_set<ST, WD>(b, m, l, rank, lane);
       }
+      if constexpr (SET == SET_M && S::M_PARTS > 1) poll_act_part<S>(a, step, l, lds, lane);
       wg_barrier();
-      if (flag[0]) return;
+      if (flag[0] | flag[1]) return;
       dot_set<ST, WD>(b, xs, part, lane);
       wg_barrier();
       wg_barrier();
@@ -907,7 +956,7 @@ __device__ bool poll_rows(const uint64_t *src, int n, uint32_t ep, float &v, int
 template <class S, int WD>
 __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
   constexpr int E = S::E, F = S::F, D = S::D, H = S::H, G = S::G;
-  constexpr int PE = E / 64, PF = F / 64, D4 = D / 4;
+  constexpr int PE = E / 64, D4 = D / 4;
   using SQ = Set<S, SET_Q>;
   using SA = Set<S, SET_A>;
   using SF = Set<S, SET_F>;
@@ -1194,14 +1243,20 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
           abort_all();
           return;
         }
-        float x[PF];
+        constexpr int PW = F / S::M_PARTS, PP = PW / 64;  // this wave's part of the activation
+        float x[PP];
         wt.start(5 * l + 3);
-        if (!poll_vec<PF>(a.act_t + ((size_t)l * NCOPY + my_copy()) * F, epD, x, lane, wt)) { abort_all(); return; }
+        if (!poll_vec<PP>(a.act_t + ((size_t)l * NCOPY + my_copy()) * F + (S::M_PARTS - 1) * PW, epD, x, lane,
+                          wt)) {
+          abort_all();
+          return;
+        }
 #pragma unroll
-        for (int j = 0; j < PF; j++) xs[vidx(lane, j)] = x[j];
+        for (int j = 0; j < PP; j++) xs[(S::M_PARTS - 1) * PW + vidx(lane, j)] = x[j];
         if (lane == 0) stamp(a, step, 5 * l + 4, 0, G);
         if (lane == 0) flag[0] = 0;
         wg_barrier();
+        if (flag[1]) return;  // a compute wave's wait failed (the error word is set)
         if (lane == 0) stamp(a, step, 5 * l + 4, 1, G);
         wg_barrier();
         if (lane == 0) stamp(a, step, 5 * l + 4, 2, G);
@@ -1265,6 +1320,8 @@ template <class S, int WD>
 __global__ void __launch_bounds__(S::NT, 1) decode_kernel(DecodeArgs a) {
   extern __shared__ float lds[];
   const int tid = threadIdx.x;
+  if (tid < 4) reinterpret_cast<int *>(lds + S::L_FLAG)[tid] = 0;
+  __syncthreads();
   if (tid >= S::NL) control_main<S, WD>(a, lds, tid - S::NL);
   else compute_main<S, WD>(a, lds, tid);
 }
