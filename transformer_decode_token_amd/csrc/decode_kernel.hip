@@ -53,7 +53,7 @@ namespace {
 // not fill (measured faster than non-temporal head loads).
 constexpr bool HEAD_NT = false;
 constexpr int CHMIN = 64;      // positions per attention chunk before a head is split
-constexpr int PSTRIDE = 256;   // LDS room for row results (>= rows per workgroup)
+constexpr int PSTRIDE = 512;   // LDS room for row results (>= rows per workgroup)
 
 template <int E_, int D_, int NCW_, int MAXCH_, int LPRH_, int LPR_, int NQ_, int NA_, int NF_, int NM_>
 struct Shape {
@@ -64,11 +64,13 @@ struct Shape {
   static constexpr int MAXCH = MAXCH_;    // attention chunks per head at most
   static constexpr int LPRH = LPRH_;      // lanes per head row
   static constexpr int LPR = LPR_;        // lanes per row of a block matrix
-  // Output head, per wave: batches streamed from memory in flight, and at most
-  // this many batches held in idle slice registers (with more than four waves
-  // a wave has 256 registers, not 512).
-  static constexpr int HEAD_BATCHES = NCW_ <= 3 ? 3 : 1;
-  static constexpr int HEAD_REG_BATCHES = NCW_ <= 3 ? 64 : 1;
+  // Output head, per wave: batches streamed from memory in flight, and
+  // batches wanted in registers through the head by a workgroup of set Q (its
+  // slice registers hold the next step's first slice by then) and by one of
+  // the later sets (whose idle slice registers hold part of them).
+  static constexpr int HEAD_BATCHES = 3;
+  static constexpr int HEAD_REGS_Q = 2, HEAD_REGS_LATE = 3;
+  static constexpr int HEAD_REGS_Q4_Q = 2, HEAD_REGS_Q4_LATE = 2;  // int4 (its head is fp32)
   // The MLP activation (the longest polled vector) is polled in this many
   // equal parts by as many waves at once: the compute waves and the control
   // wave (each part a whole number of 128-word pair loads), else by the
@@ -570,14 +572,31 @@ struct HeadGeo {
   static_assert(KC % LPR == 0 && S::NL % LPR == 0 && LPR % 8 == 0, "head geometry");
 };
 
-// Batches of head rows that the slice registers of a workgroup of set SET
-// hold during the output head: the late sets, when the register chunk type is
-// the head's (not for int4).
+// Batches of output-head rows that a workgroup of set SET holds in registers
+// during the head: head_reg_batches in its idle slice registers (the late
+// sets, when the register chunk type is the head's: not for int4), requested
+// after the set's last phase of each step, and head_extra_batches in registers
+// of their own, requested once and kept for the launch, up to a total per
+// weight type (none for fp16, whose head is bound by its arithmetic, not by
+// memory).
+template <class S, int WD, int SET>
+constexpr int head_reg_want() {
+  return WD == WD_Q4 ? (SET == SET_Q ? S::HEAD_REGS_Q4_Q : S::HEAD_REGS_Q4_LATE)
+                     : WD == WD_F16 ? 0 : (SET == SET_Q ? S::HEAD_REGS_Q : S::HEAD_REGS_LATE);
+}
 template <class S, int WD, int SET>
 constexpr int head_reg_batches() {
   using HG = HeadGeo<S, WD>;
-  constexpr int n = Set<S, SET>::NB / HG::NPH;
-  return (SET != SET_Q && WD == HG::HWD) ? (n < S::HEAD_REG_BATCHES ? n : S::HEAD_REG_BATCHES) : 0;
+  return (SET != SET_Q && WD == HG::HWD) ? Set<S, SET>::NB / HG::NPH : 0;
+}
+template <class S, int WD, int SET>
+constexpr int head_extra_batches() {
+  constexpr int x = head_reg_want<S, WD, SET>() - head_reg_batches<S, WD, SET>();
+  return x > 0 ? x : 0;
+}
+template <class S, int WD, int SET>
+constexpr int head_reg_total() {
+  return head_reg_batches<S, WD, SET>() + head_extra_batches<S, WD, SET>();
 }
 
 // Output-head rows [hr0, hr1) of workgroup w: the rows left after each
@@ -590,15 +609,17 @@ __device__ __forceinline__ void head_range(int V, int w, int &hr0, int &hr1) {
   const int even = V / S::G;
   // no workgroup may get more than PSTRIDE rows (the row results live in LDS)
   const int cap = min(even, max(0, PSTRIDE - even - 1));
-  const int eA = min(head_reg_batches<S, WD, SET_A>() * RB, cap);
-  const int eF = min(head_reg_batches<S, WD, SET_F>() * RB, cap);
-  const int eM = min(head_reg_batches<S, WD, SET_M>() * RB, cap);
-  const int rest = V - S::NA * eA - S::NF * eF - S::NM * eM;
+  const int eQ = min(head_reg_total<S, WD, SET_Q>() * RB, cap);
+  const int eA = min(head_reg_total<S, WD, SET_A>() * RB, cap);
+  const int eF = min(head_reg_total<S, WD, SET_F>() * RB, cap);
+  const int eM = min(head_reg_total<S, WD, SET_M>() * RB, cap);
+  const int rest = V - S::NQ * eQ - S::NA * eA - S::NF * eF - S::NM * eM;
   auto start = [&](int u) {
+    const int nq = min(u, S::NQ);
     const int na = min(max(u - Set<S, SET_A>::FIRST, 0), S::NA);
     const int nf = min(max(u - Set<S, SET_F>::FIRST, 0), S::NF);
     const int nm = min(max(u - Set<S, SET_M>::FIRST, 0), S::NM);
-    return (int)(((long long)u * rest) / S::G) + na * eA + nf * eF + nm * eM;
+    return (int)(((long long)u * rest) / S::G) + nq * eQ + na * eA + nf * eF + nm * eM;
   };
   hr0 = start(w);
   hr1 = start(w + 1);
@@ -633,32 +654,41 @@ __device__ void fill_head_lds(const DecodeArgs &a, float *lds, int lane) {
 // three batches in flight, the first three requested before the final
 // LayerNorm is ready.  Memory batches past the last row re-read that row, which keeps
 // every load unconditional.  False when the control wave aborted.
-// Request the NRB batches of head rows that follow the LDS-resident ones into
-// registers b (a set whose slice registers are idle until after the head).
-template <class S, int WD, int NRB, int NB>
-__device__ __forceinline__ void head_prefetch_regs(const DecodeArgs &a, Chunk<WD> (&b)[NB], int lane) {
+// Request head rows into registers, following the LDS-resident ones: NRB
+// batches into the idle slice registers b (late sets; once per step, after
+// the set's last phase), or (K0 = NRB) the NX batches after those into hx,
+// which keep them for the whole launch (requested once).  Batches past the
+// last row re-read that row.
+template <class S, int WD, int K0, int NK, class Dst>
+__device__ __forceinline__ void head_load_rows(const DecodeArgs &a, Dst &&put, int lane) {
   using HG = HeadGeo<S, WD>;
-  static_assert(NRB * HG::NPH <= NB && (NRB == 0 || WD == HG::HWD), "register batches");
-  if constexpr (NRB > 0) {
+  if constexpr (NK > 0) {
     int hr0, hr1;
     head_range<S, WD>(a.V, (int)blockIdx.x, hr0, hr1);
     const int nr = hr1 - hr0, nl = min(nr, a.head_lds_rows);
     if (nr - nl <= 0) return;
-    const WSrc src = wsrc<WD>(MatW{a.head, nullptr}, (size_t)hr0 * HG::KC);
+    const WSrc src = wsrc<HG::HWD>(MatW{a.head, nullptr}, (size_t)hr0 * HG::KC);
     const int q = lane % HG::LPR, rl = lane / HG::LPR;
 #pragma unroll
-    for (int k = 0; k < NRB; k++) {
-      const int r = min(nl + k * HG::RB + rl, nr - 1);
+    for (int k = 0; k < NK; k++) {
+      const int r = min(nl + (K0 + k) * HG::RB + rl, nr - 1);
       const uint32_t c0 = (uint32_t)(r * HG::KC + q);
 #pragma unroll
-      for (int i = 0; i < HG::NPH; i++)
-        b[k * HG::NPH + i] = ld_chunk<WD, HEAD_NT>(src, c0, (uint32_t)(i * HG::LPR));
+      for (int i = 0; i < HG::NPH; i++) put(k, i, ld_chunk<HG::HWD, HEAD_NT>(src, c0, (uint32_t)(i * HG::LPR)));
     }
   }
 }
-
 template <class S, int WD, int NRB, int NB>
-__device__ bool head_rows(const DecodeArgs &a, float *lds, int lane, const Chunk<WD> (&breg)[NB]) {
+__device__ __forceinline__ void head_prefetch_regs(const DecodeArgs &a, Chunk<WD> (&b)[NB], int lane) {
+  using HG = HeadGeo<S, WD>;
+  static_assert(NRB * HG::NPH <= NB && (NRB == 0 || WD == HG::HWD), "register batches");
+  if constexpr (NRB > 0)
+    head_load_rows<S, WD, 0, NRB>(a, [&](int k, int i, const Chunk<WD> &c) { b[k * HG::NPH + i] = c; }, lane);
+}
+
+template <class S, int WD, int NRB, int NX, int NB>
+__device__ bool head_rows(const DecodeArgs &a, float *lds, int lane, const Chunk<WD> (&breg)[NB],
+                          const Chunk<HeadGeo<S, WD>::HWD> (&hx)[NX > 0 ? NX : 1][HeadGeo<S, WD>::NPH]) {
   using HG = HeadGeo<S, WD>;
   constexpr int KC = HG::KC, LPR = HG::LPR, NPH = HG::NPH, RB = HG::RB, HWD = HG::HWD;
   const int *flag = reinterpret_cast<const int *>(lds + S::L_FLAG);
@@ -668,7 +698,7 @@ __device__ bool head_rows(const DecodeArgs &a, float *lds, int lane, const Chunk
   head_range<S, WD>(a.V, (int)blockIdx.x, hr0, hr1);
   const int nr = hr1 - hr0;
   const int nl = min(nr, a.head_lds_rows);
-  const int ng = min(nr - nl, NRB * RB);  // rows requested into registers beforehand
+  const int ng = min(nr - nl, (NRB + NX) * RB);  // rows requested into registers beforehand
   const int nh = nr - nl - ng, hb = hr0 + nl + ng;
   const WSrc src = wsrc<HWD>(MatW{a.head, nullptr}, (size_t)hb * KC);
   const int q = lane % LPR, rl = lane / LPR;
@@ -714,6 +744,11 @@ __device__ bool head_rows(const DecodeArgs &a, float *lds, int lane, const Chunk
         consume(c, nl + k * RB + rl, nl + ng);
       }
     }
+  }
+  if constexpr (NX > 0) {
+#pragma unroll
+    for (int k = 0; k < NX; k++)
+      if ((NRB + k) * RB < ng) consume(hx[k], nl + (NRB + k) * RB + rl, nl + ng);
   }
   if (nh > 0) {
     const int nb = nl + ng;
@@ -766,7 +801,8 @@ __device__ void compute_set(const DecodeArgs &a, const MatW &m, float *lds, int 
   // sets whose phase is not the first of a layer request the next step's first
   // slice only after the output head; meanwhile their slice registers hold head rows
   constexpr bool LATE = SET != SET_Q;
-  constexpr int NRB = head_reg_batches<S, WD, SET>();
+  constexpr int NRB = head_reg_batches<S, WD, SET>(), NX = head_extra_batches<S, WD, SET>();
+  Chunk<HeadGeo<S, WD>::HWD> hx[NX > 0 ? NX : 1][HeadGeo<S, WD>::NPH];
   const int *flag = reinterpret_cast<const int *>(lds + S::L_FLAG);
   float *part = lds + S::L_PART;
   const float *xs = lds + S::L_XS;
@@ -803,9 +839,14 @@ __device__ void compute_set(const DecodeArgs &a, const MatW &m, float *lds, int 
       } else {
         head_prefetch_regs<S, WD, NRB>(a, b, lane);  // idle slice registers take head rows
       }
-      if (step == 0 && l == 0) fill_head_lds<S, WD>(a, lds, lane);
+      if (step == 0 && l == 0) {
+        // output-head rows kept on chip for the launch: in LDS, and in hx
+        fill_head_lds<S, WD>(a, lds, lane);
+        head_load_rows<S, WD, NRB, NX>(
+            a, [&](int k, int i, const Chunk<HeadGeo<S, WD>::HWD> &c) { hx[k][i] = c; }, lane);
+      }
     }
-    if (!head_rows<S, WD, NRB>(a, lds, lane, b)) return;
+    if (!head_rows<S, WD, NRB, NX>(a, lds, lane, b, hx)) return;
     wg_barrier();  // the control wave has issued the logits and its argmax
     if (more && LATE && !defer_next) load_set<ST, WD>(b, m, 0, rank, lane);
     defer = defer_next;
