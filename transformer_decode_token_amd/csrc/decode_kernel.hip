@@ -28,7 +28,10 @@
 // rather than all of them, which shortens every hand-over.
 // Batch 1 makes every linear a matrix-vector product (0.5 flop per fp32 byte),
 // so there is no MFMA here: the kernel is bound by weight bytes and by the
-// latency of the 5L+1 dependent phases of a token.
+// latency of the 5L+1 dependent phases of a token.  All arithmetic is fp32;
+// the exponentials, reciprocals and the LayerNorm's reciprocal square root
+// use the hardware's 1-ulp instructions (v_exp_f32, v_rcp_f32, v_rsq_f32),
+// which shorten the single-wave chains of a phase.
 //
 // Synchronisation.  There is no grid barrier.  Each output element travels as
 // one 64-bit word (float bits | epoch << 32), written and read with device-
@@ -475,7 +478,7 @@ __device__ __forceinline__ void layernorm_to_lds(const float (&x)[E / 64], const
     q4[j % 4] = __builtin_fmaf(d, d, q4[j % 4]);
   }
   const float var = wave_sum_all((q4[0] + q4[1]) + (q4[2] + q4[3])) * (1.0f / (float)E);
-  const float r = 1.0f / sqrtf(var + eps);
+  const float r = __builtin_amdgcn_rsqf(var + eps);  // v_rsq_f32 (1 ulp)
 #pragma unroll
   for (int j = 0; j < PER; j++) dst[vidx(lane, j)] = __builtin_fmaf((x[j] - mean) * r, g[j], b[j]);
 }
@@ -487,7 +490,7 @@ __device__ __forceinline__ float gelu_new(float f) {
   t = t * 0.044715f;
   t = t + f;
   t = t * 1.5957691216057308f;
-  t = 1.0f / (1.0f + expf(-t));
+  t = __builtin_amdgcn_rcpf(1.0f + __expf(-t));  // v_exp_f32, v_rcp_f32 (1 ulp each)
   return f * t;
 }
 
@@ -940,8 +943,8 @@ struct AttChunk {
       sp = seg_bcast_last<D4>(seg_sum_last<D4>(dot4(kp, q4, 0.f)), lane) * scale;
     }
     m = wave_max_all(valid ? fmaxf(s, sp) : sp);
-    const float e = valid ? expf(s - m) : 0.f;
-    const float ep = has_p ? expf(sp - m) : 0.f;
+    const float e = valid ? __expf(s - m) : 0.f;
+    const float ep = has_p ? __expf(sp - m) : 0.f;
     lsum = wave_sum_all(e) + ep;
     float4 oo = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -1146,7 +1149,8 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
           }
         };
         if (nch == 1) {
-          publish_head(make_float4(o.x / lsum, o.y / lsum, o.z / lsum, o.w / lsum));
+          const float rl = __builtin_amdgcn_rcpf(lsum);
+          publish_head(make_float4(o.x * rl, o.y * rl, o.z * rl, o.w * rl));
         } else if (ic > 0) {
           // this chunk's (o, m, l) for chunk 0 of the head, as word pairs
           const auto prs = __builtin_amdgcn_make_buffer_rsrc(
@@ -1205,7 +1209,7 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
             lcl = scr[(lane - 1) * SP + D + 1];
           }
           const float M = wave_max_all(mcl);
-          const float fl = lane < nch ? expf(mcl - M) : 0.f;
+          const float fl = lane < nch ? __expf(mcl - M) : 0.f;
           const float Ls = wave_sum_all(lcl * fl);
           const float f0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fl), 0));
           float4 O = make_float4(o.x * f0, o.y * f0, o.z * f0, o.w * f0);
@@ -1217,7 +1221,8 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
             O.z = __builtin_fmaf(oc.z, fc, O.z);
             O.w = __builtin_fmaf(oc.w, fc, O.w);
           }
-          publish_head(make_float4(O.x / Ls, O.y / Ls, O.z / Ls, O.w / Ls));
+          const float rl = __builtin_amdgcn_rcpf(Ls);
+          publish_head(make_float4(O.x * rl, O.y * rl, O.z * rl, O.w * rl));
         }
         if (lane == 0) stamp(a, step, 5 * l + 1, 3, G);
         if (set == SET_M) wg_barrier();  // the compute waves may now request this layer's slice
