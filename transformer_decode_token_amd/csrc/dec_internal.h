@@ -48,7 +48,7 @@ struct DecodeArgs {
   uint64_t *xa_t;                    // [L][C][E]      tagged residual after attention
   uint64_t *act_t;                   // [L][C][F]      tagged gelu activations
   uint64_t *xb_t;                    // [L][C][E]      tagged residual after the MLP
-  uint64_t *amax_t;                  // [C][2][G]      tagged per-workgroup argmax (value, index)
+  uint64_t *amax_t;                  // [C][G][2]      tagged per-workgroup argmax (value, index)
   float *logits;                     // [V]            logits of the last step
   int *out_ids;                      // greedy ids
   int *err;                          // [4] flag, workgroup, phase, epoch (device-side wait timeout)

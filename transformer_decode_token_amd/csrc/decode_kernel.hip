@@ -872,16 +872,19 @@ __device__ __forceinline__ bool reduce_argmax(const DecodeArgs &a, uint32_t ep, 
   constexpr int G = S::G;
   float bv = -INFINITY;
   uint32_t bi = 0xffffffffu;
+  // workgroup g's (value, index) word pair is one 16-byte load
+  const auto ars = __builtin_amdgcn_make_buffer_rsrc(a.amax_t + (size_t)my_copy() * 2 * G, (short)0, 2 * G * 8,
+                                                     0x00020000);
   while (true) {
     bool ok = true;
     float v = -INFINITY;
     uint32_t idx = 0xffffffffu;
+#pragma unroll
     for (int g0 = lane; g0 < G; g0 += 64) {
-      const uint64_t *am = a.amax_t + (size_t)my_copy() * 2 * G;
-      const uint64_t xv = tld(am + g0), xi = tld(am + G + g0);
-      ok &= tag_is(xv, ep) && tag_is(xi, ep);
-      const float cv = payload(xv);
-      const uint32_t ci = (uint32_t)xi;
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(ars, (uint32_t)(g0 * 16), 0, AUX_SC1);
+      ok &= (x[1] == ep) && (x[3] == ep);
+      const float cv = __uint_as_float(x[0]);
+      const uint32_t ci = x[2];
       if (cv > v || (cv == v && ci < idx)) { v = cv; idx = ci; }
     }
     if (__all(ok)) { bv = v; bi = idx; break; }
@@ -1336,18 +1339,26 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
       const int nr = hr1 - hr0;
       float bv = -INFINITY;
       uint32_t bi = 0xffffffffu;
-      for (int r = lane; r < nr; r += 64) {
-        const float v = part[r];
-        a.logits[hr0 + r] = v;
-        if (v > bv || (v == bv && (uint32_t)(hr0 + r) < bi)) { bv = v; bi = (uint32_t)(hr0 + r); }
+      // (a fixed trip count, so that the row results are read from LDS in one burst)
+#pragma unroll
+      for (int k = 0; k < PSTRIDE / 64; k++) {
+        const int r = lane + 64 * k;
+        if (r < nr) {
+          const float v = part[r];
+          a.logits[hr0 + r] = v;
+          if (v > bv || (v == bv && (uint32_t)(hr0 + r) < bi)) {
+            bv = v;
+            bi = (uint32_t)(hr0 + r);
+          }
+        }
       }
       bi = wave_argmax(bv, bi, &bv);
-      if (lane == 0) {
-        #pragma unroll
-        for (int c = 0; c < NCOPY; c++) {
-          tst(a.amax_t + (size_t)c * 2 * G + w, bv, epH);
-          tst_u(a.amax_t + (size_t)c * 2 * G + G + w, bi, epH);
-        }
+      // (value, index) as one word pair per copy: lane c writes copy c
+      if (lane < NCOPY) {
+        const auto ars = __builtin_amdgcn_make_buffer_rsrc(a.amax_t, (short)0, NCOPY * 2 * G * 8, 0x00020000);
+        typedef unsigned int g2_v4u_ __attribute__((ext_vector_type(4)));
+        const g2_v4u_ pr = {__float_as_uint(bv), epH, bi, epH};
+        __builtin_amdgcn_raw_buffer_store_b128(pr, ars, (uint32_t)(((lane * G + w) * 2) * 8), 0, AUX_SC1);
       }
       if (lane == 0) stamp(a, step, 5 * a.L, 3, G);
       wg_barrier();  // stores issued: the compute waves may request the next slices
