@@ -45,6 +45,7 @@
 #include <hip/hip_fp16.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "dec_internal.h"
 
@@ -58,12 +59,17 @@ constexpr bool HEAD_NT = false;
 constexpr int CHMIN = 64;      // positions per attention chunk before a head is split
 constexpr int PSTRIDE = 512;   // LDS room for row results (>= rows per workgroup)
 
-template <int E_, int D_, int NCW_, int MAXCH_, int LPRH_, int LPR_, int NQ_, int NA_, int NF_, int NM_>
+template <int E_, int D_, int NCW_, int MAXCH_, int LPRH_, int LPR_, int NQ_, int NA_, int NF_, int NM_,
+          int CD_ = 0>
 struct Shape {
   static constexpr int E = E_, D = D_, H = E_ / D_, F = 4 * E_;
   static constexpr int NCW = NCW_;        // compute waves
   static constexpr int NL = 64 * NCW_;    // compute lanes
   static constexpr int NT = NL + 64;      // threads: compute waves + control wave
+  // CD: the control wave takes a share of every block-matrix slice too (it
+  // would otherwise idle through the dot products); NLD lanes share a slice.
+  static constexpr bool CD = CD_ != 0;
+  static constexpr int NLD = NL + (CD_ ? 64 : 0);
   static constexpr int MAXCH = MAXCH_;    // attention chunks per head at most
   static constexpr int LPRH = LPRH_;      // lanes per head row
   static constexpr int LPR = LPR_;        // lanes per row of a block matrix
@@ -99,12 +105,16 @@ struct Shape {
   static constexpr int L_HEAD = (L_TOTAL + 63) & ~63;    // output-head rows kept for the launch
 };
 
-// 124M shape: 256 workgroups x (3 compute + 1 control) waves in sets of 64
-// (QKV, 36 rows each), 32 (attention projection, 24 rows), 64 (fc, 48 rows)
-// and 96 (MLP projection, 8 rows); each set streams an equal share of its
-// matrix, so every workgroup reads 74 to 147 KB of fp32 weights per layer.
-// (Set sizes chosen by measurement among the partitions that fit.)
+// 124M shape: 256 workgroups x (3 compute + 1 control) waves.  fp32: sets of
+// 64 (QKV, 36 rows each), 32 (attention projection, 24 rows), 64 (fc, 48
+// rows) and 96 (MLP projection, 8 rows), so every workgroup reads 74 to 147
+// KB of weights per layer.  fp16 and int4, whose dot products cost more
+// vector instructions per weight: the control wave takes a share of every
+// slice too, in sets of 72 (32 rows), 24 (32 rows), 64 (48 rows) and 96 (8
+// rows), row counts that 16 (64 for K = 3072) rows per pass of 256 lanes
+// divide.  (Set sizes and the split chosen by measurement.)
 using ShapeS = Shape<768, 64, 3, 16, 16, 16, 64, 32, 64, 96>;
+using ShapeSC = Shape<768, 64, 3, 16, 16, 16, 72, 24, 64, 96, 1>;
 // tiny shape: 32 workgroups x (2 compute + 1 control) waves, sets 8/4/16/4.
 using ShapeT = Shape<128, 32, 2, 8, 8, 8, 8, 4, 16, 4>;
 
@@ -131,11 +141,11 @@ struct Set {
   static constexpr int R = ROWS / N;
   static constexpr int KC = K / 4;
   static constexpr int LPR = lpr_for(KC, S::LPR);
-  static constexpr int RP = S::NL / LPR;
+  static constexpr int RP = S::NLD / LPR;
   static constexpr int NP = (R + RP - 1) / RP;
   static constexpr int CPR = KC / LPR;
   static constexpr int NB = NP * CPR;
-  static_assert(KC % LPR == 0 && S::NL % LPR == 0 && R <= 64 && R <= PSTRIDE, "slice geometry");
+  static_assert(KC % LPR == 0 && S::NLD % LPR == 0 && R <= 64 && R <= PSTRIDE, "slice geometry");
   static_assert(R % 2 == 0, "rows are published in pairs");
   static_assert(LPR % 8 == 0, "chunk steps are whole int4 groups");
 };
@@ -1017,8 +1027,10 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
   int tok = 0;
   Waiter wt{&a, 0, 0, 0u};
   // Parameters of the set's next phase are requested right after its phase,
-  // a whole layer before use: the LayerNorm of the phase (sets Q, F) and the
-  // bias of row rank*R + lane.  The final LayerNorm is read once.
+  // a whole layer before use: the bias of row rank*R + lane and LayerNorm 1
+  // (set Q) or 2 (set F); the final LayerNorm is read once.  With a slice
+  // share (S::CD), which needs the registers, LayerNorm 2 and the final
+  // LayerNorm are requested instead as their phase's input is polled.
   float g[PE], bt[PE], gf[PE], bf[PE];
   float bias = 0.f;
   auto fetch_ln = [&](float (&gg)[PE], float (&bb)[PE], const float *gs, const float *bs) {
@@ -1035,14 +1047,52 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
     } else if (set == SET_A) {
       bias = lane < SA::R ? a.bap[l * E + rank * SA::R + lane] : 0.f;
     } else if (set == SET_F) {
-      fetch_ln(g, bt, a.ln2w + l * E, a.ln2b + l * E);
+      if constexpr (!S::CD) fetch_ln(g, bt, a.ln2w + l * E, a.ln2b + l * E);
       bias = lane < SF::R ? a.bfc[l * F + rank * SF::R + lane] : 0.f;
     } else {
       bias = lane < SM::R ? a.bpr[l * E + rank * SM::R + lane] : 0.f;
     }
   };
-  fetch_ln(gf, bf, a.lnfw, a.lnfb);
+  if constexpr (!S::CD) fetch_ln(gf, bf, a.lnfw, a.lnfb);
   fetch_params(0);
+  // This wave's share of its set's slice (lanes NL.. of the slice geometry),
+  // requested and used like the compute waves' (see compute_set): consumed
+  // between the phase's first two barriers, the next layer's requested after
+  // the third (set M: after this step's attention item, if it has one; sets
+  // other than Q: the next step's first slice after the head).
+  constexpr int CBN = S::CD ? (SF::NB > SQ::NB ? (SF::NB > SM::NB ? SF::NB : SM::NB)
+                                               : (SQ::NB > SM::NB ? SQ::NB : SM::NB))
+                            : 1;
+  Chunk<WD> cb[CBN > SA::NB || !S::CD ? CBN : SA::NB];
+  auto ctl_load = [&](int layer) {
+    if constexpr (S::CD) {
+      const int cl = S::NL + lane;
+      if (set == SET_Q) load_set<SQ, WD>(*reinterpret_cast<Chunk<WD>(*)[SQ::NB]>(cb), a.qkv, layer, rank, cl);
+      else if (set == SET_A) load_set<SA, WD>(*reinterpret_cast<Chunk<WD>(*)[SA::NB]>(cb), a.ap, layer, rank, cl);
+      else if (set == SET_F) load_set<SF, WD>(*reinterpret_cast<Chunk<WD>(*)[SF::NB]>(cb), a.fc, layer, rank, cl);
+      else load_set<SM, WD>(*reinterpret_cast<Chunk<WD>(*)[SM::NB]>(cb), a.pr, layer, rank, cl);
+    }
+  };
+  auto ctl_dot = [&]() {
+    if constexpr (S::CD) {
+      const int cl = S::NL + lane;
+      float *pt = lds + S::L_PART;
+      if (set == SET_Q) dot_set<SQ, WD>(*reinterpret_cast<Chunk<WD>(*)[SQ::NB]>(cb), xs, pt, cl);
+      else if (set == SET_A) dot_set<SA, WD>(*reinterpret_cast<Chunk<WD>(*)[SA::NB]>(cb), xs, pt, cl);
+      else if (set == SET_F) dot_set<SF, WD>(*reinterpret_cast<Chunk<WD>(*)[SF::NB]>(cb), xs, pt, cl);
+      else dot_set<SM, WD>(*reinterpret_cast<Chunk<WD>(*)[SM::NB]>(cb), xs, pt, cl);
+    }
+  };
+  auto defers = [&](int st) { return set == SET_M && st < a.nsteps && has_att_item<S>(a.pos0 + st, w); };
+  int cur_step = 0;
+  auto ctl_after_phase = [&](int l) {
+    if (l + 1 < a.L) {
+      if (!defers(cur_step)) ctl_load(l + 1);
+    } else if (cur_step + 1 < a.nsteps && set == SET_Q) {
+      ctl_load(0);
+    }
+  };
+  if (!defers(0)) ctl_load(0);
   auto abort_all = [&]() {
     if (lane == 0) flag[0] = 1;
     wg_barrier();
@@ -1050,6 +1100,7 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
   const bool needs_tok = (set == SET_Q || set == SET_A);
   for (int step = 0; step < a.nsteps; step++) {
     const int p = a.pos0 + step;
+    cur_step = step;
     // token of this step: fed, or the argmax of the previous step
     if (step < a.n_feed) tok = a.feed[step];
     if (step > 0 && needs_tok) {
@@ -1069,6 +1120,10 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
     const bool ilast = (it1 == p + 1);
     const int itg = ilast ? p : it1;  // cache rows it0..itg-1
     for (int l = 0; l < a.L; l++) {
+      // (with a slice share: an opaque copy of the lane index, so that per-lane
+      // addresses are recomputed in each layer instead of being hoisted out of
+      // the loop and held in registers)
+      if constexpr (S::CD) asm volatile("" : "+v"(lane));
       const uint32_t epA = epoch_of(a, step, 5 * l + 0), epB = epA + 1, epC = epA + 2, epD = epA + 3,
                      epE = epA + 4;
       const int lnext = l + 1 < a.L ? l + 1 : 0;
@@ -1091,6 +1146,7 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
         if (lane == 0) flag[0] = 0;
         wg_barrier();
         if (lane == 0) stamp(a, step, 5 * l + 0, 1, G);
+        ctl_dot();
         wg_barrier();
         if (lane == 0) stamp(a, step, 5 * l + 0, 2, G);
         if (lane < SQ::R)
@@ -1099,6 +1155,7 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
         if (lane == 0) stamp(a, step, 5 * l + 0, 3, G);
         wg_barrier();  // stores issued: the compute waves may request the next slice
         fetch_params(lnext);
+        ctl_after_phase(l);
       }
       // ---------------- B: attention chunk (control wave only)
       if (has_item) {
@@ -1228,7 +1285,10 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
           publish_head(make_float4(O.x * rl, O.y * rl, O.z * rl, O.w * rl));
         }
         if (lane == 0) stamp(a, step, 5 * l + 1, 3, G);
-        if (set == SET_M) wg_barrier();  // the compute waves may now request this layer's slice
+        if (set == SET_M) {
+          wg_barrier();  // the compute waves may now request this layer's slice
+          ctl_load(l);   // and so may this wave
+        }
       }
       // ---------------- C: attention projection + residual (set A)
       if (set == SET_A) {
@@ -1255,6 +1315,7 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
         if (lane == 0) flag[0] = 0;
         wg_barrier();
         if (lane == 0) stamp(a, step, 5 * l + 2, 1, G);
+        ctl_dot();
         wg_barrier();
         if (lane == 0) stamp(a, step, 5 * l + 2, 2, G);
         if (lane < SA::R) {
@@ -1264,9 +1325,11 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
         if (lane == 0) stamp(a, step, 5 * l + 2, 3, G);
         wg_barrier();  // stores issued: the compute waves may request the next slice
         fetch_params(lnext);
+        ctl_after_phase(l);
       }
       // ---------------- D: LayerNorm 2 + fc + gelu_new (set F)
       if (set == SET_F) {
+        if constexpr (S::CD) fetch_ln(g, bt, a.ln2w + l * E, a.ln2b + l * E);  // (arrives during the poll)
         float x[PE];
         wt.start(5 * l + 2);
         if (!poll_vec<PE>(a.xa_t + ((size_t)l * NCOPY + my_copy()) * E, epC, x, lane, wt)) { abort_all(); return; }
@@ -1275,6 +1338,7 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
         if (lane == 0) flag[0] = 0;
         wg_barrier();
         if (lane == 0) stamp(a, step, 5 * l + 3, 1, G);
+        ctl_dot();
         wg_barrier();
         if (lane == 0) stamp(a, step, 5 * l + 3, 2, G);
         if (lane < SF::R)
@@ -1283,6 +1347,7 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
         if (lane == 0) stamp(a, step, 5 * l + 3, 3, G);
         wg_barrier();  // stores issued: the compute waves may request the next slice
         fetch_params(lnext);
+        ctl_after_phase(l);
       }
       // ---------------- E: MLP projection + residual (set M)
       if (set == SET_M) {
@@ -1307,6 +1372,7 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
         wg_barrier();
         if (flag[1]) return;  // a compute wave's wait failed (the error word is set)
         if (lane == 0) stamp(a, step, 5 * l + 4, 1, G);
+        ctl_dot();
         wg_barrier();
         if (lane == 0) stamp(a, step, 5 * l + 4, 2, G);
         if (lane < SM::R) {
@@ -1316,11 +1382,13 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
         if (lane == 0) stamp(a, step, 5 * l + 4, 3, G);
         wg_barrier();  // stores issued: the compute waves may request the next slice
         fetch_params(lnext);
+        ctl_after_phase(l);
       }
     }
     // ---------------- H: final LayerNorm + head + local argmax
     {
       const uint32_t epH = epoch_of(a, step, 5 * a.L);
+      if constexpr (S::CD) fetch_ln(gf, bf, a.lnfw, a.lnfb);  // (arrives while the input is polled)
       float x[PE];
       wt.start(5 * a.L - 1);
       if (!poll_vec<PE>(a.xb_t + ((size_t)(a.L - 1) * NCOPY + my_copy()) * E, epH - 1, x, lane, wt)) {
@@ -1362,6 +1430,7 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
       }
       if (lane == 0) stamp(a, step, 5 * a.L, 3, G);
       wg_barrier();  // stores issued: the compute waves may request the next slices
+      if (step + 1 < a.nsteps && set != SET_Q && !defers(step + 1)) ctl_load(0);
     }
   }
   // the last step's greedy id
@@ -1400,12 +1469,20 @@ int head_lds_rows_for(int wd, size_t lds) {
   return lds > base ? (int)((lds - base) / row) : 0;
 }
 
+// The weight types a shape is built for: the 124M shape in two variants
+// (fp32; fp16 and int4), the tiny shape for all three.
+template <class S>
+constexpr bool shape_has(int wd) {
+  return std::is_same<S, ShapeS>::value ? wd == WD_F32 : std::is_same<S, ShapeSC>::value ? wd != WD_F32 : true;
+}
 template <class S>
 const void *kernel_for(int wd) {
-  switch (wd) {
-  case WD_F32: return reinterpret_cast<const void *>(&decode_kernel<S, WD_F32>);
-  case WD_F16: return reinterpret_cast<const void *>(&decode_kernel<S, WD_F16>);
-  case WD_Q4: return reinterpret_cast<const void *>(&decode_kernel<S, WD_Q4>);
+  if (wd == WD_F32) {
+    if constexpr (shape_has<S>(WD_F32)) return reinterpret_cast<const void *>(&decode_kernel<S, WD_F32>);
+  } else if (wd == WD_F16) {
+    if constexpr (shape_has<S>(WD_F16)) return reinterpret_cast<const void *>(&decode_kernel<S, WD_F16>);
+  } else if (wd == WD_Q4) {
+    if constexpr (shape_has<S>(WD_Q4)) return reinterpret_cast<const void *>(&decode_kernel<S, WD_Q4>);
   }
   return nullptr;
 }
@@ -1447,19 +1524,22 @@ void info_t(ShapeInfo *o) {
 }  // namespace
 
 bool shape_info(int E, int D, ShapeInfo *out) {
+  static_assert(ShapeS::G == ShapeSC::G && ShapeS::NT == ShapeSC::NT && ShapeS::MAXCH == ShapeSC::MAXCH,
+                "the two 124M variants share their launch geometry");
   if (E == ShapeS::E && D == ShapeS::D) { info_t<ShapeS>(out); return true; }
   if (E == ShapeT::E && D == ShapeT::D) { info_t<ShapeT>(out); return true; }
   return false;
 }
 
 hipError_t launch_decode(int E, int D, int wd, const DecodeArgs &a, hipStream_t s) {
-  if (E == ShapeS::E && D == ShapeS::D) return launch_t<ShapeS>(wd, a, s);
+  if (E == ShapeS::E && D == ShapeS::D) return wd == WD_F32 ? launch_t<ShapeS>(wd, a, s) : launch_t<ShapeSC>(wd, a, s);
   if (E == ShapeT::E && D == ShapeT::D) return launch_t<ShapeT>(wd, a, s);
   return hipErrorInvalidValue;
 }
 
 hipError_t decode_occupancy(int E, int D, int wd, int *blocks) {
-  if (E == ShapeS::E && D == ShapeS::D) return occupancy_t<ShapeS>(wd, blocks);
+  if (E == ShapeS::E && D == ShapeS::D)
+    return wd == WD_F32 ? occupancy_t<ShapeS>(wd, blocks) : occupancy_t<ShapeSC>(wd, blocks);
   if (E == ShapeT::E && D == ShapeT::D) return occupancy_t<ShapeT>(wd, blocks);
   return hipErrorInvalidValue;
 }
