@@ -315,6 +315,21 @@ __device__ __forceinline__ float seg_reduce_scatter(const float (&in)[W], int la
   return x[0];
 }
 
+// v + v of lane (lane ^ sh).  Across 16-lane rows (sh 16 or 32) by the
+// permlane swaps, which exchange rows between two registers without LDS: with
+// both operands v, the two results hold v and its partner in every lane.
+__device__ __forceinline__ float xor_sum(float v, int sh) {
+  if (sh == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  if (sh == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  return v + __shfl_xor(v, sh);
+}
+
 // Whole-wave sum / max, the same bits in every lane.
 __device__ __forceinline__ float wave_sum_all(float v) {
   const float t = seg_sum_last<64>(v);
@@ -976,10 +991,10 @@ struct AttChunk {
     }
 #pragma unroll
     for (int sh = D4; sh < 64; sh <<= 1) {
-      oo.x += __shfl_xor(oo.x, sh);
-      oo.y += __shfl_xor(oo.y, sh);
-      oo.z += __shfl_xor(oo.z, sh);
-      oo.w += __shfl_xor(oo.w, sh);
+      oo.x = xor_sum(oo.x, sh);
+      oo.y = xor_sum(oo.y, sh);
+      oo.z = xor_sum(oo.z, sh);
+      oo.w = xor_sum(oo.w, sh);
     }
     o = oo;
   }
