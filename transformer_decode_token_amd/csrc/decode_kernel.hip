@@ -99,7 +99,7 @@ struct Shape {
   static constexpr int L_Q = L_PART + PSTRIDE;           // [D] query of the attention item
   static constexpr int L_KP = L_Q + D;                   // [D] key of this position
   static constexpr int L_VP = L_KP + D;                  // [D] value of this position
-  static constexpr int L_SC = L_VP + D;                  // [64] chunk scores / weights
+  static constexpr int L_SC = L_VP + D;                  // [64] attention weights (transposed)
   static constexpr int L_FLAG = L_SC + 64;               // [4] flags: abort (control), abort (compute)
   static constexpr int L_TOTAL = L_FLAG + 4;
   static constexpr int L_HEAD = (L_TOTAL + 63) & ~63;    // output-head rows kept for the launch
@@ -921,69 +921,86 @@ __device__ __forceinline__ bool reduce_argmax(const DecodeArgs &a, uint32_t ep, 
 }
 
 // One attention chunk of head h over positions t0..t1-1 on the control wave,
-// following the attn_decode kernel: scores q.k * (1/sqrt(D)), subtract the
-// maximum, exp; the chunk's (o = sum e_t v_t, m = max, l = sum e_t).  Row p
-// (the current position) comes from LDS, the others from the cache.  Lane
-// (g, d4) handles rows t0 + g + RPL*it and dimensions 4*d4..4*d4+3.
+// following the model file's decode attention: scores q.k * (1/sqrt(D)),
+// minus their maximum, exponentials; the chunk's (o = sum e_t v_t, m = max,
+// l = sum e_t).  Row p (the current position) comes from LDS, the others from
+// the cache.  Scores: lane t holds the whole key row t0 + t and forms its
+// score alone, against the query read from LDS (every lane the same
+// addresses).  Values: lane (g, d4) holds rows t0 + g + RPL*it, dimensions
+// 4*d4..4*d4+3; the weights reach it through LDS, and the RPL row groups are
+// combined by row exchanges.  No cross-lane reduction on the score side.
 template <class S>
 struct AttChunk {
   static constexpr int D = S::D, D4 = D / 4, RPL = 64 / D4, IT = 64 / RPL;
-  float4 k[IT], v[IT];
+  float4 k[D4], v[IT];
   __device__ void fetch(const DecodeArgs &a, int l, int h, int t0, int tg, int lane) {
     const float *K = a.kc + ((size_t)(l * S::H + h) * a.P) * D;
     const float *V = a.vc + ((size_t)(l * S::H + h) * a.P) * D;
     const int g = lane / D4, d4 = lane % D4;
+    const int tk = t0 + lane;
+#pragma unroll
+    for (int i = 0; i < D4; i++) {
+      k[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (tk < tg) k[i] = reinterpret_cast<const float4 *>(K + (size_t)tk * D)[i];
+    }
 #pragma unroll
     for (int it = 0; it < IT; it++) {
       const int t = t0 + g + RPL * it;
-      k[it] = make_float4(0.f, 0.f, 0.f, 0.f);
       v[it] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (t < tg) {
-        k[it] = reinterpret_cast<const float4 *>(K + (size_t)t * D)[d4];
-        v[it] = reinterpret_cast<const float4 *>(V + (size_t)t * D)[d4];
-      }
+      if (t < tg) v[it] = reinterpret_cast<const float4 *>(V + (size_t)t * D)[d4];
     }
   }
   // The chunk's m, lsum and o (dims 4*d4..4*d4+3, summed over all its rows)
-  // in every lane.  The IT (= D4) partial scores of a lane are reduced over
-  // its D4-lane segment by a reduce-scatter that leaves lane j of the segment
-  // with the full score of the segment's row it = j, so each lane takes one
-  // exponential; the weights are then broadcast back along the segment for
-  // the weighted sum of values, and the RPL row groups are combined with xor
-  // shuffles.  Everything stays in registers.
-  __device__ void run(const float *lds, int p, int t0, int t1, int tg, int lane, float &m, float &lsum,
-                      float4 &o) {
-    static_assert(IT == D4, "one row per lane of a segment");
+  // in every lane.
+  __device__ void run(float *lds, int p, int t0, int t1, int tg, int lane, float &m, float &lsum, float4 &o) {
     const int g = lane / D4, d4 = lane % D4;
     const float scale = 1.0f / sqrtf((float)D);
-    const float4 q4 = reinterpret_cast<const float4 *>(lds + S::L_Q)[d4];
-    const bool has_p = tg < t1;  // this position closes the chunk
-    float x[IT];
+    const float4 *q4 = reinterpret_cast<const float4 *>(lds + S::L_Q);
+    // four partial sums: shorter dependency chains
+    float sa = 0.f, sb = 0.f, sc = 0.f, sd = 0.f;
 #pragma unroll
-    for (int it = 0; it < IT; it++) x[it] = dot4(k[it], q4, 0.f);
-    const float s = seg_reduce_scatter<D4>(x, lane) * scale;  // row t0 + g + RPL*d4
-    const bool valid = t0 + g + RPL * d4 < tg;
+    for (int i = 0; i < D4; i += 4) {
+      sa = dot4(k[i], q4[i], sa);
+      sb = dot4(k[i + 1], q4[i + 1], sb);
+      sc = dot4(k[i + 2], q4[i + 2], sc);
+      sd = dot4(k[i + 3], q4[i + 3], sd);
+    }
+    const float s = ((sa + sb) + (sc + sd)) * scale;  // row t0 + lane
+    const bool has_p = tg < t1;                        // this position closes the chunk
     float sp = -INFINITY;
     float4 vp = make_float4(0.f, 0.f, 0.f, 0.f);
     if (has_p) {
       const float4 kp = reinterpret_cast<const float4 *>(lds + S::L_KP)[d4];
       vp = reinterpret_cast<const float4 *>(lds + S::L_VP)[d4];
-      sp = seg_bcast_last<D4>(seg_sum_last<D4>(dot4(kp, q4, 0.f)), lane) * scale;
+      sp = seg_bcast_last<D4>(seg_sum_last<D4>(dot4(kp, q4[d4], 0.f)), lane) * scale;
     }
-    m = wave_max_all(valid ? fmaxf(s, sp) : sp);
-    const float e = valid ? __expf(s - m) : 0.f;
-    const float ep = has_p ? __expf(sp - m) : 0.f;
-    lsum = wave_sum_all(e) + ep;
+    const bool valid = t0 + lane < tg;
+    const bool isp = has_p && lane == p - t0;
+    const float sl = valid ? s : (isp ? sp : -INFINITY);
+    m = wave_max_all(sl);
+    const float e = (valid || isp) ? __expf(sl - m) : 0.f;
+    lsum = wave_sum_all(e);
+    // the weights, transposed for the value side: row t = g' + RPL*it' at g'*IT + it'
+    lds[S::L_SC + (lane % RPL) * IT + lane / RPL] = e;
+    float w[IT];
+#pragma unroll
+    for (int j = 0; j < IT; j += 4) {
+      const float4 x = reinterpret_cast<const float4 *>(lds + S::L_SC + g * IT)[j / 4];
+      w[j] = x.x;
+      w[j + 1] = x.y;
+      w[j + 2] = x.z;
+      w[j + 3] = x.w;
+    }
     float4 oo = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int it = 0; it < IT; it++) {
-      const float w = seg_bcast<D4>(e, it, lane);
-      oo.x = __builtin_fmaf(w, v[it].x, oo.x);
-      oo.y = __builtin_fmaf(w, v[it].y, oo.y);
-      oo.z = __builtin_fmaf(w, v[it].z, oo.z);
-      oo.w = __builtin_fmaf(w, v[it].w, oo.w);
+      oo.x = __builtin_fmaf(w[it], v[it].x, oo.x);
+      oo.y = __builtin_fmaf(w[it], v[it].y, oo.y);
+      oo.z = __builtin_fmaf(w[it], v[it].z, oo.z);
+      oo.w = __builtin_fmaf(w[it], v[it].w, oo.w);
     }
     if (has_p && ((p - t0) % RPL) == g) {
+      const float ep = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), p - t0));
       oo.x = __builtin_fmaf(ep, vp.x, oo.x);
       oo.y = __builtin_fmaf(ep, vp.y, oo.y);
       oo.z = __builtin_fmaf(ep, vp.z, oo.z);
