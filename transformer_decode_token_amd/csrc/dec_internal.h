@@ -41,6 +41,11 @@ struct DecodeArgs {
   const void *head;                  // [V][E] output head (fp32 = wte, or fp16 copy)
   const float *wpe;                  // [P][E]
   const float *lnfw, *lnfb;          // [E]
+  // LayerNorm folded into the next linear (the gain scales the input; per row,
+  // g* = W.gain and c* = W.shift + bias, so that row = rstd*(W.(gain*x) - mean*g*) + c*)
+  const float *gqkv, *cqkv;          // [L][3E]  QKV rows, LayerNorm 1
+  const float *gfc, *cfc;            // [L][F]   fc rows, LayerNorm 2
+  const float *ghead, *chead;        // [V]      head rows, final LayerNorm (no bias)
   float *kc, *vc;                    // [L][H][P][D] KV cache
   uint64_t *qkv_t;                   // [L][C][3E]     tagged QKV outputs (C = kTagCopies copies)
   uint64_t *att_t;                   // [L][H][MAXCH][D+2] tagged attention chunk partials
@@ -93,5 +98,11 @@ hipError_t convert_f16(const float *src, void *dst, size_t n, hipStream_t s);
 hipError_t debug_dequant(int wd, const MatW &m, size_t layer_offset_elems, int N, int K, float *dst,
                          hipStream_t s);
 hipError_t fill_f32(float *dst, size_t n, float v, hipStream_t s);
+// LayerNorm folded into the linear that follows it: for each output row n of
+// the [N][K] matrix m (of type wd, layer at element offset lofs, decoded as
+// the GEMV decodes it), gsum[n] = sum_k W[n][k]*gain[k] and
+// bsum[n] = sum_k W[n][k]*shift[k] + bias[n] (bias may be null).
+hipError_t fold_ln(int wd, const MatW &m, size_t lofs, int N, int K, const float *gain, const float *shift,
+                   const float *bias, float *gsum, float *bsum, hipStream_t s);
 
 }  // namespace gpt2dec

@@ -378,13 +378,6 @@ __device__ __forceinline__ void wg_barrier() {
 __device__ __forceinline__ uint64_t tld(const uint64_t *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void tst(uint64_t *p, float v, uint32_t ep) {
-  __hip_atomic_store(p, ((uint64_t)ep << 32) | (uint64_t)__float_as_uint(v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void tst_u(uint64_t *p, uint32_t v, uint32_t ep) {
-  __hip_atomic_store(p, ((uint64_t)ep << 32) | (uint64_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ void st_agent(float *p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -483,19 +476,30 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t copies_rsrc(uint64_t *base, in
   return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, NCOPY * stride * 8, 0x00020000);
 }
 
-// LayerNorm of E values held as a lane share (element vidx(lane, j)) into LDS,
-// following the model file's layernorm kernel: mean, biased variance,
-// ((x - mean) * rsqrt(var + eps)) * gamma + beta.
+// LayerNorm, folded into the linear that follows it.  For a row w of that
+// linear with bias b, LayerNorm gain g and shift h, and the input's mean m and
+// rstd = 1/sqrt(var + eps):
+//   w.LN(x) + b = rstd * (w.(g*x) - m * w.g) + (w.h + b),
+// so the dot products read g*x, which needs no statistics, and the
+// statistics are taken while they run.  w.g and w.h + b are per-row constants
+// (computed at load from the weights as the dot products decode them).
+// The input x, held as a lane share (element vidx(lane, j)), scaled by g into LDS:
 template <int E>
-__device__ __forceinline__ void layernorm_to_lds(const float (&x)[E / 64], const float (&g)[E / 64],
-                                                 const float (&b)[E / 64], float eps, float *dst,
-                                                 int lane) {
+__device__ __forceinline__ void gain_to_lds(const float (&x)[E / 64], const float (&g)[E / 64], float *dst,
+                                            int lane) {
+#pragma unroll
+  for (int j = 0; j < E / 64; j++) dst[vidx(lane, j)] = x[j] * g[j];
+}
+// Mean and 1/sqrt(biased variance + eps) of x, following the model file's
+// layernorm kernel (mean first, then the mean square deviation).
+template <int E>
+__device__ __forceinline__ void ln_stats(const float (&x)[E / 64], float eps, float &mean, float &rstd) {
   constexpr int PER = E / 64;
   // four independent partial sums per lane (shorter dependency chains)
   float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < PER; j++) s4[j % 4] += x[j];
-  const float mean = wave_sum_all((s4[0] + s4[1]) + (s4[2] + s4[3])) * (1.0f / (float)E);
+  mean = wave_sum_all((s4[0] + s4[1]) + (s4[2] + s4[3])) * (1.0f / (float)E);
   float q4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < PER; j++) {
@@ -503,9 +507,14 @@ __device__ __forceinline__ void layernorm_to_lds(const float (&x)[E / 64], const
     q4[j % 4] = __builtin_fmaf(d, d, q4[j % 4]);
   }
   const float var = wave_sum_all((q4[0] + q4[1]) + (q4[2] + q4[3])) * (1.0f / (float)E);
-  const float r = __builtin_amdgcn_rsqf(var + eps);  // v_rsq_f32 (1 ulp)
-#pragma unroll
-  for (int j = 0; j < PER; j++) dst[vidx(lane, j)] = __builtin_fmaf((x[j] - mean) * r, g[j], b[j]);
+  rstd = __builtin_amdgcn_rsqf(var + eps);  // v_rsq_f32 (1 ulp)
+  // (register-only work may otherwise be scheduled past the next barrier,
+  // whose asm orders memory only: the statistics are finished here)
+  asm volatile("" ::"v"(mean), "v"(rstd));
+}
+// A row of the folded linear from its dot product with g*x.
+__device__ __forceinline__ float ln_row(float dot, float mean, float rstd, float wg, float c) {
+  return __builtin_fmaf(rstd, __builtin_fmaf(-mean, wg, dot), c);
 }
 
 __device__ __forceinline__ float gelu_new(float f) {
@@ -1067,33 +1076,32 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
   int tok = 0;
   Waiter wt{&a, 0, 0, 0u};
   // Parameters of the set's next phase are requested right after its phase,
-  // a whole layer before use: the bias of row rank*R + lane and LayerNorm 1
-  // (set Q) or 2 (set F); the final LayerNorm is read once.  With a slice
-  // share (S::CD), which needs the registers, LayerNorm 2 and the final
-  // LayerNorm are requested instead as their phase's input is polled.
-  float g[PE], bt[PE], gf[PE], bf[PE];
-  float bias = 0.f;
-  auto fetch_ln = [&](float (&gg)[PE], float (&bb)[PE], const float *gs, const float *bs) {
+  // a whole layer before use: for row rank*R + lane the bias (sets A, M) or
+  // the folded LayerNorm's row constants (sets Q, F: w.g, and w.h + bias),
+  // and the LayerNorm 1 (set Q) or 2 (set F) gain; the final LayerNorm gain is
+  // read once.  With a slice share (S::CD), which needs the registers, the
+  // LayerNorm-2 and final gains are requested instead as their phase's input
+  // is polled.
+  float g[PE], gf[PE];
+  float bias = 0.f, wg = 0.f;
+  auto fetch_gain = [&](float (&gg)[PE], const float *gs) {
 #pragma unroll
-    for (int j = 0; j < PE; j++) {
-      gg[j] = gs[vidx(lane, j)];
-      bb[j] = bs[vidx(lane, j)];
-    }
+    for (int j = 0; j < PE; j++) gg[j] = gs[vidx(lane, j)];
   };
   auto fetch_params = [&](int l) {
-    if (set == SET_Q) {
-      fetch_ln(g, bt, a.ln1w + l * E, a.ln1b + l * E);
-      bias = lane < SQ::R ? a.bqkv[l * 3 * E + rank * SQ::R + lane] : 0.f;
-    } else if (set == SET_A) {
-      bias = lane < SA::R ? a.bap[l * E + rank * SA::R + lane] : 0.f;
-    } else if (set == SET_F) {
-      if constexpr (!S::CD) fetch_ln(g, bt, a.ln2w + l * E, a.ln2b + l * E);
-      bias = lane < SF::R ? a.bfc[l * F + rank * SF::R + lane] : 0.f;
-    } else {
-      bias = lane < SM::R ? a.bpr[l * E + rank * SM::R + lane] : 0.f;
+    if (set == SET_Q) fetch_gain(g, a.ln1w + l * E);
+    if constexpr (!S::CD) {
+      if (set == SET_F) fetch_gain(g, a.ln2w + l * E);
     }
+    // row constants: one pair of loads whatever the set (sets A, M: w.g unused)
+    const int R = set == SET_Q ? SQ::R : set == SET_A ? SA::R : set == SET_F ? SF::R : SM::R;
+    const size_t o = (size_t)l * (set == SET_Q ? 3 * E : set == SET_F ? F : E) + rank * R + min(lane, R - 1);
+    const float *cs = set == SET_Q ? a.cqkv : set == SET_A ? a.bap : set == SET_F ? a.cfc : a.bpr;
+    const float *gs = set == SET_Q ? a.gqkv : set == SET_F ? a.gfc : cs;
+    bias = cs[o];
+    wg = gs[o];
   };
-  if constexpr (!S::CD) fetch_ln(gf, bf, a.lnfw, a.lnfb);
+  if constexpr (!S::CD) fetch_gain(gf, a.lnfw);
   fetch_params(0);
   // This wave's share of its set's slice (lanes NL.. of the slice geometry),
   // requested and used like the compute waves' (see compute_set): consumed
@@ -1181,17 +1189,19 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
             return;
           }
         }
-        layernorm_to_lds<E>(x, g, bt, a.eps, xs, lane);
+        gain_to_lds<E>(x, g, xs, lane);
         if (lane == 0) stamp(a, step, 5 * l + 0, 0, G);
         if (lane == 0) flag[0] = 0;
         wg_barrier();
         if (lane == 0) stamp(a, step, 5 * l + 0, 1, G);
+        float mean, rstd;
+        ln_stats<E>(x, a.eps, mean, rstd);  // (while the dot products run)
         ctl_dot();
         wg_barrier();
         if (lane == 0) stamp(a, step, 5 * l + 0, 2, G);
         if (lane < SQ::R)
           tst_pairs(copies_rsrc(a.qkv_t + (size_t)l * NCOPY * 3 * E, 3 * E), 3 * E, rank * SQ::R + lane,
-                    part[lane] + bias, epA, lane);
+                    ln_row(part[lane], mean, rstd, wg, bias), epA, lane);
         if (lane == 0) stamp(a, step, 5 * l + 0, 3, G);
         wg_barrier();  // stores issued: the compute waves may request the next slice
         fetch_params(lnext);
@@ -1369,21 +1379,23 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
       }
       // ---------------- D: LayerNorm 2 + fc + gelu_new (set F)
       if (set == SET_F) {
-        if constexpr (S::CD) fetch_ln(g, bt, a.ln2w + l * E, a.ln2b + l * E);  // (arrives during the poll)
+        if constexpr (S::CD) fetch_gain(g, a.ln2w + l * E);  // (arrives during the poll)
         float x[PE];
         wt.start(5 * l + 2);
         if (!poll_vec<PE>(a.xa_t + ((size_t)l * NCOPY + my_copy()) * E, epC, x, lane, wt)) { abort_all(); return; }
-        layernorm_to_lds<E>(x, g, bt, a.eps, xs, lane);
+        gain_to_lds<E>(x, g, xs, lane);
         if (lane == 0) stamp(a, step, 5 * l + 3, 0, G);
         if (lane == 0) flag[0] = 0;
         wg_barrier();
         if (lane == 0) stamp(a, step, 5 * l + 3, 1, G);
+        float mean, rstd;
+        ln_stats<E>(x, a.eps, mean, rstd);  // (while the dot products run)
         ctl_dot();
         wg_barrier();
         if (lane == 0) stamp(a, step, 5 * l + 3, 2, G);
         if (lane < SF::R)
           tst_pairs(copies_rsrc(a.act_t + (size_t)l * NCOPY * F, F), F, rank * SF::R + lane,
-                    gelu_new(part[lane] + bias), epD, lane);
+                    gelu_new(ln_row(part[lane], mean, rstd, wg, bias)), epD, lane);
         if (lane == 0) stamp(a, step, 5 * l + 3, 3, G);
         wg_barrier();  // stores issued: the compute waves may request the next slice
         fetch_params(lnext);
@@ -1428,23 +1440,34 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
     // ---------------- H: final LayerNorm + head + local argmax
     {
       const uint32_t epH = epoch_of(a, step, 5 * a.L);
-      if constexpr (S::CD) fetch_ln(gf, bf, a.lnfw, a.lnfb);  // (arrives while the input is polled)
+      if constexpr (S::CD) fetch_gain(gf, a.lnfw);  // (arrives while the input is polled)
       float x[PE];
       wt.start(5 * a.L - 1);
       if (!poll_vec<PE>(a.xb_t + ((size_t)(a.L - 1) * NCOPY + my_copy()) * E, epH - 1, x, lane, wt)) {
         abort_all();
         return;
       }
-      layernorm_to_lds<E>(x, gf, bf, a.eps, xs, lane);
+      gain_to_lds<E>(x, gf, xs, lane);
       if (lane == 0) stamp(a, step, 5 * a.L, 0, G);
       if (lane == 0) flag[0] = 0;
       wg_barrier();
       if (lane == 0) stamp(a, step, 5 * a.L, 1, G);
-      wg_barrier();
-      if (lane == 0) stamp(a, step, 5 * a.L, 2, G);
+      // while the head's dot products run: the statistics, and the folded
+      // LayerNorm's constants of this workgroup's rows
       int hr0, hr1;
       head_range<S, WD>(a.V, w, hr0, hr1);
       const int nr = hr1 - hr0;
+      float hg[PSTRIDE / 64], hc[PSTRIDE / 64];
+#pragma unroll
+      for (int k = 0; k < PSTRIDE / 64; k++) {
+        const int r = min(lane + 64 * k, nr - 1);
+        hg[k] = a.ghead[hr0 + r];
+        hc[k] = a.chead[hr0 + r];
+      }
+      float mean, rstd;
+      ln_stats<E>(x, a.eps, mean, rstd);
+      wg_barrier();
+      if (lane == 0) stamp(a, step, 5 * a.L, 2, G);
       float bv = -INFINITY;
       uint32_t bi = 0xffffffffu;
       // (a fixed trip count, so that the row results are read from LDS in one burst)
@@ -1452,7 +1475,7 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
       for (int k = 0; k < PSTRIDE / 64; k++) {
         const int r = lane + 64 * k;
         if (r < nr) {
-          const float v = part[r];
+          const float v = ln_row(part[r], mean, rstd, hg[k], hc[k]);
           a.logits[hr0 + r] = v;
           if (v > bv || (v == bv && (uint32_t)(hr0 + r) < bi)) {
             bv = v;

@@ -252,6 +252,10 @@ int load_impl(gpt2_ctx *c, const gpt2_config *cfg, const gpt2_weights *w) {
   float *bqkv = c->dalloc<float>((size_t)L * 3 * E * 4), *bap = c->dalloc<float>((size_t)L * E * 4);
   float *bfc = c->dalloc<float>((size_t)L * F * 4), *bpr = c->dalloc<float>((size_t)L * E * 4);
   float *lnfw = c->dalloc<float>((size_t)E * 4), *lnfb = c->dalloc<float>((size_t)E * 4);
+  // LayerNorm folded into the linear after it: per-row W.gain and W.shift + bias
+  float *gqkv = c->dalloc<float>((size_t)L * 3 * E * 4), *cqkv = c->dalloc<float>((size_t)L * 3 * E * 4);
+  float *gfc = c->dalloc<float>((size_t)L * F * 4), *cfc = c->dalloc<float>((size_t)L * F * 4);
+  float *ghead = c->dalloc<float>((size_t)V * 4), *chead = c->dalloc<float>((size_t)V * 4);
   float *wte = c->dalloc<float>((size_t)V * E * 4), *wpe = c->dalloc<float>((size_t)P * E * 4);
   void *head16 = c->wd == WD_F16 ? c->dalloc<void>((size_t)V * E * 2) : nullptr;
   const size_t kv = (size_t)L * H * P * D;
@@ -275,7 +279,8 @@ int load_impl(gpt2_ctx *c, const gpt2_config *cfg, const gpt2_weights *w) {
   c->err_h = c->halloc<int>(4 * 4);
   c->logits_h = c->halloc<float>((size_t)V * 4);
   if (!mq || !ma || !mf || !mp || !stage || (c->wd == WD_Q4 && !tmp) || !ln1w || !ln1b || !ln2w || !ln2b ||
-      !bqkv || !bap || !bfc || !bpr || !lnfw || !lnfb || !wte || !wpe || (c->wd == WD_F16 && !head16) || !kc ||
+      !bqkv || !bap || !bfc || !bpr || !lnfw || !lnfb || !gqkv || !cqkv || !gfc || !cfc || !ghead || !chead ||
+      !wte || !wpe || (c->wd == WD_F16 && !head16) || !kc ||
       !vc || !logits || !c->ids_d || !c->feed_d || !c->err_d || !c->feed_h || !c->ids_h || !c->err_h ||
       !c->logits_h)
     return c->fail(GPT2_E_NOMEM, "allocation failed");
@@ -333,6 +338,18 @@ int load_impl(gpt2_ctx *c, const gpt2_config *cfg, const gpt2_weights *w) {
     }
     if (e != hipSuccess) return c->device_fail(e, "weight re-layout");
   }
+  // ---- LayerNorms folded into the QKV, fc and head rows (from the weights as decoded)
+  for (int l = 0; l < L && e == hipSuccess; l++) {
+    e = fold_ln(c->wd, MatW{mq, sq}, (size_t)l * nq, 3 * E, E, ln1w + (size_t)l * E, ln1b + (size_t)l * E,
+                bqkv + (size_t)l * 3 * E, gqkv + (size_t)l * 3 * E, cqkv + (size_t)l * 3 * E, s);
+    if (e == hipSuccess)
+      e = fold_ln(c->wd, MatW{mf, sf}, (size_t)l * nf, F, E, ln2w + (size_t)l * E, ln2b + (size_t)l * E,
+                  bfc + (size_t)l * F, gfc + (size_t)l * F, cfc + (size_t)l * F, s);
+  }
+  if (e == hipSuccess)
+    e = fold_ln(head16 ? WD_F16 : WD_F32, MatW{head16 ? head16 : static_cast<const void *>(wte), nullptr}, 0, V,
+                E, lnfw, lnfb, nullptr, ghead, chead, s);
+  if (e != hipSuccess) return c->device_fail(e, "folding the LayerNorms");
   for (int i = 0; i < 7 && e == hipSuccess; i++) e = hipMemsetAsync(c->tag_bufs[i], 0, c->tag_sizes[i], s);
   if (e == hipSuccess) e = hipMemsetAsync(kc, 0, kv * 4, s);
   if (e == hipSuccess) e = hipMemsetAsync(vc, 0, kv * 4, s);
@@ -350,6 +367,9 @@ int load_impl(gpt2_ctx *c, const gpt2_config *cfg, const gpt2_weights *w) {
   a.head = head16 ? head16 : static_cast<const void *>(wte);
   a.wpe = wpe;
   a.lnfw = lnfw; a.lnfb = lnfb;
+  a.gqkv = gqkv; a.cqkv = cqkv;
+  a.gfc = gfc; a.cfc = cfc;
+  a.ghead = ghead; a.chead = chead;
   a.kc = kc; a.vc = vc;
   a.qkv_t = c->tag_bufs[0];
   a.att_t = c->tag_bufs[1];

@@ -86,28 +86,52 @@ __global__ void __launch_bounds__(256) fill_kernel(float *dst, size_t n, float v
   if (i < n) dst[i] = v;
 }
 
-// Decode chunk-by-chunk exactly as the GEMV does (same element order and arithmetic).
+// Chunk c (4 consecutive elements) of an output-major matrix from element
+// offset lofs, decoded exactly as the GEMV does (same element order and arithmetic).
+__device__ __forceinline__ float4 chunk_f4(int wd, const void *w, const float2 *szp, size_t lofs, size_t c) {
+  if (wd == WD_F32) return reinterpret_cast<const float4 *>(w)[lofs / 4 + c];
+  if (wd == WD_F16) {
+    const uint2 h = reinterpret_cast<const uint2 *>(w)[lofs / 4 + c];
+    return make_float4(__half2float(__ushort_as_half((unsigned short)(h.x & 0xffffu))),
+                       __half2float(__ushort_as_half((unsigned short)(h.x >> 16))),
+                       __half2float(__ushort_as_half((unsigned short)(h.y & 0xffffu))),
+                       __half2float(__ushort_as_half((unsigned short)(h.y >> 16))));
+  }
+  const uint32_t q = reinterpret_cast<const uint16_t *>(w)[lofs / 4 + c];
+  const float2 p = szp[lofs / 32 + c / 8];
+  return make_float4(__builtin_fmaf((float)(q & 15u), p.x, p.y), __builtin_fmaf((float)((q >> 4) & 15u), p.x, p.y),
+                     __builtin_fmaf((float)((q >> 8) & 15u), p.x, p.y),
+                     __builtin_fmaf((float)((q >> 12) & 15u), p.x, p.y));
+}
+
 __global__ void __launch_bounds__(256) dequant_kernel(int wd, const void *w, const float2 *szp, size_t lofs,
                                                       size_t nchunks, float *__restrict__ dst) {
   const size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= nchunks) return;
-  float4 v;
-  if (wd == WD_F32) {
-    v = reinterpret_cast<const float4 *>(w)[lofs / 4 + c];
-  } else if (wd == WD_F16) {
-    const uint2 h = reinterpret_cast<const uint2 *>(w)[lofs / 4 + c];
-    v = make_float4(__half2float(__ushort_as_half((unsigned short)(h.x & 0xffffu))),
-                    __half2float(__ushort_as_half((unsigned short)(h.x >> 16))),
-                    __half2float(__ushort_as_half((unsigned short)(h.y & 0xffffu))),
-                    __half2float(__ushort_as_half((unsigned short)(h.y >> 16))));
-  } else {
-    const uint32_t q = reinterpret_cast<const uint16_t *>(w)[lofs / 4 + c];
-    const float2 p = szp[lofs / 32 + c / 8];
-    v = make_float4(__builtin_fmaf((float)(q & 15u), p.x, p.y), __builtin_fmaf((float)((q >> 4) & 15u), p.x, p.y),
-                    __builtin_fmaf((float)((q >> 8) & 15u), p.x, p.y),
-                    __builtin_fmaf((float)((q >> 12) & 15u), p.x, p.y));
+  reinterpret_cast<float4 *>(dst)[c] = chunk_f4(wd, w, szp, lofs, c);
+}
+
+// One thread per output row n of W (the weights as the GEMV decodes them):
+// gsum[n] = sum_k W[n][k] * gain[k] and bsum[n] = sum_k W[n][k] * shift[k] + bias[n],
+// accumulated in double and rounded once.
+__global__ void __launch_bounds__(256) fold_ln_kernel(int wd, const void *w, const float2 *szp, size_t lofs, int N,
+                                                      int K, const float *__restrict__ gain,
+                                                      const float *__restrict__ shift,
+                                                      const float *__restrict__ bias, float *__restrict__ gsum,
+                                                      float *__restrict__ bsum) {
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  double sg = 0.0, sb = 0.0;
+  for (int c = 0; c < K / 4; c++) {
+    const float4 v = chunk_f4(wd, w, szp, lofs, (size_t)n * (K / 4) + c);
+    const float wv[4] = {v.x, v.y, v.z, v.w};
+    for (int i = 0; i < 4; i++) {
+      sg += (double)wv[i] * (double)gain[4 * c + i];
+      sb += (double)wv[i] * (double)shift[4 * c + i];
+    }
   }
-  reinterpret_cast<float4 *>(dst)[c] = v;
+  gsum[n] = (float)sg;
+  bsum[n] = (float)(sb + (bias ? (double)bias[n] : 0.0));
 }
 
 inline unsigned blocks_for(size_t n, unsigned t) { return (unsigned)((n + t - 1) / t); }
@@ -136,6 +160,14 @@ hipError_t relayout_q4(const float *src, float *tmp, uint8_t *nib, float2 *sz, i
 
 hipError_t convert_f16(const float *src, void *dst, size_t n, hipStream_t s) {
   convert_f16_kernel<<<blocks_for(n, 256), 256, 0, s>>>(src, reinterpret_cast<__half *>(dst), n);
+  return hipGetLastError();
+}
+
+hipError_t fold_ln(int wd, const MatW &m, size_t lofs, int N, int K, const float *gain, const float *shift,
+                   const float *bias, float *gsum, float *bsum, hipStream_t s) {
+  if (N <= 0 || K % 4 != 0) return hipErrorInvalidValue;
+  fold_ln_kernel<<<blocks_for((size_t)N, 256), 256, 0, s>>>(wd, m.w, m.sz, lofs, N, K, gain, shift, bias, gsum,
+                                                           bsum);
   return hipGetLastError();
 }
 
