@@ -50,6 +50,31 @@ def test_teacher_forced_logits_and_ids(name):
     ctx.close()
 
 
+@pytest.mark.parametrize("offset", [1.0, 4.0])
+def test_layernorm_inputs_with_large_mean(offset):
+    """The GPU folds each LayerNorm into the linear after it and subtracts the
+    input's mean after the dot product: rstd * (w.(g*x) - mean * w.g) + (w.h + b),
+    a difference that cancels when the residual stream carries a large common
+    offset.  Every position embedding is shifted by `offset` (the stream's
+    spread is about 0.03, so the mean is about 35 and 140 times the spread):
+    the parity bar still holds.  (Much larger offsets exhaust fp32 in the
+    residual sums themselves, whatever the LayerNorm's arithmetic.)"""
+    cfg = CASES["tiny-rich"]
+    t = dict(synth.make_model(cfg).t)
+    t["wpe.weight"] = (t["wpe.weight"] + np.float32(offset)).astype(np.float32)
+    model = synth.Model(cfg, t)
+    orc = Oracle(model)
+    toks, logits, _ = oracle_stream(orc, synth.make_prompt(cfg), cfg.n_steps)
+    orc.close()
+    ctx = load_gpu(model)
+    worst = 0.0
+    for pos, tok in enumerate(toks):
+        am, lg = g2.gpt2_step(ctx, tok, pos)
+        worst = max(worst, compare_step(lg, am, logits[pos], f"offset {offset} pos {pos}"))
+    print(f"[parity] position-embedding offset {offset}: worst relative logit error {worst:.2e}", flush=True)
+    ctx.close()
+
+
 @pytest.mark.parametrize("name", ["tiny", "tiny-rich", "gpt2-124m-fp32", "gpt2-124m-fp16w", "gpt2-124m-int4w"])
 def test_generate_matches_oracle_greedy(name):
     """Device-chained greedy ids equal the oracle's up to the first step whose
