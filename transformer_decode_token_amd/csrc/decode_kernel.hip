@@ -232,6 +232,20 @@ __device__ __forceinline__ float dot4(float4 w, float4 x, float acc) {
   return acc;
 }
 
+// One int4 chunk against four inputs, with the group's scale s and zero z
+// taken out of the sum: sum_k (code_k*s + z)*x_k = s*sum_k code_k*x_k + z*xsum,
+// xsum = x.x + x.y + x.z + x.w.  The four codes are spread one per byte (even
+// inputs, then odd ones) and converted by byte.
+__device__ __forceinline__ float dot_q4(const Chunk<WD_Q4> &c, float4 x, float xsum, float acc) {
+  const uint32_t ev = c.q & 0x0F0Fu, od = (c.q >> 4) & 0x0F0Fu;
+  float t = (float)(ev & 0xFFu) * x.x;
+  t = __builtin_fmaf((float)(od & 0xFFu), x.y, t);
+  t = __builtin_fmaf((float)(ev >> 8), x.z, t);
+  t = __builtin_fmaf((float)(od >> 8), x.w, t);
+  acc = __builtin_fmaf(c.sz.x, t, acc);
+  return __builtin_fmaf(c.sz.y, xsum, acc);
+}
+
 // ---- DPP reductions ----------------------------------------------------------
 // Inclusive scans with row_shr 1,2,4,8 (within 16-lane rows), then
 // row_bcast:15 / row_bcast:31 across rows: the total of each W-lane segment
@@ -579,7 +593,8 @@ __device__ __forceinline__ void load_set(Chunk<WD> (&b)[ST::NB], const MatW &m, 
 
 // Row results of the slice (input vector in LDS) into part[0..R): each lane
 // sums its chunks in order (fp16 and int4: its even and its odd chunks, then
-// the two), then a DPP reduction over the row's LPR lanes.
+// the two; int4 with each group's scale and zero taken out, dot_q4), then a
+// DPP reduction over the row's LPR lanes.
 template <class ST, int WD>
 __device__ __forceinline__ void dot_set(const Chunk<WD> (&b)[ST::NB], const float *xs, float *part, int lane) {
   const int q = lane % ST::LPR;
@@ -593,11 +608,23 @@ __device__ __forceinline__ void dot_set(const Chunk<WD> (&b)[ST::NB], const floa
   float acc[ST::NP][2];
 #pragma unroll
   for (int t = 0; t < ST::NP; t++) acc[t][0] = acc[t][1] = 0.f;
+  if constexpr (WD == WD_Q4) {
+    float xsum[ST::CPR];
 #pragma unroll
-  for (int i = 0; i < ST::CPR; i++) {
+    for (int i = 0; i < ST::CPR; i++) xsum[i] = (xv[i].x + xv[i].y) + (xv[i].z + xv[i].w);
 #pragma unroll
-    for (int t = 0; t < ST::NP; t++)
-      acc[t][i % NCH] = dot4(deq<WD>(b[t * ST::CPR + i]), xv[i], acc[t][i % NCH]);
+    for (int i = 0; i < ST::CPR; i++) {
+#pragma unroll
+      for (int t = 0; t < ST::NP; t++)
+        acc[t][i % NCH] = dot_q4(b[t * ST::CPR + i], xv[i], xsum[i], acc[t][i % NCH]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < ST::CPR; i++) {
+#pragma unroll
+      for (int t = 0; t < ST::NP; t++)
+        acc[t][i % NCH] = dot4(deq<WD>(b[t * ST::CPR + i]), xv[i], acc[t][i % NCH]);
+    }
   }
 #pragma unroll
   for (int t = 0; t < ST::NP; t++) {
