@@ -22,8 +22,11 @@
 //   * the compute waves hold the workgroup's slice of one layer in registers
 //     and request the next layer's slice as soon as the phase is done, so the
 //     weights stream in during the other sets' phases;
-//   * the control wave waits for the inputs of its phase, normalises them
-//     into LDS, runs an attention chunk when it has one, and publishes.
+//   * the control wave waits for the inputs of its phase, writes them into
+//     LDS (scaled by the LayerNorm gain where a LayerNorm comes first; the
+//     LayerNorm statistics are taken while the dot products run and applied
+//     to the row results), runs an attention chunk when it has one, and
+//     publishes.
 // Each phase's inputs therefore come from, and go to, a few dozen workgroups
 // rather than all of them, which shortens every hand-over.
 // Batch 1 makes every linear a matrix-vector product (0.5 flop per fp32 byte),
@@ -717,12 +720,6 @@ __device__ void fill_head_lds(const DecodeArgs &a, float *lds, int lane) {
   }
 }
 
-// Output head over this workgroup's contiguous vocabulary rows, RB rows per
-// batch: first the rows kept in LDS, then the NRB batches requested into the
-// slice registers beforehand (late sets), then the rest from memory with
-// three batches in flight, the first three requested before the final
-// LayerNorm is ready.  Memory batches past the last row re-read that row, which keeps
-// every load unconditional.  False when the control wave aborted.
 // Request head rows into registers, following the LDS-resident ones: NRB
 // batches into the idle slice registers b (late sets; once per step, after
 // the set's last phase), or (K0 = NRB) the NX batches after those into hx,
@@ -755,6 +752,14 @@ __device__ __forceinline__ void head_prefetch_regs(const DecodeArgs &a, Chunk<WD
     head_load_rows<S, WD, 0, NRB>(a, [&](int k, int i, const Chunk<WD> &c) { b[k * HG::NPH + i] = c; }, lane);
 }
 
+// Output head over this workgroup's contiguous vocabulary rows, RB rows per
+// batch: first the rows kept in LDS, then the NRB batches requested into the
+// slice registers beforehand (late sets), then the NX batches kept in hx,
+// then the rest from memory with three batches in flight, the first three
+// requested before the head's input is in.  Memory batches past the last row
+// re-read that row, which keeps every load unconditional.  The row results
+// (dot products with the gain-scaled input) go to part[]; the control wave
+// applies the folded final LayerNorm.  False when the control wave aborted.
 template <class S, int WD, int NRB, int NX, int NB>
 __device__ bool head_rows(const DecodeArgs &a, float *lds, int lane, const Chunk<WD> (&breg)[NB],
                           const Chunk<HeadGeo<S, WD>::HWD> (&hx)[NX > 0 ? NX : 1][HeadGeo<S, WD>::NPH]) {
