@@ -567,7 +567,9 @@ __device__ __forceinline__ bool has_att_item(int p, int w) {
 }
 
 // Optional timeline of one workgroup's control wave (lane 0): inputs ready, first and
-// second workgroup barrier passed, outputs published.
+// second workgroup barrier passed, outputs published.  Compiled only into the
+// kernel variant that a traced run launches: the stamps' tests, addresses and
+// clock reads otherwise cost registers and time in every phase.
 __device__ __forceinline__ void stamp(const DecodeArgs &a, int step, int ph, int which, int G) {
   if (a.trace && step < a.trace_steps)
     a.trace[(((size_t)step * (5 * a.L + 1) + ph) * G + blockIdx.x) * 4 + which] = (long long)wall_clock64();
@@ -1091,7 +1093,7 @@ __device__ bool poll_rows(const uint64_t *src, int n, uint32_t ep, float &v, int
 // and with all workgroups H, the final LayerNorm and the output head.  The
 // residual rows a set adds come back from the published vectors (the values
 // written are the values read), so no workgroup carries state across phases.
-template <class S, int WD>
+template <class S, int WD, bool TR>
 __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
   constexpr int E = S::E, F = S::F, D = S::D, H = S::H, G = S::G;
   constexpr int PE = E / 64, D4 = D / 4;
@@ -1107,6 +1109,11 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
   const float *part = lds + S::L_PART;
   int tok = 0;
   Waiter wt{&a, 0, 0, 0u};
+  auto st = [&](int step, int ph, int which) {
+    if constexpr (TR) {
+      if (lane == 0) stamp(a, step, ph, which, G);
+    }
+  };
   // Parameters of the set's next phase are requested right after its phase,
   // a whole layer before use: for row rank*R + lane the bias (sets A, M) or
   // the folded LayerNorm's row constants (sets Q, F: w.g, and w.h + bias),
@@ -1222,19 +1229,19 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
           }
         }
         gain_to_lds<E>(x, g, xs, lane);
-        if (lane == 0) stamp(a, step, 5 * l + 0, 0, G);
+        st(step, 5 * l + 0, 0);
         if (lane == 0) flag[0] = 0;
         wg_barrier();
-        if (lane == 0) stamp(a, step, 5 * l + 0, 1, G);
+        st(step, 5 * l + 0, 1);
         float mean, rstd;
         ln_stats<E>(x, a.eps, mean, rstd);  // (while the dot products run)
         ctl_dot();
         wg_barrier();
-        if (lane == 0) stamp(a, step, 5 * l + 0, 2, G);
+        st(step, 5 * l + 0, 2);
         if (lane < SQ::R)
           tst_pairs(copies_rsrc(a.qkv_t + (size_t)l * NCOPY * 3 * E, 3 * E), 3 * E, rank * SQ::R + lane,
                     ln_row(part[lane], mean, rstd, wg, bias), epA, lane);
-        if (lane == 0) stamp(a, step, 5 * l + 0, 3, G);
+        st(step, 5 * l + 0, 3);
         wg_barrier();  // stores issued: the compute waves may request the next slice
         fetch_params(lnext);
         ctl_after_phase(l);
@@ -1268,18 +1275,18 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
           if (wt.expired()) { abort_all(); return; }
           __builtin_amdgcn_s_sleep(1);
         }
-        if (lane == 0) stamp(a, step, 5 * l + 1, 0, G);
+        st(step, 5 * l + 1, 0);
         float m, lsum;
         float4 o;
         at.run(lds, p, it0, it1, itg, lane, m, lsum, o);
-        if (lane == 0) stamp(a, step, 5 * l + 1, 1, G);
+        st(step, 5 * l + 1, 1);
         // The cache-row stores need no wait here: the next poll of this wave
         // (its own set's phase, or the output head) waits for all of its
         // outstanding memory operations, stores included, before this
         // workgroup publishes again, and every reader of row p runs at a
         // later step, after that publish.
         const int g = lane / D4, d4 = lane % D4;
-        if (lane == 0) stamp(a, step, 5 * l + 1, 2, G);
+        st(step, 5 * l + 1, 2);
         // every lane holds the head's output; row group g writes the copies c = g mod RPL
         const auto attn_rs = __builtin_amdgcn_make_buffer_rsrc(a.attn_t + (size_t)l * NCOPY * E, (short)0,
                                                                NCOPY * E * 8, 0x00020000);
@@ -1366,7 +1373,7 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
           const float rl = __builtin_amdgcn_rcpf(Ls);
           publish_head(make_float4(O.x * rl, O.y * rl, O.z * rl, O.w * rl));
         }
-        if (lane == 0) stamp(a, step, 5 * l + 1, 3, G);
+        st(step, 5 * l + 1, 3);
         if (set == SET_M) {
           wg_barrier();  // the compute waves may now request this layer's slice
           ctl_load(l);   // and so may this wave
@@ -1393,18 +1400,18 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
         if (!poll_vec<PE>(a.attn_t + ((size_t)l * NCOPY + my_copy()) * E, epB, x, lane, wt)) { abort_all(); return; }
 #pragma unroll
         for (int j = 0; j < PE; j++) xs[vidx(lane, j)] = x[j];
-        if (lane == 0) stamp(a, step, 5 * l + 2, 0, G);
+        st(step, 5 * l + 2, 0);
         if (lane == 0) flag[0] = 0;
         wg_barrier();
-        if (lane == 0) stamp(a, step, 5 * l + 2, 1, G);
+        st(step, 5 * l + 2, 1);
         ctl_dot();
         wg_barrier();
-        if (lane == 0) stamp(a, step, 5 * l + 2, 2, G);
+        st(step, 5 * l + 2, 2);
         if (lane < SA::R) {
           const float mix = part[lane] + bias;
           tst_pairs(copies_rsrc(a.xa_t + (size_t)l * NCOPY * E, E), E, rank * SA::R + lane, xr + mix, epC, lane);
         }
-        if (lane == 0) stamp(a, step, 5 * l + 2, 3, G);
+        st(step, 5 * l + 2, 3);
         wg_barrier();  // stores issued: the compute waves may request the next slice
         fetch_params(lnext);
         ctl_after_phase(l);
@@ -1416,19 +1423,19 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
         wt.start(5 * l + 2);
         if (!poll_vec<PE>(a.xa_t + ((size_t)l * NCOPY + my_copy()) * E, epC, x, lane, wt)) { abort_all(); return; }
         gain_to_lds<E>(x, g, xs, lane);
-        if (lane == 0) stamp(a, step, 5 * l + 3, 0, G);
+        st(step, 5 * l + 3, 0);
         if (lane == 0) flag[0] = 0;
         wg_barrier();
-        if (lane == 0) stamp(a, step, 5 * l + 3, 1, G);
+        st(step, 5 * l + 3, 1);
         float mean, rstd;
         ln_stats<E>(x, a.eps, mean, rstd);  // (while the dot products run)
         ctl_dot();
         wg_barrier();
-        if (lane == 0) stamp(a, step, 5 * l + 3, 2, G);
+        st(step, 5 * l + 3, 2);
         if (lane < SF::R)
           tst_pairs(copies_rsrc(a.act_t + (size_t)l * NCOPY * F, F), F, rank * SF::R + lane,
                     gelu_new(ln_row(part[lane], mean, rstd, wg, bias)), epD, lane);
-        if (lane == 0) stamp(a, step, 5 * l + 3, 3, G);
+        st(step, 5 * l + 3, 3);
         wg_barrier();  // stores issued: the compute waves may request the next slice
         fetch_params(lnext);
         ctl_after_phase(l);
@@ -1451,19 +1458,19 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
         }
 #pragma unroll
         for (int j = 0; j < PP; j++) xs[(S::M_PARTS - 1) * PW + vidx(lane, j)] = x[j];
-        if (lane == 0) stamp(a, step, 5 * l + 4, 0, G);
+        st(step, 5 * l + 4, 0);
         if (lane == 0) flag[0] = 0;
         wg_barrier();
         if (flag[1]) return;  // a compute wave's wait failed (the error word is set)
-        if (lane == 0) stamp(a, step, 5 * l + 4, 1, G);
+        st(step, 5 * l + 4, 1);
         ctl_dot();
         wg_barrier();
-        if (lane == 0) stamp(a, step, 5 * l + 4, 2, G);
+        st(step, 5 * l + 4, 2);
         if (lane < SM::R) {
           const float mix = part[lane] + bias;
           tst_pairs(copies_rsrc(a.xb_t + (size_t)l * NCOPY * E, E), E, rank * SM::R + lane, xr + mix, epE, lane);
         }
-        if (lane == 0) stamp(a, step, 5 * l + 4, 3, G);
+        st(step, 5 * l + 4, 3);
         wg_barrier();  // stores issued: the compute waves may request the next slice
         fetch_params(lnext);
         ctl_after_phase(l);
@@ -1480,10 +1487,10 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
         return;
       }
       gain_to_lds<E>(x, gf, xs, lane);
-      if (lane == 0) stamp(a, step, 5 * a.L, 0, G);
+      st(step, 5 * a.L, 0);
       if (lane == 0) flag[0] = 0;
       wg_barrier();
-      if (lane == 0) stamp(a, step, 5 * a.L, 1, G);
+      st(step, 5 * a.L, 1);
       // while the head's dot products run: the statistics, and the folded
       // LayerNorm's constants of this workgroup's rows
       int hr0, hr1;
@@ -1499,7 +1506,7 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
       float mean, rstd;
       ln_stats<E>(x, a.eps, mean, rstd);
       wg_barrier();
-      if (lane == 0) stamp(a, step, 5 * a.L, 2, G);
+      st(step, 5 * a.L, 2);
       float bv = -INFINITY;
       uint32_t bi = 0xffffffffu;
       // (a fixed trip count, so that the row results are read from LDS in one burst)
@@ -1523,7 +1530,7 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
         const g2_v4u_ pr = {__float_as_uint(bv), epH, bi, epH};
         __builtin_amdgcn_raw_buffer_store_b128(pr, ars, (uint32_t)(((lane * G + w) * 2) * 8), 0, AUX_SC1);
       }
-      if (lane == 0) stamp(a, step, 5 * a.L, 3, G);
+      st(step, 5 * a.L, 3);
       wg_barrier();  // stores issued: the compute waves may request the next slices
       if (step + 1 < a.nsteps && set != SET_Q && !defers(step + 1)) ctl_load(0);
     }
@@ -1537,13 +1544,13 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
   }
 }
 
-template <class S, int WD>
+template <class S, int WD, bool TR>
 __global__ void __launch_bounds__(S::NT, 1) decode_kernel(DecodeArgs a) {
   extern __shared__ float lds[];
   const int tid = threadIdx.x;
   if (tid < 4) reinterpret_cast<int *>(lds + S::L_FLAG)[tid] = 0;
   __syncthreads();
-  if (tid >= S::NL) control_main<S, WD>(a, lds, tid - S::NL);
+  if (tid >= S::NL) control_main<S, WD, TR>(a, lds, tid - S::NL);
   else compute_main<S, WD>(a, lds, tid);
 }
 
@@ -1570,22 +1577,27 @@ template <class S>
 constexpr bool shape_has(int wd) {
   return std::is_same<S, ShapeS>::value ? wd == WD_F32 : std::is_same<S, ShapeSC>::value ? wd != WD_F32 : true;
 }
-template <class S>
-const void *kernel_for(int wd) {
+template <class S, bool TR>
+const void *kernel_for_tr(int wd) {
   if (wd == WD_F32) {
-    if constexpr (shape_has<S>(WD_F32)) return reinterpret_cast<const void *>(&decode_kernel<S, WD_F32>);
+    if constexpr (shape_has<S>(WD_F32)) return reinterpret_cast<const void *>(&decode_kernel<S, WD_F32, TR>);
   } else if (wd == WD_F16) {
-    if constexpr (shape_has<S>(WD_F16)) return reinterpret_cast<const void *>(&decode_kernel<S, WD_F16>);
+    if constexpr (shape_has<S>(WD_F16)) return reinterpret_cast<const void *>(&decode_kernel<S, WD_F16, TR>);
   } else if (wd == WD_Q4) {
-    if constexpr (shape_has<S>(WD_Q4)) return reinterpret_cast<const void *>(&decode_kernel<S, WD_Q4>);
+    if constexpr (shape_has<S>(WD_Q4)) return reinterpret_cast<const void *>(&decode_kernel<S, WD_Q4, TR>);
   }
   return nullptr;
+}
+// The kernel of a run: with the timeline stamps only when the run records them.
+template <class S>
+const void *kernel_for(int wd, bool traced = false) {
+  return traced ? kernel_for_tr<S, true>(wd) : kernel_for_tr<S, false>(wd);
 }
 
 template <class S>
 hipError_t launch_t(int wd, const DecodeArgs &a, hipStream_t s) {
   static_assert(S::L_HEAD * sizeof(float) <= 64 * 1024, "LDS layout too large");
-  const void *k = kernel_for<S>(wd);
+  const void *k = kernel_for<S>(wd, a.trace != nullptr);
   if (!k) return hipErrorInvalidValue;
   const size_t lds = lds_budget();
   if (lds < (size_t)S::L_HEAD * sizeof(float)) return hipErrorInvalidConfiguration;
@@ -1597,13 +1609,23 @@ hipError_t launch_t(int wd, const DecodeArgs &a, hipStream_t s) {
 
 template <class S>
 hipError_t occupancy_t(int wd, int *blocks) {
-  const void *k = kernel_for<S>(wd);
-  if (!k) return hipErrorInvalidValue;
+  // both variants (with and without the timeline stamps) get the LDS size; the
+  // smaller of their occupancies is reported
   const size_t lds = lds_budget();
   if (lds < (size_t)S::L_HEAD * sizeof(float)) return hipErrorInvalidConfiguration;
-  hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k, S::NT, lds);
+  int best = -1;
+  for (int tr = 0; tr < 2; tr++) {
+    const void *k = kernel_for<S>(wd, tr != 0);
+    if (!k) return hipErrorInvalidValue;
+    hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    int b = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k, S::NT, lds);
+    if (e != hipSuccess) return e;
+    best = best < 0 ? b : std::min(best, b);
+  }
+  *blocks = best;
+  return hipSuccess;
 }
 
 template <class S>
