@@ -875,7 +875,8 @@ __device__ void poll_act_part(const DecodeArgs &a, int step, int l, float *lds, 
 // layer to arrive.  Sets whose phase comes late in the layer request the next
 // step's first slice only after the output head, whose loads it would delay.
 template <class S, int WD, int SET>
-__device__ void compute_set(const DecodeArgs &a, const MatW &m, float *lds, int lane) {
+__device__ __attribute__((always_inline)) void compute_set(const DecodeArgs &a, const MatW &m, float *lds,
+                                                           int lane) {
   using ST = Set<S, SET>;
   // sets whose phase is not the first of a layer request the next step's first
   // slice only after the output head; meanwhile their slice registers hold head rows
@@ -933,7 +934,7 @@ __device__ void compute_set(const DecodeArgs &a, const MatW &m, float *lds, int 
 }
 
 template <class S, int WD>
-__device__ void compute_main(const DecodeArgs &a, float *lds, int lane) {
+__device__ __attribute__((always_inline)) void compute_main(const DecodeArgs &a, float *lds, int lane) {
   const int w = (int)blockIdx.x;
   if (w < Set<S, SET_A>::FIRST) compute_set<S, WD, SET_Q>(a, a.qkv, lds, lane);
   else if (w < Set<S, SET_F>::FIRST) compute_set<S, WD, SET_A>(a, a.ap, lds, lane);
@@ -1093,8 +1094,8 @@ __device__ bool poll_rows(const uint64_t *src, int n, uint32_t ep, float &v, int
 // and with all workgroups H, the final LayerNorm and the output head.  The
 // residual rows a set adds come back from the published vectors (the values
 // written are the values read), so no workgroup carries state across phases.
-template <class S, int WD, bool TR>
-__device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
+template <class S, int WD, bool TR, int SET>
+__device__ __attribute__((always_inline)) void control_set(const DecodeArgs &a, float *lds, int lane) {
   constexpr int E = S::E, F = S::F, D = S::D, H = S::H, G = S::G;
   constexpr int PE = E / 64, D4 = D / 4;
   using SQ = Set<S, SET_Q>;
@@ -1102,8 +1103,9 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
   using SF = Set<S, SET_F>;
   using SM = Set<S, SET_M>;
   const int w = blockIdx.x;
-  const int set = w < SA::FIRST ? SET_Q : w < SF::FIRST ? SET_A : w < SM::FIRST ? SET_F : SET_M;
-  const int rank = w - (set == SET_Q ? 0 : set == SET_A ? SA::FIRST : set == SET_F ? SF::FIRST : SM::FIRST);
+  // (one instantiation per set: the other sets' phases compile away)
+  constexpr int set = SET;
+  const int rank = w - Set<S, SET>::FIRST;
   int *flag = reinterpret_cast<int *>(lds + S::L_FLAG);
   float *xs = lds + S::L_XS;
   const float *part = lds + S::L_PART;
@@ -1201,7 +1203,10 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
     int nch, ch;
     att_chunks<S>(p, nch, ch);
     const int item = att_item_of<S>(w);
-    const bool has_item = item < H * nch;
+    // (set Q's workgroups come first in blockIdx: they get items only when the
+    // other sets cannot hold them all)
+    constexpr bool MAY_ITEM = set != SET_Q || S::H * S::MAXCH > G - S::NQ;
+    const bool has_item = MAY_ITEM && item < H * nch;
     const int ih = has_item ? item / nch : 0, ic = has_item ? item % nch : 0;
     const int it0 = ic * ch, it1 = min(it0 + ch, p + 1);
     const bool ilast = (it1 == p + 1);
@@ -1542,6 +1547,15 @@ __device__ void control_main(const DecodeArgs &a, float *lds, int lane) {
     if (!reduce_argmax<S>(a, epoch_of(a, a.nsteps - 1, 5 * a.L), lane, wt, bi)) return;
     if (lane == 0 && a.nsteps - 1 >= a.out_from) a.out_ids[a.nsteps - 1 - a.out_from] = (int)bi;
   }
+}
+
+template <class S, int WD, bool TR>
+__device__ __attribute__((always_inline)) void control_main(const DecodeArgs &a, float *lds, int lane) {
+  const int w = (int)blockIdx.x;
+  if (w < Set<S, SET_A>::FIRST) control_set<S, WD, TR, SET_Q>(a, lds, lane);
+  else if (w < Set<S, SET_F>::FIRST) control_set<S, WD, TR, SET_A>(a, lds, lane);
+  else if (w < Set<S, SET_M>::FIRST) control_set<S, WD, TR, SET_F>(a, lds, lane);
+  else control_set<S, WD, TR, SET_M>(a, lds, lane);
 }
 
 template <class S, int WD, bool TR>
