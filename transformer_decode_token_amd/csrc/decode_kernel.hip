@@ -416,17 +416,21 @@ struct Waiter {
   int phase;
   unsigned polls;
   __device__ void start(int ph) {
-    t0 = (long long)wall_clock64();
+    t0 = 0;  // (the clock is first read once the wait is long)
     phase = ph;
     polls = 0;
   }
   __device__ bool expired() {
-    // Another workgroup's abort is looked for at every 32nd failed poll only:
-    // the error word is a memory round trip of its own, which would otherwise
-    // double the period of every poll loop.  The clock is read every time.
-    if ((++polls & 31u) == 0 && __hip_atomic_load(a->err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
-      return true;
-    if ((long long)wall_clock64() - t0 > a->timeout_ticks) {
+    // A wait that ends within a few poll rounds (nearly every one) reads
+    // nothing here: the clock and the error word are looked at on every 16th
+    // failed poll only, the time limit counted from the first of those reads.
+    // (Each is a memory or counter round trip of its own, which would
+    // otherwise lengthen every poll round.)
+    if ((++polls & 15u) != 0) return false;
+    if (__hip_atomic_load(a->err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return true;
+    const long long now = (long long)wall_clock64();
+    if (t0 == 0) t0 = now;
+    if (now - t0 > a->timeout_ticks) {
       int zero = 0;
       if (__hip_atomic_compare_exchange_strong(a->err, &zero, 1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_AGENT)) {
