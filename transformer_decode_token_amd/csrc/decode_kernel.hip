@@ -83,6 +83,10 @@ struct Shape {
   static constexpr int HEAD_BATCHES = 3;
   static constexpr int HEAD_REGS_Q = 2, HEAD_REGS_LATE = 3;
   static constexpr int HEAD_REGS_Q4_Q = 2, HEAD_REGS_Q4_LATE = 2;  // int4 (its head is fp32)
+  // Batches (of 64/LPRH rows) of output-head rows the control wave keeps in its
+  // own registers for the launch and takes during the head (none with a slice
+  // share, whose registers it needs).
+  static constexpr int HEAD_CTL_BATCHES = CD_ ? 0 : 2;
   // The MLP activation (the longest polled vector) is polled in this many
   // equal parts by as many waves at once: the compute waves and the control
   // wave (each part a whole number of 128-word pair loads), else by the
@@ -646,6 +650,7 @@ __device__ __forceinline__ void dot_set(const Chunk<WD> (&b)[ST::NB], const floa
 template <class S, int WD>
 struct HeadGeo {
   static constexpr int KC = S::E / 4, LPR = S::LPRH, NPH = KC / LPR, RB = S::NL / LPR;
+  static constexpr int RBC = 64 / LPR, CTL_ROWS = S::HEAD_CTL_BATCHES * RBC;  // the control wave's rows
   static constexpr int HWD = (WD == WD_F16) ? WD_F16 : WD_F32;
   static_assert(KC % LPR == 0 && S::NL % LPR == 0 && LPR % 8 == 0, "head geometry");
 };
@@ -678,19 +683,22 @@ constexpr int head_reg_total() {
 }
 
 // Output-head rows [hr0, hr1) of workgroup w: the rows left after each
-// workgroup's register batches are split evenly, and each workgroup adds the
-// rows its registers hold (capped so that no workgroup exceeds PSTRIDE rows),
-// so every workgroup streams about the same number of rows during the head.
+// workgroup's register batches (the compute waves' and the control wave's)
+// are split evenly, and each workgroup adds the rows its registers hold
+// (capped so that no workgroup exceeds PSTRIDE rows), so every workgroup
+// streams about the same number of rows during the head.  A workgroup's
+// rows are, in order: LDS-resident, compute-wave registers, control-wave
+// registers, streamed.
 template <class S, int WD>
 __device__ __forceinline__ void head_range(int V, int w, int &hr0, int &hr1) {
   constexpr int RB = HeadGeo<S, WD>::RB;
   const int even = V / S::G;
   // no workgroup may get more than PSTRIDE rows (the row results live in LDS)
   const int cap = min(even, max(0, PSTRIDE - even - 1));
-  const int eQ = min(head_reg_total<S, WD, SET_Q>() * RB, cap);
-  const int eA = min(head_reg_total<S, WD, SET_A>() * RB, cap);
-  const int eF = min(head_reg_total<S, WD, SET_F>() * RB, cap);
-  const int eM = min(head_reg_total<S, WD, SET_M>() * RB, cap);
+  const int eQ = min(head_reg_total<S, WD, SET_Q>() * RB + HeadGeo<S, WD>::CTL_ROWS, cap);
+  const int eA = min(head_reg_total<S, WD, SET_A>() * RB + HeadGeo<S, WD>::CTL_ROWS, cap);
+  const int eF = min(head_reg_total<S, WD, SET_F>() * RB + HeadGeo<S, WD>::CTL_ROWS, cap);
+  const int eM = min(head_reg_total<S, WD, SET_M>() * RB + HeadGeo<S, WD>::CTL_ROWS, cap);
   const int rest = V - S::NQ * eQ - S::NA * eA - S::NF * eF - S::NM * eM;
   auto start = [&](int u) {
     const int nq = min(u, S::NQ);
@@ -779,7 +787,8 @@ __device__ bool head_rows(const DecodeArgs &a, float *lds, int lane, const Chunk
   const int nr = hr1 - hr0;
   const int nl = min(nr, a.head_lds_rows);
   const int ng = min(nr - nl, (NRB + NX) * RB);  // rows requested into registers beforehand
-  const int nh = nr - nl - ng, hb = hr0 + nl + ng;
+  const int nc = min(nr - nl - ng, HG::CTL_ROWS);  // the control wave's rows
+  const int nh = nr - nl - ng - nc, hb = hr0 + nl + ng + nc;
   const WSrc src = wsrc<HWD>(MatW{a.head, nullptr}, (size_t)hb * KC);
   const int q = lane % LPR, rl = lane / LPR;
   constexpr int HB = S::HEAD_BATCHES;  // batches streamed from memory in flight
@@ -834,7 +843,7 @@ __device__ bool head_rows(const DecodeArgs &a, float *lds, int lane, const Chunk
       if ((NRB + k) * RB < ng) consume(hx[k], nl + (NRB + k) * RB + rl, nl + ng);
   }
   if (nh > 0) {
-    const int nb = nl + ng;
+    const int nb = nl + ng + nc;
     for (int r0 = 0; r0 < nh; r0 += HB * RB) {
 #pragma unroll
       for (int k = 0; k < HB; k++) {
@@ -1186,6 +1195,31 @@ __device__ __attribute__((always_inline)) void control_set(const DecodeArgs &a, 
     }
   };
   if (!defers(0)) ctl_load(0);
+  // Output-head rows kept in this wave's registers for the launch (after the
+  // workgroup's LDS and compute-wave register rows), requested once.
+  using HG = HeadGeo<S, WD>;
+  constexpr int NXC = S::HEAD_CTL_BATCHES;
+  Chunk<HG::HWD> cx[NXC > 0 ? NXC : 1][HG::NPH];
+  int hc_first = 0, hc_n = 0;  // this wave's first row in the workgroup's range, and how many
+  if constexpr (NXC > 0) {
+    int r0, r1;
+    head_range<S, WD>(a.V, w, r0, r1);
+    const int nr = r1 - r0, nl = min(nr, a.head_lds_rows);
+    const int ng = min(nr - nl, head_reg_total<S, WD, SET>() * HG::RB);
+    hc_first = nl + ng;
+    hc_n = min(nr - hc_first, HG::CTL_ROWS);
+    if (hc_n > 0) {
+      const WSrc src = wsrc<HG::HWD>(MatW{a.head, nullptr}, (size_t)r0 * HG::KC);
+      const int q = lane % HG::LPR, rl = lane / HG::LPR;
+#pragma unroll
+      for (int k = 0; k < NXC; k++) {
+        const int r = hc_first + min(k * HG::RBC + rl, hc_n - 1);
+#pragma unroll
+        for (int i = 0; i < HG::NPH; i++)
+          cx[k][i] = ld_chunk<HG::HWD, HEAD_NT>(src, (uint32_t)(r * HG::KC + q), (uint32_t)(i * HG::LPR));
+      }
+    }
+  }
   auto abort_all = [&]() {
     if (lane == 0) flag[0] = 1;
     wg_barrier();
@@ -1514,6 +1548,23 @@ __device__ __attribute__((always_inline)) void control_set(const DecodeArgs &a, 
       }
       float mean, rstd;
       ln_stats<E>(x, a.eps, mean, rstd);
+      // this wave's own head rows, while the compute waves take theirs
+      if constexpr (NXC > 0) {
+        if (hc_n > 0) {
+          const int q = lane % HG::LPR, rl = lane / HG::LPR;
+          float4 xv[HG::NPH];
+#pragma unroll
+          for (int i = 0; i < HG::NPH; i++) xv[i] = reinterpret_cast<const float4 *>(xs)[i * HG::LPR + q];
+#pragma unroll
+          for (int k = 0; k < NXC; k++) {
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < HG::NPH; i++) acc = dot4(deq<HG::HWD>(cx[k][i]), xv[i], acc);
+            acc = seg_sum_last<HG::LPR>(acc);
+            if (q == HG::LPR - 1 && k * HG::RBC + rl < hc_n) lds[S::L_PART + hc_first + k * HG::RBC + rl] = acc;
+          }
+        }
+      }
       wg_barrier();
       st(step, 5 * a.L, 2);
       float bv = -INFINITY;
