@@ -1225,12 +1225,21 @@ __device__ __attribute__((always_inline)) void control_set(const DecodeArgs &a, 
     wg_barrier();
   };
   const bool needs_tok = (set == SET_Q || set == SET_A);
+  // Set Q: the embedding input of the next step when its token is fed (known
+  // ahead), requested during this step's head.
+  float xn[PE];
+#pragma unroll
+  for (int j = 0; j < PE; j++) xn[j] = 0.f;
+  // Token of each step: fed, or the argmax of the previous step.  While the
+  // tokens are fed, the previous step's argmax is waited for only where an id
+  // is recorded, so the first layer of a fed step can start while the
+  // previous step's head is still running elsewhere.
+  const int argmax_from = max(1, w == 0 ? min(a.n_feed, a.out_from + 1) : a.n_feed);
   for (int step = 0; step < a.nsteps; step++) {
     const int p = a.pos0 + step;
     cur_step = step;
-    // token of this step: fed, or the argmax of the previous step
     if (step < a.n_feed) tok = a.feed[step];
-    if (step > 0 && needs_tok) {
+    if (needs_tok && step >= argmax_from) {
       uint32_t bi = 0;
       wt.start(5 * a.L);
       if (!reduce_argmax<S>(a, epoch_of(a, step - 1, 5 * a.L), lane, wt, bi)) { abort_all(); return; }
@@ -1260,7 +1269,10 @@ __device__ __attribute__((always_inline)) void control_set(const DecodeArgs &a, 
       // ---------------- A: LayerNorm 1 + QKV (set Q)
       if (set == SET_Q) {
         float x[PE];
-        if (l == 0) {
+        if (l == 0 && step > 0 && step < a.n_feed) {
+#pragma unroll
+          for (int j = 0; j < PE; j++) x[j] = xn[j];
+        } else if (l == 0) {
 #pragma unroll
           for (int j = 0; j < PE; j++)
             x[j] = a.wte[(size_t)tok * E + vidx(lane, j)] + a.wpe[(size_t)p * E + vidx(lane, j)];
@@ -1523,6 +1535,12 @@ __device__ __attribute__((always_inline)) void control_set(const DecodeArgs &a, 
     {
       const uint32_t epH = epoch_of(a, step, 5 * a.L);
       if constexpr (S::CD) fetch_gain(gf, a.lnfw);  // (arrives while the input is polled)
+      if (set == SET_Q && step + 1 < a.n_feed && step + 1 < a.nsteps) {
+        const int tn = a.feed[step + 1];
+#pragma unroll
+        for (int j = 0; j < PE; j++)
+          xn[j] = a.wte[(size_t)tn * E + vidx(lane, j)] + a.wpe[(size_t)(p + 1) * E + vidx(lane, j)];
+      }
       float x[PE];
       wt.start(5 * a.L - 1);
       if (!poll_vec<PE>(a.xb_t + ((size_t)(a.L - 1) * NCOPY + my_copy()) * E, epH - 1, x, lane, wt)) {
