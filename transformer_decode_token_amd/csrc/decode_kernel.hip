@@ -253,6 +253,27 @@ __device__ __forceinline__ float dot_q4(const Chunk<WD_Q4> &c, float4 x, float x
   return __builtin_fmaf(c.sz.y, xsum, acc);
 }
 
+// Two neighbouring int4 chunks of one group (8 inputs, the 8 codes in one
+// 32-bit word) against their inputs x0, x1: one scale and one zero per 8
+// weights.  The codes are spread one per byte (even inputs, then odd ones)
+// and each byte is converted by the byte-select conversion.
+__device__ __forceinline__ float dot_q4x2(uint32_t q, float2 sz, float4 x0, float4 x1, float xsum, float acc) {
+  uint32_t ev = q & 0x0F0F0F0Fu, od = (q >> 4) & 0x0F0F0F0Fu;
+  // (opaque: the compiler would otherwise narrow each byte to its nibble and
+  // extract it with a bit-field instruction before converting)
+  __asm__("" : "+v"(ev), "+v"(od));
+  float t = (float)(ev & 0xFFu) * x0.x;
+  t = __builtin_fmaf((float)(od & 0xFFu), x0.y, t);
+  t = __builtin_fmaf((float)((ev >> 8) & 0xFFu), x0.z, t);
+  t = __builtin_fmaf((float)((od >> 8) & 0xFFu), x0.w, t);
+  t = __builtin_fmaf((float)((ev >> 16) & 0xFFu), x1.x, t);
+  t = __builtin_fmaf((float)((od >> 16) & 0xFFu), x1.y, t);
+  t = __builtin_fmaf((float)(ev >> 24), x1.z, t);
+  t = __builtin_fmaf((float)(od >> 24), x1.w, t);
+  acc = __builtin_fmaf(sz.x, t, acc);
+  return __builtin_fmaf(sz.y, xsum, acc);
+}
+
 // ---- DPP reductions ----------------------------------------------------------
 // Inclusive scans with row_shr 1,2,4,8 (within 16-lane rows), then
 // row_bcast:15 / row_bcast:31 across rows: the total of each W-lane segment
@@ -598,9 +619,24 @@ __device__ __forceinline__ void load_set(Chunk<WD> (&b)[ST::NB], const MatW &m, 
 #pragma unroll
   for (int t = 0; t < ST::NP; t++) {
     const int r = min(t * ST::RP + lane / ST::LPR, ST::R - 1);
-    const uint32_t c0 = (uint32_t)(r * ST::KC + q);
+    if constexpr (WD == WD_Q4) {
+      // int4: lane q takes chunk pairs (2q, 2q+1) + 2*LPR*i, each pair one
+      // 32-bit word of codes inside one group; entry t*CPR + i holds pair i
+      const uint32_t c0 = (uint32_t)(r * ST::KC + 2 * q);
 #pragma unroll
-    for (int i = 0; i < ST::CPR; i++) b[t * ST::CPR + i] = ld_chunk<WD>(src, c0, (uint32_t)(i * ST::LPR));
+      for (int i = 0; i < ST::CPR / 2; i++) {
+        const uint32_t ck = (uint32_t)(2 * ST::LPR * i);
+        Chunk<WD_Q4> c;
+        c.q = __builtin_amdgcn_raw_buffer_load_b32(src.w, c0 * 2u, ck * 2u, 2);
+        const g2_v2u z = __builtin_amdgcn_raw_buffer_load_b64(src.sz, (c0 / 8u) * 8u, ck, 2);
+        c.sz = make_float2(__uint_as_float(z.x), __uint_as_float(z.y));
+        b[t * ST::CPR + i] = c;
+      }
+    } else {
+      const uint32_t c0 = (uint32_t)(r * ST::KC + q);
+#pragma unroll
+      for (int i = 0; i < ST::CPR; i++) b[t * ST::CPR + i] = ld_chunk<WD>(src, c0, (uint32_t)(i * ST::LPR));
+    }
   }
 }
 
@@ -611,10 +647,13 @@ __device__ __forceinline__ void load_set(Chunk<WD> (&b)[ST::NB], const MatW &m, 
 template <class ST, int WD>
 __device__ __forceinline__ void dot_set(const Chunk<WD> (&b)[ST::NB], const float *xs, float *part, int lane) {
   const int q = lane % ST::LPR;
-  // all input chunks first: one burst of LDS reads instead of one round trip per chunk
+  // all input chunks first: one burst of LDS reads instead of one round trip per
+  // chunk (int4: the chunks of its pairs, (2q, 2q+1) + 2*LPR*i)
   float4 xv[ST::CPR];
 #pragma unroll
-  for (int i = 0; i < ST::CPR; i++) xv[i] = reinterpret_cast<const float4 *>(xs)[i * ST::LPR + q];
+  for (int i = 0; i < ST::CPR; i++)
+    xv[i] = WD == WD_Q4 ? reinterpret_cast<const float4 *>(xs)[2 * q + (i & 1) + 2 * ST::LPR * (i >> 1)]
+                        : reinterpret_cast<const float4 *>(xs)[i * ST::LPR + q];
   // fp16 and int4: two partial sums per row (even and odd chunks), two
   // independent chains (measured faster there; fp32 keeps one)
   constexpr int NCH = WD == WD_F32 ? 1 : 2;
@@ -622,14 +661,20 @@ __device__ __forceinline__ void dot_set(const Chunk<WD> (&b)[ST::NB], const floa
 #pragma unroll
   for (int t = 0; t < ST::NP; t++) acc[t][0] = acc[t][1] = 0.f;
   if constexpr (WD == WD_Q4) {
-    float xsum[ST::CPR];
+    static_assert(ST::CPR % 2 == 0, "int4 chunk pairs");
+    float xsum[ST::CPR / 2];
 #pragma unroll
-    for (int i = 0; i < ST::CPR; i++) xsum[i] = (xv[i].x + xv[i].y) + (xv[i].z + xv[i].w);
+    for (int i = 0; i < ST::CPR / 2; i++) {
+      const float4 u = xv[2 * i], v = xv[2 * i + 1];
+      xsum[i] = ((u.x + u.y) + (u.z + u.w)) + ((v.x + v.y) + (v.z + v.w));
+    }
 #pragma unroll
-    for (int i = 0; i < ST::CPR; i++) {
+    for (int i = 0; i < ST::CPR / 2; i++) {
 #pragma unroll
-      for (int t = 0; t < ST::NP; t++)
-        acc[t][i % NCH] = dot_q4(b[t * ST::CPR + i], xv[i], xsum[i], acc[t][i % NCH]);
+      for (int t = 0; t < ST::NP; t++) {
+        const Chunk<WD> &c = b[t * ST::CPR + i];
+        acc[t][i % NCH] = dot_q4x2(c.q, c.sz, xv[2 * i], xv[2 * i + 1], xsum[i], acc[t][i % NCH]);
+      }
     }
   } else {
 #pragma unroll
