@@ -158,6 +158,8 @@ struct Set {
 };
 
 // ---- weight chunks: 4 consecutive inputs of one output row ----------------
+// (int4: two neighbouring chunks of one group, 8 codes in q, with the group's
+// scale and zero; loaded by load_set, taken by dot_q4x2)
 template <int WD> struct Chunk;
 template <> struct Chunk<WD_F32> { float4 v; };
 template <> struct Chunk<WD_F16> { uint2 v; };
@@ -195,17 +197,14 @@ __device__ __forceinline__ WSrc wsrc(const MatW &m, size_t c0) {
 template <int WD, bool NT = true>
 __device__ __forceinline__ Chunk<WD> ld_chunk(const WSrc &s, uint32_t cl, uint32_t ck = 0) {
   constexpr int AUX = NT ? 2 : 0;  // nt
+  static_assert(WD != WD_Q4, "int4 chunks are loaded in pairs (load_set)");
   Chunk<WD> r;
   if constexpr (WD == WD_F32) {
     const g2_v4u v = __builtin_amdgcn_raw_buffer_load_b128(s.w, cl * 16u, ck * 16u, AUX);
     r.v = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
-  } else if constexpr (WD == WD_F16) {
+  } else {
     const g2_v2u v = __builtin_amdgcn_raw_buffer_load_b64(s.w, cl * 8u, ck * 8u, AUX);
     r.v = make_uint2(v.x, v.y);
-  } else {
-    r.q = __builtin_amdgcn_raw_buffer_load_b16(s.w, cl * 2u, ck * 2u, AUX);
-    const g2_v2u z = __builtin_amdgcn_raw_buffer_load_b64(s.sz, (cl / 8u) * 8u, ck, AUX);
-    r.sz = make_float2(__uint_as_float(z.x), __uint_as_float(z.y));
   }
   return r;
 }
@@ -214,20 +213,14 @@ __device__ __forceinline__ float h2f(uint32_t bits16) {
   return __half2float(__ushort_as_half((unsigned short)(bits16 & 0xffffu)));
 }
 
-// The weights a chunk stands for, as fp32.  fp16 widening is exact; int4 is
-// dequantised with one fused multiply-add per weight: fma(code, scale, zero).
+// The weights a chunk stands for, as fp32 (fp16 widening is exact).
 template <int WD>
 __device__ __forceinline__ float4 deq(const Chunk<WD> &c) {
+  static_assert(WD != WD_Q4, "int4 chunks are taken in pairs (dot_q4x2)");
   if constexpr (WD == WD_F32) {
     return c.v;
-  } else if constexpr (WD == WD_F16) {
-    return make_float4(h2f(c.v.x), h2f(c.v.x >> 16), h2f(c.v.y), h2f(c.v.y >> 16));
   } else {
-    const float s = c.sz.x, z = c.sz.y;
-    return make_float4(__builtin_fmaf((float)(c.q & 15u), s, z),
-                       __builtin_fmaf((float)((c.q >> 4) & 15u), s, z),
-                       __builtin_fmaf((float)((c.q >> 8) & 15u), s, z),
-                       __builtin_fmaf((float)((c.q >> 12) & 15u), s, z));
+    return make_float4(h2f(c.v.x), h2f(c.v.x >> 16), h2f(c.v.y), h2f(c.v.y >> 16));
   }
 }
 
@@ -239,22 +232,10 @@ __device__ __forceinline__ float dot4(float4 w, float4 x, float acc) {
   return acc;
 }
 
-// One int4 chunk against four inputs, with the group's scale s and zero z
-// taken out of the sum: sum_k (code_k*s + z)*x_k = s*sum_k code_k*x_k + z*xsum,
-// xsum = x.x + x.y + x.z + x.w.  The four codes are spread one per byte (even
-// inputs, then odd ones) and converted by byte.
-__device__ __forceinline__ float dot_q4(const Chunk<WD_Q4> &c, float4 x, float xsum, float acc) {
-  const uint32_t ev = c.q & 0x0F0Fu, od = (c.q >> 4) & 0x0F0Fu;
-  float t = (float)(ev & 0xFFu) * x.x;
-  t = __builtin_fmaf((float)(od & 0xFFu), x.y, t);
-  t = __builtin_fmaf((float)(ev >> 8), x.z, t);
-  t = __builtin_fmaf((float)(od >> 8), x.w, t);
-  acc = __builtin_fmaf(c.sz.x, t, acc);
-  return __builtin_fmaf(c.sz.y, xsum, acc);
-}
-
 // Two neighbouring int4 chunks of one group (8 inputs, the 8 codes in one
-// 32-bit word) against their inputs x0, x1: one scale and one zero per 8
+// 32-bit word) against their inputs x0, x1, with the group's scale s and zero
+// z taken out of the sum: sum_k (code_k*s + z)*x_k = s*sum_k code_k*x_k +
+// z*xsum, xsum the sum of the 8 inputs: one scale and one zero per 8
 // weights.  The codes are spread one per byte (even inputs, then odd ones)
 // and each byte is converted by the byte-select conversion.
 __device__ __forceinline__ float dot_q4x2(uint32_t q, float2 sz, float4 x0, float4 x1, float xsum, float acc) {
@@ -641,9 +622,9 @@ __device__ __forceinline__ void load_set(Chunk<WD> (&b)[ST::NB], const MatW &m, 
 }
 
 // Row results of the slice (input vector in LDS) into part[0..R): each lane
-// sums its chunks in order (fp16 and int4: its even and its odd chunks, then
-// the two; int4 with each group's scale and zero taken out, dot_q4), then a
-// DPP reduction over the row's LPR lanes.
+// sums its chunks in order (fp16: its even and its odd chunks, then the two;
+// int4: its even and its odd chunk pairs, each with its group's scale and zero
+// taken out, dot_q4x2), then a DPP reduction over the row's LPR lanes.
 template <class ST, int WD>
 __device__ __forceinline__ void dot_set(const Chunk<WD> (&b)[ST::NB], const float *xs, float *part, int lane) {
   const int q = lane % ST::LPR;
