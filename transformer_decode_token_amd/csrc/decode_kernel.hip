@@ -159,7 +159,7 @@ struct Set {
 
 // ---- weight chunks: 4 consecutive inputs of one output row ----------------
 // (int4: two neighbouring chunks of one group, 8 codes in q, with the group's
-// scale and zero; loaded by load_set, taken by dot_q4x2)
+// scale and zero; loaded by load_set, taken by dot_q4x2m)
 template <int WD> struct Chunk;
 template <> struct Chunk<WD_F32> { float4 v; };
 template <> struct Chunk<WD_F16> { uint2 v; };
@@ -216,7 +216,7 @@ __device__ __forceinline__ float h2f(uint32_t bits16) {
 // The weights a chunk stands for, as fp32 (fp16 widening is exact).
 template <int WD>
 __device__ __forceinline__ float4 deq(const Chunk<WD> &c) {
-  static_assert(WD != WD_Q4, "int4 chunks are taken in pairs (dot_q4x2)");
+  static_assert(WD != WD_Q4, "int4 chunks are taken in pairs (dot_q4x2m)");
   if constexpr (WD == WD_F32) {
     return c.v;
   } else {
@@ -235,24 +235,27 @@ __device__ __forceinline__ float dot4(float4 w, float4 x, float acc) {
 // Two neighbouring int4 chunks of one group (8 inputs, the 8 codes in one
 // 32-bit word) against their inputs x0, x1, with the group's scale s and zero
 // z taken out of the sum: sum_k (code_k*s + z)*x_k = s*sum_k code_k*x_k +
-// z*xsum, xsum the sum of the 8 inputs: one scale and one zero per 8
-// weights.  The codes are spread one per byte (even inputs, then odd ones)
-// and each byte is converted by the byte-select conversion.
-__device__ __forceinline__ float dot_q4x2(uint32_t q, float2 sz, float4 x0, float4 x1, float xsum, float acc) {
-  uint32_t ev = q & 0x0F0F0F0Fu, od = (q >> 4) & 0x0F0F0F0Fu;
-  // (opaque: the compiler would otherwise narrow each byte to its nibble and
-  // extract it with a bit-field instruction before converting)
-  __asm__("" : "+v"(ev), "+v"(od));
-  float t = (float)(ev & 0xFFu) * x0.x;
-  t = __builtin_fmaf((float)(od & 0xFFu), x0.y, t);
-  t = __builtin_fmaf((float)((ev >> 8) & 0xFFu), x0.z, t);
-  t = __builtin_fmaf((float)((od >> 8) & 0xFFu), x0.w, t);
-  t = __builtin_fmaf((float)((ev >> 16) & 0xFFu), x1.x, t);
-  t = __builtin_fmaf((float)((od >> 16) & 0xFFu), x1.y, t);
-  t = __builtin_fmaf((float)(ev >> 24), x1.z, t);
-  t = __builtin_fmaf((float)(od >> 24), x1.w, t);
-  acc = __builtin_fmaf(sz.x, t, acc);
-  return __builtin_fmaf(sz.y, xsum, acc);
+// z*xsum, xsum the sum of the 8 inputs, so one scale and one zero per 8
+// weights.  Each code is taken as an fp16 subnormal: a code n alone in a
+// 16-bit half (two masks per shift spread the 8 codes over four words) is
+// exactly n * 2^-24, which the mixed-precision multiply-add widens and
+// multiplies in one instruction, with no conversion (fp16 subnormals are kept,
+// the default floating-point mode).  The scale terms accumulate in as (times
+// 2^-24, exactly), the zero terms in az; the row result is as * 2^24 + az.
+__device__ __forceinline__ void dot_q4x2m(uint32_t q, float2 sz, float4 x0, float4 x1, float xsum, float &as,
+                                          float &az) {
+  const uint32_t c04 = q & 0x000F000Fu, c15 = (q >> 4) & 0x000F000Fu;
+  const uint32_t c26 = (q >> 8) & 0x000F000Fu, c37 = (q >> 12) & 0x000F000Fu;
+  float t = __builtin_fmaf(h2f(c04), x0.x, 0.f);
+  t = __builtin_fmaf(h2f(c15), x0.y, t);
+  t = __builtin_fmaf(h2f(c26), x0.z, t);
+  t = __builtin_fmaf(h2f(c37), x0.w, t);
+  t = __builtin_fmaf(h2f(c04 >> 16), x1.x, t);
+  t = __builtin_fmaf(h2f(c15 >> 16), x1.y, t);
+  t = __builtin_fmaf(h2f(c26 >> 16), x1.z, t);
+  t = __builtin_fmaf(h2f(c37 >> 16), x1.w, t);
+  as = __builtin_fmaf(sz.x, t, as);
+  az = __builtin_fmaf(sz.y, xsum, az);
 }
 
 // ---- DPP reductions ----------------------------------------------------------
@@ -623,8 +626,9 @@ __device__ __forceinline__ void load_set(Chunk<WD> (&b)[ST::NB], const MatW &m, 
 
 // Row results of the slice (input vector in LDS) into part[0..R): each lane
 // sums its chunks in order (fp16: its even and its odd chunks, then the two;
-// int4: its even and its odd chunk pairs, each with its group's scale and zero
-// taken out, dot_q4x2), then a DPP reduction over the row's LPR lanes.
+// int4: its chunk pairs, each with its group's scale and zero taken out, the
+// scale and the zero terms in two sums, dot_q4x2m), then a DPP reduction over
+// the row's LPR lanes.
 template <class ST, int WD>
 __device__ __forceinline__ void dot_set(const Chunk<WD> (&b)[ST::NB], const float *xs, float *part, int lane) {
   const int q = lane % ST::LPR;
@@ -654,8 +658,13 @@ __device__ __forceinline__ void dot_set(const Chunk<WD> (&b)[ST::NB], const floa
 #pragma unroll
       for (int t = 0; t < ST::NP; t++) {
         const Chunk<WD> &c = b[t * ST::CPR + i];
-        acc[t][i % NCH] = dot_q4x2(c.q, c.sz, xv[2 * i], xv[2 * i + 1], xsum[i], acc[t][i % NCH]);
+        dot_q4x2m(c.q, c.sz, xv[2 * i], xv[2 * i + 1], xsum[i], acc[t][0], acc[t][1]);
       }
+    }
+#pragma unroll
+    for (int t = 0; t < ST::NP; t++) {
+      acc[t][0] = __builtin_fmaf(acc[t][0], 16777216.0f, acc[t][1]);
+      acc[t][1] = 0.f;
     }
   } else {
 #pragma unroll
