@@ -321,3 +321,30 @@ def test_generate_edges():
     assert g2.gpt2_filled(ctx) == P
     orc.close()
     ctx.close()
+
+
+@pytest.mark.parametrize("name", ["tiny-rich", "tiny-rich-int4", "gpt2-124m-fp32"])
+def test_long_prompt_in_one_run(name):
+    """A long prompt fed in one device-chained run.  While the tokens are fed,
+    a step's first layer may start before the previous step's output head has
+    finished everywhere (its argmax is not needed); the cache rows those
+    steps leave are checked through the logits of the next single step, and
+    the run's ids against the oracle."""
+    cfg = CASES[name]
+    model = synth.make_model(cfg)
+    orc = Oracle(model)
+    rng = np.random.default_rng(91)
+    n_prompt = min(48, cfg.n_positions - 4)
+    prompt = [int(t) for t in rng.integers(0, cfg.vocab, n_prompt)]
+    ctx = load_gpu(model)
+    got = g2.gpt2_generate(ctx, np.array(prompt, np.int32), 2)
+    want, mg = _oracle_greedy(orc, prompt, 0, 2)
+    _assert_ids(got, want, mg, "long prompt")
+    assert g2.gpt2_filled(ctx) == n_prompt + 1
+    # one more pass, fed the oracle's id: its logits read every cache row above
+    am, lg = g2.gpt2_step(ctx, int(want[1]), n_prompt + 1, want_logits=True)
+    am_o, lg_o = orc.step(int(want[1]), n_prompt + 1)
+    compare_step(lg, am, lg_o, f"after a {n_prompt}-id prompt")
+    if top2_margin(lg_o) > 1e-3:
+        assert am == am_o
+    ctx.close()
