@@ -695,12 +695,12 @@ struct HeadGeo {
 // sets, when the register chunk type is the head's: not for int4), requested
 // after the set's last phase of each step, and head_extra_batches in registers
 // of their own, requested once and kept for the launch, up to a total per
-// weight type (none for fp16, whose head is bound by its arithmetic, not by
-// memory).
+// weight type (the same batch counts for fp32 and fp16 heads: more fp16
+// batches, though half the registers each, measured slower).
 template <class S, int WD, int SET>
 constexpr int head_reg_want() {
   return WD == WD_Q4 ? (SET == SET_Q ? S::HEAD_REGS_Q4_Q : S::HEAD_REGS_Q4_LATE)
-                     : WD == WD_F16 ? 0 : (SET == SET_Q ? S::HEAD_REGS_Q : S::HEAD_REGS_LATE);
+                     : (SET == SET_Q ? S::HEAD_REGS_Q : S::HEAD_REGS_LATE);
 }
 template <class S, int WD, int SET>
 constexpr int head_reg_batches() {
