@@ -82,7 +82,7 @@ struct Shape {
   // the later sets (whose idle slice registers hold part of them).
   static constexpr int HEAD_BATCHES = 3;
   static constexpr int HEAD_REGS_Q = 2, HEAD_REGS_LATE = 3;
-  static constexpr int HEAD_REGS_Q4_Q = 2, HEAD_REGS_Q4_LATE = 2;  // int4 (its head is fp32)
+  static constexpr int HEAD_REGS_Q4_Q = 2, HEAD_REGS_Q4_LATE = 3;  // int4 (its head is fp32)
   // Batches (of 64/LPRH rows) of output-head rows the control wave keeps in its
   // own registers for the launch and takes during the head (none with a slice
   // share, whose registers it needs).
