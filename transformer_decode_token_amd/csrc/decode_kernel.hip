@@ -237,24 +237,27 @@ __device__ __forceinline__ float dot4(float4 w, float4 x, float acc) {
 // z taken out of the sum: sum_k (code_k*s + z)*x_k = s*sum_k code_k*x_k +
 // z*xsum, xsum the sum of the 8 inputs, so one scale and one zero per 8
 // weights.  Each code is taken as an fp16 subnormal: a code n alone in a
-// 16-bit half (two masks per shift spread the 8 codes over four words) is
-// exactly n * 2^-24, which the mixed-precision multiply-add widens and
-// multiplies in one instruction, with no conversion (fp16 subnormals are kept,
-// the default floating-point mode).  The scale terms accumulate in as (times
-// 2^-24, exactly), the zero terms in az; the row result is as * 2^24 + az.
+// 16-bit half, in the half's bits 0-3 or 4-7, is exactly n * 2^-24 or
+// n * 2^-20, which the mixed-precision multiply-add widens and multiplies in
+// one instruction, with no conversion (fp16 subnormals are kept, the default
+// floating-point mode).  Four masks and one shift spread the 8 codes over four
+// words; the two kinds are summed apart and joined with an exact factor 1/16.
+// The scale terms accumulate in as (times 2^-24, exactly), the zero terms in
+// az; the row result is as * 2^24 + az.
 __device__ __forceinline__ void dot_q4x2m(uint32_t q, float2 sz, float4 x0, float4 x1, float xsum, float &as,
                                           float &az) {
-  const uint32_t c04 = q & 0x000F000Fu, c15 = (q >> 4) & 0x000F000Fu;
-  const uint32_t c26 = (q >> 8) & 0x000F000Fu, c37 = (q >> 12) & 0x000F000Fu;
-  float t = __builtin_fmaf(h2f(c04), x0.x, 0.f);
-  t = __builtin_fmaf(h2f(c15), x0.y, t);
-  t = __builtin_fmaf(h2f(c26), x0.z, t);
-  t = __builtin_fmaf(h2f(c37), x0.w, t);
-  t = __builtin_fmaf(h2f(c04 >> 16), x1.x, t);
-  t = __builtin_fmaf(h2f(c15 >> 16), x1.y, t);
-  t = __builtin_fmaf(h2f(c26 >> 16), x1.z, t);
-  t = __builtin_fmaf(h2f(c37 >> 16), x1.w, t);
-  as = __builtin_fmaf(sz.x, t, as);
+  const uint32_t u = q >> 8;
+  const uint32_t c04 = q & 0x000F000Fu, c26 = u & 0x000F000Fu;  // n * 2^-24
+  const uint32_t c15 = q & 0x00F000F0u, c37 = u & 0x00F000F0u;  // n * 2^-20
+  float ta = __builtin_fmaf(h2f(c04), x0.x, 0.f);
+  float tb = __builtin_fmaf(h2f(c15), x0.y, 0.f);
+  ta = __builtin_fmaf(h2f(c26), x0.z, ta);
+  tb = __builtin_fmaf(h2f(c37), x0.w, tb);
+  ta = __builtin_fmaf(h2f(c04 >> 16), x1.x, ta);
+  tb = __builtin_fmaf(h2f(c15 >> 16), x1.y, tb);
+  ta = __builtin_fmaf(h2f(c26 >> 16), x1.z, ta);
+  tb = __builtin_fmaf(h2f(c37 >> 16), x1.w, tb);
+  as = __builtin_fmaf(sz.x, __builtin_fmaf(tb, 0.0625f, ta), as);
   az = __builtin_fmaf(sz.y, xsum, az);
 }
 
