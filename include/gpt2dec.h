@@ -21,8 +21,9 @@
  *    gpt2_set_stream); every call that returns host data synchronizes it.
  *  - Return value 0 = success, or one of the negative GPT2_E_* codes below.
  *    Arguments are validated before any device work, so a rejected call
- *    changes nothing.  After GPT2_E_DEVICE the context is poisoned: every
- *    later call except gpt2_last_error/gpt2_free returns GPT2_E_STATE.
+ *    changes nothing.  After GPT2_E_DEVICE or GPT2_E_NUMERIC the context is
+ *    poisoned: every later call except gpt2_last_error/gpt2_free returns
+ *    GPT2_E_STATE.
  *  - A context must not be used by two threads at once.
  */
 #ifndef GPT2DEC_H
@@ -44,6 +45,8 @@ extern "C" {
 #define GPT2_E_NOMEM (-2)   /* host or device allocation failed                 */
 #define GPT2_E_DEVICE (-3)  /* HIP error, no GPU, or a device-side wait timeout */
 #define GPT2_E_STATE (-4)   /* context poisoned by an earlier device error      */
+#define GPT2_E_NUMERIC (-5) /* every logit of a pass is NaN: no greedy id exists
+                               (the context is poisoned: its cache holds the pass) */
 
 /* Storage of the 48 block matrices (and, for fp16, the output head).  fp32 is
  * the model file's f32 linears ("--fir-f32"); fp16 is the gpt2.s "-h" option
@@ -97,7 +100,8 @@ GPT2DEC_API int gpt2_set_stream(gpt2_ctx *c, void *hip_stream);
  * overwritten and positions 0..position are read, exactly as the model
  * file's attn_decode kernel does).  Afterwards filled = position + 1.
  * logits_out: NULL or host float[V]; argmax_out: NULL or host int (lowest id
- * among equal maxima).  Errors: GPT2_E_INVAL, GPT2_E_DEVICE, GPT2_E_STATE. */
+ * among equal maxima; NaN logits are never the maximum).  Errors: GPT2_E_INVAL,
+ * GPT2_E_DEVICE, GPT2_E_NUMERIC (all logits NaN), GPT2_E_STATE. */
 GPT2DEC_API int gpt2_step(gpt2_ctx *c, int token_id, int position, float *logits_out, int *argmax_out);
 
 /* Greedy generation chained on the device (one kernel launch, no host round
@@ -124,10 +128,13 @@ GPT2DEC_API int gpt2_filled(const gpt2_ctx *c);
 
 /* ---- test hooks (not needed for decoding) ------------------------------ */
 
-/* Effective weights of one matrix as the GPU kernels see them, dequantised by
- * the same device code the GEMV uses, output-major: which = 0 QKV [3E][E],
- * 1 attention projection [E][E], 2 fc [F][E], 3 MLP projection [E][F],
- * 4 output head [V][E] (layer ignored).  out: host float[N*K]. */
+/* Effective weights of one matrix as stored on the GPU, output-major: which =
+ * 0 QKV [3E][E], 1 attention projection [E][E], 2 fc [F][E], 3 MLP projection
+ * [E][F], 4 output head [V][E] (layer ignored).  fp32 as is, fp16 widened,
+ * int4 as zero + code * scale (one rounding) from the stored codes, scales and
+ * zeros.  The int4 GEMV reads the same stored data but sums
+ * scale * sum(code * x) + zero * sum(x) per group, so this pins the stored
+ * weights, not the GEMV's arithmetic.  out: host float[N*K]. */
 GPT2DEC_API int gpt2_debug_dequant(gpt2_ctx *c, int layer, int which, float *out);
 
 /* Fill every KV-cache entry with `value` (e.g. NaN) so that a read of a row
@@ -135,14 +142,19 @@ GPT2DEC_API int gpt2_debug_dequant(gpt2_ctx *c, int layer, int which, float *out
 GPT2DEC_API int gpt2_debug_fill_kv(gpt2_ctx *c, float value);
 
 /* Timeline of the decode kernel (profiling aid).  With out == NULL: from now
- * on record the first `steps` steps of every run (0 = stop recording).  With
- * out != NULL: copy the last run's record, then apply `steps` as above.
+ * on record the first `steps` steps of every run (0 = stop recording; -1 =
+ * keep the current setting, e.g. to only read the record or its size).  With
+ * out != NULL: copy the last run's record (out holds out_len values; a smaller
+ * out_len than the record is GPT2_E_INVAL and copies nothing), then apply
+ * `steps` as above.  recorded_steps (nullable) receives the number of steps
+ * the current record holds, so a caller can size out.
  * Layout: [steps][5L+1 phases][workgroups][4] int64 device wall-clock ticks
  * (inputs ready, first and second workgroup barrier passed, outputs
  * published; 0 where a workgroup had no such event), phases
  * per layer l: 5l QKV, 5l+1 attention, 5l+2 attention projection, 5l+3 fc,
  * 5l+4 MLP projection; phase 5L is the output head. */
-GPT2DEC_API int gpt2_debug_trace(gpt2_ctx *c, int steps, long long *out);
+GPT2DEC_API int gpt2_debug_trace(gpt2_ctx *c, int steps, long long *out, long long out_len,
+                                 int *recorded_steps);
 
 /* Launch geometry: workgroups and threads per workgroup of the decode kernel. */
 GPT2DEC_API int gpt2_debug_geometry(const gpt2_ctx *c, int *workgroups, int *threads);

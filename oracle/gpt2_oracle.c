@@ -1,27 +1,47 @@
 /*
  * gpt2_oracle.c -- CPU oracle for batch-1 GPT-2 decode (TEST INFRASTRUCTURE ONLY).
  *
- * Plain, sequential loops.  Every step follows the "model.fir" page (the
- * gpt2-125m model file) node by node, in its order, with its micro-kernels'
- * arithmetic:
- *   - g2.add              : out = a + b
- *   - g2.layernorm        : mean, then biased variance, ((x-mean)*rsqrt(var+eps))*gamma+beta
- *   - g2.gelu_new         : x * sigmoid(2*sqrt(2/pi) * (x + 0.044715*x^3))
- *   - g2.attn_decode      : append K/V at `position`, scores q.k * (1/sqrt(headdim))
- *                           over 0..position, max-subtracted exp, divide by the sum,
- *                           weighted sum of values
- *   - fir.linear          : y = x . W with W in Conv1D [input][output] layout
- *   - fir.linear_t        : logits = wte . n (tied head, no bias)
- * Greedy pick = argmax ("Let's make GPT-2 in assembly", Step 7), lowest index on ties.
+ * A plain, slow, single-threaded statement of what one decode step computes,
+ * written from the textbook definition of the GPT-2 network rather than from
+ * any listing: a pre-LayerNorm transformer decoder whose blocks are
  *
- * Build: gcc -O3 -ffp-contract=off (no fast-math), so every product is rounded
- * before it is added and sums run in ascending index order.
+ *   h <- h + Attn(LN_1(h)),   h <- h + MLP(LN_2(h)),
  *
- * Pinned by tests/test_oracle_pins.py against: Hugging Face GPT2LMHeadModel in
- * float64 on the same weights, numpy float64 matmul with the inner-product error
- * bound, torch layer_norm / tanh-form gelu, closed-form softmax cases, numpy
- * float16 casts, a brute-force search for the nearest int4 code, the KV-cache-free
- * brute-force recompute and the float64 build of this same file.
+ * followed by a final LayerNorm and an output head that reuses the token
+ * embedding matrix (the gpt2-125m model file's header and node list; "Let's
+ * make GPT-2 in assembly", Steps 4-7).  Each piece below is its defining
+ * formula written out:
+ *
+ *   LayerNorm   y_i = gamma_i * (x_i - mu) / sqrt(sigma^2 + eps) + beta_i,
+ *               mu and sigma^2 the mean and the biased variance of x
+ *   gelu_new    x * logistic(2 * sqrt(2/pi) * (x + 0.044715 x^3)), the tanh
+ *               approximation of GELU, 0.5 x (1 + tanh(z)) = x * logistic(2z)
+ *               (model file, gelu_new comment; the blog writes the tanh form)
+ *   attention   per head, softmax over t = 0..p of q.k_t / sqrt(headdim), the
+ *               weights then applied to the values v_t (blog Step 6; the
+ *               model file's decode attention reads positions 0..p only)
+ *   linear      y = x W + b with W stored [input][output] (Hugging Face Conv1D,
+ *               as both pages note)
+ *   head        logits_v = wte_v . LN_f(h), no bias (tied to wte)
+ *   greedy      the id of the largest logit, the lowest id among equal ones
+ *   sampling    (blog Step 7; gpt2.s docs "-t") weights exp((l_i - max l)/T),
+ *               the first id whose running sum of weights exceeds u times
+ *               their total, u uniform in [0,1) drawn with xorshift64*
+ *
+ * Keys and values of earlier positions depend only on the tokens up to them,
+ * so each is computed once and kept (the blog's cache); oracle_prefill_last
+ * recomputes them from the token sequence alone, for the cache check.
+ *
+ * Arithmetic: sums run sequentially in ascending index order; the build uses
+ * -O3 -ffp-contract=off without fast-math, so every product is rounded before
+ * it is added.  `real` is float (the precision the model file fixes: every
+ * buffer is f32) or double (a second build that bounds the float build's
+ * drift).  Quantised weights are always formed in float, since they define the
+ * model being run.
+ *
+ * The HIP library shares no code with this file; tests/test_oracle_pins.py
+ * pins it to Hugging Face GPT-2 in float64, numpy, torch, scipy, closed forms,
+ * invariants and brute force.
  */
 #include "gpt2_oracle.h"
 
@@ -30,462 +50,520 @@
 #include <string.h>
 
 #ifdef ORACLE_REAL_IS_DOUBLE
-#define R_EXP exp
-#define R_SQRT sqrt
+#define EXP_R exp
+#define SQRT_R sqrt
 #else
-#define R_EXP expf
-#define R_SQRT sqrtf
+#define EXP_R expf
+#define SQRT_R sqrtf
 #endif
 
 typedef oracle_real real;
 
+/* One transformer block's parameters.  Matrices in the checkpoint's
+ * [input][output] layout, already replaced by their effective (rounded or
+ * quantised) values. */
 typedef struct {
-    real *ln1_w, *ln1_b;
-    real *qkv_w, *qkv_b;  /* [E][3E], [3E] */
-    real *ap_w, *ap_b;    /* [E][E],  [E]  */
-    real *ln2_w, *ln2_b;
-    real *fc_w, *fc_b;    /* [E][F],  [F]  */
-    real *pr_w, *pr_b;    /* [F][E],  [E]  */
-} layer_t;
+    real *gamma1, *beta1;        /* LayerNorm before attention      [E] */
+    real *w_qkv, *b_qkv;         /* query|key|value projection  [E][3E], [3E] */
+    real *w_out, *b_out;         /* attention output projection [E][E],  [E] */
+    real *gamma2, *beta2;        /* LayerNorm before the MLP        [E] */
+    real *w_up, *b_up;           /* MLP expansion               [E][4E], [4E] */
+    real *w_down, *b_down;       /* MLP contraction             [4E][E], [E] */
+} block_params;
 
 struct oracle_model {
-    int L, E, H, D, F, P, V, wdtype, group;
+    int n_layer, d_model, n_heads, d_head, d_ff, n_ctx, n_vocab, wmode, qgroup;
     real eps;
-    real *wte;   /* [V][E] embedding table (always the fp32 values) */
-    real *head;  /* [V][E] output head (fp16-rounded in the fp16 mode) */
-    real *wpe;   /* [P][E] */
-    real *lnf_w, *lnf_b;
-    layer_t *layers;
-    real *kc, *vc; /* [L][P][E] key and value caches (model file layout) */
-    int filled;
-    /* activations of one step (model file buffers) */
-    real *x, *pos_embed, *norm, *qkv, *attn, *mix, *fc, *act, *scores, *logits;
+    real *tok_emb;      /* [V][E] token embedding (always the fp32 values)       */
+    real *unembed;      /* [V][E] output head: tok_emb, fp16-rounded in fp16 mode */
+    real *pos_emb;      /* [P][E] */
+    real *gamma_f, *beta_f;
+    block_params *blocks;
+    real *keys, *values; /* [L][P][E]: key and value of each position, per layer */
+    int n_cached;        /* positions 0..n_cached-1 hold valid keys and values   */
 };
 
 int oracle_real_bytes(void) { return (int)sizeof(real); }
 
-int oracle_n_tensors(int n_layer) { return 2 + 12 * n_layer + 2; }
+/* wte, wpe, 12 tensors per block, ln_f weight and bias. */
+int oracle_n_tensors(int n_layer) { return 4 + 12 * n_layer; }
 
 /* ------------------------------------------------------------------ */
-/* IEEE 754 binary16, round to nearest even, subnormals kept.          */
+/* IEEE 754 binary16 with round-to-nearest-even, subnormals kept       */
+/* (gpt2.s docs: "-h" stores the matrices fp16, products stay fp32).   */
 /* ------------------------------------------------------------------ */
 uint16_t oracle_f32_to_f16(float f)
 {
-    uint32_t x;
-    memcpy(&x, &f, 4);
-    uint32_t sign = (x >> 16) & 0x8000u;
-    uint32_t ex = (x >> 23) & 0xffu;
-    uint32_t man = x & 0x7fffffu;
-    if (ex == 0xffu) {                      /* inf / nan */
-        if (man == 0) return (uint16_t)(sign | 0x7c00u);
-        return (uint16_t)(sign | 0x7e00u | (man >> 13));
+    uint32_t bits;
+    memcpy(&bits, &f, 4);
+    const uint16_t sign = (uint16_t)((bits >> 16) & 0x8000u);
+    const int exp32 = (int)((bits >> 23) & 0xffu);
+    const uint32_t frac = bits & 0x7fffffu;
+    if (exp32 == 0xff) /* infinity keeps its sign; a NaN stays quiet with its top payload bits */
+        return (uint16_t)(sign | 0x7c00u | (frac ? 0x200u | (frac >> 13) : 0u));
+    if (exp32 == 0) return sign; /* zero or fp32 subnormal: below half the smallest fp16 step */
+    /* |f| = sig * 2^(exp32 - 150) with a 24-bit significand sig */
+    const uint32_t sig = frac | 0x800000u;
+    const int e = exp32 - 127;               /* unbiased exponent */
+    uint32_t keep;                           /* significand bits kept, before rounding */
+    int drop;                                /* low bits of sig rounded away */
+    uint32_t base;                           /* exponent field to add */
+    if (e >= -14) {                          /* a normal fp16 if it does not overflow */
+        drop = 13;
+        base = (uint32_t)(e + 15) << 10;
+        keep = (sig >> drop) & 0x3ffu;       /* 10 fraction bits; the hidden bit is in base */
+    } else {                                 /* subnormal fp16: units of 2^-24 */
+        drop = -e - 1;                       /* 14 .. 126 */
+        if (drop > 24) return sign;          /* below 2^-25: rounds to zero */
+        base = 0;
+        keep = sig >> drop;
     }
-    int e16 = (int)ex - 127 + 15;           /* biased binary16 exponent */
-    if (e16 >= 31) return (uint16_t)(sign | 0x7c00u);
-    if (e16 <= 0) {
-        /* result is subnormal or zero: value = (man|hidden) * 2^(ex-150);
-         * in units of 2^-24 that is (man|hidden) >> (126-ex). */
-        if (ex == 0) return (uint16_t)sign;  /* fp32 zero / subnormal: far below 2^-25 */
-        uint32_t mm = man | 0x800000u;
-        int shift = 126 - (int)ex;           /* >= 14 */
-        if (shift >= 25) return (uint16_t)sign; /* < 2^-25 (half of the smallest step): 0 */
-        uint32_t q = mm >> shift;
-        uint32_t rem = mm & ((1u << shift) - 1u);
-        uint32_t half = 1u << (shift - 1);
-        if (rem > half || (rem == half && (q & 1u))) q++;
-        return (uint16_t)(sign | q);
-    }
-    uint32_t q = ((uint32_t)e16 << 10) | (man >> 13);
-    uint32_t rem = man & 0x1fffu;
-    if (rem > 0x1000u || (rem == 0x1000u && (q & 1u))) q++; /* carry may reach inf: correct */
-    return (uint16_t)(sign | q);
+    uint32_t out = base + keep;              /* exponent carries are the right result */
+    const uint32_t rest = sig & ((1u << drop) - 1u), half = 1u << (drop - 1);
+    if (rest > half || (rest == half && (out & 1u))) out += 1; /* may carry into the exponent */
+    if (out >= 0x7c00u) out = 0x7c00u;       /* overflow: infinity */
+    return (uint16_t)(sign | out);
 }
 
 float oracle_f16_to_f32(uint16_t h)
 {
-    uint32_t sign = ((uint32_t)h & 0x8000u) << 16;
-    uint32_t ex = (h >> 10) & 0x1fu;
-    uint32_t man = h & 0x3ffu;
-    float out;
-    if (ex == 0) {
-        out = (float)man * 5.9604644775390625e-08f; /* man * 2^-24, exact */
-        uint32_t b;
-        memcpy(&b, &out, 4);
-        b |= sign;
-        memcpy(&out, &b, 4);
-        return out;
-    }
-    uint32_t b;
-    if (ex == 31) b = sign | 0x7f800000u | (man << 13);
-    else b = sign | ((ex - 15 + 127) << 23) | (man << 13);
-    memcpy(&out, &b, 4);
-    return out;
+    const int e = (h >> 10) & 0x1f;
+    const int m = h & 0x3ff;
+    float mag;
+    if (e == 0x1f) mag = m ? NAN : INFINITY;
+    else if (e == 0) mag = ldexpf((float)m, -24);         /* subnormal: m * 2^-24 */
+    else mag = ldexpf((float)(m | 0x400), e - 25);        /* (1024 + m) * 2^(e-25) */
+    return (h & 0x8000u) ? -mag : mag;
 }
 
 /* ------------------------------------------------------------------ */
-/* Grouped asymmetric int4 (model.fir header: transpose to [out][in],   */
-/* then quantise groups along the input).  Reading of the rule:         */
-/* lo/hi = group min/max, scale = (hi-lo)/15, zero = lo,                */
-/* q = clamp(rint((w-lo)/scale), 0, 15) (q = 0 when scale == 0),        */
-/* dequantised weight = fma(q, scale, zero).                            */
+/* Grouped asymmetric int4 (model file header: the loader transposes   */
+/* each block matrix to [output][input], then quantises groups of      */
+/* inputs of each output row).  Reading of the unstated details: the   */
+/* group's minimum is the zero point and (max - min)/15 the step; a    */
+/* weight takes the nearest of the 16 levels (round half to even,      */
+/* clamped to 0..15; every code 0 when the step is 0); the level is    */
+/* zero + code * step with one rounding.                               */
 /* ------------------------------------------------------------------ */
 void oracle_q4_group(const float *w, int n, uint8_t *q, float *s, float *mn, float *deq)
 {
-    float lo = w[0], hi = w[0];
-    for (int i = 1; i < n; i++) {
-        if (w[i] < lo) lo = w[i];
-        if (w[i] > hi) hi = w[i];
-    }
-    float scale = (hi - lo) / 15.0f;
+    float lo = INFINITY, hi = -INFINITY;
     for (int i = 0; i < n; i++) {
-        int c = 0;
-        if (scale != 0.0f) {
-            float r = rintf((w[i] - lo) / scale);
-            if (r < 0.0f) r = 0.0f;
-            if (r > 15.0f) r = 15.0f;
-            c = (int)r;
-        }
-        q[i] = (uint8_t)c;
-        if (deq) deq[i] = fmaf((float)c, scale, lo);
+        lo = fminf(lo, w[i]);
+        hi = fmaxf(hi, w[i]);
     }
-    *s = scale;
+    const float step = (hi - lo) / 15.0f;
+    for (int i = 0; i < n; i++) {
+        float code = 0.0f;
+        if (step != 0.0f) code = fminf(fmaxf(rintf((w[i] - lo) / step), 0.0f), 15.0f);
+        q[i] = (uint8_t)code;
+        if (deq) deq[i] = fmaf(code, step, lo);
+    }
+    *s = step;
     *mn = lo;
 }
 
 /* ------------------------------------------------------------------ */
-/* Micro-kernels                                                       */
+/* The pieces of the network, each its defining formula               */
 /* ------------------------------------------------------------------ */
-void oracle_layernorm(const real *x, const real *g, const real *b, int n, real eps, real *y)
+void oracle_layernorm(const real *x, const real *gamma, const real *beta, int n, real eps, real *y)
 {
-    const real inv_n = (real)(1.0 / (double)n);
-    real mean = 0;
-    for (int i = 0; i < n; i++) mean = mean + x[i];
-    mean = mean * inv_n;
-    real var = 0;
-    for (int i = 0; i < n; i++) {
-        real d = x[i] - mean;
-        var = var + d * d;
-    }
-    var = var * inv_n;
-    var = var + eps;
-    real r = (real)1 / R_SQRT(var);
-    for (int i = 0; i < n; i++) {
-        real t = x[i] - mean;
-        t = t * r;
-        t = t * g[i];
-        y[i] = t + b[i];
-    }
+    real sum = 0;
+    for (int i = 0; i < n; i++) sum += x[i];
+    const real mu = sum / (real)n;
+    real sq = 0;
+    for (int i = 0; i < n; i++) sq += (x[i] - mu) * (x[i] - mu);
+    const real sigma = SQRT_R(sq / (real)n + eps);
+    for (int i = 0; i < n; i++) y[i] = gamma[i] * ((x[i] - mu) / sigma) + beta[i];
 }
 
 real oracle_gelu_new(real x)
 {
-    const real c3 = (real)0.044715;
-    const real k0 = (real)(2.0 * 0.79788456080286535587989211986876); /* 2*sqrt(2/pi) */
-    real t = x * x;
-    t = t * x;
-    t = t * c3;
-    t = t + x;
-    t = t * k0;
-    t = (real)1 / ((real)1 + R_EXP(-t)); /* sigmoid */
-    return x * t;
+    const real root_2_over_pi = (real)0.79788456080286535588; /* sqrt(2/pi) */
+    const real z = root_2_over_pi * (x + (real)0.044715 * (x * x * x));
+    return x / ((real)1 + EXP_R(-(real)2 * z)); /* x * logistic(2z) */
 }
 
 void oracle_linear_conv1d(const real *x, const real *W, const real *b, int K, int N, real *y)
 {
-    /* axpy order: each y[o] still accumulates its products in ascending i */
+    /* y_o = sum_i x_i W[i][o] (+ b_o): the rows of W are visited in order, so
+     * each y_o still adds its products in ascending i */
     for (int o = 0; o < N; o++) y[o] = 0;
-    for (int i = 0; i < K; i++) {
-        const real xi = x[i];
-        const real *row = W + (size_t)i * N;
-        for (int o = 0; o < N; o++) y[o] = y[o] + xi * row[o];
-    }
+    for (int i = 0; i < K; i++)
+        for (int o = 0; o < N; o++) y[o] += x[i] * W[(size_t)i * N + o];
     if (b)
-        for (int o = 0; o < N; o++) y[o] = y[o] + b[o];
+        for (int o = 0; o < N; o++) y[o] += b[o];
 }
 
-void oracle_attn_head(const real *q, const real *Kc, const real *Vc, int pos, int stride,
-                      int D, real *probs, real *out)
+void oracle_attn_head(const real *q, const real *Kc, const real *Vc, int pos, int stride, int D,
+                      real *probs, real *out)
 {
-    const real scale = (real)(1.0 / sqrt((double)D));
-    real *s = (real *)malloc(sizeof(real) * (size_t)(pos + 1));
-    real m = (real)-3e38;
-    for (int t = 0; t <= pos; t++) {
-        real acc = 0;
-        const real *k = Kc + (size_t)t * stride;
-        for (int d = 0; d < D; d++) acc = acc + q[d] * k[d];
-        acc = acc * scale;
-        s[t] = acc;
-        if (m < acc) m = acc;
+    const int n = pos + 1; /* positions 0..pos, nothing later */
+    real *w = n > 0 ? (real *)malloc(sizeof(real) * (size_t)n) : NULL;
+    if (!w) {
+        for (int d = 0; d < D; d++) out[d] = (real)NAN; /* no positions (or no memory): nothing to attend */
+        return;
     }
-    real sum = 0;
-    for (int t = 0; t <= pos; t++) {
-        s[t] = R_EXP(s[t] - m);
-        sum = sum + s[t];
+    const real root_d = (real)sqrt((double)D);
+    for (int t = 0; t < n; t++) {
+        real dot = 0;
+        for (int d = 0; d < D; d++) dot += q[d] * Kc[(size_t)t * stride + d];
+        w[t] = dot / root_d;
     }
-    for (int t = 0; t <= pos; t++) s[t] = s[t] / sum;
+    real top = w[0];
+    for (int t = 1; t < n; t++) top = w[t] > top ? w[t] : top;
+    real z = 0;
+    for (int t = 0; t < n; t++) {
+        w[t] = EXP_R(w[t] - top);
+        z += w[t];
+    }
+    for (int t = 0; t < n; t++) w[t] /= z; /* softmax weights */
     for (int d = 0; d < D; d++) {
         real acc = 0;
-        for (int t = 0; t <= pos; t++) acc = acc + s[t] * Vc[(size_t)t * stride + d];
+        for (int t = 0; t < n; t++) acc += w[t] * Vc[(size_t)t * stride + d];
         out[d] = acc;
     }
-    if (probs)
-        for (int t = 0; t <= pos; t++) probs[t] = s[t];
-    free(s);
+    if (probs) memcpy(probs, w, sizeof(real) * (size_t)n);
+    free(w);
 }
 
-static int argmax_lowest(const real *v, int n)
+int oracle_argmax(const real *v, int n)
 {
     int best = 0;
     for (int i = 1; i < n; i++)
-        if (v[i] > v[best]) best = i;
+        if (v[i] > v[best]) best = i; /* strictly larger: ties keep the lower id */
     return best;
+}
+
+/* xorshift64* (S. Vigna, "An experimental exploration of Marsaglia's xorshift
+ * generators, scrambled", ACM TOMS 42(4), 2016): the xorshift state update
+ * with shift triple (12, 25, 27), output scrambled by the multiplier
+ * 2685821657736338717. */
+uint64_t oracle_xorshift64s(uint64_t *state)
+{
+    uint64_t s = *state;
+    s ^= s >> 12;
+    s ^= s << 25;
+    s ^= s >> 27;
+    *state = s;
+    return s * 2685821657736338717ull;
+}
+
+/* A uniform number in [0,1) from one draw: its top 24 bits times 2^-24
+ * (exact in float). */
+float oracle_uniform(uint64_t *state)
+{
+    return (float)(oracle_xorshift64s(state) >> 40) * 0x1p-24f;
+}
+
+int oracle_sample(const real *logits, int n, real temperature, real u)
+{
+    if (n < 1 || !(temperature >= 0) || !(u >= 0 && u < 1)) return -1;
+    const int top = oracle_argmax(logits, n);
+    if (temperature == 0) return top; /* greedy */
+    real *w = (real *)malloc(sizeof(real) * (size_t)n);
+    if (!w) return -1;
+    real total = 0;
+    for (int i = 0; i < n; i++) {
+        w[i] = EXP_R((logits[i] - logits[top]) / temperature);
+        total += w[i];
+    }
+    const real target = u * total;
+    real run = 0;
+    int pick = -1, last = top;
+    for (int i = 0; i < n && pick < 0; i++) {
+        if (w[i] > 0) last = i;
+        run += w[i];
+        if (run > target) pick = i;
+    }
+    /* rounding can leave the running total a hair under u * total */
+    if (pick < 0) {
+        for (int i = n - 1; i >= 0; i--)
+            if (w[i] > 0) { last = i; break; }
+        pick = last;
+    }
+    free(w);
+    return pick;
 }
 
 /* ------------------------------------------------------------------ */
 /* Model construction                                                  */
 /* ------------------------------------------------------------------ */
-static real *alloc_real(size_t n)
-{
-    return (real *)calloc(n ? n : 1, sizeof(real));
-}
+static real *zeros(size_t n) { return (real *)calloc(n ? n : 1, sizeof(real)); }
 
-static real *copy_real(const float *src, size_t n)
+static real *widen(const float *src, size_t n)
 {
-    real *d = alloc_real(n);
-    if (!d) return NULL;
-    for (size_t i = 0; i < n; i++) d[i] = (real)src[i];
+    real *d = zeros(n);
+    if (d)
+        for (size_t i = 0; i < n; i++) d[i] = (real)src[i];
     return d;
 }
 
-/* Effective value of a block matrix W[K][N] (Conv1D) under the weight mode,
- * returned in the same [K][N] layout. */
-static real *quantised_block(const float *W, int K, int N, int wdtype, int group)
+/* The weights a block matrix W[K][N] ([input][output]) stands for in the
+ * chosen storage, still as [K][N]: fp32 as is; fp16 each weight rounded to
+ * binary16; int4 each output's column cut into groups of `group` consecutive
+ * inputs, each group quantised on its own. */
+static real *effective_matrix(const float *W, int K, int N, int mode, int group)
 {
-    real *d = alloc_real((size_t)K * N);
-    if (!d) return NULL;
-    if (wdtype == ORACLE_W_FP32) {
-        for (size_t i = 0; i < (size_t)K * N; i++) d[i] = (real)W[i];
-    } else if (wdtype == ORACLE_W_FP16) {
-        for (size_t i = 0; i < (size_t)K * N; i++) d[i] = (real)oracle_f16_to_f32(oracle_f32_to_f16(W[i]));
-    } else {
-        /* transpose to [N][K] rows, quantise groups of `group` inputs, write back */
-        float *g = (float *)malloc(sizeof(float) * (size_t)group);
-        float *dq = (float *)malloc(sizeof(float) * (size_t)group);
-        uint8_t *qc = (uint8_t *)malloc((size_t)group);
-        if (!g || !dq || !qc) { free(g); free(dq); free(qc); free(d); return NULL; }
-        for (int o = 0; o < N; o++) {
-            for (int k0 = 0; k0 < K; k0 += group) {
-                for (int j = 0; j < group; j++) g[j] = W[(size_t)(k0 + j) * N + o];
-                float s, mn;
-                oracle_q4_group(g, group, qc, &s, &mn, dq);
-                for (int j = 0; j < group; j++) d[(size_t)(k0 + j) * N + o] = (real)dq[j];
-            }
-        }
-        free(g); free(dq); free(qc);
+    real *out = zeros((size_t)K * N);
+    if (!out) return NULL;
+    if (mode != ORACLE_W_INT4) {
+        for (size_t i = 0; i < (size_t)K * N; i++)
+            out[i] = mode == ORACLE_W_FP16 ? (real)oracle_f16_to_f32(oracle_f32_to_f16(W[i])) : (real)W[i];
+        return out;
     }
-    return d;
+    float *col = (float *)malloc(sizeof(float) * (size_t)group * 2);
+    uint8_t *codes = (uint8_t *)malloc((size_t)group);
+    if (!col || !codes) {
+        free(col); free(codes); free(out);
+        return NULL;
+    }
+    float *deq = col + group;
+    for (int o = 0; o < N; o++)
+        for (int k0 = 0; k0 < K; k0 += group) {
+            float step, zero;
+            for (int j = 0; j < group; j++) col[j] = W[(size_t)(k0 + j) * N + o];
+            oracle_q4_group(col, group, codes, &step, &zero, deq);
+            for (int j = 0; j < group; j++) out[(size_t)(k0 + j) * N + o] = (real)deq[j];
+        }
+    free(col);
+    free(codes);
+    return out;
 }
 
 void oracle_free(oracle_model *m)
 {
     if (!m) return;
-    free(m->wte); free(m->head); free(m->wpe); free(m->lnf_w); free(m->lnf_b);
-    if (m->layers) {
-        for (int l = 0; l < m->L; l++) {
-            layer_t *ly = &m->layers[l];
-            free(ly->ln1_w); free(ly->ln1_b); free(ly->qkv_w); free(ly->qkv_b);
-            free(ly->ap_w); free(ly->ap_b); free(ly->ln2_w); free(ly->ln2_b);
-            free(ly->fc_w); free(ly->fc_b); free(ly->pr_w); free(ly->pr_b);
+    if (m->blocks)
+        for (int l = 0; l < m->n_layer; l++) {
+            block_params *b = &m->blocks[l];
+            real *all[] = {b->gamma1, b->beta1, b->w_qkv, b->b_qkv, b->w_out, b->b_out,
+                           b->gamma2, b->beta2, b->w_up, b->b_up, b->w_down, b->b_down};
+            for (size_t i = 0; i < sizeof all / sizeof all[0]; i++) free(all[i]);
         }
-        free(m->layers);
-    }
-    free(m->kc); free(m->vc);
-    free(m->x); free(m->pos_embed); free(m->norm); free(m->qkv); free(m->attn);
-    free(m->mix); free(m->fc); free(m->act); free(m->scores); free(m->logits);
+    free(m->blocks);
+    free(m->tok_emb); free(m->unembed); free(m->pos_emb); free(m->gamma_f); free(m->beta_f);
+    free(m->keys); free(m->values);
     free(m);
 }
 
 oracle_model *oracle_new(const int *shape, float ln_eps, int wdtype, int q4_group,
                          const float *const *t)
 {
-    int L = shape[0], E = shape[1], H = shape[2], P = shape[3], V = shape[4];
-    if (L <= 0 || E <= 0 || H <= 0 || P <= 0 || V <= 0 || E % H != 0) return NULL;
-    if (wdtype < 0 || wdtype > 2) return NULL;
-    int F = 4 * E;
-    if (wdtype == ORACLE_W_INT4 && (q4_group <= 0 || E % q4_group != 0 || F % q4_group != 0))
-        return NULL;
-    oracle_model *m = (oracle_model *)calloc(1, sizeof(oracle_model));
+    const int L = shape[0], E = shape[1], H = shape[2], P = shape[3], V = shape[4];
+    if (L < 1 || E < 1 || H < 1 || P < 1 || V < 1 || E % H) return NULL;
+    if (wdtype < ORACLE_W_FP32 || wdtype > ORACLE_W_INT4) return NULL;
+    if (wdtype == ORACLE_W_INT4 && (q4_group < 1 || E % q4_group)) return NULL; /* 4E then divides too */
+    oracle_model *m = (oracle_model *)calloc(1, sizeof *m);
     if (!m) return NULL;
-    m->L = L; m->E = E; m->H = H; m->D = E / H; m->F = F; m->P = P; m->V = V;
-    m->wdtype = wdtype; m->group = q4_group; m->eps = (real)ln_eps;
-    int ok = 1;
-    m->wte = copy_real(t[0], (size_t)V * E);
-    if (wdtype == ORACLE_W_FP16) {
-        m->head = alloc_real((size_t)V * E);
-        if (m->head)
-            for (size_t i = 0; i < (size_t)V * E; i++)
-                m->head[i] = (real)oracle_f16_to_f32(oracle_f32_to_f16(t[0][i]));
-    } else {
-        m->head = copy_real(t[0], (size_t)V * E);
-    }
-    m->wpe = copy_real(t[1], (size_t)P * E);
-    m->layers = (layer_t *)calloc((size_t)L, sizeof(layer_t));
-    ok = m->wte && m->head && m->wpe && m->layers;
+    m->n_layer = L; m->d_model = E; m->n_heads = H; m->d_head = E / H; m->d_ff = 4 * E;
+    m->n_ctx = P; m->n_vocab = V; m->wmode = wdtype; m->qgroup = q4_group; m->eps = (real)ln_eps;
+    const int F = m->d_ff;
+    /* the flat list: wte, wpe, then per block in checkpoint order, then ln_f */
+    m->tok_emb = widen(t[0], (size_t)V * E);
+    m->unembed = zeros((size_t)V * E);
+    if (m->unembed)
+        for (size_t i = 0; i < (size_t)V * E; i++)
+            m->unembed[i] = wdtype == ORACLE_W_FP16 ? (real)oracle_f16_to_f32(oracle_f32_to_f16(t[0][i]))
+                                                    : (real)t[0][i];
+    m->pos_emb = widen(t[1], (size_t)P * E);
+    m->blocks = (block_params *)calloc((size_t)L, sizeof(block_params));
+    int ok = m->tok_emb && m->unembed && m->pos_emb && m->blocks;
     for (int l = 0; ok && l < L; l++) {
         const float *const *p = t + 2 + 12 * l;
-        layer_t *ly = &m->layers[l];
-        ly->ln1_w = copy_real(p[0], E);
-        ly->ln1_b = copy_real(p[1], E);
-        ly->qkv_w = quantised_block(p[2], E, 3 * E, wdtype, q4_group);
-        ly->qkv_b = copy_real(p[3], 3 * E);
-        ly->ap_w = quantised_block(p[4], E, E, wdtype, q4_group);
-        ly->ap_b = copy_real(p[5], E);
-        ly->ln2_w = copy_real(p[6], E);
-        ly->ln2_b = copy_real(p[7], E);
-        ly->fc_w = quantised_block(p[8], E, F, wdtype, q4_group);
-        ly->fc_b = copy_real(p[9], F);
-        ly->pr_w = quantised_block(p[10], F, E, wdtype, q4_group);
-        ly->pr_b = copy_real(p[11], E);
-        ok = ly->ln1_w && ly->ln1_b && ly->qkv_w && ly->qkv_b && ly->ap_w && ly->ap_b &&
-             ly->ln2_w && ly->ln2_b && ly->fc_w && ly->fc_b && ly->pr_w && ly->pr_b;
+        block_params *b = &m->blocks[l];
+        b->gamma1 = widen(p[0], E);
+        b->beta1 = widen(p[1], E);
+        b->w_qkv = effective_matrix(p[2], E, 3 * E, wdtype, q4_group);
+        b->b_qkv = widen(p[3], 3 * (size_t)E);
+        b->w_out = effective_matrix(p[4], E, E, wdtype, q4_group);
+        b->b_out = widen(p[5], E);
+        b->gamma2 = widen(p[6], E);
+        b->beta2 = widen(p[7], E);
+        b->w_up = effective_matrix(p[8], E, F, wdtype, q4_group);
+        b->b_up = widen(p[9], F);
+        b->w_down = effective_matrix(p[10], F, E, wdtype, q4_group);
+        b->b_down = widen(p[11], E);
+        ok = b->gamma1 && b->beta1 && b->w_qkv && b->b_qkv && b->w_out && b->b_out && b->gamma2 &&
+             b->beta2 && b->w_up && b->b_up && b->w_down && b->b_down;
     }
     if (ok) {
-        const float *const *p = t + 2 + 12 * L;
-        m->lnf_w = copy_real(p[0], E);
-        m->lnf_b = copy_real(p[1], E);
-        m->kc = alloc_real((size_t)L * P * E);
-        m->vc = alloc_real((size_t)L * P * E);
-        m->x = alloc_real(E); m->pos_embed = alloc_real(E); m->norm = alloc_real(E);
-        m->qkv = alloc_real(3 * (size_t)E); m->attn = alloc_real(E); m->mix = alloc_real(E);
-        m->fc = alloc_real(F); m->act = alloc_real(F);
-        m->scores = alloc_real((size_t)H * P); m->logits = alloc_real(V);
-        ok = m->lnf_w && m->lnf_b && m->kc && m->vc && m->x && m->pos_embed && m->norm &&
-             m->qkv && m->attn && m->mix && m->fc && m->act && m->scores && m->logits;
+        m->gamma_f = widen(t[2 + 12 * L], E);
+        m->beta_f = widen(t[3 + 12 * L], E);
+        m->keys = zeros((size_t)L * P * E);
+        m->values = zeros((size_t)L * P * E);
+        ok = m->gamma_f && m->beta_f && m->keys && m->values;
     }
-    if (!ok) { oracle_free(m); return NULL; }
+    if (!ok) {
+        oracle_free(m);
+        return NULL;
+    }
     return m;
 }
 
-void oracle_reset(oracle_model *m) { m->filled = 0; }
+void oracle_reset(oracle_model *m) { m->n_cached = 0; }
 
 void oracle_poison_cache_after(oracle_model *m, int position, float value)
 {
-    for (int l = 0; l < m->L; l++)
-        for (int t = position + 1; t < m->P; t++)
-            for (int i = 0; i < m->E; i++) {
-                size_t o = ((size_t)l * m->P + t) * m->E + i;
-                m->kc[o] = (real)value;
-                m->vc[o] = (real)value;
+    const size_t E = (size_t)m->d_model;
+    for (int l = 0; l < m->n_layer; l++)
+        for (int t = position + 1; t < m->n_ctx; t++)
+            for (size_t i = 0; i < E; i++) {
+                m->keys[((size_t)l * m->n_ctx + t) * E + i] = (real)value;
+                m->values[((size_t)l * m->n_ctx + t) * E + i] = (real)value;
             }
 }
 
-/* The per-layer node sequence of the model file, for one position whose
- * residual stream is in x; kc/vc are this layer's caches ([P][E]). */
-static void layer_forward(oracle_model *m, const layer_t *ly, real *kc, real *vc, int pos,
-                          real *x)
+/* ------------------------------------------------------------------ */
+/* The forward pass                                                    */
+/* ------------------------------------------------------------------ */
+
+/* Scratch vectors of one position's pass through a block. */
+typedef struct {
+    real *a;     /* normalised input of a sub-layer     [E]  */
+    real *qkv;   /* query | key | value                 [3E] */
+    real *ctx;   /* attention output, heads side by side [E]  */
+    real *proj;  /* a sub-layer's output before the add [E]  */
+    real *up;    /* MLP hidden activations              [4E] */
+} work_vecs;
+
+static int work_alloc(work_vecs *w, int E)
 {
-    const int E = m->E, D = m->D, F = m->F;
-    oracle_layernorm(x, ly->ln1_w, ly->ln1_b, E, m->eps, m->norm);          /* ln1 */
-    oracle_linear_conv1d(m->norm, ly->qkv_w, NULL, E, 3 * E, m->qkv);        /* qkv_linear */
-    for (int o = 0; o < 3 * E; o++) m->qkv[o] = m->qkv[o] + ly->qkv_b[o];  /* qkv_bias */
-    /* attention: append this position's K/V, then one head at a time */
-    for (int i = 0; i < E; i++) {
-        kc[(size_t)pos * E + i] = m->qkv[E + i];
-        vc[(size_t)pos * E + i] = m->qkv[2 * E + i];
-    }
-    for (int h = 0; h < m->H; h++)
-        oracle_attn_head(m->qkv + h * D, kc + h * D, vc + h * D, pos, E, D,
-                         m->scores + (size_t)h * m->P, m->attn + h * D);
-    oracle_linear_conv1d(m->attn, ly->ap_w, NULL, E, E, m->mix);             /* attention_linear */
-    for (int o = 0; o < E; o++) m->mix[o] = m->mix[o] + ly->ap_b[o];        /* attention_bias */
-    for (int o = 0; o < E; o++) x[o] = x[o] + m->mix[o];                    /* attention_residual */
-    oracle_layernorm(x, ly->ln2_w, ly->ln2_b, E, m->eps, m->norm);          /* ln2 */
-    oracle_linear_conv1d(m->norm, ly->fc_w, NULL, E, F, m->fc);              /* fc_linear */
-    for (int o = 0; o < F; o++) m->fc[o] = m->fc[o] + ly->fc_b[o];          /* fc_bias */
-    for (int o = 0; o < F; o++) m->act[o] = oracle_gelu_new(m->fc[o]);      /* gelu */
-    oracle_linear_conv1d(m->act, ly->pr_w, NULL, F, E, m->mix);              /* proj_linear */
-    for (int o = 0; o < E; o++) m->mix[o] = m->mix[o] + ly->pr_b[o];        /* proj_bias */
-    for (int o = 0; o < E; o++) x[o] = x[o] + m->mix[o];                    /* mlp_residual */
+    w->a = zeros(E); w->qkv = zeros(3 * (size_t)E); w->ctx = zeros(E); w->proj = zeros(E);
+    w->up = zeros(4 * (size_t)E);
+    return w->a && w->qkv && w->ctx && w->proj && w->up;
 }
 
-static void head_forward(oracle_model *m, const real *x, real *logits)
+static void work_free(work_vecs *w)
 {
-    const int E = m->E;
-    oracle_layernorm(x, m->lnf_w, m->lnf_b, E, m->eps, m->norm);            /* final_norm */
-    for (int v = 0; v < m->V; v++) {                                         /* head (linear_t) */
-        const real *row = m->head + (size_t)v * E;
-        real acc = 0;
-        for (int i = 0; i < E; i++) acc = acc + row[i] * m->norm[i];
-        logits[v] = acc;
+    free(w->a); free(w->qkv); free(w->ctx); free(w->proj); free(w->up);
+}
+
+/* h <- h + Attn(LN_1(h)) for one position t.  The query is this position's;
+ * keys/values of positions 0..t are rows of `kv_k` / `kv_v`, `kv_stride`
+ * apart, and this position's own key and value are written to row t first. */
+static void attention_sublayer(const oracle_model *m, const block_params *b, real *h, int t, real *kv_k,
+                               real *kv_v, int kv_stride, work_vecs *w)
+{
+    const int E = m->d_model, Dh = m->d_head;
+    oracle_layernorm(h, b->gamma1, b->beta1, E, m->eps, w->a);
+    oracle_linear_conv1d(w->a, b->w_qkv, b->b_qkv, E, 3 * E, w->qkv);
+    memcpy(kv_k + (size_t)t * kv_stride, w->qkv + E, sizeof(real) * (size_t)E);
+    memcpy(kv_v + (size_t)t * kv_stride, w->qkv + 2 * E, sizeof(real) * (size_t)E);
+    for (int hd = 0; hd < m->n_heads; hd++)
+        oracle_attn_head(w->qkv + hd * Dh, kv_k + hd * Dh, kv_v + hd * Dh, t, kv_stride, Dh, NULL,
+                         w->ctx + hd * Dh);
+    oracle_linear_conv1d(w->ctx, b->w_out, b->b_out, E, E, w->proj);
+    for (int i = 0; i < E; i++) h[i] += w->proj[i];
+}
+
+/* h <- h + MLP(LN_2(h)), MLP(a) = gelu_new(a W_up + b_up) W_down + b_down. */
+static void mlp_sublayer(const oracle_model *m, const block_params *b, real *h, work_vecs *w)
+{
+    const int E = m->d_model, F = m->d_ff;
+    oracle_layernorm(h, b->gamma2, b->beta2, E, m->eps, w->a);
+    oracle_linear_conv1d(w->a, b->w_up, b->b_up, E, F, w->up);
+    for (int i = 0; i < F; i++) w->up[i] = oracle_gelu_new(w->up[i]);
+    oracle_linear_conv1d(w->up, b->w_down, b->b_down, F, E, w->proj);
+    for (int i = 0; i < E; i++) h[i] += w->proj[i];
+}
+
+/* logits_v = unembed_v . LN_f(h) */
+static void output_head(const oracle_model *m, const real *h, real *a, real *logits)
+{
+    const int E = m->d_model;
+    oracle_layernorm(h, m->gamma_f, m->beta_f, E, m->eps, a);
+    for (int v = 0; v < m->n_vocab; v++) {
+        real dot = 0;
+        for (int i = 0; i < E; i++) dot += m->unembed[(size_t)v * E + i] * a[i];
+        logits[v] = dot;
     }
+}
+
+static void embed(const oracle_model *m, int token, int position, real *h)
+{
+    const int E = m->d_model;
+    for (int i = 0; i < E; i++)
+        h[i] = m->tok_emb[(size_t)token * E + i] + m->pos_emb[(size_t)position * E + i];
 }
 
 int oracle_step(oracle_model *m, int token, int position, real *logits_out)
 {
-    if (!m || token < 0 || token >= m->V || position < 0 || position >= m->P ||
-        position > m->filled)
+    if (!m || token < 0 || token >= m->n_vocab || position < 0 || position >= m->n_ctx ||
+        position > m->n_cached)
         return -1;
-    const int E = m->E;
-    for (int i = 0; i < E; i++) {                                            /* token, positional */
-        m->x[i] = m->wte[(size_t)token * E + i];
-        m->pos_embed[i] = m->wpe[(size_t)position * E + i];
+    const int E = m->d_model;
+    real *h = zeros(E), *logits = zeros(m->n_vocab);
+    work_vecs w;
+    int ok = work_alloc(&w, E) && h && logits;
+    int id = -1;
+    if (ok) {
+        embed(m, token, position, h);
+        for (int l = 0; l < m->n_layer; l++) {
+            const size_t layer_rows = (size_t)l * m->n_ctx * E;
+            attention_sublayer(m, &m->blocks[l], h, position, m->keys + layer_rows, m->values + layer_rows, E,
+                               &w);
+            mlp_sublayer(m, &m->blocks[l], h, &w);
+        }
+        output_head(m, h, w.a, logits);
+        /* a position at or below the cached ones rewinds: its rows were rewritten */
+        m->n_cached = position + 1;
+        if (logits_out) memcpy(logits_out, logits, sizeof(real) * (size_t)m->n_vocab);
+        id = oracle_argmax(logits, m->n_vocab);
     }
-    for (int i = 0; i < E; i++) m->x[i] = m->x[i] + m->pos_embed[i];         /* embeddings */
-    for (int l = 0; l < m->L; l++)
-        layer_forward(m, &m->layers[l], m->kc + (size_t)l * m->P * E,
-                      m->vc + (size_t)l * m->P * E, position, m->x);
-    head_forward(m, m->x, m->logits);
-    m->filled = position + 1;
-    if (logits_out)
-        for (int v = 0; v < m->V; v++) logits_out[v] = m->logits[v];
-    return argmax_lowest(m->logits, m->V);
+    work_free(&w);
+    free(h);
+    free(logits);
+    return id;
 }
 
 int oracle_prefill_last(oracle_model *m, const int *toks, int n, real *logits_out)
 {
-    if (!m || n <= 0 || n > m->P) return -1;
+    if (!m || n < 1 || n > m->n_ctx) return -1;
     for (int t = 0; t < n; t++)
-        if (toks[t] < 0 || toks[t] >= m->V) return -1;
-    const int E = m->E;
-    /* private caches and residual streams: one row per position */
-    real *X = alloc_real((size_t)n * E);
-    real *kc = alloc_real((size_t)n * E);
-    real *vc = alloc_real((size_t)n * E);
-    real *logits = alloc_real(m->V);
-    if (!X || !kc || !vc || !logits) { free(X); free(kc); free(vc); free(logits); return -1; }
-    for (int t = 0; t < n; t++)
-        for (int i = 0; i < E; i++)
-            X[(size_t)t * E + i] = m->wte[(size_t)toks[t] * E + i] + m->wpe[(size_t)t * E + i];
-    /* layer by layer over the whole sequence; the K/V rows of every position
-     * are rebuilt from the sequence itself in each layer */
-    for (int l = 0; l < m->L; l++)
-        for (int t = 0; t < n; t++)
-            layer_forward(m, &m->layers[l], kc, vc, t, X + (size_t)t * E);
-    head_forward(m, X + (size_t)(n - 1) * E, logits);
-    int am = argmax_lowest(logits, m->V);
-    if (logits_out)
-        for (int v = 0; v < m->V; v++) logits_out[v] = logits[v];
-    free(X); free(kc); free(vc); free(logits);
-    return am;
+        if (toks[t] < 0 || toks[t] >= m->n_vocab) return -1;
+    const int E = m->d_model;
+    /* every position's hidden state, and one block's keys and values rebuilt
+     * from the sequence itself (nothing is taken from the decode cache) */
+    real *H = zeros((size_t)n * E), *K = zeros((size_t)n * E), *Vv = zeros((size_t)n * E);
+    real *logits = zeros(m->n_vocab);
+    work_vecs w;
+    int ok = work_alloc(&w, E) && H && K && Vv && logits;
+    int id = -1;
+    if (ok) {
+        for (int t = 0; t < n; t++) embed(m, toks[t], t, H + (size_t)t * E);
+        for (int l = 0; l < m->n_layer; l++) {
+            for (int t = 0; t < n; t++) attention_sublayer(m, &m->blocks[l], H + (size_t)t * E, t, K, Vv, E, &w);
+            for (int t = 0; t < n; t++) mlp_sublayer(m, &m->blocks[l], H + (size_t)t * E, &w);
+        }
+        output_head(m, H + (size_t)(n - 1) * E, w.a, logits);
+        if (logits_out) memcpy(logits_out, logits, sizeof(real) * (size_t)m->n_vocab);
+        id = oracle_argmax(logits, m->n_vocab);
+    }
+    work_free(&w);
+    free(H); free(K); free(Vv); free(logits);
+    return id;
 }
 
 long oracle_get_weight(const oracle_model *m, int layer, int which, float *out)
 {
+    const int E = m->d_model, F = m->d_ff;
+    if (which == 4) {
+        for (size_t i = 0; i < (size_t)m->n_vocab * E; i++) out[i] = (float)m->unembed[i];
+        return (long)m->n_vocab * E;
+    }
+    if (layer < 0 || layer >= m->n_layer) return -1;
+    const block_params *b = &m->blocks[layer];
     const real *W;
     int K, N;
-    if (which == 4) {
-        for (size_t i = 0; i < (size_t)m->V * m->E; i++) out[i] = (float)m->head[i];
-        return (long)m->V * m->E;
-    }
-    if (layer < 0 || layer >= m->L) return -1;
-    const layer_t *ly = &m->layers[layer];
     switch (which) {
-    case 0: W = ly->qkv_w; K = m->E; N = 3 * m->E; break;
-    case 1: W = ly->ap_w; K = m->E; N = m->E; break;
-    case 2: W = ly->fc_w; K = m->E; N = m->F; break;
-    case 3: W = ly->pr_w; K = m->F; N = m->E; break;
+    case 0: W = b->w_qkv; K = E; N = 3 * E; break;
+    case 1: W = b->w_out; K = E; N = E; break;
+    case 2: W = b->w_up; K = E; N = F; break;
+    case 3: W = b->w_down; K = F; N = E; break;
     default: return -1;
     }
+    /* returned output-major: out[o][k] = W[k][o] */
     for (int o = 0; o < N; o++)
         for (int k = 0; k < K; k++) out[(size_t)o * K + k] = (float)W[(size_t)k * N + o];
     return (long)N * K;

@@ -49,6 +49,14 @@ class OracleLib:
         u8p = np.ctypeslib.ndpointer(np.uint8, flags="C_CONTIGUOUS")
         L.oracle_q4_group.argtypes = [f32p, C.c_int, u8p, C.POINTER(C.c_float),
                                       C.POINTER(C.c_float), f32p]
+        L.oracle_argmax.argtypes = [rp, C.c_int]
+        L.oracle_argmax.restype = C.c_int
+        L.oracle_xorshift64s.argtypes = [C.POINTER(C.c_uint64)]
+        L.oracle_xorshift64s.restype = C.c_uint64
+        L.oracle_uniform.argtypes = [C.POINTER(C.c_uint64)]
+        L.oracle_uniform.restype = C.c_float
+        L.oracle_sample.argtypes = [rp, C.c_int, self._rt(), self._rt()]
+        L.oracle_sample.restype = C.c_int
 
     def _rt(self):
         return C.c_float if self.kind == "f32" else C.c_double
@@ -103,6 +111,24 @@ class OracleLib:
         mn = C.c_float()
         self.lib.oracle_q4_group(w, w.size, q, C.byref(s), C.byref(mn), deq)
         return q, np.float32(s.value), np.float32(mn.value), deq
+
+    def argmax(self, v):
+        v = np.ascontiguousarray(v, self.real)
+        return self.lib.oracle_argmax(v, v.size)
+
+    def xorshift64s(self, seed, n):
+        """n successive xorshift64* outputs from state `seed`; returns (outputs, state)."""
+        st = C.c_uint64(seed)
+        out = np.array([self.lib.oracle_xorshift64s(C.byref(st)) for _ in range(n)], np.uint64)
+        return out, st.value
+
+    def uniforms(self, seed, n):
+        st = C.c_uint64(seed)
+        return np.array([self.lib.oracle_uniform(C.byref(st)) for _ in range(n)], np.float32)
+
+    def sample(self, logits, temperature, u):
+        logits = np.ascontiguousarray(logits, self.real)
+        return self.lib.oracle_sample(logits, logits.size, temperature, u)
 
 
 def load_lib(kind: str = "f32") -> OracleLib:

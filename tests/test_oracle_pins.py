@@ -9,6 +9,7 @@ import math
 import numpy as np
 import pytest
 import scipy.special
+import scipy.stats
 import torch
 
 import synth
@@ -182,21 +183,32 @@ def test_float_build_drift_small_shape():
 
 
 def test_parameter_count_and_sizes():
-    """148 tensors (blog Step 1), 124M parameters (about 498 MB in fp32, blog
-    Step 4), block matrices 340 MB and 75 MB KV cache (gpt2.s README)."""
+    """The sizes the pages print (tests/golden/page_figures.json, each with its
+    citation) against the tensor list both sides load: 148 tensors, about
+    500 MB of fp32 weights read per token, 340 MB of block matrices, a 154 MB
+    head padded to 50,304 rows, a 75 MB KV cache, 1,024 positions, 50,257 ids."""
+    import json
+    import os
     from oracle import load_lib
+    with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "page_figures.json")) as f:
+        fig = {k: v["value"] for k, v in json.load(f).items() if not k.startswith("_")}
     cfg = synth.CONFIGS[2]
-    assert load_lib("f32").lib.oracle_n_tensors(12) == 148
+    E, L, V, P = cfg.n_embd, cfg.n_layer, cfg.vocab, cfg.n_positions
+    assert V == fig["vocab"] and P == fig["context"]
+    assert load_lib("f32").lib.oracle_n_tensors(L) == fig["tensor_count"]
     shapes = synth.tensor_shapes(cfg)
-    assert len(shapes) == 148
+    assert len(shapes) == fig["tensor_count"]
     n = sum(int(np.prod(s)) for _, s in shapes)
-    assert n == 124_439_808 and abs(n * 4 / 1e6 - 498) < 0.5
-    E = cfg.n_embd
-    block = 12 * (3 * E * E + E * E + 4 * E * E + 4 * E * E) * 4
-    assert block == 339_738_624 and round(block / 1e6) == 340
-    assert round(50304 * E * 4 / 1e6) == 155 or round(50304 * E * 4 / 2**20) == 147
-    kv = 2 * 12 * 1024 * E * 4
-    assert round(kv / 1e6) == 75 or round(kv / 2**20) == 72
+    assert n == 124_439_808
+    # weights read per token: everything but the position table, whose one row is read
+    per_token = (n - P * E + E) * 4
+    assert abs(per_token / 1e6 - fig["weights_read_per_token_MB"]) < 0.02 * fig["weights_read_per_token_MB"]
+    block = L * (3 * E * E + E * E + 4 * E * E + 4 * E * E) * 4
+    assert round(block / 1e6) == fig["block_tiles_MB"]
+    assert fig["head_padded_rows"] == -(-V // 64) * 64
+    assert round(fig["head_padded_rows"] * E * 4 / 1e6) in (fig["head_tiles_MB"], fig["head_tiles_MB"] + 1)
+    kv = 2 * L * P * E * 4
+    assert round(kv / 1e6) == fig["kv_cache_MB"]
 
 
 # ---------------------------------------------------------------- primitives
@@ -343,29 +355,196 @@ def test_q4_group_properties_and_bruteforce(olib):
         del levels
 
 
-def test_long_context_fixture_is_the_oracles_run():
-    """The stored long-context run (tests/golden/gpt2_124m_fp32_long.json, written by
-    tests/golden/make_long_context.py from the oracle alone) is what the current
-    oracle and input generators produce: its prompt, and its first 12 steps."""
-    import json
-    import os
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "gpt2_124m_fp32_long.json")
-    with open(path) as f:
-        fx = json.load(f)
-    cfg = synth.CONFIGS[5]
-    assert fx["n_steps"] == cfg.n_steps and fx["n_prompt"] == cfg.n_prompt
-    assert fx["prompt"] == [int(t) for t in synth.make_prompt(cfg)]
-    orc = Oracle(synth.make_model(cfg))
-    for pos in range(12):
-        st = fx["steps"][pos]
-        am, lg = orc.step(st["tok"], pos)
-        lg = np.asarray(lg, np.float64)
-        assert am == st["argmax"]
-        assert abs(np.abs(lg).max() - st["maxabs"]) <= 1e-12 * st["maxabs"]
-        if str(pos) in fx["samples"]:
-            smp = fx["samples"][str(pos)]
-            assert np.array_equal(lg[smp["ids"]], np.asarray(smp["logits"]))
+# ------------------------------------------------------- effective weights
+def _two_sum_exact(a, b):
+    """True where the float64 sum a + b is exact (Knuth's TwoSum error term is 0)."""
+    s = a + b
+    bb = s - a
+    err = (a - (s - bb)) + (b - bb)
+    return err == 0
+
+
+def _q4_rows_numpy(W, group=32):
+    """Grouped asymmetric int4 restated in numpy from the model file's header
+    ("transposes to [output,input] before grouped asymmetric int4
+    quantization") and the reading of the unstated details (minimum as the
+    zero, (max - min)/15 as the step, round half to even, clamp to 0..15,
+    level = zero + code * step rounded once): W is the checkpoint's
+    [input][output] matrix; returns the dequantised [output][input] rows."""
+    T = np.ascontiguousarray(W.T)                       # [N][K]
+    N, K = T.shape
+    g = T.reshape(N, K // group, group)
+    lo = g.min(axis=2, keepdims=True)
+    hi = g.max(axis=2, keepdims=True)
+    step = (hi - lo) / np.float32(15)                   # float32 arithmetic throughout
+    with np.errstate(divide="ignore", invalid="ignore"):
+        code = np.where(step != 0, np.clip(np.rint((g - lo) / step), 0, 15), 0).astype(np.float32)
+    # the one-rounding level: code * step is exact in float64 (4 x 24 bits); the
+    # sum is checked exact, so rounding it to float32 is the fused multiply-add
+    prod = code.astype(np.float64) * step.astype(np.float64)
+    lo64 = np.broadcast_to(lo.astype(np.float64), prod.shape)
+    assert np.all(_two_sum_exact(prod, lo64))
+    return (prod + lo64).astype(np.float32).reshape(N, K)
+
+
+def _q4_along_output(W, group=32):
+    """The plausible mistake: groups of consecutive outputs instead of inputs."""
+    return _q4_rows_numpy(np.ascontiguousarray(W.T), group).T   # quantise W.T's rows = W's columns
+
+
+MATS = {0: "attn.c_attn.weight", 1: "attn.c_proj.weight", 2: "mlp.c_fc.weight", 3: "mlp.c_proj.weight"}
+
+
+@pytest.mark.parametrize("cfg,layers", [
+    (synth.variant(tiny_rich(), wdtype="fp16", name="tiny-fp16"), None),
+    (synth.variant(tiny_rich(), wdtype="int4", name="tiny-int4"), None),
+    (synth.variant(tiny_rich(), wdtype="fp32", name="tiny-fp32"), None),
+    (synth.CONFIGS[3], (0, 11)),
+    (synth.CONFIGS[4], (0, 11)),
+], ids=lambda v: v.name if hasattr(v, "name") else str(v))
+def test_effective_weights_restated_in_numpy(cfg, layers):
+    """Which tensors each storage mode changes, and how, rebuilt from the
+    checkpoint arrays in numpy with no oracle code: fp16 ("-h", gpt2.s docs
+    Build and run) rounds the 48 block matrices and the output head to
+    binary16 (numpy's cast) and keeps the embedding fp32; int4 (model file
+    header) quantises each block matrix in groups of 32 consecutive inputs of
+    one output row, and keeps the tied head exactly fp32.  Compared bit for bit
+    with the weights the oracle runs; a grouping along the output would fail."""
+    model = synth.make_model(cfg)
+    orc = Oracle(model, "f32")
+    t = model.t
+    E, V = cfg.n_embd, cfg.vocab
+    for l in (range(cfg.n_layer) if layers is None else layers):
+        for which, name in MATS.items():
+            W = t[f"h.{l}.{name}"]
+            got = orc.weight(l, which).reshape(W.shape[1], W.shape[0])
+            if cfg.wdtype == "fp32":
+                want = W.T
+            elif cfg.wdtype == "fp16":
+                want = W.T.astype(np.float16).astype(np.float32)
+            else:
+                want = _q4_rows_numpy(W)
+                assert not np.array_equal(got, _q4_along_output(W)), (l, which)
+            assert np.array_equal(got.view(np.uint32), np.ascontiguousarray(want).view(np.uint32)), (l, which)
+    head = orc.weight(0, 4).reshape(V, E)
+    want = t["wte.weight"].astype(np.float16).astype(np.float32) if cfg.wdtype == "fp16" else t["wte.weight"]
+    assert np.array_equal(head.view(np.uint32), want.view(np.uint32))
+    if cfg.wdtype == "fp16":
+        assert not np.array_equal(head, t["wte.weight"])
     orc.close()
-    # the stored ids follow the greedy rule: each step after the prompt feeds the previous argmax
-    for pos in range(cfg.n_prompt, cfg.n_steps):
-        assert fx["steps"][pos]["tok"] == fx["steps"][pos - 1]["argmax"]
+
+
+# ---------------------------------------------------------------- sampling
+_P64 = (1 << 64) - 1
+# prime factors of 2^64 - 1
+_FACTORS_2_64_M1 = (3, 5, 17, 257, 641, 65537, 6700417)
+
+
+def _gf2_mul(A, B):
+    """64x64 bit matrices over GF(2), each a list of 64 row ints (bit j of row
+    i = entry (i, j)); returns A.B."""
+    out = []
+    for i in range(64):
+        r, a = 0, A[i]
+        j = 0
+        while a:
+            if a & 1:
+                r ^= B[j]
+            a >>= 1
+            j += 1
+        out.append(r)
+    return out
+
+
+def _gf2_pow(A, e):
+    R = [1 << i for i in range(64)]
+    while e:
+        if e & 1:
+            R = _gf2_mul(R, A)
+        A = _gf2_mul(A, A)
+        e >>= 1
+    return R
+
+
+def test_xorshift_state_update_has_full_period(olib):
+    """The state update of xorshift64* is a linear map T over GF(2)^64 (three
+    shifts and three xors, blog Step 7).  Its matrix, read off the oracle by
+    updating the 64 unit states, must have order exactly 2^64 - 1 (every
+    non-zero state on one cycle): the defining property of the shift triples
+    the generator is built on, which a wrong shift amount or direction breaks.
+    The output is the state times an odd constant (one multiply), so it is a
+    bijection of the state."""
+    import ctypes as C
+    cols = []
+    for i in range(64):
+        st = C.c_uint64(1 << i)
+        olib.lib.oracle_xorshift64s(C.byref(st))
+        cols.append(st.value)
+    # T as rows: entry (r, c) = bit r of T e_c
+    T = [sum(((cols[c] >> r) & 1) << c for c in range(64)) for r in range(64)]
+    ident = [1 << i for i in range(64)]
+    assert _gf2_pow(T, _P64) == ident
+    for p in _FACTORS_2_64_M1:
+        assert _gf2_pow(T, _P64 // p) != ident, p
+    # the update is linear: T(a ^ b) = T(a) ^ T(b)
+    rng = np.random.default_rng(8)
+    for _ in range(20):
+        a, b = (int(v) for v in rng.integers(1, 2 ** 63, 2, dtype=np.int64))
+        sa, sb, sab = C.c_uint64(a), C.c_uint64(b), C.c_uint64(a ^ b)
+        for s in (sa, sb, sab):
+            olib.lib.oracle_xorshift64s(C.byref(s))
+        assert sab.value == sa.value ^ sb.value
+    # output = new state * odd constant (mod 2^64): invertible, and the same
+    # constant for every state
+    outs, _ = olib.xorshift64s(12345, 1)
+    st = C.c_uint64(12345)
+    olib.lib.oracle_xorshift64s(C.byref(st))
+    mult = (int(outs[0]) * pow(st.value, -1, 1 << 64)) % (1 << 64) if st.value % 2 else None
+    if mult is not None:
+        assert mult % 2 == 1
+        for seed in (1, 99, 2 ** 40 + 7):
+            o, s2 = olib.xorshift64s(seed, 1)
+            assert int(o[0]) == (s2 * mult) % (1 << 64)
+
+
+def test_uniform_draws_are_uniform(olib):
+    """u = top 24 bits of an output times 2^-24: in [0,1), on the 2^-24 grid,
+    and uniform (Kolmogorov-Smirnov over 200,000 draws)."""
+    u = olib.uniforms(2024, 200_000).astype(np.float64)
+    assert u.min() >= 0 and u.max() < 1
+    assert np.all(u * 2 ** 24 == np.floor(u * 2 ** 24))
+    assert scipy.stats.kstest(u, "uniform").pvalue > 1e-4
+
+
+def test_sample_is_inverse_cdf_of_tempered_softmax(olib, olib64):
+    """Sampling (blog Step 7: divide the scores by a temperature, softmax, draw):
+    temperature 0 is the argmax; otherwise the pick is the first id whose
+    cumulative softmax(logits/T) weight exceeds u (brute force in float64, away
+    from the cumulative boundaries), shifting every logit by a constant changes
+    nothing, and the picks of many uniform draws follow softmax(logits/T)
+    (chi-square)."""
+    rng = np.random.default_rng(4)
+    lg = rng.standard_normal(9)
+    assert olib.sample(lg, 0.0, 0.5) == int(np.argmax(lg))
+    assert olib.sample(lg, -1.0, 0.5) == -1 and olib.sample(lg, 1.0, 1.0) == -1
+    for T in (0.3, 0.8, 2.0):
+        p = scipy.special.softmax(lg / T)
+        cdf = np.cumsum(p)
+        for u in np.linspace(0, 1, 997, endpoint=False):
+            if np.min(np.abs(cdf - u)) < 1e-5:
+                continue
+            want = int(np.argmax(cdf > u))
+            assert olib.sample(lg.astype(np.float32), T, u) == want
+            assert olib64.sample(lg, T, u) == want
+            assert olib.sample((lg + 3.5).astype(np.float32), T, u) == want
+    # frequencies
+    T = 0.8
+    lg = rng.standard_normal(6)
+    us = olib.uniforms(77, 60_000)
+    picks = np.array([olib.sample(lg.astype(np.float32), T, float(u)) for u in us])
+    counts = np.bincount(picks, minlength=6)
+    expect = scipy.special.softmax(lg / T) * len(us)
+    assert scipy.stats.chisquare(counts, expect).pvalue > 1e-4
+    # a very high temperature: every id equally likely
+    flat = np.array([olib.sample(lg.astype(np.float32), 1e6, float(u)) for u in us[:30_000]])
+    assert scipy.stats.chisquare(np.bincount(flat, minlength=6)).pvalue > 1e-4

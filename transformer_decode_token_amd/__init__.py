@@ -13,11 +13,12 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgpt2dec.so")
 
-GPT2_OK, GPT2_E_INVAL, GPT2_E_NOMEM, GPT2_E_DEVICE, GPT2_E_STATE = 0, -1, -2, -3, -4
+GPT2_OK, GPT2_E_INVAL, GPT2_E_NOMEM, GPT2_E_DEVICE, GPT2_E_STATE, GPT2_E_NUMERIC = 0, -1, -2, -3, -4, -5
 GPT2_W_FP32, GPT2_W_FP16, GPT2_W_INT4 = 0, 1, 2
 WDTYPES = {"fp32": GPT2_W_FP32, "fp16": GPT2_W_FP16, "int4": GPT2_W_INT4}
 ERROR_NAMES = {GPT2_E_INVAL: "GPT2_E_INVAL", GPT2_E_NOMEM: "GPT2_E_NOMEM",
-               GPT2_E_DEVICE: "GPT2_E_DEVICE", GPT2_E_STATE: "GPT2_E_STATE"}
+               GPT2_E_DEVICE: "GPT2_E_DEVICE", GPT2_E_STATE: "GPT2_E_STATE",
+               GPT2_E_NUMERIC: "GPT2_E_NUMERIC"}
 
 # the symbols include/gpt2dec.h declares
 ABI_FUNCTIONS = ("gpt2_load", "gpt2_set_stream", "gpt2_step", "gpt2_generate", "gpt2_reset",
@@ -71,7 +72,8 @@ def lib():
         L.gpt2_debug_dequant.argtypes = [C.c_void_p, C.c_int, C.c_int, C.c_void_p]
         L.gpt2_debug_fill_kv.argtypes = [C.c_void_p, C.c_float]
         L.gpt2_debug_geometry.argtypes = [C.c_void_p, C.POINTER(C.c_int), C.POINTER(C.c_int)]
-        L.gpt2_debug_trace.argtypes = [C.c_void_p, C.c_int, C.c_void_p]
+        L.gpt2_debug_trace.argtypes = [C.c_void_p, C.c_int, C.c_void_p, C.c_longlong,
+                                       C.POINTER(C.c_int)]
         _lib = L
     return _lib
 
@@ -193,13 +195,17 @@ def gpt2_debug_geometry(ctx):
     return g.value, t.value
 
 
-def gpt2_debug_trace(ctx, steps, fetch_steps=None):
-    """Start recording `steps` steps per run; if fetch_steps is given, first return
-    the previous run's record as int64 [fetch_steps][5L+1][G][4]."""
+def gpt2_debug_trace(ctx, steps, fetch=False):
+    """Record `steps` steps of every later run (-1: leave the setting as it is); with
+    fetch=True, first return the last run's record as int64 [recorded steps][5L+1][G][4]
+    (None if nothing is recorded)."""
     out = None
-    if fetch_steps:
-        g, _ = gpt2_debug_geometry(ctx)
-        out = np.zeros((fetch_steps, 5 * ctx.cfg.n_layer + 1, g, 4), np.int64)
-    _check(lib().gpt2_debug_trace(ctx.handle, int(steps), out.ctypes.data if out is not None else None),
-           ctx.handle)
+    if fetch:
+        rec = C.c_int(0)
+        _check(lib().gpt2_debug_trace(ctx.handle, -1, None, 0, C.byref(rec)), ctx.handle)
+        if rec.value > 0:
+            g, _ = gpt2_debug_geometry(ctx)
+            out = np.zeros((rec.value, 5 * ctx.cfg.n_layer + 1, g, 4), np.int64)
+            _check(lib().gpt2_debug_trace(ctx.handle, -1, out.ctypes.data, out.size, None), ctx.handle)
+    _check(lib().gpt2_debug_trace(ctx.handle, int(steps), None, 0, None), ctx.handle)
     return out

@@ -16,6 +16,13 @@ enum { WD_F32 = 0, WD_F16 = 1, WD_Q4 = 2 };
 #endif
 constexpr int kTagCopies = G2_NCOPY;
 
+// Fed ids carried in the kernel arguments themselves (a longer prompt is
+// uploaded to a device buffer instead).
+constexpr int kFeedInline = 64;
+
+// Codes of the device error word (DecodeArgs::err[0]).
+enum { ERR_NONE = 0, ERR_TIMEOUT = 1, ERR_NO_ARGMAX = 2 };
+
 // One weight matrix of every layer, output-major [N][K] per layer, layers
 // back to back.  For int4: `w` holds the nibbles ([N][K/2] bytes, element k in
 // byte k/2, low nibble for even k) and `sz` the (scale, zero) pair of each
@@ -55,9 +62,11 @@ struct DecodeArgs {
   uint64_t *xb_t;                    // [L][C][E]      tagged residual after the MLP
   uint64_t *amax_t;                  // [C][G][2]      tagged per-workgroup argmax (value, index)
   float *logits;                     // [V]            logits of the last step
-  int *out_ids;                      // greedy ids
-  int *err;                          // [4] flag, workgroup, phase, epoch (device-side wait timeout)
-  const int *feed;                   // [n_feed] ids fed at the first steps
+  int *out_ids;                      // greedy ids (host memory mapped into the device)
+  int *err;                          // [4] device: code, workgroup, phase, step of the first failure
+  int *err_host;                     // [4] host-mapped copy of err, written by the failing workgroup
+  const int *feed;                   // [n_feed] ids fed at the first steps (n_feed > kFeedInline)
+  int feed_inline[kFeedInline];      // the same ids when n_feed <= kFeedInline (no upload)
   int n_feed;
   int pos0;                          // position of step 0
   int nsteps;

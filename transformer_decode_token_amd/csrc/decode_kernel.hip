@@ -420,6 +420,29 @@ static_assert(NCOPY % 8 == 0, "copies per XCD");
 __device__ __forceinline__ int my_copy() { return (int)(blockIdx.x % NCOPY); }
 __device__ __forceinline__ float payload(uint64_t x) { return __uint_as_float((uint32_t)x); }
 
+// The first failure of a run: the error word (which every bounded wait reads,
+// so that all workgroups stop) and its host-mapped copy, which the host reads
+// once the launch has ended.
+__device__ __forceinline__ void raise_error(const DecodeArgs &a, int code, int phase, int step) {
+  int zero = 0;
+  if (__hip_atomic_compare_exchange_strong(a.err, &zero, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT)) {
+    __hip_atomic_store(a.err + 1, (int)blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.err + 2, phase, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.err + 3, step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    a.err_host[1] = (int)blockIdx.x;
+    a.err_host[2] = phase;
+    a.err_host[3] = step;
+    a.err_host[0] = code;
+  }
+}
+
+// The id fed at `step` (< n_feed): from the kernel arguments, or from the
+// uploaded buffer for a long prompt.
+__device__ __forceinline__ int fed_token(const DecodeArgs &a, int step) {
+  return a.n_feed <= kFeedInline ? a.feed_inline[step] : a.feed[step];
+}
+
 // Bounded waiting: a wait that outlives the time limit, or sees another
 // workgroup's abort, sets the error word and makes the caller stop.
 struct Waiter {
@@ -443,12 +466,7 @@ struct Waiter {
     const long long now = (long long)wall_clock64();
     if (t0 == 0) t0 = now;
     if (now - t0 > a->timeout_ticks) {
-      int zero = 0;
-      if (__hip_atomic_compare_exchange_strong(a->err, &zero, 1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT)) {
-        __hip_atomic_store(a->err + 1, (int)blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(a->err + 2, phase, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      raise_error(*a, ERR_TIMEOUT, phase, -1);
       return true;
     }
     return false;
@@ -1276,14 +1294,21 @@ __device__ __attribute__((always_inline)) void control_set(const DecodeArgs &a, 
   for (int step = 0; step < a.nsteps; step++) {
     const int p = a.pos0 + step;
     cur_step = step;
-    if (step < a.n_feed) tok = a.feed[step];
+    if (step < a.n_feed) tok = fed_token(a, step);
     if (needs_tok && step >= argmax_from) {
       uint32_t bi = 0;
       wt.start(5 * a.L);
       if (!reduce_argmax<S>(a, epoch_of(a, step - 1, 5 * a.L), lane, wt, bi)) { abort_all(); return; }
       if (w == 0 && lane == 0 && step - 1 >= a.out_from) a.out_ids[step - 1 - a.out_from] = (int)bi;
-      // (an all-NaN head cannot name a row; keep the index in range)
-      if (step >= a.n_feed) tok = bi < (uint32_t)a.V ? (int)bi : 0;
+      if (step >= a.n_feed) {
+        // a step whose logits are all NaN names no row: the run stops with an error
+        if (bi >= (uint32_t)a.V) {
+          raise_error(a, ERR_NO_ARGMAX, 5 * a.L, step - 1);
+          abort_all();
+          return;
+        }
+        tok = (int)bi;
+      }
     }
     int nch, ch;
     att_chunks<S>(p, nch, ch);
@@ -1574,7 +1599,7 @@ __device__ __attribute__((always_inline)) void control_set(const DecodeArgs &a, 
       const uint32_t epH = epoch_of(a, step, 5 * a.L);
       if constexpr (S::CD) fetch_gain(gf, a.lnfw);  // (arrives while the input is polled)
       if (set == SET_Q && step + 1 < a.n_feed && step + 1 < a.nsteps) {
-        const int tn = a.feed[step + 1];
+        const int tn = fed_token(a, step + 1);
 #pragma unroll
         for (int j = 0; j < PE; j++)
           xn[j] = a.wte[(size_t)tn * E + vidx(lane, j)] + a.wpe[(size_t)(p + 1) * E + vidx(lane, j)];

@@ -38,8 +38,11 @@ struct gpt2_ctx {
   std::vector<void *> dev_allocs;
   std::vector<void *> host_allocs;
   DecodeArgs base{};
-  int *feed_d = nullptr, *ids_d = nullptr, *err_d = nullptr;
-  int *feed_h = nullptr, *ids_h = nullptr, *err_h = nullptr;
+  int *feed_d = nullptr, *err_d = nullptr;
+  // host memory the kernel writes directly (mapped into the device): greedy
+  // ids, and the copy of the error word; plus staging for uploads and logits
+  int *ids_h = nullptr, *err_h = nullptr, *ids_dev = nullptr, *err_dev = nullptr;
+  int *feed_h = nullptr;
   float *logits_h = nullptr;
   uint64_t *tag_bufs[7] = {};
   size_t tag_sizes[7] = {};
@@ -66,8 +69,9 @@ struct gpt2_ctx {
   }
   template <typename T>
   T *dalloc(size_t bytes) {
-    static const bool inject = getenv("GPT2DEC_FAIL_ALLOC") && atoi(getenv("GPT2DEC_FAIL_ALLOC")) != 0;
-    if (inject) return nullptr;
+    // (fault injection for the tests: every device allocation fails)
+    const char *inject = getenv("GPT2DEC_FAIL_ALLOC");
+    if (inject && atoi(inject) != 0) return nullptr;
     void *p = nullptr;
     if (hipMalloc(&p, bytes ? bytes : 4) != hipSuccess) {
       (void)hipGetLastError();
@@ -79,7 +83,7 @@ struct gpt2_ctx {
   template <typename T>
   T *halloc(size_t bytes) {
     void *p = nullptr;
-    if (hipHostMalloc(&p, bytes ? bytes : 4, hipHostMallocDefault) != hipSuccess) {
+    if (hipHostMalloc(&p, bytes ? bytes : 4, hipHostMallocMapped) != hipSuccess) {
       (void)hipGetLastError();
       return nullptr;
     }
@@ -159,13 +163,23 @@ int run(gpt2_ctx *c, const int *feed, int n_feed, int pos0, int nsteps, int out_
     }
     c->epoch = 0;
   }
-  memcpy(c->feed_h, feed, sizeof(int) * (size_t)n_feed);
-  e = hipMemcpyAsync(c->feed_d, c->feed_h, sizeof(int) * (size_t)n_feed, hipMemcpyHostToDevice, c->stream);
-  if (e == hipSuccess) e = hipMemsetAsync(c->err_d, 0, 4 * sizeof(int), c->stream);
-  if (e != hipSuccess) return c->device_fail(e, "staging inputs");
   DecodeArgs a = c->base;
-  a.feed = c->feed_d;
   a.n_feed = n_feed;
+  if (n_feed <= kFeedInline) {
+    // the fed ids travel in the kernel arguments
+    memcpy(a.feed_inline, feed, sizeof(int) * (size_t)n_feed);
+    a.feed = nullptr;
+  } else {
+    memcpy(c->feed_h, feed, sizeof(int) * (size_t)n_feed);
+    e = hipMemcpyAsync(c->feed_d, c->feed_h, sizeof(int) * (size_t)n_feed, hipMemcpyHostToDevice, c->stream);
+    if (e != hipSuccess) return c->device_fail(e, "uploading the fed ids");
+    a.feed = c->feed_d;
+  }
+  // The kernel writes the ids and (on failure) the error word's copy straight
+  // into mapped host memory: cleared here, read after the stream has drained.
+  // (The device error word itself is zero: any failure poisons the context.)
+  memset(c->err_h, 0, 4 * sizeof(int));
+  for (int i = 0; i < n_out; i++) c->ids_h[i] = -1;
   a.pos0 = pos0;
   a.nsteps = nsteps;
   a.out_from = out_from;
@@ -180,20 +194,28 @@ int run(gpt2_ctx *c, const int *feed, int n_feed, int pos0, int nsteps, int out_
   e = launch_decode(c->E, c->D, c->wd, a, c->stream);
   c->epoch += (uint32_t)used;
   if (e != hipSuccess) return c->device_fail(e, "decode launch");
-  e = hipMemcpyAsync(c->ids_h, c->ids_d, sizeof(int) * (size_t)n_out, hipMemcpyDeviceToHost, c->stream);
-  if (e == hipSuccess)
-    e = hipMemcpyAsync(c->err_h, c->err_d, 4 * sizeof(int), hipMemcpyDeviceToHost, c->stream);
-  if (e == hipSuccess && logits_out)
+  if (logits_out)
     e = hipMemcpyAsync(c->logits_h, c->base.logits, sizeof(float) * (size_t)c->V, hipMemcpyDeviceToHost,
                        c->stream);
   if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
   if (e != hipSuccess) return c->device_fail(e, "decode run");
-  if (c->err_h[0] != 0) {
+  const volatile int *eh = c->err_h;
+  if (eh[0] == ERR_TIMEOUT) {
     c->poisoned = true;
-    return c->fail(GPT2_E_DEVICE, "device wait timed out (workgroup %d, producer phase %d)", c->err_h[1],
-                   c->err_h[2]);
+    return c->fail(GPT2_E_DEVICE, "device wait timed out (workgroup %d, producer phase %d)", eh[1], eh[2]);
   }
-  memcpy(ids_out, c->ids_h, sizeof(int) * (size_t)n_out);
+  if (eh[0] != ERR_NONE) {
+    c->poisoned = true;
+    return c->fail(GPT2_E_NUMERIC, "every logit of pass %d of the run is NaN: no greedy id to feed", eh[3]);
+  }
+  const volatile int *ih = c->ids_h;
+  for (int i = 0; i < n_out; i++) {
+    if (ih[i] < 0 || ih[i] >= c->V) {
+      c->poisoned = true;
+      return c->fail(GPT2_E_NUMERIC, "every logit of pass %d of the run is NaN: no greedy id", out_from + i);
+    }
+    ids_out[i] = ih[i];
+  }
   if (logits_out) memcpy(logits_out, c->logits_h, sizeof(float) * (size_t)c->V);
   return GPT2_OK;
 }
@@ -271,7 +293,6 @@ int load_impl(gpt2_ctx *c, const gpt2_config *cfg, const gpt2_weights *w) {
   c->tag_sizes[6] = NC * L * E * 8;
   for (int i = 0; i < 7; i++) c->tag_bufs[i] = c->dalloc<uint64_t>(c->tag_sizes[i]);
   float *logits = c->dalloc<float>((size_t)V * 4);
-  c->ids_d = c->dalloc<int>((size_t)P * 4);
   c->feed_d = c->dalloc<int>((size_t)P * 4);
   c->err_d = c->dalloc<int>(4 * 4);
   c->feed_h = c->halloc<int>((size_t)P * 4);
@@ -281,9 +302,13 @@ int load_impl(gpt2_ctx *c, const gpt2_config *cfg, const gpt2_weights *w) {
   if (!mq || !ma || !mf || !mp || !stage || (c->wd == WD_Q4 && !tmp) || !ln1w || !ln1b || !ln2w || !ln2b ||
       !bqkv || !bap || !bfc || !bpr || !lnfw || !lnfb || !gqkv || !cqkv || !gfc || !cfc || !ghead || !chead ||
       !wte || !wpe || (c->wd == WD_F16 && !head16) || !kc ||
-      !vc || !logits || !c->ids_d || !c->feed_d || !c->err_d || !c->feed_h || !c->ids_h || !c->err_h ||
+      !vc || !logits || !c->feed_d || !c->err_d || !c->feed_h || !c->ids_h || !c->err_h ||
       !c->logits_h)
     return c->fail(GPT2_E_NOMEM, "allocation failed");
+  // the device addresses of the mapped host buffers the kernel writes
+  e = hipHostGetDevicePointer(reinterpret_cast<void **>(&c->ids_dev), c->ids_h, 0);
+  if (e == hipSuccess) e = hipHostGetDevicePointer(reinterpret_cast<void **>(&c->err_dev), c->err_h, 0);
+  if (e != hipSuccess) return c->device_fail(e, "mapping host buffers");
   for (int i = 0; i < 7; i++)
     if (!c->tag_bufs[i]) return c->fail(GPT2_E_NOMEM, "allocation failed");
 
@@ -351,6 +376,7 @@ int load_impl(gpt2_ctx *c, const gpt2_config *cfg, const gpt2_weights *w) {
                 E, lnfw, lnfb, nullptr, ghead, chead, s);
   if (e != hipSuccess) return c->device_fail(e, "folding the LayerNorms");
   for (int i = 0; i < 7 && e == hipSuccess; i++) e = hipMemsetAsync(c->tag_bufs[i], 0, c->tag_sizes[i], s);
+  if (e == hipSuccess) e = hipMemsetAsync(c->err_d, 0, 4 * sizeof(int), s);
   if (e == hipSuccess) e = hipMemsetAsync(kc, 0, kv * 4, s);
   if (e == hipSuccess) e = hipMemsetAsync(vc, 0, kv * 4, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
@@ -379,8 +405,9 @@ int load_impl(gpt2_ctx *c, const gpt2_config *cfg, const gpt2_weights *w) {
   a.amax_t = c->tag_bufs[5];
   a.attn_t = c->tag_bufs[6];
   a.logits = logits;
-  a.out_ids = c->ids_d;
+  a.out_ids = c->ids_dev;
   a.err = c->err_d;
+  a.err_host = c->err_dev;
   a.L = L; a.V = V; a.P = P;
   a.eps = cfg->ln_eps;
   return GPT2_OK;
@@ -541,17 +568,20 @@ int gpt2_debug_fill_kv(gpt2_ctx *c, float value) {
   return GPT2_OK;
 }
 
-int gpt2_debug_trace(gpt2_ctx *c, int steps, long long *out) {
+int gpt2_debug_trace(gpt2_ctx *c, int steps, long long *out, long long out_len, int *recorded_steps) {
   int rc;
   if (!usable(c, &rc)) return rc;
-  if (steps < 0) return c->fail(GPT2_E_INVAL, "steps must be >= 0");
+  if (steps < -1) return c->fail(GPT2_E_INVAL, "steps must be >= -1");
   const size_t n = (size_t)c->trace_steps * (5 * c->L + 1) * c->si.G * 4;
+  if (recorded_steps) *recorded_steps = c->trace_steps;
+  if (out && c->trace_d && (out_len < 0 || (size_t)out_len < n))
+    return c->fail(GPT2_E_INVAL, "out holds %lld values; the record has %zu", out_len, n);
   if (out && c->trace_d) {
     hipError_t e = hipMemcpyAsync(out, c->trace_d, n * 8, hipMemcpyDeviceToHost, c->stream);
     if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
     if (e != hipSuccess) return c->device_fail(e, "trace copy");
   }
-  if (steps != c->trace_steps) {
+  if (steps >= 0 && steps != c->trace_steps) {
     if (c->trace_d) {
       (void)hipStreamSynchronize(c->stream);
       (void)hipFree(c->trace_d);

@@ -87,7 +87,12 @@ __global__ void __launch_bounds__(256) fill_kernel(float *dst, size_t n, float v
 }
 
 // Chunk c (4 consecutive elements) of an output-major matrix from element
-// offset lofs, decoded exactly as the GEMV does (same element order and arithmetic).
+// offset lofs, as the weights the stored data stand for: fp32 as is, fp16
+// widened (exact), int4 as zero + code * scale with one rounding.  This reads
+// the same stored codes, scales and zeros as the GEMV, but the int4 GEMV does
+// not form these values: it sums scale * sum(code * x) + zero * sum(x) over a
+// group's inputs.  So a bitwise comparison of this decode pins the stored
+// data; the int4 dot products are pinned through the logits only.
 __device__ __forceinline__ float4 chunk_f4(int wd, const void *w, const float2 *szp, size_t lofs, size_t c) {
   if (wd == WD_F32) return reinterpret_cast<const float4 *>(w)[lofs / 4 + c];
   if (wd == WD_F16) {
