@@ -146,6 +146,9 @@ def main():
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # torch creates an event at its first record: do that outside the timed loop
+    for ev in starts + ends:
+        ev.record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):

@@ -25,8 +25,9 @@ CASES = {
     "tiny-rich": tiny_rich(),
     "tiny-rich-fp16": tiny_rich(wdtype="fp16"),
     "tiny-rich-int4": tiny_rich(wdtype="int4"),
-    # long context on the tiny shape: up to 8 attention chunks per head
-    "tiny-long": tiny_rich(n_positions=512, n_new=400),
+    # long context on the tiny shape: up to 8 attention chunks per head, all
+    # 512 positions (at 8 chunks every one of the 32 workgroups runs one)
+    "tiny-long": tiny_rich(n_positions=512, n_new=505),
     "gpt2-124m-fp32": synth.CONFIGS[2],
     "gpt2-124m-fp16w": synth.CONFIGS[3],
     "gpt2-124m-int4w": synth.CONFIGS[4],

@@ -88,7 +88,7 @@ struct ShapeInfo {
 };
 bool shape_info(int E, int D, ShapeInfo *out);
 
-// Launch the decode kernel (cooperative: all workgroups are co-resident).
+// Launch the decode kernel (all its workgroups are resident at once: one per CU).
 hipError_t launch_decode(int E, int D, int wd, const DecodeArgs &a, hipStream_t s);
 // Occupancy check: blocks of the decode kernel per CU.
 hipError_t decode_occupancy(int E, int D, int wd, int *blocks_per_cu);

@@ -1,6 +1,6 @@
 // decode_kernel.hip -- the persistent batch-1 GPT-2 decode kernel for gfx950.
 //
-// One cooperative launch runs `nsteps` whole forward passes (one token each).
+// One launch runs `nsteps` whole forward passes (one token each).
 // The per-token work follows the node order of the gpt2-125m "model.fir" file:
 // embedding add, then per layer
 //   A: LayerNorm 1 + QKV linear + bias
@@ -1754,7 +1754,14 @@ hipError_t launch_t(int wd, const DecodeArgs &a, hipStream_t s) {
   DecodeArgs copy = a;
   copy.head_lds_rows = head_lds_rows_for<S>(wd, lds);
   void *args[] = {&copy};
-  return hipLaunchCooperativeKernel(k, dim3(S::G), dim3(S::NT), args, lds, s);
+  // An ordinary launch (a cooperative one costs about 8 us more host time per
+  // call).  Every workgroup must be resident at once, and is: the LDS size
+  // allows one workgroup per CU, the grid has no more workgroups than the
+  // device has CUs (checked when the model is loaded), and nothing in the grid
+  // waits for a workgroup that has not started except through bounded waits,
+  // so a grid that cannot be placed whole (the CUs busy with other work for
+  // seconds) ends with the timeout error instead of hanging.
+  return hipLaunchKernel(k, dim3(S::G), dim3(S::NT), args, lds, s);
 }
 
 template <class S>

@@ -2,7 +2,7 @@
 //
 // Owns the device memory of one model (re-laid-out weights, KV cache, tagged
 // activation words), validates every call before touching the device, and
-// drives the decode kernel: one cooperative launch per gpt2_step (one token)
+// drives the decode kernel: one launch per gpt2_step (one token)
 // or per gpt2_generate (the whole greedy run chained on the device).
 #include <hip/hip_runtime.h>
 
