@@ -113,6 +113,22 @@ GPT2DEC_API int gpt2_step(gpt2_ctx *c, int token_id, int position, float *logits
  * filled += n_prompt + n_new - 1.  Errors as gpt2_step. */
 GPT2DEC_API int gpt2_generate(gpt2_ctx *c, const int *prompt, int n_prompt, int n_new, int *out_ids);
 
+/* Generation with sampling ("Let's make GPT-2 in assembly", Step 7: divide the
+ * scores by a temperature, apply softmax, draw at random; gpt2.s docs, "-t"),
+ * chained on the device like gpt2_generate.  Each new id is the first id whose
+ * running sum of exp((logit - max)/temperature), in id order, exceeds u times
+ * the total, for one uniform number u in [0,1) per id: the top 24 bits of the
+ * next xorshift64* output (S. Vigna's scrambled xorshift, shifts 12/25/27,
+ * multiplier 2685821657736338717) times 2^-24, the generator's state starting
+ * at `seed` (non-zero).  The id comes from the logits as the kernel computes
+ * them, so where u falls within rounding of a cumulative boundary the choice
+ * may differ from a host computation.  temperature 0 = greedy (gpt2_generate).
+ * Errors: GPT2_E_INVAL (temperature negative, not finite or so small that its
+ * reciprocal overflows; seed 0; and as gpt2_generate), GPT2_E_DEVICE,
+ * GPT2_E_NUMERIC, GPT2_E_STATE. */
+GPT2DEC_API int gpt2_generate_sample(gpt2_ctx *c, const int *prompt, int n_prompt, int n_new, float temperature,
+                                     unsigned long long seed, int *out_ids);
+
 /* filled = 0.  The cache need not be cleared: reads never pass `position`. */
 GPT2DEC_API int gpt2_reset(gpt2_ctx *c);
 

@@ -74,6 +74,7 @@ def test_null_arguments(lib):
     assert not h.value
     assert lib.gpt2_step(None, 0, 0, None, None) == g2.GPT2_E_INVAL
     assert lib.gpt2_reset(None) == g2.GPT2_E_INVAL
+    assert lib.gpt2_generate_sample(None, None, 0, 0, 0.8, 1, None) == g2.GPT2_E_INVAL
     assert lib.gpt2_filled(None) == -1
     lib.gpt2_free(None)
 

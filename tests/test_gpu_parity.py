@@ -480,3 +480,104 @@ def test_debug_trace_record_and_capacity():
     assert np.all(head[..., 0] > 0) and np.all(head[..., 3] >= head[..., 0])
     assert g2.gpt2_debug_trace(ctx, 0, fetch=True) is None
     ctx.close()
+
+
+# ------------------------------------------------------------------ sampling
+def _oracle_sampled(orc, olib, prompt, n_new, T, seed):
+    """The oracle's sampled run ("Let's make GPT-2 in assembly", Step 7): ids drawn
+    from softmax(logits/T) with its own xorshift64* draws from `seed`.  Returns the
+    ids and, per drawn id, the distance (float64) of u from the nearest cumulative
+    boundary of the oracle's softmax."""
+    import scipy.special
+    us = olib.uniforms(seed, n_new)
+    toks = [int(t) for t in prompt]
+    ids, dists = [], []
+    for pos in range(len(prompt) + n_new - 1):
+        _, lg = orc.step(toks[pos], pos)
+        if pos >= len(prompt) - 1:
+            u = float(us[len(ids)])
+            pick = olib.sample(lg, T, u)
+            cdf = np.cumsum(scipy.special.softmax(np.asarray(lg, np.float64) / T))
+            ids.append(pick)
+            dists.append(float(np.min(np.abs(cdf - u))))
+            if pos + 1 >= len(toks):
+                toks.append(pick)
+    return ids, dists
+
+
+@pytest.mark.parametrize("name,T,n_new", [("tiny-rich", 0.8, 40), ("tiny-rich", 2.0, 40),
+                                          ("gpt2-124m-fp32", 0.05, 20), ("gpt2-124m-fp16w", 0.05, 20)])
+def test_sampled_generate_matches_oracle(name, T, n_new):
+    """Device-chained sampling against the oracle with the same seed: the same ids
+    up to the first draw whose u lies within 1e-5 of a cumulative boundary (where
+    the two summation orders may decide differently).  (At 50,257 ids the
+    boundaries of a flat distribution are about 2e-5 apart, within float32
+    rounding of either side's running sum, so the 124M shape runs at a low
+    temperature, where the mass sits on few ids.)"""
+    from oracle import load_lib
+    cfg = CASES[name]
+    model = synth.make_model(cfg)
+    orc = Oracle(model)
+    prompt = synth.make_prompt(cfg)
+    seed = 0x9E3779B97F4A7C15
+    want, dists = _oracle_sampled(orc, load_lib("f32"), prompt, n_new, T, seed)
+    orc.close()
+    ctx = load_gpu(model)
+    got = g2.gpt2_generate_sample(ctx, prompt, n_new, T, seed)
+    assert g2.gpt2_filled(ctx) == len(prompt) + n_new - 1
+    k = 0
+    for k in range(n_new):
+        if dists[k] < 1e-5:
+            break
+        assert int(got[k]) == want[k], f"{name} T={T}: id {k} differs: gpu {got[k]} oracle {want[k]}"
+    assert k >= 3, f"only {k} draws away from a boundary"
+    print(f"[sample] {name} T={T}: ids agree for the first {k + 1} of {n_new} draws", flush=True)
+    # temperature 0 is the greedy run
+    g2.gpt2_reset(ctx)
+    greedy = g2.gpt2_generate(ctx, prompt, 8)
+    g2.gpt2_reset(ctx)
+    assert np.array_equal(g2.gpt2_generate_sample(ctx, prompt, 8, 0.0, seed), greedy)
+    ctx.close()
+
+
+def test_sampling_follows_tempered_softmax():
+    """The first drawn id after a fixed prompt, over 3,000 seeds, follows
+    softmax(logits/T) of the oracle's logits (chi-square); the same seed always
+    draws the same id."""
+    import scipy.special
+    import scipy.stats
+    cfg = CASES["tiny-rich"]
+    model = synth.make_model(cfg)
+    prompt = synth.make_prompt(cfg)[:4]
+    orc = Oracle(model)
+    for pos, t in enumerate(prompt):
+        _, lg = orc.step(int(t), pos)
+    orc.close()
+    T = 1.0
+    p = scipy.special.softmax(np.asarray(lg, np.float64) / T)
+    ctx = load_gpu(model)
+    n = 3000
+    draws = np.empty(n, np.int64)
+    for i in range(n):
+        g2.gpt2_reset(ctx)
+        draws[i] = g2.gpt2_generate_sample(ctx, prompt, 1, T, 1 + 7919 * i)[0]
+    g2.gpt2_reset(ctx)
+    assert g2.gpt2_generate_sample(ctx, prompt, 1, T, 1)[0] == draws[0]
+    ctx.close()
+    counts = np.bincount(draws, minlength=cfg.vocab).astype(np.float64)
+    expect = p * n
+    big = expect >= 5
+    obs = np.append(counts[big], counts[~big].sum())
+    exp = np.append(expect[big], expect[~big].sum())
+    assert scipy.stats.chisquare(obs, exp).pvalue > 1e-4
+
+
+def test_sampling_argument_errors():
+    cfg = CASES["tiny"]
+    ctx = load_gpu(synth.make_model(cfg))
+    for T, seed in ((-1.0, 1), (float("nan"), 1), (float("inf"), 1), (1e-45, 1), (0.8, 0)):
+        with pytest.raises(g2.Gpt2Error) as e:
+            g2.gpt2_generate_sample(ctx, [1, 2], 3, T, seed)
+        assert e.value.code == g2.GPT2_E_INVAL
+    assert g2.gpt2_filled(ctx) == 0
+    ctx.close()

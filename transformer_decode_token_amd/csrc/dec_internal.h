@@ -61,6 +61,9 @@ struct DecodeArgs {
   uint64_t *act_t;                   // [L][C][F]      tagged gelu activations
   uint64_t *xb_t;                    // [L][C][E]      tagged residual after the MLP
   uint64_t *amax_t;                  // [C][G][2]      tagged per-workgroup argmax (value, index)
+  uint64_t *ssum_t;                  // [C][G]         sampling: tagged sum of exp((logit - max)/T) over
+                                     //                the workgroup's rows (max = its argmax value)
+  uint64_t *logit_t;                 // [V]            sampling: tagged logits (one copy)
   float *logits;                     // [V]            logits of the last step
   int *out_ids;                      // greedy ids (host memory mapped into the device)
   int *err;                          // [4] device: code, workgroup, phase, step of the first failure
@@ -71,6 +74,8 @@ struct DecodeArgs {
   int pos0;                          // position of step 0
   int nsteps;
   int out_from;                      // step whose argmax is out_ids[0]
+  float inv_temp;                    // 0: greedy; else 1/T: the ids from out_from on are sampled
+  const float *draws;                // [nsteps - out_from] uniform numbers in [0,1), one per sampled id
   int L, V, P;
   float eps;
   uint32_t epoch0;                   // epochs used: epoch0 + 1 .. epoch0 + nsteps*(5L+1)

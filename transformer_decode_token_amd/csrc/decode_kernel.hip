@@ -1041,6 +1041,143 @@ __device__ __forceinline__ bool reduce_argmax(const DecodeArgs &a, uint32_t ep, 
   return true;
 }
 
+// Sampling at temperature T ("Let's make GPT-2 in assembly", Step 7: divide the
+// scores by T, softmax, draw): the id whose running sum of the weights
+// exp((logit - max)/T), in id order, first exceeds u times their total.
+// Workgroup g published its rows' maximum m_g (the argmax pair), the sum s_g
+// of exp((logit - m_g)/T) over its rows, and its logits as tagged words.
+// Each lane takes PL consecutive workgroups: the sums scaled to the largest
+// maximum M, s_g * exp((m_g - M)/T), and a wave prefix sum locate the
+// workgroup g* in whose range the threshold falls; then each lane takes 8
+// consecutive rows of g*, weights exp((logit - M)/T), and a second prefix sum
+// locates the row.  Every reader runs the same code on the same words, so all
+// arrive at the same id.  Rounding can leave the running sum a hair short of
+// the threshold: then the last workgroup (or row) with a weight is taken.  No
+// weight at all (every logit NaN) gives 0xffffffff.
+template <class S, int WD>
+__device__ bool reduce_sample(const DecodeArgs &a, uint32_t ep, float u, int lane, Waiter &wt, uint32_t &out_idx) {
+  constexpr int G = S::G, PL = (G + 63) / 64, RPL = PSTRIDE / 64;
+  const float it = a.inv_temp;
+  const auto ars = __builtin_amdgcn_make_buffer_rsrc(a.amax_t + (size_t)my_copy() * 2 * G, (short)0, 2 * G * 8,
+                                                     0x00020000);
+  const auto srs = __builtin_amdgcn_make_buffer_rsrc(a.ssum_t + (size_t)my_copy() * G, (short)0, G * 8, 0x00020000);
+  float m[PL], sg[PL];
+  while (true) {
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < PL; j++) {
+      const int g = min(lane * PL + j, G - 1);
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(ars, (uint32_t)(g * 16), 0, AUX_SC1);
+      const auto y = __builtin_amdgcn_raw_buffer_load_b64(srs, (uint32_t)(g * 8), 0, AUX_SC1);
+      ok &= (x[1] == ep) && (x[3] == ep) && (y[1] == ep);
+      m[j] = __uint_as_float(x[0]);
+      sg[j] = __uint_as_float(y[0]);
+    }
+    if (__all(ok)) break;
+    if (wt.expired()) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < PL; j++)
+    if (lane * PL + j < G) mloc = fmaxf(mloc, m[j]);
+  const float M = wave_max_all(mloc);
+  // workgroups: scaled sums, prefix in workgroup order
+  float sc[PL], lsum = 0.f;
+#pragma unroll
+  for (int j = 0; j < PL; j++) {
+    const bool valid = lane * PL + j < G && m[j] > -INFINITY;
+    sc[j] = valid ? sg[j] * __expf((m[j] - M) * it) : 0.f;
+    lsum += sc[j];
+  }
+  const float incl = seg_sum_last<64>(lsum);  // inclusive prefix over the lanes
+  const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
+  const float thr = u * total;
+  float run = incl - lsum;
+  uint32_t cand = 0xffffffffu;
+  int lastg = -1;
+  float bef[PL];
+#pragma unroll
+  for (int j = 0; j < PL; j++) {
+    bef[j] = run;
+    run += sc[j];
+    if (sc[j] > 0.f) lastg = lane * PL + j;
+    if (cand == 0xffffffffu && run > thr) cand = (uint32_t)(lane * PL + j);
+  }
+  uint32_t gs = wave_min_u32_all(cand);
+  if (gs == 0xffffffffu) {
+    const int lg = (int)(~wave_min_u32_all(~(uint32_t)(lastg + 1))) - 1;  // the largest lastg
+    if (lg < 0) {
+      out_idx = 0xffffffffu;
+      return true;
+    }
+    gs = (uint32_t)lg;
+  }
+  // the running sum before g*, from the lane that holds it
+  float bsel = 0.f;
+#pragma unroll
+  for (int j = 0; j < PL; j++)
+    if ((int)(gs % PL) == j) bsel = bef[j];
+  const float thr2 = thr - __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bsel), (int)(gs / PL)));
+  // rows of g*: lane L takes rows 8L.. of its range
+  int hr0, hr1;
+  head_range<S, WD>(a.V, (int)gs, hr0, hr1);
+  const int nr = hr1 - hr0;
+  const auto lrs = __builtin_amdgcn_make_buffer_rsrc(a.logit_t + hr0, (short)0, PSTRIDE * 8, 0x00020000);
+  float lv[RPL];
+  while (true) {
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < RPL; j++) {
+      const int r = min(RPL * lane + j, nr - 1);
+      const auto y = __builtin_amdgcn_raw_buffer_load_b64(lrs, (uint32_t)(r * 8), 0, AUX_SC1);
+      ok &= y[1] == ep;
+      lv[j] = __uint_as_float(y[0]);
+    }
+    if (__all(ok)) break;
+    if (wt.expired()) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  float wv[RPL], rsum = 0.f;
+#pragma unroll
+  for (int j = 0; j < RPL; j++) {
+    const bool valid = RPL * lane + j < nr && lv[j] == lv[j];
+    wv[j] = valid ? __expf((lv[j] - M) * it) : 0.f;
+    rsum += wv[j];
+  }
+  const float rincl = seg_sum_last<64>(rsum);
+  float rrun = rincl - rsum;
+  uint32_t rc = 0xffffffffu;
+  int lastr = -1;
+#pragma unroll
+  for (int j = 0; j < RPL; j++) {
+    rrun += wv[j];
+    if (wv[j] > 0.f) lastr = RPL * lane + j;
+    if (rc == 0xffffffffu && rrun > thr2) rc = (uint32_t)(RPL * lane + j);
+  }
+  uint32_t rs = wave_min_u32_all(rc);
+  if (rs == 0xffffffffu) {
+    const int lr = (int)(~wave_min_u32_all(~(uint32_t)(lastr + 1))) - 1;
+    if (lr < 0) {
+      out_idx = 0xffffffffu;
+      return true;
+    }
+    rs = (uint32_t)lr;
+  }
+  out_idx = (uint32_t)hr0 + rs;
+  return true;
+}
+
+// The id chosen at step `st` (its logits complete with epoch ep): sampled
+// from the run's draws when the run samples and the id is recorded, else the
+// argmax.
+template <class S, int WD>
+__device__ __forceinline__ bool choose_token(const DecodeArgs &a, int st, int lane, Waiter &wt, uint32_t &out) {
+  const uint32_t ep = epoch_of(a, st, 5 * a.L);
+  if (a.inv_temp > 0.f && st >= a.out_from) return reduce_sample<S, WD>(a, ep, a.draws[st - a.out_from], lane, wt, out);
+  return reduce_argmax<S>(a, ep, lane, wt, out);
+}
+
 // One attention chunk of head h over positions t0..t1-1 on the control wave,
 // following the model file's decode attention: scores q.k * (1/sqrt(D)),
 // minus their maximum, exponentials; the chunk's (o = sum e_t v_t, m = max,
@@ -1298,7 +1435,7 @@ __device__ __attribute__((always_inline)) void control_set(const DecodeArgs &a, 
     if (needs_tok && step >= argmax_from) {
       uint32_t bi = 0;
       wt.start(5 * a.L);
-      if (!reduce_argmax<S>(a, epoch_of(a, step - 1, 5 * a.L), lane, wt, bi)) { abort_all(); return; }
+      if (!choose_token<S, WD>(a, step - 1, lane, wt, bi)) { abort_all(); return; }
       if (w == 0 && lane == 0 && step - 1 >= a.out_from) a.out_ids[step - 1 - a.out_from] = (int)bi;
       if (step >= a.n_feed) {
         // a step whose logits are all NaN names no row: the run stops with an error
@@ -1650,12 +1787,15 @@ __device__ __attribute__((always_inline)) void control_set(const DecodeArgs &a, 
       st(step, 5 * a.L, 2);
       float bv = -INFINITY;
       uint32_t bi = 0xffffffffu;
+      float vv[PSTRIDE / 64];  // this lane's logits (for sampling)
       // (a fixed trip count, so that the row results are read from LDS in one burst)
 #pragma unroll
       for (int k = 0; k < PSTRIDE / 64; k++) {
         const int r = lane + 64 * k;
+        vv[k] = 0.f;
         if (r < nr) {
           const float v = ln_row(part[r], mean, rstd, hg[k], hc[k]);
+          vv[k] = v;
           a.logits[hr0 + r] = v;
           if (v > bv || (v == bv && (uint32_t)(hr0 + r) < bi)) {
             bv = v;
@@ -1664,6 +1804,24 @@ __device__ __attribute__((always_inline)) void control_set(const DecodeArgs &a, 
         }
       }
       bi = wave_argmax(bv, bi, &bv);
+      if (a.inv_temp > 0.f && step >= a.out_from) {
+        // sampling: the sum of exp((logit - max)/T) over these rows, with the
+        // maximum (the argmax pair below), and the logits as tagged words
+        float ssum = 0.f;
+#pragma unroll
+        for (int k = 0; k < PSTRIDE / 64; k++) {
+          const int r = lane + 64 * k;
+          if (r < nr) {
+            if (vv[k] == vv[k] && bv > -INFINITY) ssum += __expf((vv[k] - bv) * a.inv_temp);
+            __hip_atomic_store(a.logit_t + hr0 + r, (uint64_t)__float_as_uint(vv[k]) | ((uint64_t)epH << 32),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+        ssum = wave_sum_all(ssum);
+        if (lane < NCOPY)
+          __hip_atomic_store(a.ssum_t + (size_t)lane * G + w, (uint64_t)__float_as_uint(ssum) | ((uint64_t)epH << 32),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       // (value, index) as one word pair per copy: lane c writes copy c
       if (lane < NCOPY) {
         const auto ars = __builtin_amdgcn_make_buffer_rsrc(a.amax_t, (short)0, NCOPY * 2 * G * 8, 0x00020000);
@@ -1680,7 +1838,7 @@ __device__ __attribute__((always_inline)) void control_set(const DecodeArgs &a, 
   if (w == 0) {
     uint32_t bi = 0;
     wt.start(5 * a.L);
-    if (!reduce_argmax<S>(a, epoch_of(a, a.nsteps - 1, 5 * a.L), lane, wt, bi)) return;
+    if (!choose_token<S, WD>(a, a.nsteps - 1, lane, wt, bi)) return;
     if (lane == 0 && a.nsteps - 1 >= a.out_from) a.out_ids[a.nsteps - 1 - a.out_from] = (int)bi;
   }
 }

@@ -44,8 +44,10 @@ struct gpt2_ctx {
   int *ids_h = nullptr, *err_h = nullptr, *ids_dev = nullptr, *err_dev = nullptr;
   int *feed_h = nullptr;
   float *logits_h = nullptr;
-  uint64_t *tag_bufs[7] = {};
-  size_t tag_sizes[7] = {};
+  static constexpr int kTagBufs = 9;
+  uint64_t *tag_bufs[kTagBufs] = {};
+  size_t tag_sizes[kTagBufs] = {};
+  float *draws_d = nullptr, *draws_h = nullptr;  // uniform numbers of a sampled run
   uint32_t epoch = 0;
   int filled = 0;
   bool poisoned = false;
@@ -149,15 +151,16 @@ int validate_config(const gpt2_config *c, ShapeInfo *si, std::string &msg) {
   return GPT2_OK;
 }
 
-// Launch `nsteps` forward passes; see gpt2_step / gpt2_generate.
+// Launch `nsteps` forward passes; see gpt2_step / gpt2_generate.  With
+// inv_temp > 0 the n_out recorded ids are drawn (draws[k] for the k-th).
 int run(gpt2_ctx *c, const int *feed, int n_feed, int pos0, int nsteps, int out_from, int n_out, int *ids_out,
-        float *logits_out) {
+        float *logits_out, float inv_temp = 0.f, const float *draws = nullptr) {
   hipError_t e = hipSetDevice(c->device);
   if (e != hipSuccess) return c->device_fail(e, "hipSetDevice");
   const uint64_t used = (uint64_t)nsteps * (uint64_t)(5 * c->L + 1);
   if ((uint64_t)c->epoch + used >= 0xffffff00ull) {
     // epochs would wrap: clear every tagged word (tag 0 is never expected) and restart
-    for (int i = 0; i < 7; i++) {
+    for (int i = 0; i < gpt2_ctx::kTagBufs; i++) {
       e = hipMemsetAsync(c->tag_bufs[i], 0, c->tag_sizes[i], c->stream);
       if (e != hipSuccess) return c->device_fail(e, "hipMemsetAsync");
     }
@@ -174,6 +177,12 @@ int run(gpt2_ctx *c, const int *feed, int n_feed, int pos0, int nsteps, int out_
     e = hipMemcpyAsync(c->feed_d, c->feed_h, sizeof(int) * (size_t)n_feed, hipMemcpyHostToDevice, c->stream);
     if (e != hipSuccess) return c->device_fail(e, "uploading the fed ids");
     a.feed = c->feed_d;
+  }
+  a.inv_temp = inv_temp;
+  if (inv_temp > 0.f) {
+    memcpy(c->draws_h, draws, sizeof(float) * (size_t)n_out);
+    e = hipMemcpyAsync(c->draws_d, c->draws_h, sizeof(float) * (size_t)n_out, hipMemcpyHostToDevice, c->stream);
+    if (e != hipSuccess) return c->device_fail(e, "uploading the draws");
   }
   // The kernel writes the ids and (on failure) the error word's copy straight
   // into mapped host memory: cleared here, read after the stream has drained.
@@ -291,7 +300,12 @@ int load_impl(gpt2_ctx *c, const gpt2_config *cfg, const gpt2_weights *w) {
   c->tag_sizes[4] = NC * L * E * 8;
   c->tag_sizes[5] = NC * 2 * G * 8;
   c->tag_sizes[6] = NC * L * E * 8;
-  for (int i = 0; i < 7; i++) c->tag_bufs[i] = c->dalloc<uint64_t>(c->tag_sizes[i]);
+  c->tag_sizes[7] = NC * G * 8;        // sampling: per-workgroup sums
+  c->tag_sizes[8] = (size_t)V * 8;     // sampling: tagged logits
+  for (int i = 0; i < gpt2_ctx::kTagBufs; i++) c->tag_bufs[i] = c->dalloc<uint64_t>(c->tag_sizes[i]);
+  c->draws_d = c->dalloc<float>((size_t)P * 4);
+  c->draws_h = c->halloc<float>((size_t)P * 4);
+  if (!c->draws_d || !c->draws_h) return c->fail(GPT2_E_NOMEM, "allocation failed");
   float *logits = c->dalloc<float>((size_t)V * 4);
   c->feed_d = c->dalloc<int>((size_t)P * 4);
   c->err_d = c->dalloc<int>(4 * 4);
@@ -309,7 +323,7 @@ int load_impl(gpt2_ctx *c, const gpt2_config *cfg, const gpt2_weights *w) {
   e = hipHostGetDevicePointer(reinterpret_cast<void **>(&c->ids_dev), c->ids_h, 0);
   if (e == hipSuccess) e = hipHostGetDevicePointer(reinterpret_cast<void **>(&c->err_dev), c->err_h, 0);
   if (e != hipSuccess) return c->device_fail(e, "mapping host buffers");
-  for (int i = 0; i < 7; i++)
+  for (int i = 0; i < gpt2_ctx::kTagBufs; i++)
     if (!c->tag_bufs[i]) return c->fail(GPT2_E_NOMEM, "allocation failed");
 
   // ---- small parameters
@@ -375,7 +389,8 @@ int load_impl(gpt2_ctx *c, const gpt2_config *cfg, const gpt2_weights *w) {
     e = fold_ln(head16 ? WD_F16 : WD_F32, MatW{head16 ? head16 : static_cast<const void *>(wte), nullptr}, 0, V,
                 E, lnfw, lnfb, nullptr, ghead, chead, s);
   if (e != hipSuccess) return c->device_fail(e, "folding the LayerNorms");
-  for (int i = 0; i < 7 && e == hipSuccess; i++) e = hipMemsetAsync(c->tag_bufs[i], 0, c->tag_sizes[i], s);
+  for (int i = 0; i < gpt2_ctx::kTagBufs && e == hipSuccess; i++)
+    e = hipMemsetAsync(c->tag_bufs[i], 0, c->tag_sizes[i], s);
   if (e == hipSuccess) e = hipMemsetAsync(c->err_d, 0, 4 * sizeof(int), s);
   if (e == hipSuccess) e = hipMemsetAsync(kc, 0, kv * 4, s);
   if (e == hipSuccess) e = hipMemsetAsync(vc, 0, kv * 4, s);
@@ -404,6 +419,10 @@ int load_impl(gpt2_ctx *c, const gpt2_config *cfg, const gpt2_weights *w) {
   a.xb_t = c->tag_bufs[4];
   a.amax_t = c->tag_bufs[5];
   a.attn_t = c->tag_bufs[6];
+  a.ssum_t = c->tag_bufs[7];
+  a.logit_t = c->tag_bufs[8];
+  a.inv_temp = 0.f;
+  a.draws = c->draws_d;
   a.logits = logits;
   a.out_ids = c->ids_dev;
   a.err = c->err_d;
@@ -501,6 +520,41 @@ int gpt2_generate(gpt2_ctx *c, const int *prompt, int n_prompt, int n_new, int *
     if (prompt[i] < 0 || prompt[i] >= c->V)
       return c->fail(GPT2_E_INVAL, "prompt[%d] = %d outside [0, %d)", i, prompt[i], c->V);
   rc = run(c, prompt, n_prompt, c->filled, (int)steps, n_prompt - 1, n_new, out_ids, nullptr);
+  if (rc != GPT2_OK) return rc;
+  c->filled += (int)steps;
+  return GPT2_OK;
+}
+
+int gpt2_generate_sample(gpt2_ctx *c, const int *prompt, int n_prompt, int n_new, float temperature,
+                         unsigned long long seed, int *out_ids) {
+  int rc;
+  if (!usable(c, &rc)) return rc;
+  if (!(temperature >= 0.0f) || !std::isfinite(temperature))
+    return c->fail(GPT2_E_INVAL, "temperature must be finite and >= 0");
+  if (temperature == 0.0f) return gpt2_generate(c, prompt, n_prompt, n_new, out_ids);
+  if (seed == 0) return c->fail(GPT2_E_INVAL, "seed must be non-zero (the xorshift64* state)");
+  if (!prompt || !out_ids) return c->fail(GPT2_E_INVAL, "prompt or out_ids is NULL");
+  if (n_prompt < 1 || n_new < 1) return c->fail(GPT2_E_INVAL, "n_prompt and n_new must be >= 1");
+  const long long steps = (long long)n_prompt + n_new - 1;
+  if ((long long)c->filled + steps > c->P)
+    return c->fail(GPT2_E_INVAL, "%lld steps from position %d exceed n_positions %d", steps, c->filled, c->P);
+  for (int i = 0; i < n_prompt; i++)
+    if (prompt[i] < 0 || prompt[i] >= c->V)
+      return c->fail(GPT2_E_INVAL, "prompt[%d] = %d outside [0, %d)", i, prompt[i], c->V);
+  const float inv_temp = 1.0f / temperature;
+  if (!std::isfinite(inv_temp)) return c->fail(GPT2_E_INVAL, "temperature %g is too small", (double)temperature);
+  // one uniform number per drawn id: the top 24 bits of an xorshift64* output
+  // (S. Vigna, ACM TOMS 42(4), 2016: shifts 12, 25, 27, multiplier
+  // 2685821657736338717) times 2^-24
+  std::vector<float> u((size_t)n_new);
+  uint64_t st = seed;
+  for (int k = 0; k < n_new; k++) {
+    st ^= st >> 12;
+    st ^= st << 25;
+    st ^= st >> 27;
+    u[(size_t)k] = (float)((st * 2685821657736338717ull) >> 40) * 0x1p-24f;
+  }
+  rc = run(c, prompt, n_prompt, c->filled, (int)steps, n_prompt - 1, n_new, out_ids, nullptr, inv_temp, u.data());
   if (rc != GPT2_OK) return rc;
   c->filled += (int)steps;
   return GPT2_OK;
