@@ -113,6 +113,18 @@ GPT2DEC_API int gpt2_step(gpt2_ctx *c, int token_id, int position, float *logits
  * filled += n_prompt + n_new - 1.  Errors as gpt2_step. */
 GPT2DEC_API int gpt2_generate(gpt2_ctx *c, const int *prompt, int n_prompt, int n_new, int *out_ids);
 
+/* gpt2_generate for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same ids and cache rows as gpt2_generate, but the kernel's working words
+ * (tagged activations, argmax slots, error word) live in a static device array
+ * of 16 MiB that the library holds on each GPU until the process ends; the call
+ * allocates nothing.  Every such call on a GPU shares that array: it clears the
+ * words it uses first, and calls that overlap on one GPU race.  A model whose
+ * working words exceed the array is GPT2_E_INVAL (the 124M shape needs about
+ * 7.6 MB).  Errors as gpt2_generate; GPT2_E_DEVICE if the array has no address
+ * on this device. */
+GPT2DEC_API int gpt2_generate_noalloc(gpt2_ctx *c, const int *prompt, int n_prompt, int n_new, int *out_ids);
+
 /* Generation with sampling ("Let's make GPT-2 in assembly", Step 7: divide the
  * scores by a temperature, apply softmax, draw at random; gpt2.s docs, "-t"),
  * chained on the device like gpt2_generate.  Each new id is the first id whose

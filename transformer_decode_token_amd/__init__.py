@@ -21,7 +21,8 @@ ERROR_NAMES = {GPT2_E_INVAL: "GPT2_E_INVAL", GPT2_E_NOMEM: "GPT2_E_NOMEM",
                GPT2_E_NUMERIC: "GPT2_E_NUMERIC"}
 
 # the symbols include/gpt2dec.h declares
-ABI_FUNCTIONS = ("gpt2_load", "gpt2_set_stream", "gpt2_step", "gpt2_generate", "gpt2_generate_sample",
+ABI_FUNCTIONS = ("gpt2_load", "gpt2_set_stream", "gpt2_step", "gpt2_generate", "gpt2_generate_noalloc",
+                 "gpt2_generate_sample",
                  "gpt2_reset",
                  "gpt2_free", "gpt2_last_error", "gpt2_filled", "gpt2_debug_dequant",
                  "gpt2_debug_fill_kv", "gpt2_debug_geometry", "gpt2_debug_trace")
@@ -64,6 +65,7 @@ def lib():
         L.gpt2_set_stream.argtypes = [C.c_void_p, C.c_void_p]
         L.gpt2_step.argtypes = [C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.POINTER(C.c_int)]
         L.gpt2_generate.argtypes = [C.c_void_p, C.POINTER(C.c_int), C.c_int, C.c_int, C.POINTER(C.c_int)]
+        L.gpt2_generate_noalloc.argtypes = [C.c_void_p, C.POINTER(C.c_int), C.c_int, C.c_int, C.POINTER(C.c_int)]
         L.gpt2_generate_sample.argtypes = [C.c_void_p, C.POINTER(C.c_int), C.c_int, C.c_int, C.c_float,
                                            C.c_ulonglong, C.POINTER(C.c_int)]
         L.gpt2_reset.argtypes = [C.c_void_p]
@@ -158,6 +160,15 @@ def gpt2_generate(ctx, prompt, n_new):
     out = np.empty(int(n_new), np.int32)
     rc = lib().gpt2_generate(ctx.handle, p.ctypes.data_as(C.POINTER(C.c_int)), p.size, int(n_new),
                              out.ctypes.data_as(C.POINTER(C.c_int)))
+    _check(rc, ctx.handle)
+    return out
+
+
+def gpt2_generate_noalloc(ctx, prompt, n_new):
+    p = np.ascontiguousarray(prompt, np.int32)
+    out = np.empty(int(n_new), np.int32)
+    rc = lib().gpt2_generate_noalloc(ctx.handle, p.ctypes.data_as(C.POINTER(C.c_int)), p.size, int(n_new),
+                                     out.ctypes.data_as(C.POINTER(C.c_int)))
     _check(rc, ctx.handle)
     return out
 

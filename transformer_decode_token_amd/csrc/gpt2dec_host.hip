@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -19,8 +20,41 @@
 
 using namespace gpt2dec;
 
+// Working words of gpt2_generate_noalloc, for callers that cannot allocate
+// device memory: the tagged activation words, argmax and sampling slots and
+// the error word of one run live here instead of in the context's buffers.
+// Each GPU the library runs on holds its own copy until the process ends;
+// every no-allocation call on a GPU shares it (calls that overlap on one GPU
+// race).  Host code takes its address per device from hipGetSymbolAddress
+// (the array's name in host code is not a device address).
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) uint64_t scratch[kScratchBytes / 8];
+
 namespace {
 thread_local std::string g_load_error;
+
+// The scratch array's address on each device, taken once per device with that
+// device current (nullptr until then, or if the runtime refused).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+bool g_scratch_done[kMaxDevices] = {};
+uint64_t *g_scratch_ptr[kMaxDevices] = {};
+
+uint64_t *scratch_on(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_done[device]) {
+    g_scratch_done[device] = true;
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess) {
+      g_scratch_ptr[device] = static_cast<uint64_t *>(ptr);
+    } else {
+      (void)hipGetLastError();
+      g_scratch_ptr[device] = nullptr;
+    }
+  }
+  return g_scratch_ptr[device];
+}
 
 size_t wd_bytes(int wd, size_t elems) {
   if (wd == WD_F32) return elems * 4;
@@ -48,6 +82,11 @@ struct gpt2_ctx {
   uint64_t *tag_bufs[kTagBufs] = {};
   size_t tag_sizes[kTagBufs] = {};
   float *draws_d = nullptr, *draws_h = nullptr;  // uniform numbers of a sampled run
+  // the no-allocation path: this device's static scratch, the word offsets of
+  // the error word and of each tagged buffer in it, and the words one run needs
+  uint64_t *scratch = nullptr;
+  size_t scratch_off[kTagBufs] = {};
+  size_t scratch_words = 0;
   uint32_t epoch = 0;
   int filled = 0;
   bool poisoned = false;
@@ -153,12 +192,14 @@ int validate_config(const gpt2_config *c, ShapeInfo *si, std::string &msg) {
 
 // Launch `nsteps` forward passes; see gpt2_step / gpt2_generate.  With
 // inv_temp > 0 the n_out recorded ids are drawn (draws[k] for the k-th).
+// With in_scratch the run's working words are the device's static scratch,
+// cleared first (its epochs restart at 1), and nothing is allocated.
 int run(gpt2_ctx *c, const int *feed, int n_feed, int pos0, int nsteps, int out_from, int n_out, int *ids_out,
-        float *logits_out, float inv_temp = 0.f, const float *draws = nullptr) {
+        float *logits_out, float inv_temp = 0.f, const float *draws = nullptr, bool in_scratch = false) {
   hipError_t e = hipSetDevice(c->device);
   if (e != hipSuccess) return c->device_fail(e, "hipSetDevice");
   const uint64_t used = (uint64_t)nsteps * (uint64_t)(5 * c->L + 1);
-  if ((uint64_t)c->epoch + used >= 0xffffff00ull) {
+  if (!in_scratch && (uint64_t)c->epoch + used >= 0xffffff00ull) {
     // epochs would wrap: clear every tagged word (tag 0 is never expected) and restart
     for (int i = 0; i < gpt2_ctx::kTagBufs; i++) {
       e = hipMemsetAsync(c->tag_bufs[i], 0, c->tag_sizes[i], c->stream);
@@ -196,12 +237,32 @@ int run(gpt2_ctx *c, const int *feed, int n_feed, int pos0, int nsteps, int out_
   a.timeout_ticks = c->timeout_ticks;
   a.trace = c->trace_d;
   a.trace_steps = c->trace_d ? c->trace_steps : 0;
-  if (c->trace_d) {
+  if (in_scratch) {
+    // the scratch keeps whatever the last call on this device left: clear the
+    // words this run uses (a fill kernel), then number its phases from 1
+    uint64_t *sc = c->scratch;
+    e = fill_f32(reinterpret_cast<float *>(sc), 2 * c->scratch_words, 0.0f, c->stream);
+    if (e != hipSuccess) return c->device_fail(e, "clearing the scratch");
+    a.err = reinterpret_cast<int *>(sc);
+    a.qkv_t = sc + c->scratch_off[0];
+    a.att_t = sc + c->scratch_off[1];
+    a.xa_t = sc + c->scratch_off[2];
+    a.act_t = sc + c->scratch_off[3];
+    a.xb_t = sc + c->scratch_off[4];
+    a.amax_t = sc + c->scratch_off[5];
+    a.attn_t = sc + c->scratch_off[6];
+    a.ssum_t = sc + c->scratch_off[7];
+    a.logit_t = sc + c->scratch_off[8];
+    a.epoch0 = 0;
+    a.trace = nullptr;
+    a.trace_steps = 0;
+  }
+  if (a.trace) {
     e = hipMemsetAsync(c->trace_d, 0, (size_t)c->trace_steps * (5 * c->L + 1) * c->si.G * 4 * 8, c->stream);
     if (e != hipSuccess) return c->device_fail(e, "trace reset");
   }
   e = launch_decode(c->E, c->D, c->wd, a, c->stream);
-  c->epoch += (uint32_t)used;
+  if (!in_scratch) c->epoch += (uint32_t)used;
   if (e != hipSuccess) return c->device_fail(e, "decode launch");
   if (logits_out)
     e = hipMemcpyAsync(c->logits_h, c->base.logits, sizeof(float) * (size_t)c->V, hipMemcpyDeviceToHost,
@@ -303,6 +364,16 @@ int load_impl(gpt2_ctx *c, const gpt2_config *cfg, const gpt2_weights *w) {
   c->tag_sizes[7] = NC * G * 8;        // sampling: per-workgroup sums
   c->tag_sizes[8] = (size_t)V * 8;     // sampling: tagged logits
   for (int i = 0; i < gpt2_ctx::kTagBufs; i++) c->tag_bufs[i] = c->dalloc<uint64_t>(c->tag_sizes[i]);
+  // the same words' layout in the static scratch: the error word, then each
+  // tagged buffer at a 256-byte boundary
+  {
+    size_t off = 32;
+    for (int i = 0; i < gpt2_ctx::kTagBufs; i++) {
+      c->scratch_off[i] = off;
+      off += (c->tag_sizes[i] / 8 + 31) & ~(size_t)31;
+    }
+    c->scratch_words = off;
+  }
   c->draws_d = c->dalloc<float>((size_t)P * 4);
   c->draws_h = c->halloc<float>((size_t)P * 4);
   if (!c->draws_d || !c->draws_h) return c->fail(GPT2_E_NOMEM, "allocation failed");
@@ -425,6 +496,8 @@ int load_impl(gpt2_ctx *c, const gpt2_config *cfg, const gpt2_weights *w) {
   a.draws = c->draws_d;
   a.logits = logits;
   a.out_ids = c->ids_dev;
+  // this device's static scratch, for gpt2_generate_noalloc
+  c->scratch = scratch_on(c->device);
   a.err = c->err_d;
   a.err_host = c->err_dev;
   a.L = L; a.V = V; a.P = P;
@@ -520,6 +593,27 @@ int gpt2_generate(gpt2_ctx *c, const int *prompt, int n_prompt, int n_new, int *
     if (prompt[i] < 0 || prompt[i] >= c->V)
       return c->fail(GPT2_E_INVAL, "prompt[%d] = %d outside [0, %d)", i, prompt[i], c->V);
   rc = run(c, prompt, n_prompt, c->filled, (int)steps, n_prompt - 1, n_new, out_ids, nullptr);
+  if (rc != GPT2_OK) return rc;
+  c->filled += (int)steps;
+  return GPT2_OK;
+}
+
+int gpt2_generate_noalloc(gpt2_ctx *c, const int *prompt, int n_prompt, int n_new, int *out_ids) {
+  int rc;
+  if (!usable(c, &rc)) return rc;
+  if (!prompt || !out_ids) return c->fail(GPT2_E_INVAL, "prompt or out_ids is NULL");
+  if (n_prompt < 1 || n_new < 1) return c->fail(GPT2_E_INVAL, "n_prompt and n_new must be >= 1");
+  if (c->scratch_words * 8 > kScratchBytes)
+    return c->fail(GPT2_E_INVAL, "this model's working words need %zu bytes; the static scratch holds %zu",
+                   c->scratch_words * 8, kScratchBytes);
+  if (!c->scratch) return c->fail(GPT2_E_DEVICE, "the static scratch has no address on this device");
+  const long long steps = (long long)n_prompt + n_new - 1;
+  if ((long long)c->filled + steps > c->P)
+    return c->fail(GPT2_E_INVAL, "%lld steps from position %d exceed n_positions %d", steps, c->filled, c->P);
+  for (int i = 0; i < n_prompt; i++)
+    if (prompt[i] < 0 || prompt[i] >= c->V)
+      return c->fail(GPT2_E_INVAL, "prompt[%d] = %d outside [0, %d)", i, prompt[i], c->V);
+  rc = run(c, prompt, n_prompt, c->filled, (int)steps, n_prompt - 1, n_new, out_ids, nullptr, 0.f, nullptr, true);
   if (rc != GPT2_OK) return rc;
   c->filled += (int)steps;
   return GPT2_OK;
