@@ -6,7 +6,12 @@ the device by gpt2_generate).  `value` is forward passes (decoded tokens) per
 second over the timed steps, with weights and prompt already resident on the
 GPU.  Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--config 2..5] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--config 2..5] [--only] [--no-cpu-baseline]
+
+The headline workload (--config, default 2) gives the line's value and roofline;
+the other three 124M workloads are timed in the same run, each in
+"other_configs" with its own value, per-pass time and roofline (--only skips
+them).
 """
 import argparse
 import hashlib
@@ -63,7 +68,7 @@ def load_traffic(cfg_key):
     e = d.get(str(cfg_key))
     if not e or e.get("kernel_hash") != kernel_source_hash():
         return None
-    return e.get("bytes_per_launch")
+    return e
 
 
 def cpu_baseline(cfg, seconds=10.0):
@@ -94,12 +99,97 @@ def cpu_baseline(cfg, seconds=10.0):
                       f"repeated ({runs} started), {dt:.1f} s, one thread"}
 
 
+def time_config(cfg, steps, warmup, sync_steps, torch, g2):
+    """Load one workload, time `steps` device-chained greedy runs of it (HIP
+    events on the library's stream, and the host clock around the loop), and the
+    synchronous one-token call.  Returns a dict of measurements."""
+    import synth
+    model = synth.make_model(cfg)
+    prompt = synth.make_prompt(cfg)
+    ctx = g2.gpt2_load(cfg.n_layer, cfg.n_embd, cfg.n_head, cfg.n_positions, cfg.vocab, model.t,
+                       wdtype=cfg.wdtype, ln_eps=cfg.ln_eps, q4_group=cfg.q4_group)
+    del model
+    stream = torch.cuda.current_stream()
+    g2.gpt2_set_stream(ctx, stream.cuda_stream)
+    for _ in range(warmup):
+        g2.gpt2_reset(ctx)
+        g2.gpt2_generate(ctx, prompt, cfg.n_new)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    # torch creates an event at its first record: do that outside the timed loop
+    for ev in starts + ends:
+        ev.record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        g2.gpt2_reset(ctx)
+        starts[i].record(stream)
+        g2.gpt2_generate(ctx, prompt, cfg.n_new)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_launch = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)]))
+    # synchronous one-token calls (host round trip per token)
+    g2.gpt2_reset(ctx)
+    torch.cuda.synchronize()
+    ns = min(sync_steps, cfg.n_steps)
+    ts = time.perf_counter()
+    for pos in range(ns):
+        g2.gpt2_step(ctx, int(prompt[pos % len(prompt)]), pos, want_logits=False)
+    sync_tok_s = ns / (time.perf_counter() - ts) if ns else None
+    ctx.close()
+    torch.cuda.synchronize()
+    return {"wall_s": wall, "ms_launch": ms_launch, "sync_tok_s": sync_tok_s}
+
+
+def roofline(cfg, ms_launch):
+    """HBM roofline of the decode kernel for one launch of the workload:
+    algorithmic bytes (every weight once per pass + the K/V rows read) per event-
+    timed launch, and the rocprofv3-counted DRAM-side bytes when they were taken
+    for this kernel source."""
+    alg_bytes = sum(bytes_per_step(cfg, p) for p in range(cfg.n_steps))
+    achieved = alg_bytes / (ms_launch * 1e-3) / 1e9
+    tr = load_traffic(cfg.key)
+    out = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": tr["bytes_per_launch"] if tr else None}
+    if tr:
+        # the same launch's bytes fetched from the memory side (FETCH_SIZE, calibrated),
+        # which for fp16/int4 include memory-side-cache hits
+        out["dram_read_bytes"] = tr["fetch_bytes"]
+        out["dram_read_frac"] = round(tr["fetch_bytes"] / (ms_launch * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        out["dram_read_over_algorithmic"] = round(tr["fetch_bytes"] / alg_bytes, 3)
+    return out, alg_bytes
+
+
+def config_line(cfg, m):
+    """The per-workload figures of one time_config result."""
+    rf, alg = roofline(cfg, m["ms_launch"])
+    return {
+        "workload": workload_name(cfg),
+        "value": round(cfg.n_steps * m["steps"] / m["wall_s"], 2),
+        "unit": "tok/s",
+        "ms_per_step": round(m["wall_s"] * 1e3 / m["steps"], 4),
+        "decode_kernel_ms_per_launch": round(m["ms_launch"], 4),
+        "us_per_token": round(m["ms_launch"] * 1e3 / cfg.n_steps, 2),
+        "algorithmic_bytes_per_launch": alg,
+        "roofline": rf,
+        "sync_step_tok_per_s": round(m["sync_tok_s"], 1) if m["sync_tok_s"] else None,
+    }
+
+
+def workload_name(cfg):
+    return (f"{cfg.name}: {cfg.n_prompt} prompt ids + {cfg.n_new} greedy ids = {cfg.n_steps} one-token "
+            f"forward passes, batch 1")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--config", type=int, default=2, help="the headline workload (2..5)")
+    ap.add_argument("--only", action="store_true",
+                    help="time the headline workload alone (no per-config lines for the others)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sync-steps", type=int, default=30,
                     help="gpt2_step calls timed for the synchronous per-token rate")
@@ -126,85 +216,48 @@ def main():
     import synth
     import transformer_decode_token_amd as g2
 
-    cfg = synth.CONFIGS[args.config]
-    print(f"[bench] config {cfg.key} {cfg.name}: generating weights", file=sys.stderr, flush=True)
-    model = synth.make_model(cfg)
-    prompt = synth.make_prompt(cfg)
     torch.cuda.init()
-    ctx = g2.gpt2_load(cfg.n_layer, cfg.n_embd, cfg.n_head, cfg.n_positions, cfg.vocab, model.t,
-                       wdtype=cfg.wdtype, ln_eps=cfg.ln_eps, q4_group=cfg.q4_group)
-    stream = torch.cuda.current_stream()
-    g2.gpt2_set_stream(ctx, stream.cuda_stream)
-    print("[bench] loaded; warming up", file=sys.stderr, flush=True)
-
-    def run():
-        g2.gpt2_reset(ctx)
-        return g2.gpt2_generate(ctx, prompt, cfg.n_new)
-
-    for _ in range(args.warmup):
-        run()
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    # torch creates an event at its first record: do that outside the timed loop
-    for ev in starts + ends:
-        ev.record(stream)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        g2.gpt2_reset(ctx)
-        starts[i].record(stream)
-        g2.gpt2_generate(ctx, prompt, cfg.n_new)
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    ms_launch = float(np.mean(launch_ms))
-    ms_per_step = wall * 1e3 / args.steps
-    tok_per_s = cfg.n_steps * args.steps / wall
-
-    # synchronous one-token calls (host round trip per token)
-    g2.gpt2_reset(ctx)
-    torch.cuda.synchronize()
-    ts = time.perf_counter()
-    ns = min(args.sync_steps, cfg.n_steps)
-    for pos in range(ns):
-        g2.gpt2_step(ctx, int(prompt[pos % len(prompt)]), pos, want_logits=False)
-    sync_tok_s = ns / (time.perf_counter() - ts)
-
-    alg_bytes = sum(bytes_per_step(cfg, p) for p in range(cfg.n_steps))
-    achieved = alg_bytes / (ms_launch * 1e-3) / 1e9
-    traffic = load_traffic(cfg.key)
+    head_cfg = synth.CONFIGS[args.config]
+    others = [] if args.only else [k for k in (2, 3, 4, 5) if k != args.config]
+    results = {}
+    for k in [args.config] + others:
+        cfg = synth.CONFIGS[k]
+        print(f"[bench] config {k} {cfg.name}: {args.warmup} warm-up + {args.steps} timed runs of "
+              f"{cfg.n_steps} passes", file=sys.stderr, flush=True)
+        m = time_config(cfg, args.steps, args.warmup, args.sync_steps, torch, g2)
+        m["steps"] = args.steps
+        results[k] = config_line(cfg, m)
+        print(f"[bench] config {k}: {results[k]['us_per_token']} us per pass, "
+              f"{results[k]['roofline']['frac']} of the HBM peak", file=sys.stderr, flush=True)
+    h = results[args.config]
     out = {
         "metric": "batch-1 decode tok/s GPT-2 124M fp32/fp16/int4; achieved HBM GB/s vs peak",
-        "value": round(tok_per_s, 2),
+        "value": h["value"],
         "unit": "tok/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": h["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"fp32": "f32", "fp16": "f16 weights, f32 math", "int4": "u4 weights, f32 math"}[cfg.wdtype],
+        "dtype": {"fp32": "f32", "fp16": "f16 weights, f32 math", "int4": "u4 weights, f32 math"}[head_cfg.wdtype],
         "data": "synthetic (seeded random weights of the GPT-2 124M shape; seeded prompt ids)",
-        "config": {"workload": f"{cfg.name}: {cfg.n_prompt} prompt ids + {cfg.n_new} greedy ids = "
-                               f"{cfg.n_steps} one-token forward passes, batch 1",
-                   "n_layer": cfg.n_layer, "n_embd": cfg.n_embd, "n_head": cfg.n_head,
-                   "vocab": cfg.vocab, "weights": cfg.wdtype, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
-        "decode_kernel_ms_per_launch": round(ms_launch, 4),
-        "us_per_token": round(ms_launch * 1e3 / cfg.n_steps, 2),
-        "algorithmic_bytes_per_launch": alg_bytes,
-        "generated_tok_per_s": round(cfg.n_new * args.steps / wall, 2),
-        "sync_step_tok_per_s": round(sync_tok_s, 1),
+        "config": {"workload": h["workload"],
+                   "n_layer": head_cfg.n_layer, "n_embd": head_cfg.n_embd, "n_head": head_cfg.n_head,
+                   "vocab": head_cfg.vocab, "weights": head_cfg.wdtype, "parallelism": "single GPU"},
+        "roofline": h["roofline"],
+        "roofline_note": "frac = algorithmic bytes (each weight once per pass + K/V rows read) over the "
+                         "event-timed launch; dram_read_frac = the counted FETCH_SIZE bytes over the same time",
+        "decode_kernel_ms_per_launch": h["decode_kernel_ms_per_launch"],
+        "us_per_token": h["us_per_token"],
+        "algorithmic_bytes_per_launch": h["algorithmic_bytes_per_launch"],
+        "sync_step_tok_per_s": h["sync_step_tok_per_s"],
+        "other_configs": {str(k): results[k] for k in others},
     }
-    ctx.close()
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(cfg)
+        out["cpu_baseline"] = cpu_baseline(head_cfg)
     print(json.dumps(out), flush=True)
 
 
