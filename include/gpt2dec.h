@@ -91,6 +91,24 @@ typedef struct gpt2_ctx gpt2_ctx;
  * Errors: GPT2_E_INVAL (bad cfg / null pointer), GPT2_E_NOMEM, GPT2_E_DEVICE. */
 GPT2DEC_API int gpt2_load(const gpt2_config *cfg, const gpt2_weights *w, gpt2_ctx **out);
 
+/* gpt2_load from the files Hugging Face publishes, as they are ("Let's make
+ * GPT-2 in assembly", Step 1; gpt2.s docs, "Inner Workings"): the mapped
+ * safetensors file's 148 tensors found by name in its JSON header (with or
+ * without a "transformer." prefix; F32, the shapes the model file declares),
+ * and config.json checked as the gpt2-125m model file's "require config" lines
+ * do (model_type gpt2, activation_function gelu_new, scale_attn_weights true,
+ * scale_attn_by_inverse_layer_idx, reorder_and_upcast_attn and
+ * add_cross_attention false, each passing when absent; n_embd a multiple of
+ * n_head; n_inner null or 4 * n_embd; layer_norm_epsilon 1e-5 when absent).
+ * wdtype as gpt2_config; int4 groups of 32.  Every file and configuration check
+ * runs before any device work: a rejected call is GPT2_E_INVAL with the reason
+ * in gpt2_last_error(NULL).  Otherwise errors as gpt2_load. */
+GPT2DEC_API int gpt2_load_safetensors(const char *safetensors_path, const char *config_path, int wdtype,
+                                      gpt2_ctx **out);
+
+/* The configuration c was loaded with. */
+GPT2DEC_API int gpt2_get_config(const gpt2_ctx *c, gpt2_config *out);
+
 /* Run later work on `hip_stream` (a hipStream_t, e.g. torch's current stream;
  * NULL = the library's own stream).  The stream must outlive its use. */
 GPT2DEC_API int gpt2_set_stream(gpt2_ctx *c, void *hip_stream);
@@ -153,6 +171,37 @@ GPT2DEC_API const char *gpt2_last_error(const gpt2_ctx *c);
 
 /* Number of filled positions (the next appending position). -1 if c is NULL. */
 GPT2DEC_API int gpt2_filled(const gpt2_ctx *c);
+
+/* ---- byte-level BPE tokenizer ("Let's make GPT-2 in assembly", Step 3;
+ * gpt2.s docs, "File Contents" and "Limitations") ------------------------- */
+typedef struct gpt2_tokenizer gpt2_tokenizer;
+
+/* Read vocab.json (token strings in GPT-2's byte-level alphabet -> ids) and
+ * merges.txt (pairs in rank order after a "#version" line), as published.
+ * Every byte must have a token; every merge's parts and result must be tokens.
+ * GPT2_E_INVAL with the reason in gpt2_last_error(NULL); GPT2_E_NOMEM. */
+GPT2DEC_API int gpt2_tokenizer_load(const char *vocab_json_path, const char *merges_txt_path,
+                                    gpt2_tokenizer **out);
+
+/* Token ids of len bytes of text: the text is cut into chunks (an ending 's,
+ * 't, 're, 've, 'm, 'll or 'd; a run of letters, digits or other symbols with
+ * one optional space in front; a whitespace run, leaving its last character to
+ * a non-space after it), and each chunk's bytes join pairwise, the lowest-
+ * ranked neighbouring pair first, until no pair has a rank.  Every byte above
+ * 127 counts as a letter (exact for ASCII text, as the gpt2.s docs say of
+ * theirs).  *n_ids receives the count; ids holds cap ids (ids may be NULL with
+ * cap 0 to ask for the count).  GPT2_E_INVAL if cap is too small (the first
+ * cap ids are written) or on a bad argument. */
+GPT2DEC_API int gpt2_tokenize(const gpt2_tokenizer *t, const char *text, size_t len, int *ids, int cap,
+                              int *n_ids);
+
+/* The bytes of n ids, concatenated.  *len receives their count; buf holds cap
+ * bytes (NULL with cap 0 to ask).  GPT2_E_INVAL for an id without a token or a
+ * too small buffer (nothing written). */
+GPT2DEC_API int gpt2_detokenize(const gpt2_tokenizer *t, const int *ids, int n, char *buf, size_t cap,
+                                size_t *len);
+
+GPT2DEC_API void gpt2_tokenizer_free(gpt2_tokenizer *t);
 
 /* ---- test hooks (not needed for decoding) ------------------------------ */
 

@@ -150,3 +150,51 @@ def make_prompt(cfg) -> np.ndarray:
 
 def variant(cfg: Config, **kw) -> Config:
     return replace(cfg, **kw)
+
+
+# ---------------------------------------------------------------- tokenizer
+def synthetic_text(seed: int, n_words: int = 20000) -> str:
+    """Seeded English-like text for training and exercising a byte-level BPE:
+    pseudo-words from a Zipf-weighted lexicon, some capitalised or with an
+    ending such as 's, 't, 're, 've, 'm, 'll or 'd, numbers, punctuation, and
+    spaces, runs of spaces, tabs and newlines between them."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    letters = np.array(list("etaoinshrdlcumwfgypbvkjxqz"))
+    freq = np.array([12.7, 9.1, 8.2, 7.5, 7.0, 6.7, 6.3, 6.1, 6.0, 4.3, 4.0, 2.8, 2.8, 2.4, 2.4, 2.2, 2.0,
+                     2.0, 1.9, 1.5, 1.0, 0.8, 0.15, 0.15, 0.1, 0.07])
+    freq = freq / freq.sum()
+    lexicon = ["".join(rng.choice(letters, size=int(rng.integers(1, 9)), p=freq)) for _ in range(3000)]
+    zipf = 1.0 / np.arange(1, len(lexicon) + 1)
+    zipf /= zipf.sum()
+    endings = ["'s", "'t", "'re", "'ve", "'m", "'ll", "'d"]
+    puncts = [".", ",", "!", "?", ";", ":", "-", "(", ")", "\"", "...", "--", "'", "@", "#", "$", "%", "&", "*"]
+    seps = [" "] * 40 + ["  ", "   ", "\n", "\n\n", "\t", " \n", "\t\t", "\r\n"]
+    out = []
+    for _ in range(n_words):
+        r = rng.random()
+        if r < 0.06:
+            out.append(str(int(rng.integers(0, 10 ** int(rng.integers(1, 6))))))
+        elif r < 0.12:
+            out.append(puncts[int(rng.integers(len(puncts)))])
+        else:
+            w = lexicon[int(rng.choice(len(lexicon), p=zipf))]
+            if rng.random() < 0.1:
+                w = w.capitalize()
+            if rng.random() < 0.05:
+                w += endings[int(rng.integers(len(endings)))]
+            out.append(w)
+        out.append(seps[int(rng.integers(len(seps)))])
+    return "".join(out)
+
+
+def make_bpe_files(folder: str, seed: int = 3001, vocab_size: int = 2000):
+    """vocab.json and merges.txt in GPT-2's format for a byte-level BPE trained
+    by the tokenizers package on synthetic_text(seed) (the published GPT-2 files
+    are not available).  Returns their paths."""
+    import os
+    from tokenizers import ByteLevelBPETokenizer
+    os.makedirs(folder, exist_ok=True)
+    tok = ByteLevelBPETokenizer()
+    tok.train_from_iterator([synthetic_text(seed)], vocab_size=vocab_size, min_frequency=2, show_progress=False)
+    tok.save_model(folder)
+    return os.path.join(folder, "vocab.json"), os.path.join(folder, "merges.txt")

@@ -581,3 +581,35 @@ def test_sampling_argument_errors():
         assert e.value.code == g2.GPT2_E_INVAL
     assert g2.gpt2_filled(ctx) == 0
     ctx.close()
+
+
+# ------------------------------------------------------- published file formats
+@pytest.mark.parametrize("name,prefix", [("tiny-rich", ""), ("tiny-rich-int4", "transformer."),
+                                         ("gpt2-124m-fp32", "")])
+def test_load_from_published_files(name, prefix, tmp_path):
+    """gpt2_load_safetensors on the files written by the safetensors package
+    (148 tensors for the 124M shape, optionally under the transformer. prefix)
+    with their config.json: the configuration read back, the stored weights and
+    every logit of a prompt bit for bit those of the same model loaded from the
+    arrays."""
+    from tests.hf_writer import write_model
+    cfg = CASES[name]
+    model = synth.make_model(cfg)
+    st, cj = write_model(model, str(tmp_path), prefix=prefix)
+    a = load_gpu(model)
+    b = g2.gpt2_load_safetensors(st, cj, cfg.wdtype)
+    c = g2.gpt2_get_config(b)
+    assert (c.n_layer, c.n_embd, c.n_head, c.n_positions, c.vocab_size) == \
+        (cfg.n_layer, cfg.n_embd, cfg.n_head, cfg.n_positions, cfg.vocab)
+    assert c.ln_eps == np.float32(cfg.ln_eps)
+    for l in (0, cfg.n_layer - 1):
+        for which in range(4):
+            assert np.array_equal(g2.gpt2_debug_dequant(a, l, which).view(np.uint32),
+                                  g2.gpt2_debug_dequant(b, l, which).view(np.uint32)), (l, which)
+    assert np.array_equal(g2.gpt2_debug_dequant(a, 0, 4), g2.gpt2_debug_dequant(b, 0, 4))
+    for pos, tok in enumerate(synth.make_prompt(cfg)):
+        _, la = g2.gpt2_step(a, int(tok), pos)
+        _, lb = g2.gpt2_step(b, int(tok), pos)
+        assert np.array_equal(la, lb), pos
+    a.close()
+    b.close()

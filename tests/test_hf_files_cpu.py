@@ -1,0 +1,108 @@
+"""gpt2_load_safetensors on a machine without a GPU: the published file formats
+are parsed and every check runs before any device work, so a valid pair of
+files reaches the device step (GPT2_E_DEVICE here, no CPU fallback) and each
+malformed file or configuration is GPT2_E_INVAL with its reason."""
+import json
+import os
+import struct
+
+import numpy as np
+import pytest
+
+import synth
+import transformer_decode_token_amd as g2
+from tests.hf_writer import write_model
+
+
+def _no_gpu():
+    try:
+        import torch
+        return not torch.cuda.is_available()
+    except Exception:
+        return True
+
+
+pytestmark = pytest.mark.skipif(not _no_gpu(), reason="checks the validation that precedes device work")
+
+
+@pytest.fixture(scope="module")
+def model():
+    return synth.make_model(synth.variant(synth.CONFIGS[1], init="small", weight_seed=1101, name="tiny-rich"))
+
+
+def load(st, cj, wdtype="fp32"):
+    with pytest.raises(g2.Gpt2Error) as e:
+        g2.gpt2_load_safetensors(st, cj, wdtype)
+    return e.value.code, g2.gpt2_last_error()
+
+
+@pytest.mark.parametrize("prefix", ["", "transformer."])
+def test_valid_files_reach_the_device_step(model, tmp_path, prefix):
+    st, cj = write_model(model, str(tmp_path), prefix=prefix)
+    code, msg = load(st, cj)
+    assert code == g2.GPT2_E_DEVICE and "device" in msg.lower()
+    # absent configuration keys pass (the model file's rule)
+    st, cj = write_model(model, str(tmp_path / "b"), config_overrides={
+        "model_type": ..., "activation_function": ..., "scale_attn_weights": ..., "n_inner": ...,
+        "layer_norm_epsilon": ..., "reorder_and_upcast_attn": ..., "add_cross_attention": ...})
+    assert load(st, cj)[0] == g2.GPT2_E_DEVICE
+
+
+@pytest.mark.parametrize("override,needle", [
+    ({"model_type": "gpt_neo"}, "model_type"),
+    ({"activation_function": "gelu"}, "activation_function"),
+    ({"scale_attn_weights": False}, "scale_attn_weights"),
+    ({"scale_attn_by_inverse_layer_idx": True}, "scale_attn_by_inverse_layer_idx"),
+    ({"reorder_and_upcast_attn": True}, "reorder_and_upcast_attn"),
+    ({"add_cross_attention": True}, "add_cross_attention"),
+    ({"n_head": 3}, "n_head"),
+    ({"n_inner": 1000}, "n_inner"),
+    ({"n_layer": ...}, "n_layer"),
+    ({"vocab_size": 2.5}, "vocab_size"),
+    ({"layer_norm_epsilon": -1}, "layer_norm_epsilon"),
+])
+def test_config_checks(model, tmp_path, override, needle):
+    st, cj = write_model(model, str(tmp_path), config_overrides=override)
+    code, msg = load(st, cj)
+    assert code == g2.GPT2_E_INVAL and needle in msg, msg
+
+
+def test_tensor_checks(model, tmp_path):
+    cases = [
+        (dict(drop={"h.1.mlp.c_fc.bias"}), "h.1.mlp.c_fc.bias is missing"),
+        (dict(replace={"h.0.attn.c_attn.weight": model.t["h.0.attn.c_attn.weight"].T.copy()}), "wrong shape"),
+        (dict(replace={"wpe.weight": model.t["wpe.weight"][:, None, :].copy()}), "wrong rank"),
+        (dict(replace={"ln_f.bias": model.t["ln_f.bias"].astype(np.float16)}), "not F32"),
+    ]
+    for i, (kw, needle) in enumerate(cases):
+        st, cj = write_model(model, str(tmp_path / str(i)), **kw)
+        code, msg = load(st, cj)
+        assert code == g2.GPT2_E_INVAL and needle in msg, msg
+
+
+def test_malformed_files(model, tmp_path):
+    st, cj = write_model(model, str(tmp_path))
+    raw = open(st, "rb").read()
+    n = struct.unpack("<Q", raw[:8])[0]
+    bad = {
+        "short": raw[:5],
+        "length_beyond": struct.pack("<Q", len(raw)) + raw[8:],
+        "truncated_data": raw[: len(raw) - 100],
+        "header_not_json": raw[:8] + b"{" + b" " * (n - 1) + raw[8 + n:],
+    }
+    for k, blob in bad.items():
+        p = tmp_path / f"{k}.safetensors"
+        p.write_bytes(blob)
+        code, msg = load(str(p), cj)
+        assert code == g2.GPT2_E_INVAL, (k, msg)
+    assert load(str(tmp_path / "absent.safetensors"), cj)[0] == g2.GPT2_E_INVAL
+    (tmp_path / "bad.json").write_text("{\"n_layer\": 2,")
+    assert load(st, str(tmp_path / "bad.json"))[0] == g2.GPT2_E_INVAL
+    # a tensor whose byte range runs past the data
+    hdr = json.loads(raw[8:8 + n])
+    hdr["ln_f.bias"]["data_offsets"][1] += 4
+    h2 = json.dumps(hdr).encode()
+    p = tmp_path / "offsets.safetensors"
+    p.write_bytes(struct.pack("<Q", len(h2)) + h2 + raw[8 + n:])
+    code, msg = load(str(p), cj)
+    assert code == g2.GPT2_E_INVAL and "offsets" in msg

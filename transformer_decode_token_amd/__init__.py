@@ -21,11 +21,12 @@ ERROR_NAMES = {GPT2_E_INVAL: "GPT2_E_INVAL", GPT2_E_NOMEM: "GPT2_E_NOMEM",
                GPT2_E_NUMERIC: "GPT2_E_NUMERIC"}
 
 # the symbols include/gpt2dec.h declares
-ABI_FUNCTIONS = ("gpt2_load", "gpt2_set_stream", "gpt2_step", "gpt2_generate", "gpt2_generate_noalloc",
+ABI_FUNCTIONS = ("gpt2_load", "gpt2_load_safetensors", "gpt2_get_config", "gpt2_set_stream", "gpt2_step", "gpt2_generate", "gpt2_generate_noalloc",
                  "gpt2_generate_sample",
                  "gpt2_reset",
                  "gpt2_free", "gpt2_last_error", "gpt2_filled", "gpt2_debug_dequant",
-                 "gpt2_debug_fill_kv", "gpt2_debug_geometry", "gpt2_debug_trace")
+                 "gpt2_debug_fill_kv", "gpt2_debug_geometry", "gpt2_debug_trace",
+                 "gpt2_tokenizer_load", "gpt2_tokenize", "gpt2_detokenize", "gpt2_tokenizer_free")
 
 
 class Gpt2Error(RuntimeError):
@@ -62,6 +63,8 @@ def lib():
             raise ImportError(f"{LIB_PATH} is not built; run python -m transformer_decode_token_amd.build")
         L = C.CDLL(LIB_PATH)
         L.gpt2_load.argtypes = [C.POINTER(gpt2_config), C.POINTER(gpt2_weights), C.POINTER(C.c_void_p)]
+        L.gpt2_load_safetensors.argtypes = [C.c_char_p, C.c_char_p, C.c_int, C.POINTER(C.c_void_p)]
+        L.gpt2_get_config.argtypes = [C.c_void_p, C.POINTER(gpt2_config)]
         L.gpt2_set_stream.argtypes = [C.c_void_p, C.c_void_p]
         L.gpt2_step.argtypes = [C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.POINTER(C.c_int)]
         L.gpt2_generate.argtypes = [C.c_void_p, C.POINTER(C.c_int), C.c_int, C.c_int, C.POINTER(C.c_int)]
@@ -79,6 +82,12 @@ def lib():
         L.gpt2_debug_geometry.argtypes = [C.c_void_p, C.POINTER(C.c_int), C.POINTER(C.c_int)]
         L.gpt2_debug_trace.argtypes = [C.c_void_p, C.c_int, C.c_void_p, C.c_longlong,
                                        C.POINTER(C.c_int)]
+        L.gpt2_tokenizer_load.argtypes = [C.c_char_p, C.c_char_p, C.POINTER(C.c_void_p)]
+        L.gpt2_tokenize.argtypes = [C.c_void_p, C.c_char_p, C.c_size_t, C.c_void_p, C.c_int, C.POINTER(C.c_int)]
+        L.gpt2_detokenize.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_char_p, C.c_size_t,
+                                      C.POINTER(C.c_size_t)]
+        L.gpt2_tokenizer_free.argtypes = [C.c_void_p]
+        L.gpt2_tokenizer_free.restype = None
         _lib = L
     return _lib
 
@@ -139,6 +148,23 @@ def gpt2_load(n_layer, n_embd, n_head, n_positions, vocab_size, tensors, wdtype=
     rc = lib().gpt2_load(C.byref(cfg), C.byref(w), C.byref(h))
     _check(rc, None)
     return Context(h, cfg)
+
+
+def gpt2_load_safetensors(safetensors_path, config_path, wdtype="fp32"):
+    """Load from a Hugging Face model.safetensors and its config.json, as published."""
+    h = C.c_void_p()
+    rc = lib().gpt2_load_safetensors(os.fsencode(safetensors_path), os.fsencode(config_path),
+                                     WDTYPES[wdtype] if isinstance(wdtype, str) else int(wdtype), C.byref(h))
+    _check(rc, None)
+    cfg = gpt2_config()
+    _check(lib().gpt2_get_config(h, C.byref(cfg)), h)
+    return Context(h, cfg)
+
+
+def gpt2_get_config(ctx):
+    cfg = gpt2_config()
+    _check(lib().gpt2_get_config(ctx.handle, C.byref(cfg)), ctx.handle)
+    return cfg
 
 
 def gpt2_set_stream(ctx, hip_stream):
@@ -232,3 +258,47 @@ def gpt2_debug_trace(ctx, steps, fetch=False):
             _check(lib().gpt2_debug_trace(ctx.handle, -1, out.ctypes.data, out.size, None), ctx.handle)
     _check(lib().gpt2_debug_trace(ctx.handle, int(steps), None, 0, None), ctx.handle)
     return out
+
+
+class Tokenizer:
+    """Owns one gpt2_tokenizer*; freed with gpt2_tokenizer_free."""
+
+    def __init__(self, handle):
+        self.handle = handle
+
+    def close(self):
+        if self.handle:
+            lib().gpt2_tokenizer_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def gpt2_tokenizer_load(vocab_json_path, merges_txt_path):
+    h = C.c_void_p()
+    _check(lib().gpt2_tokenizer_load(os.fsencode(vocab_json_path), os.fsencode(merges_txt_path), C.byref(h)), None)
+    return Tokenizer(h)
+
+
+def gpt2_tokenize(tok, text):
+    """Token ids (int32 array) of a str (encoded UTF-8) or bytes."""
+    data = text.encode("utf-8") if isinstance(text, str) else bytes(text)
+    n = C.c_int(0)
+    _check(lib().gpt2_tokenize(tok.handle, data, len(data), None, 0, C.byref(n)), None)
+    out = np.empty(n.value, np.int32)
+    _check(lib().gpt2_tokenize(tok.handle, data, len(data), out.ctypes.data, out.size, C.byref(n)), None)
+    return out
+
+
+def gpt2_detokenize(tok, ids):
+    """The bytes of the ids."""
+    ids = np.ascontiguousarray(ids, np.int32)
+    m = C.c_size_t(0)
+    _check(lib().gpt2_detokenize(tok.handle, ids.ctypes.data, ids.size, None, 0, C.byref(m)), None)
+    buf = C.create_string_buffer(max(m.value, 1))
+    _check(lib().gpt2_detokenize(tok.handle, ids.ctypes.data, ids.size, buf, m.value, C.byref(m)), None)
+    return buf.raw[:m.value]

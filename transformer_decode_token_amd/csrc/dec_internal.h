@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <string>
+
 namespace gpt2dec {
 
 enum { WD_F32 = 0, WD_F16 = 1, WD_Q4 = 2 };
@@ -84,6 +86,9 @@ struct DecodeArgs {
   int trace_steps;                   //   (inputs ready, barrier 1, barrier 2, published) per phase
   int head_lds_rows;                 // output-head rows a workgroup keeps in LDS (set at launch)
 };
+
+// The message gpt2_last_error(NULL) returns for this thread (a failed load).
+void set_load_error(const std::string &msg);
 
 // Shape instantiations compiled into the library.
 struct ShapeInfo {

@@ -505,6 +505,12 @@ int load_impl(gpt2_ctx *c, const gpt2_config *cfg, const gpt2_weights *w) {
   return GPT2_OK;
 }
 
+}  // namespace
+
+void gpt2dec::set_load_error(const std::string &msg) { g_load_error = msg; }
+
+namespace {
+
 bool usable(gpt2_ctx *c, int *rc) {
   if (!c) { *rc = GPT2_E_INVAL; return false; }
   if (c->poisoned) {
@@ -669,6 +675,12 @@ const char *gpt2_last_error(const gpt2_ctx *c) {
 }
 
 int gpt2_filled(const gpt2_ctx *c) { return c ? c->filled : -1; }
+
+int gpt2_get_config(const gpt2_ctx *c, gpt2_config *out) {
+  if (!c || !out) return GPT2_E_INVAL;
+  *out = c->cfg;
+  return GPT2_OK;
+}
 
 int gpt2_debug_dequant(gpt2_ctx *c, int layer, int which, float *out) {
   int rc;
