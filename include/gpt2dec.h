@@ -131,6 +131,19 @@ GPT2DEC_API int gpt2_step(gpt2_ctx *c, int token_id, int position, float *logits
  * filled += n_prompt + n_new - 1.  Errors as gpt2_step. */
 GPT2DEC_API int gpt2_generate(gpt2_ctx *c, const int *prompt, int n_prompt, int n_new, int *out_ids);
 
+/* Batched prompt prefill: the n tokens at positions filled .. filled+n-1 go
+ * through every layer together, so each linear is one GEMM of n rows against
+ * the weights (read once per layer, not once per position) on the matrix
+ * cores; their key and value rows are appended to the cache, as n gpt2_step
+ * calls would append them ("Let's make GPT-2 in assembly", "What GPT-2 does":
+ * the prompt, then the loop; gpt2.s docs: 10 prompt tokens before the 60
+ * generated).  Returns the last position's logits (logits_out: NULL or host
+ * float[V]) and argmax.  Afterwards filled += n.  The results agree with
+ * per-position steps up to the order of the sums.  Errors: GPT2_E_INVAL (n < 1,
+ * filled + n > n_positions, a token out of range), GPT2_E_DEVICE,
+ * GPT2_E_NUMERIC, GPT2_E_STATE. */
+GPT2DEC_API int gpt2_prefill(gpt2_ctx *c, const int *tokens, int n, float *logits_out, int *argmax_out);
+
 /* gpt2_generate for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same ids and cache rows as gpt2_generate, but the kernel's working words

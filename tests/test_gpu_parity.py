@@ -613,3 +613,67 @@ def test_load_from_published_files(name, prefix, tmp_path):
         assert np.array_equal(la, lb), pos
     a.close()
     b.close()
+
+
+# ------------------------------------------------------------ batched prefill
+@pytest.mark.parametrize("name,n_prompt", [("tiny-rich", 8), ("tiny-rich-fp16", 8), ("tiny-rich-int4", 8),
+                                           ("tiny-long", 300), ("gpt2-124m-fp32", 10), ("gpt2-124m-fp16w", 10),
+                                           ("gpt2-124m-int4w", 10), ("gpt2-124m-fp32", 100)])
+def test_prefill_matches_oracle(name, n_prompt):
+    """gpt2_prefill (the prompt's positions through every layer together, the
+    linears as GEMMs on the matrix cores) against the oracle fed the same prompt
+    one position at a time: the last position's logits within the bar and its
+    argmax; then decode steps that read the cache rows the prefill wrote, fed
+    the oracle's greedy ids."""
+    cfg = CASES[name]
+    model = synth.make_model(cfg)
+    rng = np.random.default_rng(n_prompt)
+    prompt = [int(t) for t in rng.integers(0, cfg.vocab, n_prompt)]
+    orc = Oracle(model)
+    for pos, tok in enumerate(prompt):
+        am_o, lg_o = orc.step(tok, pos)
+    ctx = load_gpu(model)
+    am, lg = g2.gpt2_prefill(ctx, prompt)
+    assert g2.gpt2_filled(ctx) == n_prompt
+    worst = compare_step(lg, am, lg_o, f"{name} prefill of {n_prompt}")
+    tok = am_o
+    for pos in range(n_prompt, min(n_prompt + 6, cfg.n_positions)):
+        am_o, lg_o = orc.step(tok, pos)
+        am, lg = g2.gpt2_step(ctx, tok, pos)
+        worst = max(worst, compare_step(lg, am, lg_o, f"{name} step {pos} after the prefill"))
+        tok = am_o
+    print(f"[prefill] {name} n={n_prompt}: worst relative logit error {worst:.2e}", flush=True)
+    orc.close()
+    ctx.close()
+
+
+def test_prefill_in_parts_and_then_generate():
+    """A prompt prefilled in three calls (the later ones attending to rows
+    already in the cache), then a device-chained greedy run from its argmax:
+    the oracle's logits and ids; a fourth call past n_positions is refused and
+    changes nothing; one that fills the last position works."""
+    cfg = CASES["tiny-rich"]
+    model = synth.make_model(cfg)
+    rng = np.random.default_rng(3)
+    prompt = [int(t) for t in rng.integers(0, cfg.vocab, 20)]
+    orc = Oracle(model)
+    for pos, tok in enumerate(prompt):
+        am_o, lg_o = orc.step(tok, pos)
+    ctx = load_gpu(model)
+    g2.gpt2_prefill(ctx, prompt[:7], want_logits=False)
+    g2.gpt2_prefill(ctx, prompt[7:8], want_logits=False)
+    am, lg = g2.gpt2_prefill(ctx, prompt[8:])
+    compare_step(lg, am, lg_o, "three-part prefill")
+    want, mg = _oracle_greedy(orc, [am_o], len(prompt), 10)
+    got = g2.gpt2_generate(ctx, np.array([am_o], np.int32), 10)
+    _assert_ids(got, want, mg, "generate after the prefill")
+    filled = g2.gpt2_filled(ctx)
+    assert filled == len(prompt) + 10   # one fed id + 10 new ids - 1 = 10 passes after the prompt
+    rest = cfg.n_positions - filled
+    with pytest.raises(g2.Gpt2Error) as e:
+        g2.gpt2_prefill(ctx, [1] * (rest + 1))
+    assert e.value.code == g2.GPT2_E_INVAL and g2.gpt2_filled(ctx) == filled
+    g2.gpt2_prefill(ctx, [1] * rest, want_logits=False)
+    assert g2.gpt2_filled(ctx) == cfg.n_positions
+    orc.close()
+    ctx.close()

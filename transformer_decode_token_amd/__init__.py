@@ -21,7 +21,7 @@ ERROR_NAMES = {GPT2_E_INVAL: "GPT2_E_INVAL", GPT2_E_NOMEM: "GPT2_E_NOMEM",
                GPT2_E_NUMERIC: "GPT2_E_NUMERIC"}
 
 # the symbols include/gpt2dec.h declares
-ABI_FUNCTIONS = ("gpt2_load", "gpt2_load_safetensors", "gpt2_get_config", "gpt2_set_stream", "gpt2_step", "gpt2_generate", "gpt2_generate_noalloc",
+ABI_FUNCTIONS = ("gpt2_load", "gpt2_load_safetensors", "gpt2_get_config", "gpt2_set_stream", "gpt2_prefill", "gpt2_step", "gpt2_generate", "gpt2_generate_noalloc",
                  "gpt2_generate_sample",
                  "gpt2_reset",
                  "gpt2_free", "gpt2_last_error", "gpt2_filled", "gpt2_debug_dequant",
@@ -68,6 +68,7 @@ def lib():
         L.gpt2_set_stream.argtypes = [C.c_void_p, C.c_void_p]
         L.gpt2_step.argtypes = [C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.POINTER(C.c_int)]
         L.gpt2_generate.argtypes = [C.c_void_p, C.POINTER(C.c_int), C.c_int, C.c_int, C.POINTER(C.c_int)]
+        L.gpt2_prefill.argtypes = [C.c_void_p, C.POINTER(C.c_int), C.c_int, C.c_void_p, C.POINTER(C.c_int)]
         L.gpt2_generate_noalloc.argtypes = [C.c_void_p, C.POINTER(C.c_int), C.c_int, C.c_int, C.POINTER(C.c_int)]
         L.gpt2_generate_sample.argtypes = [C.c_void_p, C.POINTER(C.c_int), C.c_int, C.c_int, C.c_float,
                                            C.c_ulonglong, C.POINTER(C.c_int)]
@@ -188,6 +189,17 @@ def gpt2_generate(ctx, prompt, n_new):
                              out.ctypes.data_as(C.POINTER(C.c_int)))
     _check(rc, ctx.handle)
     return out
+
+
+def gpt2_prefill(ctx, tokens, want_logits=True):
+    """All tokens in one batched pass; returns (argmax of the last position, its logits or None)."""
+    t = np.ascontiguousarray(tokens, np.int32)
+    logits = np.empty(ctx.cfg.vocab_size, np.float32) if want_logits else None
+    am = C.c_int(-1)
+    rc = lib().gpt2_prefill(ctx.handle, t.ctypes.data_as(C.POINTER(C.c_int)), t.size,
+                            logits.ctypes.data if want_logits else None, C.byref(am))
+    _check(rc, ctx.handle)
+    return am.value, logits
 
 
 def gpt2_generate_noalloc(ctx, prompt, n_new):

@@ -7,7 +7,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgpt2dec.so")
-SOURCES = ["decode_kernel.hip", "relayout.hip", "gpt2dec_host.hip", "hf_files.cpp"]
+SOURCES = ["decode_kernel.hip", "prefill.hip", "relayout.hip", "gpt2dec_host.hip", "hf_files.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
     # packed fp32 instructions stay off (plain v_fma_f32 / v_add_f32 only)

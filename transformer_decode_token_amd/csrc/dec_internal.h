@@ -103,6 +103,20 @@ hipError_t launch_decode(int E, int D, int wd, const DecodeArgs &a, hipStream_t 
 // Occupancy check: blocks of the decode kernel per CU.
 hipError_t decode_occupancy(int E, int D, int wd, int *blocks_per_cu);
 
+// Batched prompt prefill (prefill.hip): n positions p0 .. p0+n-1 through every
+// layer together (their cache rows written), then the last row's logits and
+// argmax (-1 when all are NaN).
+struct PrefillArgs {
+  const DecodeArgs *dec;     // the context's weights, cache, logits
+  int wd, head_wd;           // block-matrix and head storage
+  int L, E, D, P, V;
+  int n, p0;
+  const int *tok;            // [n] device
+  float *x, *qkv, *att, *act;  // device work rows: [n][E], [n][3E], [n][E], [n][4E]
+  int *argmax;               // the argmax (device-visible)
+};
+hipError_t launch_prefill(const PrefillArgs &p, hipStream_t s);
+
 // Load-time re-layout (relayout.hip).
 // src: Conv1D [K][N] fp32 (device); dst: [N][K] fp32.
 hipError_t relayout_f32(const float *src, float *dst, int K, int N, hipStream_t s);

@@ -82,6 +82,7 @@ struct gpt2_ctx {
   uint64_t *tag_bufs[kTagBufs] = {};
   size_t tag_sizes[kTagBufs] = {};
   float *draws_d = nullptr, *draws_h = nullptr;  // uniform numbers of a sampled run
+  float *pf_x = nullptr, *pf_qkv = nullptr, *pf_att = nullptr, *pf_act = nullptr;  // prefill work rows
   // the no-allocation path: this device's static scratch, the word offsets of
   // the error word and of each tagged buffer in it, and the words one run needs
   uint64_t *scratch = nullptr;
@@ -375,6 +376,11 @@ int load_impl(gpt2_ctx *c, const gpt2_config *cfg, const gpt2_weights *w) {
     c->scratch_words = off;
   }
   c->draws_d = c->dalloc<float>((size_t)P * 4);
+  c->pf_x = c->dalloc<float>((size_t)P * E * 4);
+  c->pf_qkv = c->dalloc<float>((size_t)P * 3 * E * 4);
+  c->pf_att = c->dalloc<float>((size_t)P * E * 4);
+  c->pf_act = c->dalloc<float>((size_t)P * F * 4);
+  if (!c->pf_x || !c->pf_qkv || !c->pf_att || !c->pf_act) return c->fail(GPT2_E_NOMEM, "allocation failed");
   c->draws_h = c->halloc<float>((size_t)P * 4);
   if (!c->draws_d || !c->draws_h) return c->fail(GPT2_E_NOMEM, "allocation failed");
   float *logits = c->dalloc<float>((size_t)V * 4);
@@ -601,6 +607,50 @@ int gpt2_generate(gpt2_ctx *c, const int *prompt, int n_prompt, int n_new, int *
   rc = run(c, prompt, n_prompt, c->filled, (int)steps, n_prompt - 1, n_new, out_ids, nullptr);
   if (rc != GPT2_OK) return rc;
   c->filled += (int)steps;
+  return GPT2_OK;
+}
+
+int gpt2_prefill(gpt2_ctx *c, const int *tokens, int n, float *logits_out, int *argmax_out) {
+  int rc;
+  if (!usable(c, &rc)) return rc;
+  if (!tokens) return c->fail(GPT2_E_INVAL, "tokens is NULL");
+  if (n < 1) return c->fail(GPT2_E_INVAL, "n must be >= 1");
+  if ((long long)c->filled + n > c->P)
+    return c->fail(GPT2_E_INVAL, "%d positions from position %d exceed n_positions %d", n, c->filled, c->P);
+  for (int i = 0; i < n; i++)
+    if (tokens[i] < 0 || tokens[i] >= c->V)
+      return c->fail(GPT2_E_INVAL, "tokens[%d] = %d outside [0, %d)", i, tokens[i], c->V);
+  hipError_t e = hipSetDevice(c->device);
+  if (e != hipSuccess) return c->device_fail(e, "hipSetDevice");
+  memcpy(c->feed_h, tokens, sizeof(int) * (size_t)n);
+  e = hipMemcpyAsync(c->feed_d, c->feed_h, sizeof(int) * (size_t)n, hipMemcpyHostToDevice, c->stream);
+  if (e != hipSuccess) return c->device_fail(e, "uploading the tokens");
+  PrefillArgs p{};
+  p.dec = &c->base;
+  p.wd = c->wd;
+  p.head_wd = c->wd == WD_F16 ? WD_F16 : WD_F32;
+  p.L = c->L; p.E = c->E; p.D = c->D; p.P = c->P; p.V = c->V;
+  p.n = n;
+  p.p0 = c->filled;
+  p.tok = c->feed_d;
+  p.x = c->pf_x; p.qkv = c->pf_qkv; p.att = c->pf_att; p.act = c->pf_act;
+  p.argmax = c->ids_dev;
+  c->ids_h[0] = -2;
+  e = launch_prefill(p, c->stream);
+  if (e != hipSuccess) return c->device_fail(e, "prefill launch");
+  if (logits_out)
+    e = hipMemcpyAsync(c->logits_h, c->base.logits, sizeof(float) * (size_t)c->V, hipMemcpyDeviceToHost,
+                       c->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) return c->device_fail(e, "prefill run");
+  const int id = *static_cast<volatile int *>(c->ids_h);
+  c->filled += n;
+  if (id < 0 || id >= c->V) {
+    c->poisoned = true;
+    return c->fail(GPT2_E_NUMERIC, "every logit of the last prefilled position is NaN: no greedy id");
+  }
+  if (argmax_out) *argmax_out = id;
+  if (logits_out) memcpy(logits_out, c->logits_h, sizeof(float) * (size_t)c->V);
   return GPT2_OK;
 }
 
