@@ -1,27 +1,34 @@
 // prefill.hip -- batched prompt prefill: the n prompt positions of a call go
 // through every layer together, so each linear is a GEMM of n rows against the
 // weights (read once per layer instead of once per position), run on the
-// matrix cores.
+// matrix cores, and attention is a causal tile loop on the matrix cores too.
 //
-// Per layer (n rows at positions p0 .. p0+n-1):
-//   gemm  LN1 of the rows (in the prologue), x W_qkv^T + b, and the new key and
-//         value rows written into the cache (in the epilogue)
-//   attn  per (row, head): causal softmax over the cached positions 0..p, the
-//         weighted sum of values (running maximum and sum, 64 positions a step)
-//   gemm  x += attn W_ap^T + b
-//   gemm  gelu_new(LN2 of the rows W_fc^T + b)
-//   gemm  x += act W_pr^T + b
-// then the last row's final LayerNorm, the head (its logits) and the argmax.
+// Per layer (rows t = 0..n-1 at positions p0 + t; x_n = the rows after the
+// LayerNorm that comes next, written by the kernel that last changed x):
+//   gemm  x_n W_qkv^T + b; the new key and value rows also go into the cache
+//   attn  per (16 rows, head): causal softmax over cache rows 0..p0+t and the
+//         weighted sum of values, 64 keys a step with a running maximum and sum
+//   gemm  attn W_ap^T in K-split partials; row pass: x += sum + b, x_n = LN2(x)
+//   gemm  act = gelu_new(x_n W_fc^T + b)
+//   gemm  act W_pr^T in K-split partials; row pass: x += sum + b, x_n = the
+//         next layer's LN1 (after the last layer the final LayerNorm)
+// then the head (the last row's logits) and the argmax.
 //
-// GEMM tile: a workgroup of four waves computes 16 rows x 16 output columns
-// with v_mfma_f32_16x16x4f32 (lane l holds A[l%16][l/16] and B[l/16][l%16];
-// result element i of lane l is C[4*(l/16)+i][l%16]).  Wave w contracts the
-// quarter w of K; inside it the MFMA's four k slots take four contiguous runs
-// of S = K/16 inputs (slot g: kq + g*S + s for step s), so each lane reads its
-// A and W values as float4 runs.  The four partial tiles are summed in LDS in
-// wave order.  fp16 weights are widened exactly; int4 weights become
-// zero + code * scale with one rounding, the values the quantised model
-// defines; the products and sums are fp32 throughout.
+// Matrix-core layout (v_mfma_f32_16x16x4f32, 64 lanes, lane l = 16 g + r):
+// lane l supplies A[r][slot g] and B[slot g][r] and holds C[4 g + e][r] in
+// result element e.  A contraction is cut into four runs, slot g taking the
+// g-th run one input per step, so a lane reads its operands as float4 runs.
+//
+// GEMM: C[n][N] = A[n][K] W[N][K]^T with output-major weights, tiles of
+// BM x 64 outputs per workgroup of four waves, K in stages of 32 or 64 through LDS
+// (double-buffered: the next stage's loads are in flight while the current one
+// is multiplied).  fp16 weights are widened exactly and int4 weights become
+// zero + code * scale with one rounding (the quantised model's values) as a
+// stage is written to LDS; products and sums are fp32.  Tiles are numbered so
+// that the workgroups on one XCD share weight columns (its L2 holds them).
+// The two projections (N = E) have few column tiles, so their K is split in up
+// to three parts that run as separate tiles; the row pass adds the parts in
+// order, so results do not depend on scheduling.
 #include <hip/hip_fp16.h>
 
 #include <utility>
@@ -33,36 +40,14 @@ namespace {
 
 typedef float pf_f4 __attribute__((ext_vector_type(4)));
 
-enum { PF_QKV = 0, PF_RESID = 1, PF_GELU = 2, PF_HEAD = 3 };
+enum { PF_QKV = 0, PF_PART = 1, PF_GELU = 2 };
+
+constexpr int BN = 64;        // output columns per GEMM tile
+constexpr int HEAD_XCH = 8;   // float4 chunks of a row a lane keeps (row passes, head): E <= 2048
 
 __device__ __forceinline__ float pf_wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   return v;
-}
-__device__ __forceinline__ float pf_wave_max(float v) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-
-// Four consecutive weights of output row `row` from input k (a multiple of 4),
-// as fp32.
-template <int WD>
-__device__ __forceinline__ float4 pf_w4(const void *w, const float2 *sz, size_t row, int K, int k) {
-  if constexpr (WD == WD_F32) {
-    return *reinterpret_cast<const float4 *>(static_cast<const float *>(w) + row * K + k);
-  } else if constexpr (WD == WD_F16) {
-    const uint2 h = *reinterpret_cast<const uint2 *>(static_cast<const __half *>(w) + row * K + k);
-    return make_float4(__half2float(__ushort_as_half((unsigned short)(h.x & 0xffffu))),
-                       __half2float(__ushort_as_half((unsigned short)(h.x >> 16))),
-                       __half2float(__ushort_as_half((unsigned short)(h.y & 0xffffu))),
-                       __half2float(__ushort_as_half((unsigned short)(h.y >> 16))));
-  } else {
-    const uint32_t q = *reinterpret_cast<const uint16_t *>(static_cast<const uint8_t *>(w) + (row * K + k) / 2);
-    const float2 p = sz[(row * K + k) / 32];
-    return make_float4(__builtin_fmaf((float)(q & 15u), p.x, p.y), __builtin_fmaf((float)((q >> 4) & 15u), p.x, p.y),
-                       __builtin_fmaf((float)((q >> 8) & 15u), p.x, p.y),
-                       __builtin_fmaf((float)((q >> 12) & 15u), p.x, p.y));
-  }
 }
 
 __device__ __forceinline__ float pf_gelu_new(float x) {
@@ -71,149 +56,491 @@ __device__ __forceinline__ float pf_gelu_new(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + __expf(-z2));
 }
 
+__device__ __forceinline__ float pf_half(unsigned bits) { return __half2float(__ushort_as_half((unsigned short)bits)); }
+
+// ---------------------------------------------------------------- row passes
+// One wave per row; lane l holds the row's float4 chunks l, l + 64, ... (at most
+// HEAD_XCH of them: E <= 2048) in registers.
+
+// xn = (x - mean) / sqrt(var + eps) * gamma + beta for the row held in xv
+// (mean first, then the mean squared deviation).
+__device__ __forceinline__ void pf_layernorm_row(const float4 (&xv)[HEAD_XCH], int E, const float *gamma,
+                                                 const float *beta, float eps, float *o, int l) {
+  const int nch = E / 4;
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < HEAD_XCH; j++)
+    if (l + 64 * j < nch) s += (xv[j].x + xv[j].y) + (xv[j].z + xv[j].w);
+  const float mean = pf_wave_sum(s) / (float)E;
+  float q = 0.f;
+#pragma unroll
+  for (int j = 0; j < HEAD_XCH; j++)
+    if (l + 64 * j < nch) {
+      const float a = xv[j].x - mean, b = xv[j].y - mean, c = xv[j].z - mean, d = xv[j].w - mean;
+      q = __builtin_fmaf(a, a, q);
+      q = __builtin_fmaf(b, b, q);
+      q = __builtin_fmaf(c, c, q);
+      q = __builtin_fmaf(d, d, q);
+    }
+  const float rstd = __builtin_amdgcn_rsqf(pf_wave_sum(q) / (float)E + eps);
+#pragma unroll
+  for (int j = 0; j < HEAD_XCH; j++) {
+    const int c = l + 64 * j;
+    if (c >= nch) break;
+    const float4 g = *reinterpret_cast<const float4 *>(gamma + 4 * c);
+    const float4 b = *reinterpret_cast<const float4 *>(beta + 4 * c);
+    *reinterpret_cast<float4 *>(o + 4 * c) =
+        make_float4((xv[j].x - mean) * rstd * g.x + b.x, (xv[j].y - mean) * rstd * g.y + b.y,
+                    (xv[j].z - mean) * rstd * g.z + b.z, (xv[j].w - mean) * rstd * g.w + b.w);
+  }
+}
+
+// x[t] = wte[token t] + wpe[p0 + t], and xn[t] = LN(x[t]).
+__global__ void __launch_bounds__(256) prefill_embed_ln(const int *tok, const float *wte, const float *wpe, int E,
+                                                        int p0, int n, const float *gamma, const float *beta,
+                                                        float eps, float *x, float *xn) {
+  const int t = blockIdx.x * 4 + threadIdx.x / 64, l = threadIdx.x % 64;
+  if (t >= n) return;
+  const int nch = E / 4;
+  float *xr = x + (size_t)t * E;
+  const float *we = wte + (size_t)tok[t] * E, *pe = wpe + (size_t)(p0 + t) * E;
+  float4 xv[HEAD_XCH];
+#pragma unroll
+  for (int j = 0; j < HEAD_XCH; j++) {
+    const int c = l + 64 * j;
+    xv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c < nch) {
+      const float4 a = *reinterpret_cast<const float4 *>(we + 4 * c);
+      const float4 b = *reinterpret_cast<const float4 *>(pe + 4 * c);
+      xv[j] = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+      *reinterpret_cast<float4 *>(xr + 4 * c) = xv[j];
+    }
+  }
+  pf_layernorm_row(xv, E, gamma, beta, eps, xn + (size_t)t * E, l);
+}
+
+// x[t] += (part_0[t] + part_1[t] + ...) + bias, then xn[t] = LN(x[t]).  The
+// parts are a projection's K-split partial sums [S][n][E], added in order.
+__global__ void __launch_bounds__(256) prefill_resid_ln(const float *part, int S, int n, int E, const float *bias,
+                                                        const float *gamma, const float *beta, float eps, float *x,
+                                                        float *xn) {
+  const int t = blockIdx.x * 4 + threadIdx.x / 64, l = threadIdx.x % 64;
+  if (t >= n) return;
+  const int nch = E / 4;
+  float *xr = x + (size_t)t * E;
+  const size_t ps = (size_t)n * E;
+  const float *pr = part + (size_t)t * E;
+  float4 xv[HEAD_XCH];
+#pragma unroll
+  for (int j = 0; j < HEAD_XCH; j++) {
+    const int c = l + 64 * j;
+    xv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c < nch) {
+      float4 v = *reinterpret_cast<const float4 *>(pr + 4 * c);
+      for (int sp = 1; sp < S; sp++) {
+        const float4 w = *reinterpret_cast<const float4 *>(pr + sp * ps + 4 * c);
+        v = make_float4(v.x + w.x, v.y + w.y, v.z + w.z, v.w + w.w);
+      }
+      const float4 b = *reinterpret_cast<const float4 *>(bias + 4 * c);
+      const float4 x0 = *reinterpret_cast<const float4 *>(xr + 4 * c);
+      xv[j] = make_float4(x0.x + (v.x + b.x), x0.y + (v.y + b.y), x0.z + (v.z + b.z), x0.w + (v.w + b.w));
+      *reinterpret_cast<float4 *>(xr + 4 * c) = xv[j];
+    }
+  }
+  pf_layernorm_row(xv, E, gamma, beta, eps, xn + (size_t)t * E, l);
+}
+
+// ---------------------------------------------------------------- GEMM
 struct GemmArgs {
-  const float *a;        // [rows][K] input rows (the residual stream for the LayerNorm modes)
-  int a_row0;            // first input row of the call (the head: the last row)
-  int n_rows;            // rows of the call
+  const float *a;        // [n_rows][K] input rows
+  int n_rows;
   const void *w;         // [N][K] output-major weights of this layer
   const float2 *sz;      // int4: (scale, zero) per group of 32
-  const float *bias;     // [N] or null
-  const float *gamma, *beta;  // LayerNorm modes
-  float eps;
+  const float *bias;     // [N]
   int N, K;
-  float *out;            // [rows][N] (QKV, gelu), the residual [rows][N] (RESID), [N] logits (HEAD)
+  float *out;            // [n_rows][N] (QKV, GELU) or partial sums [splits][n_rows][N] (PART)
   float *kc, *vc;        // QKV: this layer's cache blocks [H][P][D]
   int E, D, P, p0;
+  int splits;            // K parts (PART only; else 1)
+  int tiles_m, tiles_n, n_tiles;  // M tiles, N tiles, all tiles (x splits)
 };
 
-template <int WD, int MODE>
+// One stage of weights (64 rows x BK inputs, BK = 32 or 64) in flight, in its
+// storage type; store() writes it to LDS as fp32 rows of BK + 4 floats.
+template <int WD, int BK>
+struct WStage;
+template <int BK>
+struct WStage<WD_F32, BK> {
+  static constexpr int C4 = BK / 4, N = 64 * C4 / 256;  // float4 per row; per thread
+  float4 v[N];
+  __device__ void load(const GemmArgs &g, int n0, int k0, int tid) {
+    const float *w = static_cast<const float *>(g.w);
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+      const int f = tid + i * 256, row = f / C4, c4 = f % C4;
+      v[i] = *reinterpret_cast<const float4 *>(w + (size_t)(n0 + row) * g.K + k0 + c4 * 4);
+    }
+  }
+  __device__ void store(float (*ws)[BK + 4], int tid) const {
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+      const int f = tid + i * 256, row = f / C4, c4 = f % C4;
+      *reinterpret_cast<float4 *>(&ws[row][c4 * 4]) = v[i];
+    }
+  }
+};
+template <int BK>
+struct WStage<WD_F16, BK> {
+  static constexpr int C8 = BK / 8, N = 64 * C8 / 256;  // 8-half pieces per row; per thread
+  uint4 v[N];
+  __device__ void load(const GemmArgs &g, int n0, int k0, int tid) {
+    const __half *w = static_cast<const __half *>(g.w);
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+      const int f = tid + i * 256;
+      v[i] = *reinterpret_cast<const uint4 *>(w + (size_t)(n0 + f / C8) * g.K + k0 + (f % C8) * 8);
+    }
+  }
+  __device__ void store(float (*ws)[BK + 4], int tid) const {
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+      const int f = tid + i * 256;
+      float *d = &ws[f / C8][(f % C8) * 8];
+      *reinterpret_cast<float4 *>(d) = make_float4(pf_half(v[i].x & 0xffffu), pf_half(v[i].x >> 16),
+                                                   pf_half(v[i].y & 0xffffu), pf_half(v[i].y >> 16));
+      *reinterpret_cast<float4 *>(d + 4) = make_float4(pf_half(v[i].z & 0xffffu), pf_half(v[i].z >> 16),
+                                                       pf_half(v[i].w & 0xffffu), pf_half(v[i].w >> 16));
+    }
+  }
+};
+template <int BK>
+struct WStage<WD_Q4, BK> {
+  // four threads per row, each BK/4 codes (even input in the low nibble) of
+  // one group of 32, and that group's (scale, zero)
+  static constexpr int NW = BK / 32;  // 32-bit words of codes per thread
+  uint32_t q[NW];
+  float2 s;
+  __device__ void load(const GemmArgs &g, int n0, int k0, int tid) {
+    const size_t e0 = (size_t)(n0 + (tid >> 2)) * g.K + k0 + (tid & 3) * (BK / 4);
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(static_cast<const uint8_t *>(g.w) + e0 / 2);
+#pragma unroll
+    for (int i = 0; i < NW; i++) q[i] = src[i];
+    s = g.sz[e0 / 32];
+  }
+  __device__ void store(float (*ws)[BK + 4], int tid) const {
+    float *d = &ws[tid >> 2][(tid & 3) * (BK / 4)];
+#pragma unroll
+    for (int i = 0; i < NW; i++) {
+      float f[8];
+#pragma unroll
+      for (int j = 0; j < 8; j++) f[j] = __builtin_fmaf((float)((q[i] >> (4 * j)) & 15u), s.x, s.y);
+      *reinterpret_cast<float4 *>(d + 8 * i) = make_float4(f[0], f[1], f[2], f[3]);
+      *reinterpret_cast<float4 *>(d + 8 * i + 4) = make_float4(f[4], f[5], f[6], f[7]);
+    }
+  }
+};
+
+template <int WD, int MODE, int BM, int BK>
 __global__ void __launch_bounds__(256) prefill_gemm(GemmArgs g) {
-  constexpr bool LN = (MODE == PF_QKV || MODE == PF_GELU || MODE == PF_HEAD);
-  __shared__ float red[4][16][17];
-  extern __shared__ float as[];  // LayerNorm modes: [16][K + 4] normalised rows
-  const int tid = threadIdx.x, wv = tid / 64, l = tid % 64;
-  const int o0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
-  const int nv = min(16, g.n_rows - t0);  // valid rows of this tile
-  const int K = g.K, AS = K + 4;
-  if constexpr (LN) {
-    // wave wv normalises rows wv, wv+4, ... of the tile (zeros past the valid rows)
-    for (int r = wv; r < 16; r += 4) {
-      float *dst = as + r * AS;
-      if (r < nv) {
-        const float *x = g.a + (size_t)(g.a_row0 + t0 + r) * K;
-        float s = 0.f;
-        for (int k = l; k < K; k += 64) s += x[k];
-        const float mean = pf_wave_sum(s) / (float)K;
-        float q = 0.f;
-        for (int k = l; k < K; k += 64) {
-          const float d = x[k] - mean;
-          q = __builtin_fmaf(d, d, q);
+  constexpr int LDK = BK + 4;  // padded stage row, floats
+  // waves WM x WN over the tile; each wave owns TM x TN blocks of 16 x 16
+  constexpr int WM = BM >= 32 ? 2 : 1, WN = 4 / WM;
+  constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
+  constexpr int AF4 = BM * BK / 4;                  // float4 of an A stage
+  constexpr int AI = (AF4 + 255) / 256;             // per thread
+  __shared__ float as[2][BM][LDK];
+  __shared__ float ws[2][BN][LDK];
+  // XCD-aware tile order: workgroup id -> XCD id % 8; each XCD takes a run of
+  // consecutive tiles, which walk the M tiles of one weight column block first
+  const int per = gridDim.x / 8;
+  const int t = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (t >= g.n_tiles) return;
+  const int m0 = (t % g.tiles_m) * BM, rest = t / g.tiles_m;
+  const int n0 = (rest % g.tiles_n) * BN, sp = rest / g.tiles_n;
+  const int tid = threadIdx.x, wv = tid / 64, l = tid % 64, r = l & 15, gs = l >> 4;
+  const int mw = (wv / WN) * (BM / WM), nw = (wv % WN) * (BN / WN);
+  const int KT = g.K / BK / g.splits, kbase = sp * KT * BK;  // this tile's part of K
+
+  constexpr int AC4 = BK / 4;                       // float4 per A row
+  float4 av[AI];
+  WStage<WD, BK> wst;
+  auto load_a = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < AI; i++) {
+      const int f = tid + i * 256, row = f / AC4, c4 = f % AC4;
+      av[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (f < AF4 && m0 + row < g.n_rows)
+        av[i] = *reinterpret_cast<const float4 *>(g.a + (size_t)(m0 + row) * g.K + k0 + c4 * 4);
+    }
+  };
+  auto store_a = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < AI; i++) {
+      const int f = tid + i * 256, row = f / AC4, c4 = f % AC4;
+      if (f < AF4) *reinterpret_cast<float4 *>(&as[b][row][c4 * 4]) = av[i];
+    }
+  };
+
+  pf_f4 c[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; i++)
+#pragma unroll
+    for (int j = 0; j < TN; j++) c[i][j] = pf_f4{0.f, 0.f, 0.f, 0.f};
+
+  load_a(kbase);
+  wst.load(g, n0, kbase, tid);
+  store_a(0);
+  wst.store(ws[0], tid);
+  __syncthreads();
+  for (int kt = 0; kt < KT; kt++) {
+    const int b = kt & 1;
+    if (kt + 1 < KT) {
+      load_a(kbase + (kt + 1) * BK);
+      wst.load(g, n0, kbase + (kt + 1) * BK, tid);
+    }
+    // slot gs of the stage: inputs gs*BK/4 .. (gs+1)*BK/4 - 1, one per step
+    constexpr int RUN = BK / 16;  // float4 per run
+    float4 ar[TM][RUN], wr[TN][RUN];
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+      for (int h = 0; h < RUN; h++)
+        ar[i][h] = *reinterpret_cast<const float4 *>(&as[b][mw + i * 16 + r][gs * (BK / 4) + 4 * h]);
+#pragma unroll
+    for (int j = 0; j < TN; j++)
+#pragma unroll
+      for (int h = 0; h < RUN; h++)
+        wr[j][h] = *reinterpret_cast<const float4 *>(&ws[b][nw + j * 16 + r][gs * (BK / 4) + 4 * h]);
+#pragma unroll
+    for (int h = 0; h < RUN; h++) {
+#pragma unroll
+      for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++) {
+          c[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ar[i][h].x, wr[j][h].x, c[i][j], 0, 0, 0);
+          c[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ar[i][h].y, wr[j][h].y, c[i][j], 0, 0, 0);
+          c[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ar[i][h].z, wr[j][h].z, c[i][j], 0, 0, 0);
+          c[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ar[i][h].w, wr[j][h].w, c[i][j], 0, 0, 0);
         }
-        const float rstd = __builtin_amdgcn_rsqf(pf_wave_sum(q) / (float)K + g.eps);
-        for (int k = l; k < K; k += 64) dst[k] = (x[k] - mean) * rstd * g.gamma[k] + g.beta[k];
-      } else {
-        for (int k = l; k < K; k += 64) dst[k] = 0.f;
-      }
+    }
+    if (kt + 1 < KT) {
+      store_a(b ^ 1);
+      wst.store(ws[b ^ 1], tid);
     }
     __syncthreads();
   }
-  // this wave's quarter of K, the lane's k slot and row/column
-  const int KQ = K / 4, S = K / 16, kq = wv * KQ;
-  const int gs = l / 16, r = l % 16;
-  const int kb = kq + gs * S;  // the lane's run of S inputs
-  const size_t wrow = (size_t)min(o0 + r, g.N - 1);
-  const int arow = min(r, max(nv - 1, 0));
-  const float *ag = g.a + (size_t)(g.a_row0 + t0 + arow) * K;
-  pf_f4 c = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < S; s += 4) {
-    const float4 wq = pf_w4<WD>(g.w, g.sz, wrow, K, kb + s);
-    float4 av;
-    if constexpr (LN) av = *reinterpret_cast<const float4 *>(as + r * AS + kb + s);
-    else av = (r < nv) ? *reinterpret_cast<const float4 *>(ag + kb + s) : make_float4(0.f, 0.f, 0.f, 0.f);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, wq.x, c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, wq.y, c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, wq.z, c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, wq.w, c, 0, 0, 0);
+
+  // epilogue: block (i, j), element e is row m0 + mw + 16 i + 4 gs + e, column n0 + nw + 16 j + r
+#pragma unroll
+  for (int i = 0; i < TM; i++)
+#pragma unroll
+    for (int j = 0; j < TN; j++) {
+      const int o = n0 + nw + j * 16 + r;
+      const float bo = MODE == PF_PART ? 0.f : g.bias[o];
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int row = m0 + mw + i * 16 + gs * 4 + e;
+        if (row >= g.n_rows) continue;
+        const float y = c[i][j][e] + bo;
+        if constexpr (MODE == PF_PART) {
+          g.out[((size_t)sp * g.n_rows + row) * g.N + o] = c[i][j][e];
+        } else if constexpr (MODE == PF_GELU) {
+          g.out[(size_t)row * g.N + o] = pf_gelu_new(y);
+        } else {  // QKV: the row, and its key / value part into the cache at position p0 + row
+          g.out[(size_t)row * g.N + o] = y;
+          if (o >= g.E) {
+            const int ev = (o - g.E) % g.E, hh = ev / g.D, d = ev % g.D;
+            float *cache = (o < 2 * g.E) ? g.kc : g.vc;
+            cache[((size_t)hh * g.P + g.p0 + row) * g.D + d] = y;
+          }
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------- attention
+// One workgroup of four waves per (16 rows, head); wave w takes the 64-key
+// steps w, w + 4, ... and the four partial results (running maximum, sum and
+// weighted values per row) are merged through LDS in wave order.
+//
+// Scores are formed transposed, S^T = K Q^T (keys as the A rows, the rows'
+// queries as the B columns), so each lane holds the scores of one row (r) for
+// four keys per 16-key block, which is exactly the B operand of O^T = V^T P^T:
+// the weights never leave the registers.  The running maximum and sum belong
+// to row r in every lane that holds it; the row's maximum over a step is
+// combined over the four lanes of the row (lanes r, r+16, r+32, r+48).  Output
+// dims are spread as d = (D/16) r' + db over the D/16 result blocks db, so a
+// lane reads each value row as one run.
+template <int D>
+__global__ void __launch_bounds__(256) prefill_attention(const float *qkv, const float *kc, const float *vc, int E,
+                                                         int P, int p0, int n, float *out) {
+  constexpr int RQ = D / 4;   // a lane's run of dims in the score contraction
+  constexpr int DV = D / 16;  // value dims a lane reads per key (result blocks)
+  __shared__ float sm[4][16], sl[4][16];
+  __shared__ float so[4][D][17];
+  const int wv = threadIdx.x / 64, l = threadIdx.x % 64, r = l & 15, gs = l >> 4;
+  const int nqb = gridDim.x, qb = nqb - 1 - (int)blockIdx.x;  // longest blocks first
+  const int h = blockIdx.y;
+  const int t0 = qb * 16, t = t0 + r;
+  const int jmax = p0 + min(t0 + 15, n - 1);  // last cache row the block may read
+  const int pq = min(p0 + t, jmax);           // last key of row r
+  const float scale = 1.0f / sqrtf((float)D);
+  float q[RQ];
+  {
+    const float *qr = qkv + (size_t)min(t, n - 1) * 3 * E + h * D + gs * RQ;
+#pragma unroll
+    for (int i = 0; i < RQ / 4; i++) {
+      const float4 v = *reinterpret_cast<const float4 *>(qr + 4 * i);
+      q[4 * i] = v.x;
+      q[4 * i + 1] = v.y;
+      q[4 * i + 2] = v.z;
+      q[4 * i + 3] = v.w;
+    }
+  }
+  const float *Kh = kc + (size_t)h * P * D, *Vh = vc + (size_t)h * P * D;
+  float m = -INFINITY, lsum = 0.f;
+  pf_f4 o[DV];
+#pragma unroll
+  for (int db = 0; db < DV; db++) o[db] = pf_f4{0.f, 0.f, 0.f, 0.f};
+
+  for (int j0 = 64 * wv; j0 <= jmax; j0 += 256) {
+    // scores: block kb, element e is key j0 + 16 kb + 4 gs + e of row r
+    pf_f4 s[4];
+    float kr[4][RQ];
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++) {
+      const float *kp = Kh + (size_t)min(j0 + kb * 16 + r, jmax) * D + gs * RQ;
+#pragma unroll
+      for (int i = 0; i < RQ / 4; i++) {
+        const float4 v = *reinterpret_cast<const float4 *>(kp + 4 * i);
+        kr[kb][4 * i] = v.x;
+        kr[kb][4 * i + 1] = v.y;
+        kr[kb][4 * i + 2] = v.z;
+        kr[kb][4 * i + 3] = v.w;
+      }
+      s[kb] = pf_f4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < RQ; i++)
+#pragma unroll
+      for (int kb = 0; kb < 4; kb++) s[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[kb][i], q[i], s[kb], 0, 0, 0);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int j = j0 + kb * 16 + gs * 4 + e;
+        s[kb][e] = (j <= pq) ? s[kb][e] * scale : -INFINITY;
+        mx = fmaxf(mx, s[kb][e]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // a row with no key in this step keeps its maximum (mx = -inf); one whose
+    // first key this is starts from m = -inf, where alpha is 0
+    const float mn = fmaxf(m, mx);
+    const float alpha = mn == -INFINITY ? 1.f : __expf(m - mn);
+    m = mn;
+    float ps = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const float p = (j0 + kb * 16 + gs * 4 + e <= pq) ? __expf(s[kb][e] - mn) : 0.f;
+        s[kb][e] = p;
+        ps += p;
+      }
+    lsum = __builtin_fmaf(lsum, alpha, ps);
+#pragma unroll
+    for (int db = 0; db < DV; db++) o[db] *= alpha;
+    // O^T += V^T P^T: step e of block kb takes key j0 + 16 kb + 4 gs + e
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const float *vp = Vh + (size_t)min(j0 + kb * 16 + gs * 4 + e, jmax) * D + r * DV;
+        float vv[DV];
+        if constexpr (DV == 4) {
+          const float4 v = *reinterpret_cast<const float4 *>(vp);
+          vv[0] = v.x; vv[1] = v.y; vv[2] = v.z; vv[3] = v.w;
+        } else {
+#pragma unroll
+          for (int db = 0; db < DV; db++) vv[db] = vp[db];
+        }
+#pragma unroll
+        for (int db = 0; db < DV; db++) o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv[db], s[kb][e], o[db], 0, 0, 0);
+      }
+  }
+  // this wave's partials: row maximum and sum, and O^T (block db, element e:
+  // dim DV (4 gs + e) + db of row r)
+  float tot = lsum + __shfl_xor(lsum, 16);
+  tot += __shfl_xor(tot, 32);
+  if (gs == 0) {
+    sm[wv][r] = m;
+    sl[wv][r] = tot;
   }
 #pragma unroll
-  for (int i = 0; i < 4; i++) red[wv][4 * gs + i][r] = c[i];
+  for (int db = 0; db < DV; db++)
+#pragma unroll
+    for (int e = 0; e < 4; e++) so[wv][DV * (4 * gs + e) + db][r] = o[db][e];
   __syncthreads();
-  // epilogue: thread (row i, column cc) sums the four waves' partials in order
-  const int i = tid / 16, cc = tid % 16;
-  const int t = t0 + i, o = o0 + cc;
-  if (i >= nv || o >= g.N) return;
-  const float v = ((red[0][i][cc] + red[1][i][cc]) + red[2][i][cc]) + red[3][i][cc];
-  if constexpr (MODE == PF_HEAD) {
-    g.out[o] = v;
-  } else if constexpr (MODE == PF_RESID) {
-    float *x = g.out + (size_t)t * g.N + o;
-    *x = *x + (v + g.bias[o]);
-  } else if constexpr (MODE == PF_GELU) {
-    g.out[(size_t)t * g.N + o] = pf_gelu_new(v + g.bias[o]);
-  } else {  // QKV: the row, and its key / value part into the cache at position p0 + t
-    const float y = v + g.bias[o];
-    g.out[(size_t)t * g.N + o] = y;
-    if (o >= g.E) {
-      const int e = (o - g.E) % g.E, h = e / g.D, d = e % g.D;
-      float *cache = (o < 2 * g.E) ? g.kc : g.vc;
-      cache[((size_t)h * g.P + g.p0 + t) * g.D + d] = y;
+  // merge: thread i takes outputs i, i + 256, ... of the 16 x D block (row-major)
+  for (int i = threadIdx.x; i < 16 * D; i += 256) {
+    const int rr = i / D, d = i % D;
+    if (t0 + rr >= n) break;
+    float mm = sm[0][rr];
+#pragma unroll
+    for (int w = 1; w < 4; w++) mm = fmaxf(mm, sm[w][rr]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+      const float f = sm[w][rr] == -INFINITY ? 0.f : __expf(sm[w][rr] - mm);  // waves with no keys add nothing
+      num = __builtin_fmaf(f, so[w][d][rr], num);
+      den = __builtin_fmaf(f, sl[w][rr], den);
     }
+    out[(size_t)(t0 + rr) * E + h * D + d] = num / den;
   }
 }
 
-// x[t] = wte[token t] + wpe[p0 + t]
-__global__ void __launch_bounds__(256) prefill_embed(const int *tok, const float *wte, const float *wpe, int E,
-                                                     int p0, float *x) {
-  const int t = blockIdx.y, i = blockIdx.x * 256 + threadIdx.x;
-  if (i < E) x[(size_t)t * E + i] = wte[(size_t)tok[t] * E + i] + wpe[(size_t)(p0 + t) * E + i];
-}
-
-// One wave per (row t, head h): causal attention of position p0 + t over the
-// cache rows 0 .. p0 + t of this layer, 64 positions a step (lane = position
-// for the scores, lane = dimension for the values), with a running maximum and
-// sum.  out[t][h*D ..] = the weighted sum of values.
-__global__ void __launch_bounds__(64) prefill_attention(const float *qkv, const float *kc, const float *vc, int E,
-                                                        int D, int P, int p0, float *out) {
-  __shared__ float q[64];
-  __shared__ float e[64];
-  const int t = blockIdx.x, h = blockIdx.y, l = threadIdx.x;
-  const int p = p0 + t;
-  const float scale = 1.0f / sqrtf((float)D);
-  if (l < D) q[l] = qkv[(size_t)t * 3 * E + h * D + l];
-  __syncthreads();
-  const float *K = kc + (size_t)h * P * D, *V = vc + (size_t)h * P * D;
-  float m = -INFINITY, ssum = 0.f, acc = 0.f;
-  for (int j0 = 0; j0 <= p; j0 += 64) {
-    const int j = j0 + l;
-    float sc = -INFINITY;
-    if (j <= p) {
-      const float *kr = K + (size_t)j * D;
-      float d0 = 0.f;
-      for (int d = 0; d < D; d += 4) {
-        const float4 kk = *reinterpret_cast<const float4 *>(kr + d);
-        d0 = __builtin_fmaf(kk.x, q[d], d0);
-        d0 = __builtin_fmaf(kk.y, q[d + 1], d0);
-        d0 = __builtin_fmaf(kk.z, q[d + 2], d0);
-        d0 = __builtin_fmaf(kk.w, q[d + 3], d0);
+// ---------------------------------------------------------------- head
+// logits[v] = head row v . xn for the one normalised row xn; each wave takes
+// four rows at a time, a lane the float4 chunks l, l + 64, ...
+template <int HWD>
+__global__ void __launch_bounds__(256) prefill_head(const void *head, const float *xn, int E, int V,
+                                                    float *logits) {
+  const int l = threadIdx.x % 64, nch = E / 4;
+  const int row0 = (blockIdx.x * 4 + threadIdx.x / 64) * 4;
+  float4 xv[HEAD_XCH];
+#pragma unroll
+  for (int j = 0; j < HEAD_XCH; j++) {
+    const int c = l + 64 * j;
+    xv[j] = c < nch ? *reinterpret_cast<const float4 *>(xn + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < HEAD_XCH; j++) {
+    const int c = l + 64 * j;
+    if (c >= nch) break;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int row = min(row0 + i, V - 1);
+      float4 w;
+      if constexpr (HWD == WD_F32) {
+        w = *reinterpret_cast<const float4 *>(static_cast<const float *>(head) + (size_t)row * E + 4 * c);
+      } else {
+        const uint2 hb = *reinterpret_cast<const uint2 *>(static_cast<const __half *>(head) + (size_t)row * E + 4 * c);
+        w = make_float4(pf_half(hb.x & 0xffffu), pf_half(hb.x >> 16), pf_half(hb.y & 0xffffu), pf_half(hb.y >> 16));
       }
-      sc = d0 * scale;
+      acc[i] = __builtin_fmaf(w.x, xv[j].x, acc[i]);
+      acc[i] = __builtin_fmaf(w.y, xv[j].y, acc[i]);
+      acc[i] = __builtin_fmaf(w.z, xv[j].z, acc[i]);
+      acc[i] = __builtin_fmaf(w.w, xv[j].w, acc[i]);
     }
-    const float mn = fmaxf(m, pf_wave_max(sc));
-    const float w = (j <= p) ? __expf(sc - mn) : 0.f;
-    const float alpha = __expf(m - mn);  // 0 on the first step (m = -inf)
-    ssum = ssum * alpha + pf_wave_sum(w);
-    e[l] = w;
-    __syncthreads();
-    if (l < D) {
-      float a = acc * alpha;
-      const int jn = min(64, p + 1 - j0);
-      for (int jj = 0; jj < jn; jj++) a = __builtin_fmaf(e[jj], V[(size_t)(j0 + jj) * D + l], a);
-      acc = a;
-    }
-    m = mn;
-    __syncthreads();
   }
-  if (l < D) out[(size_t)t * E + h * D + l] = acc / ssum;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const float v = pf_wave_sum(acc[i]);
+    if (l == 0 && row0 + i < V) logits[row0 + i] = v;
+  }
 }
 
 // The id of the largest logit, the lowest among equal ones (NaN never wins;
@@ -249,37 +576,56 @@ __global__ void __launch_bounds__(1024) prefill_argmax(const float *logits, int 
   if (threadIdx.x == 0) *out = bi[0];
 }
 
+// Rows per tile: the largest of 64, 32, 16 that still gives about one tile per
+// CU.  64-row tiles take K in stages of 32 (37 KB of LDS: four workgroups fit a
+// CU), the shorter ones in stages of 64 (half the barriers per input).
+int pick_bm(int n, int N, int splits) {
+  const int tn = N / BN * splits;
+  if (tn * ((n + 63) / 64) >= 240) return 64;
+  if (tn * ((n + 31) / 32) >= 240) return 32;
+  return 16;
+}
+
 template <int WD, int MODE>
-hipError_t gemm_launch(const GemmArgs &g, int m_tiles, hipStream_t s) {
-  const dim3 grid((unsigned)((g.N + 15) / 16), (unsigned)m_tiles);
-  const size_t lds = (MODE == PF_RESID) ? 0 : (size_t)16 * (g.K + 4) * sizeof(float);
-  if (lds > 64 * 1024) {  // wide models: the normalised rows take more than the default 64 KiB
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill_gemm<WD, MODE>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  prefill_gemm<WD, MODE><<<grid, 256, lds, s>>>(g);
+hipError_t gemm_bm(GemmArgs g, hipStream_t s) {
+  const int bm = pick_bm(g.n_rows, g.N, g.splits);
+  g.tiles_m = (g.n_rows + bm - 1) / bm;
+  g.tiles_n = g.N / BN;
+  g.n_tiles = g.tiles_m * g.tiles_n * g.splits;
+  const dim3 grid((unsigned)((g.n_tiles + 7) / 8 * 8));
+  if (bm == 64) prefill_gemm<WD, MODE, 64, 32><<<grid, 256, 0, s>>>(g);
+  else if (bm == 32) prefill_gemm<WD, MODE, 32, 64><<<grid, 256, 0, s>>>(g);
+  else prefill_gemm<WD, MODE, 16, 64><<<grid, 256, 0, s>>>(g);
   return hipGetLastError();
 }
 
 template <int MODE>
-hipError_t gemm_wd(int wd, const GemmArgs &g, int m_tiles, hipStream_t s) {
-  if (wd == WD_F32) return gemm_launch<WD_F32, MODE>(g, m_tiles, s);
-  if (wd == WD_F16) return gemm_launch<WD_F16, MODE>(g, m_tiles, s);
-  return gemm_launch<WD_Q4, MODE>(g, m_tiles, s);
+hipError_t gemm_wd(int wd, const GemmArgs &g, hipStream_t s) {
+  if (wd == WD_F32) return gemm_bm<WD_F32, MODE>(g, s);
+  if (wd == WD_F16) return gemm_bm<WD_F16, MODE>(g, s);
+  return gemm_bm<WD_Q4, MODE>(g, s);
+}
+
+// K parts of a projection: three where K's stages of 64 divide evenly (the
+// partials [3][n][E] fill the n x 3E work buffer at most), else two, else one.
+int pick_splits(int K) {
+  const int st = K / 64;
+  return st % 3 == 0 ? 3 : st % 2 == 0 ? 2 : 1;
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs &p, hipStream_t s) {
   const int E = p.E, F = 4 * p.E, D = p.D, H = p.E / p.D, n = p.n;
-  // (K = E or 4E: a multiple of 64 makes each lane's run of K/16 inputs whole float4 steps)
-  // (the LayerNorm tiles hold 16 rows of E + 4 floats in LDS: at most 160 KiB)
-  if (n < 1 || E % 64 != 0 || D % 4 != 0 || D > 64 || (size_t)16 * (E + 4) * 4 > 160 * 1024)
-    return hipErrorInvalidValue;
-  const int mt = (n + 15) / 16;
+  // E % 64: whole GEMM column tiles (N = 3E, E, 4E) and stages of 64 (K = E, 4E);
+  // E <= 2048: the head's input chunks fit its registers; D of 32 or 64
+  if (n < 1 || E % 64 != 0 || E > 4 * 64 * HEAD_XCH || (D != 32 && D != 64)) return hipErrorInvalidValue;
   const DecodeArgs &a = *p.dec;
-  prefill_embed<<<dim3((unsigned)((E + 255) / 256), (unsigned)n), 256, 0, s>>>(p.tok, a.wte, a.wpe, E, p.p0, p.x);
+  const dim3 rows((unsigned)((n + 3) / 4));
+  // x_n lives in p.att (the attention output's buffer) whenever attention is not
+  // using it; the projections' partial sums in p.qkv once attention has read it
+  float *xn = p.att;
+  prefill_embed_ln<<<rows, 256, 0, s>>>(p.tok, a.wte, a.wpe, E, p.p0, n, a.ln1w, a.ln1b, a.eps, p.x, xn);
   hipError_t e = hipGetLastError();
   const size_t wq = (size_t)3 * E * E, wa = (size_t)E * E, wf = (size_t)F * E;
   auto wptr = [&](const MatW &m, size_t elems_per_layer, int l) {
@@ -292,48 +638,58 @@ hipError_t launch_prefill(const PrefillArgs &p, hipStream_t s) {
   for (int l = 0; l < p.L && e == hipSuccess; l++) {
     GemmArgs g{};
     g.n_rows = n;
-    g.eps = a.eps;
     g.E = E;
     g.D = D;
     g.P = p.P;
     g.p0 = p.p0;
-    // LN1 + QKV, with the new cache rows
+    g.splits = 1;
+    // QKV with the new cache rows (x_n = LN1 of the rows)
     auto q = wptr(a.qkv, wq, l);
-    g.a = p.x; g.w = q.first; g.sz = q.second; g.bias = a.bqkv + (size_t)l * 3 * E;
-    g.gamma = a.ln1w + (size_t)l * E; g.beta = a.ln1b + (size_t)l * E;
+    g.a = xn; g.w = q.first; g.sz = q.second; g.bias = a.bqkv + (size_t)l * 3 * E;
     g.N = 3 * E; g.K = E; g.out = p.qkv;
     g.kc = a.kc + (size_t)l * H * p.P * D; g.vc = a.vc + (size_t)l * H * p.P * D;
-    e = gemm_wd<PF_QKV>(p.wd, g, mt, s);
+    e = gemm_wd<PF_QKV>(p.wd, g, s);
     if (e != hipSuccess) break;
-    prefill_attention<<<dim3((unsigned)n, (unsigned)H), 64, 0, s>>>(p.qkv, g.kc, g.vc, E, D, p.P, p.p0, p.att);
+    const dim3 ag((unsigned)((n + 15) / 16), (unsigned)H);
+    if (D == 64) prefill_attention<64><<<ag, 256, 0, s>>>(p.qkv, g.kc, g.vc, E, p.P, p.p0, n, p.att);
+    else prefill_attention<32><<<ag, 256, 0, s>>>(p.qkv, g.kc, g.vc, E, p.P, p.p0, n, p.att);
     e = hipGetLastError();
     if (e != hipSuccess) break;
-    // attention projection + residual
+    // attention projection (partials), then x += sum + b and x_n = LN2(x)
     auto ap = wptr(a.ap, wa, l);
-    g.a = p.att; g.w = ap.first; g.sz = ap.second; g.bias = a.bap + (size_t)l * E;
-    g.N = E; g.K = E; g.out = p.x;
-    e = gemm_wd<PF_RESID>(p.wd, g, mt, s);
+    g.a = p.att; g.w = ap.first; g.sz = ap.second; g.bias = nullptr;
+    g.N = E; g.K = E; g.out = p.qkv; g.splits = pick_splits(E);
+    e = gemm_wd<PF_PART>(p.wd, g, s);
     if (e != hipSuccess) break;
-    // LN2 + fc + gelu_new
+    prefill_resid_ln<<<rows, 256, 0, s>>>(p.qkv, g.splits, n, E, a.bap + (size_t)l * E, a.ln2w + (size_t)l * E,
+                                          a.ln2b + (size_t)l * E, a.eps, p.x, xn);
+    e = hipGetLastError();
+    if (e != hipSuccess) break;
+    // fc + gelu_new
     auto fc = wptr(a.fc, wf, l);
-    g.a = p.x; g.w = fc.first; g.sz = fc.second; g.bias = a.bfc + (size_t)l * F;
-    g.gamma = a.ln2w + (size_t)l * E; g.beta = a.ln2b + (size_t)l * E;
-    g.N = F; g.K = E; g.out = p.act;
-    e = gemm_wd<PF_GELU>(p.wd, g, mt, s);
+    g.a = xn; g.w = fc.first; g.sz = fc.second; g.bias = a.bfc + (size_t)l * F;
+    g.N = F; g.K = E; g.out = p.act; g.splits = 1;
+    e = gemm_wd<PF_GELU>(p.wd, g, s);
     if (e != hipSuccess) break;
-    // MLP projection + residual
+    // MLP projection (partials), then x += sum + b and x_n = the next LayerNorm
     auto pr = wptr(a.pr, wf, l);
-    g.a = p.act; g.w = pr.first; g.sz = pr.second; g.bias = a.bpr + (size_t)l * E;
-    g.N = E; g.K = F; g.out = p.x;
-    e = gemm_wd<PF_RESID>(p.wd, g, mt, s);
+    g.a = p.act; g.w = pr.first; g.sz = pr.second; g.bias = nullptr;
+    g.N = E; g.K = F; g.out = p.qkv; g.splits = pick_splits(F);
+    e = gemm_wd<PF_PART>(p.wd, g, s);
+    if (e != hipSuccess) break;
+    const bool last = l + 1 == p.L;
+    const float *gam = last ? a.lnfw : a.ln1w + (size_t)(l + 1) * E;
+    const float *bet = last ? a.lnfb : a.ln1b + (size_t)(l + 1) * E;
+    prefill_resid_ln<<<rows, 256, 0, s>>>(p.qkv, g.splits, n, E, a.bpr + (size_t)l * E, gam, bet, a.eps, p.x, xn);
+    e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
-  // final LayerNorm of the last row, the head, the argmax
-  GemmArgs g{};
-  g.a = p.x; g.a_row0 = n - 1; g.n_rows = 1;
-  g.w = a.head; g.sz = nullptr; g.bias = nullptr; g.gamma = a.lnfw; g.beta = a.lnfb; g.eps = a.eps;
-  g.N = p.V; g.K = E; g.out = a.logits;
-  e = gemm_wd<PF_HEAD>(p.head_wd, g, 1, s);
+  // the head on the last row of x_n (the final LayerNorm), the argmax
+  const float *xl = xn + (size_t)(n - 1) * E;
+  const dim3 hg((unsigned)((p.V + 15) / 16));
+  if (p.head_wd == WD_F16) prefill_head<WD_F16><<<hg, 256, 0, s>>>(a.head, xl, E, p.V, a.logits);
+  else prefill_head<WD_F32><<<hg, 256, 0, s>>>(a.head, xl, E, p.V, a.logits);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   prefill_argmax<<<1, 1024, 0, s>>>(a.logits, p.V, p.argmax);
   return hipGetLastError();
