@@ -172,20 +172,20 @@ struct WStage;
 template <int BK>
 struct WStage<WD_F32, BK> {
   static constexpr int C4 = BK / 4, N = 64 * C4 / 256;  // float4 per row; per thread
-  float4 v[N];
+  pf_f4 v[N];
   __device__ void load(const GemmArgs &g, int n0, int k0, int tid) {
     const float *w = static_cast<const float *>(g.w);
 #pragma unroll
     for (int i = 0; i < N; i++) {
       const int f = tid + i * 256, row = f / C4, c4 = f % C4;
-      v[i] = *reinterpret_cast<const float4 *>(w + (size_t)(n0 + row) * g.K + k0 + c4 * 4);
+      v[i] = *reinterpret_cast<const pf_f4 *>(w + (size_t)(n0 + row) * g.K + k0 + c4 * 4);
     }
   }
   __device__ void store(float (*ws)[BK + 4], int tid) const {
 #pragma unroll
     for (int i = 0; i < N; i++) {
       const int f = tid + i * 256, row = f / C4, c4 = f % C4;
-      *reinterpret_cast<float4 *>(&ws[row][c4 * 4]) = v[i];
+      *reinterpret_cast<pf_f4 *>(&ws[row][c4 * 4]) = v[i];
     }
   }
 };
@@ -247,7 +247,7 @@ __global__ void __launch_bounds__(256) prefill_gemm(GemmArgs g) {
   constexpr int WM = BM >= 32 ? 2 : 1, WN = 4 / WM;
   constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
   constexpr int AF4 = BM * BK / 4;                  // float4 of an A stage
-  constexpr int AI = (AF4 + 255) / 256;             // per thread
+  constexpr int AI = AF4 / 256;                     // per thread
   __shared__ float as[2][BM][LDK];
   __shared__ float ws[2][BN][LDK];
   // XCD-aware tile order: workgroup id -> XCD id % 8; each XCD takes a run of
@@ -262,22 +262,25 @@ __global__ void __launch_bounds__(256) prefill_gemm(GemmArgs g) {
   const int KT = g.K / BK / g.splits, kbase = sp * KT * BK;  // this tile's part of K
 
   constexpr int AC4 = BK / 4;                       // float4 per A row
-  float4 av[AI];
+  pf_f4 av[AI];
   WStage<WD, BK> wst;
+  // Rows past the last (a ragged last tile) load the last row again: they only
+  // feed output rows that are never written.  The loads are unconditional so
+  // that nothing waits for them before the stage's products.  (Staging values
+  // are native vectors: arrays of the float4 struct were kept in scratch.)
+  static_assert(AF4 % 256 == 0, "an A stage is whole float4 per thread");
   auto load_a = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < AI; i++) {
-      const int f = tid + i * 256, row = f / AC4, c4 = f % AC4;
-      av[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (f < AF4 && m0 + row < g.n_rows)
-        av[i] = *reinterpret_cast<const float4 *>(g.a + (size_t)(m0 + row) * g.K + k0 + c4 * 4);
+      const int f = tid + i * 256, row = min(m0 + f / AC4, g.n_rows - 1), c4 = f % AC4;
+      av[i] = *reinterpret_cast<const pf_f4 *>(g.a + (size_t)row * g.K + k0 + c4 * 4);
     }
   };
   auto store_a = [&](int b) {
 #pragma unroll
     for (int i = 0; i < AI; i++) {
       const int f = tid + i * 256, row = f / AC4, c4 = f % AC4;
-      if (f < AF4) *reinterpret_cast<float4 *>(&as[b][row][c4 * 4]) = av[i];
+      *reinterpret_cast<pf_f4 *>(&as[b][row][c4 * 4]) = av[i];
     }
   };
 
@@ -300,27 +303,27 @@ __global__ void __launch_bounds__(256) prefill_gemm(GemmArgs g) {
     }
     // slot gs of the stage: inputs gs*BK/4 .. (gs+1)*BK/4 - 1, one per step
     constexpr int RUN = BK / 16;  // float4 per run
-    float4 ar[TM][RUN], wr[TN][RUN];
+    pf_f4 ar[TM][RUN], wr[TN][RUN];
 #pragma unroll
     for (int i = 0; i < TM; i++)
 #pragma unroll
       for (int h = 0; h < RUN; h++)
-        ar[i][h] = *reinterpret_cast<const float4 *>(&as[b][mw + i * 16 + r][gs * (BK / 4) + 4 * h]);
+        ar[i][h] = *reinterpret_cast<const pf_f4 *>(&as[b][mw + i * 16 + r][gs * (BK / 4) + 4 * h]);
 #pragma unroll
     for (int j = 0; j < TN; j++)
 #pragma unroll
       for (int h = 0; h < RUN; h++)
-        wr[j][h] = *reinterpret_cast<const float4 *>(&ws[b][nw + j * 16 + r][gs * (BK / 4) + 4 * h]);
+        wr[j][h] = *reinterpret_cast<const pf_f4 *>(&ws[b][nw + j * 16 + r][gs * (BK / 4) + 4 * h]);
 #pragma unroll
     for (int h = 0; h < RUN; h++) {
 #pragma unroll
       for (int i = 0; i < TM; i++)
 #pragma unroll
         for (int j = 0; j < TN; j++) {
-          c[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ar[i][h].x, wr[j][h].x, c[i][j], 0, 0, 0);
-          c[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ar[i][h].y, wr[j][h].y, c[i][j], 0, 0, 0);
-          c[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ar[i][h].z, wr[j][h].z, c[i][j], 0, 0, 0);
-          c[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ar[i][h].w, wr[j][h].w, c[i][j], 0, 0, 0);
+          c[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ar[i][h][0], wr[j][h][0], c[i][j], 0, 0, 0);
+          c[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ar[i][h][1], wr[j][h][1], c[i][j], 0, 0, 0);
+          c[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ar[i][h][2], wr[j][h][2], c[i][j], 0, 0, 0);
+          c[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ar[i][h][3], wr[j][h][3], c[i][j], 0, 0, 0);
         }
     }
     if (kt + 1 < KT) {
