@@ -7,11 +7,14 @@ second over the timed steps, with weights and prompt already resident on the
 GPU.  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--config 2..5] [--only] [--no-cpu-baseline]
+                  [--prefill-only]
 
 The headline workload (--config, default 2) gives the line's value and roofline;
 the other three 124M workloads are timed in the same run, each in
 "other_configs" with its own value, per-pass time and roofline (--only skips
-them).
+them).  "prefill" times gpt2_prefill on the fp32 124M model: one call takes a
+1024-id prompt through every layer at once (GEMMs and attention on the matrix
+cores), so it is rated in tokens/s and against the fp32 matrix-core peak.
 """
 import argparse
 import hashlib
@@ -26,6 +29,8 @@ sys.path.insert(0, ROOT)
 import numpy as np  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+MFMA_F32_PEAK_TFS = 157.3  # MI355X dense fp32 matrix-core peak, TFLOP/s
+PREFILL_N = 1024       # prompt ids per timed prefill call
 
 
 def bytes_per_step(cfg, p):
@@ -177,6 +182,65 @@ def config_line(cfg, m):
     }
 
 
+def prefill_flops(cfg, n, p0=0):
+    """Algorithmic flops of one gpt2_prefill call of n ids from position p0:
+    2 per multiply-add of the four block linears for every row, the causal
+    attention (q.k and the weighted value sum over keys 0..p0+t for row t), and
+    the head for the last row."""
+    E, V, L = cfg.n_embd, cfg.vocab, cfg.n_layer
+    linears = 2 * n * L * (3 * E * E + E * E + 4 * E * E + 4 * E * E)
+    keys = sum(p0 + t + 1 for t in range(n))
+    attention = L * 2 * 2 * E * keys
+    return linears + attention + 2 * V * E
+
+
+def time_prefill(cfg, n, steps, warmup, torch, g2):
+    """Time `steps` gpt2_prefill calls of one seeded n-id prompt from position 0
+    (HIP events on the library's stream, and the host clock around the loop)."""
+    import synth
+    model = synth.make_model(cfg)
+    ctx = g2.gpt2_load(cfg.n_layer, cfg.n_embd, cfg.n_head, cfg.n_positions, cfg.vocab, model.t,
+                       wdtype=cfg.wdtype, ln_eps=cfg.ln_eps, q4_group=cfg.q4_group)
+    del model
+    prompt = np.random.default_rng(20241).integers(0, cfg.vocab, n).astype(np.int32)
+    stream = torch.cuda.current_stream()
+    g2.gpt2_set_stream(ctx, stream.cuda_stream)
+    for _ in range(warmup):
+        g2.gpt2_reset(ctx)
+        g2.gpt2_prefill(ctx, prompt, want_logits=False)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for ev in starts + ends:
+        ev.record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        g2.gpt2_reset(ctx)
+        starts[i].record(stream)
+        g2.gpt2_prefill(ctx, prompt, want_logits=False)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)]))
+    ctx.close()
+    torch.cuda.synchronize()
+    flops = prefill_flops(cfg, n)
+    achieved = flops / (ms * 1e-3) / 1e12
+    return {
+        "workload": f"{cfg.name}: one {n}-id prompt from position 0 through every layer in one gpt2_prefill "
+                    f"call (then its last row's logits and argmax), batch 1",
+        "value": round(n * steps / wall, 1),
+        "unit": "tok/s",
+        "ms_per_call": round(wall * 1e3 / steps, 4),
+        "event_ms_per_call": round(ms, 4),
+        "flops_per_call": flops,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F32_PEAK_TFS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_F32_PEAK_TFS, 4), "traffic": None},
+        "roofline_note": "algorithmic flops of the whole call (linears, causal attention, head) over its "
+                         "event-timed duration, against the dense fp32 matrix-core peak",
+    }
+
+
 def workload_name(cfg):
     return (f"{cfg.name}: {cfg.n_prompt} prompt ids + {cfg.n_new} greedy ids = {cfg.n_steps} one-token "
             f"forward passes, batch 1")
@@ -191,6 +255,8 @@ def main():
     ap.add_argument("--only", action="store_true",
                     help="time the headline workload alone (no per-config lines for the others)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only gpt2_prefill (fp32 124M, one 1024-id prompt per call) and print its line")
     ap.add_argument("--sync-steps", type=int, default=30,
                     help="gpt2_step calls timed for the synchronous per-token rate")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -217,6 +283,12 @@ def main():
     import transformer_decode_token_amd as g2
 
     torch.cuda.init()
+    if args.prefill_only:
+        print(f"[bench] prefill: {args.warmup} warm-up + {args.steps} timed calls of {PREFILL_N} ids",
+              file=sys.stderr, flush=True)
+        print(json.dumps({"prefill": time_prefill(synth.CONFIGS[2], PREFILL_N, args.steps, args.warmup, torch, g2)}),
+              flush=True)
+        return
     head_cfg = synth.CONFIGS[args.config]
     others = [] if args.only else [k for k in (2, 3, 4, 5) if k != args.config]
     results = {}
@@ -255,6 +327,10 @@ def main():
         "sync_step_tok_per_s": h["sync_step_tok_per_s"],
         "other_configs": {str(k): results[k] for k in others},
     }
+    if not args.only:
+        print(f"[bench] prefill: {args.warmup} warm-up + {args.steps} timed calls of {PREFILL_N} ids",
+              file=sys.stderr, flush=True)
+        out["prefill"] = time_prefill(synth.CONFIGS[2], PREFILL_N, args.steps, args.warmup, torch, g2)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(head_cfg)

@@ -5,8 +5,6 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include <string>
-
 namespace gpt2dec {
 
 enum { WD_F32 = 0, WD_F16 = 1, WD_Q4 = 2 };
@@ -87,9 +85,6 @@ struct DecodeArgs {
   int head_lds_rows;                 // output-head rows a workgroup keeps in LDS (set at launch)
 };
 
-// The message gpt2_last_error(NULL) returns for this thread (a failed load).
-void set_load_error(const std::string &msg);
-
 // Shape instantiations compiled into the library.
 struct ShapeInfo {
   int E, D, G, threads;
@@ -102,20 +97,6 @@ bool shape_info(int E, int D, ShapeInfo *out);
 hipError_t launch_decode(int E, int D, int wd, const DecodeArgs &a, hipStream_t s);
 // Occupancy check: blocks of the decode kernel per CU.
 hipError_t decode_occupancy(int E, int D, int wd, int *blocks_per_cu);
-
-// Batched prompt prefill (prefill.hip): n positions p0 .. p0+n-1 through every
-// layer together (their cache rows written), then the last row's logits and
-// argmax (-1 when all are NaN).
-struct PrefillArgs {
-  const DecodeArgs *dec;     // the context's weights, cache, logits
-  int wd, head_wd;           // block-matrix and head storage
-  int L, E, D, P, V;
-  int n, p0;
-  const int *tok;            // [n] device
-  float *x, *qkv, *att, *act;  // device work rows: [n][E], [n][3E], [n][E], [n][4E]
-  int *argmax;               // the argmax (device-visible)
-};
-hipError_t launch_prefill(const PrefillArgs &p, hipStream_t s);
 
 // Load-time re-layout (relayout.hip).
 // src: Conv1D [K][N] fp32 (device); dst: [N][K] fp32.

@@ -16,7 +16,7 @@
 #include <vector>
 
 #include "../../include/gpt2dec.h"
-#include "dec_internal.h"
+#include "lib_internal.h"
 
 using namespace gpt2dec;
 

@@ -24,7 +24,7 @@
 #include <vector>
 
 #include "../../include/gpt2dec.h"
-#include "dec_internal.h"
+#include "lib_internal.h"
 #include "json_min.h"
 
 using gpt2dec::JParser;

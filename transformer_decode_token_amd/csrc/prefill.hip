@@ -33,7 +33,7 @@
 
 #include <utility>
 
-#include "dec_internal.h"
+#include "lib_internal.h"
 
 namespace gpt2dec {
 namespace {
