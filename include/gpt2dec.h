@@ -18,7 +18,12 @@
  *    them and they are only read (or written, for outputs) during the call.
  *  - The library owns all device memory and the context.  Work runs on the
  *    context's HIP stream (library-created, or the caller's via
- *    gpt2_set_stream); every call that returns host data synchronizes it.
+ *    gpt2_set_stream).  A call returns once its host results are final:
+ *    gpt2_step without logits and the gpt2_generate calls (except
+ *    gpt2_generate_noalloc) return as soon as their ids have reached host
+ *    memory, when nothing of the launch can fail any more, possibly before its
+ *    workgroups have exited; later work on the same stream stays ordered
+ *    after it.  Every other call synchronizes the stream.
  *  - Return value 0 = success, or one of the negative GPT2_E_* codes below.
  *    Arguments are validated before any device work, so a rejected call
  *    changes nothing.  After GPT2_E_DEVICE or GPT2_E_NUMERIC the context is
@@ -110,7 +115,9 @@ GPT2DEC_API int gpt2_load_safetensors(const char *safetensors_path, const char *
 GPT2DEC_API int gpt2_get_config(const gpt2_ctx *c, gpt2_config *out);
 
 /* Run later work on `hip_stream` (a hipStream_t, e.g. torch's current stream;
- * NULL = the library's own stream).  The stream must outlive its use. */
+ * NULL = the library's own stream).  The stream must outlive its use.  The
+ * previous stream is synchronized first, so no launch of this context runs
+ * on two streams at once.  Errors: GPT2_E_DEVICE, GPT2_E_STATE. */
 GPT2DEC_API int gpt2_set_stream(gpt2_ctx *c, void *hip_stream);
 
 /* One decode step: token_id at `position` (0 <= position <= filled and

@@ -6,6 +6,7 @@
 // or per gpt2_generate (the whole greedy run chained on the device).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -191,6 +192,31 @@ int validate_config(const gpt2_config *c, ShapeInfo *si, std::string &msg) {
   return GPT2_OK;
 }
 
+// Waits for the n_out ids of the launch just queued to appear in mapped host
+// memory.  Workgroup 0 writes the last one after every workgroup has published
+// its part of the last pass, and no wait of the launch comes after it, so once
+// every id is visible the launch can no longer fail: the caller returns without
+// waiting for the kernel's exit (the stream keeps later launches behind it).
+// False, with nothing consumed, when the error word is raised or the stream
+// drains without the ids: the caller then takes the synchronising path.
+bool wait_for_ids(gpt2_ctx *c, int n_out) {
+  const volatile int *ih = c->ids_h;
+  const volatile int *eh = c->err_h;
+  for (unsigned it = 1;; it++) {
+    if (eh[0] != ERR_NONE) return false;
+    if (ih[n_out - 1] != -1) {
+      bool all = true;
+      for (int i = 0; i < n_out - 1; i++) all = all && ih[i] != -1;
+      if (all) {
+        std::atomic_thread_fence(std::memory_order_acquire);
+        return true;
+      }
+    }
+    if ((it & 1023) == 0 && hipStreamQuery(c->stream) != hipErrorNotReady) return false;
+    __builtin_ia32_pause();
+  }
+}
+
 // Launch `nsteps` forward passes; see gpt2_step / gpt2_generate.  With
 // inv_temp > 0 the n_out recorded ids are drawn (draws[k] for the k-th).
 // With in_scratch the run's working words are the device's static scratch,
@@ -265,11 +291,15 @@ int run(gpt2_ctx *c, const int *feed, int n_feed, int pos0, int nsteps, int out_
   e = launch_decode(c->E, c->D, c->wd, a, c->stream);
   if (!in_scratch) c->epoch += (uint32_t)used;
   if (e != hipSuccess) return c->device_fail(e, "decode launch");
-  if (logits_out)
-    e = hipMemcpyAsync(c->logits_h, c->base.logits, sizeof(float) * (size_t)c->V, hipMemcpyDeviceToHost,
-                       c->stream);
-  if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
-  if (e != hipSuccess) return c->device_fail(e, "decode run");
+  if (!logits_out && !a.trace && !in_scratch && n_out > 0 && wait_for_ids(c, n_out)) {
+    // the ids are in: the launch's remaining work is its workgroups' exit
+  } else {
+    if (logits_out)
+      e = hipMemcpyAsync(c->logits_h, c->base.logits, sizeof(float) * (size_t)c->V, hipMemcpyDeviceToHost,
+                         c->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    if (e != hipSuccess) return c->device_fail(e, "decode run");
+  }
   const volatile int *eh = c->err_h;
   if (eh[0] == ERR_TIMEOUT) {
     c->poisoned = true;
@@ -572,6 +602,10 @@ int gpt2_load(const gpt2_config *cfg, const gpt2_weights *w, gpt2_ctx **out) {
 int gpt2_set_stream(gpt2_ctx *c, void *hip_stream) {
   int rc;
   if (!usable(c, &rc)) return rc;
+  // a launch may still be finishing on the old stream (its ids already
+  // returned): the next one, on the new stream, must not overlap it
+  const hipError_t e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) return c->device_fail(e, "draining the previous stream");
   c->stream = hip_stream ? static_cast<hipStream_t>(hip_stream) : c->own_stream;
   return GPT2_OK;
 }
