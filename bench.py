@@ -76,6 +76,24 @@ def load_traffic(cfg_key):
     return e
 
 
+def cpu_info():
+    """The host CPU's model name and the number of CPUs this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count()
+    return model, n
+
+
 def cpu_baseline(cfg, seconds=10.0):
     """The oracle (fp32 build), single-threaded, on the GPU host: the same greedy
     run from position 0, repeated until about `seconds` of work."""
@@ -99,9 +117,37 @@ def cpu_baseline(cfg, seconds=10.0):
         runs += 1
     dt = time.perf_counter() - t0
     orc.close()
+    # the algorithmic bytes of the passes timed (the same accounting as the GPU roofline)
+    done, byts = 0, 0
+    while done < n:
+        k = min(cfg.n_steps, n - done)
+        byts += sum(bytes_per_step(cfg, p) for p in range(k))
+        done += k
+    model, ncpu = cpu_info()
     return {"value": round(n / dt, 3), "unit": "tok/s", "cores": 1, "kind": "oracle",
+            "gb_per_s": round(byts / dt / 1e9, 3), "cpu": model, "cpus_available": ncpu,
             "sample": f"{n} forward passes: the {cfg.n_steps}-pass greedy run from position 0, "
                       f"repeated ({runs} started), {dt:.1f} s, one thread"}
+
+
+def stream_read_ceiling(torch, gib=4):
+    """A measured streaming-read rate of this GPU (context for the 8 TB/s vendor
+    peak): torch's sum over a `gib` GiB fp32 tensor, best of 5."""
+    x = torch.ones((gib << 30) // 4, dtype=torch.float32, device="cuda")
+    x.sum()
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        x.sum()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        best = ms if best is None else min(best, ms)
+    del x
+    torch.cuda.empty_cache()
+    return round((gib << 30) / (best * 1e-3) / 1e9, 1)
 
 
 def time_config(cfg, steps, warmup, sync_steps, torch, g2):
@@ -133,7 +179,9 @@ def time_config(cfg, steps, warmup, sync_steps, torch, g2):
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_launch = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)]))
+    times = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    ms_launch = float(np.mean(times))
+    ms_median = float(np.median(times))
     # synchronous one-token calls (host round trip per token)
     g2.gpt2_reset(ctx)
     torch.cuda.synchronize()
@@ -144,7 +192,7 @@ def time_config(cfg, steps, warmup, sync_steps, torch, g2):
     sync_tok_s = ns / (time.perf_counter() - ts) if ns else None
     ctx.close()
     torch.cuda.synchronize()
-    return {"wall_s": wall, "ms_launch": ms_launch, "sync_tok_s": sync_tok_s}
+    return {"wall_s": wall, "ms_launch": ms_launch, "ms_median": ms_median, "sync_tok_s": sync_tok_s}
 
 
 def roofline(cfg, ms_launch):
@@ -174,7 +222,9 @@ def config_line(cfg, m):
         "value": round(cfg.n_steps * m["steps"] / m["wall_s"], 2),
         "unit": "tok/s",
         "ms_per_step": round(m["wall_s"] * 1e3 / m["steps"], 4),
+        "generated_tok_per_s": round(cfg.n_new * m["steps"] / m["wall_s"], 2),
         "decode_kernel_ms_per_launch": round(m["ms_launch"], 4),
+        "median_us_per_token": round(m["ms_median"] * 1e3 / cfg.n_steps, 2),
         "us_per_token": round(m["ms_launch"] * 1e3 / cfg.n_steps, 2),
         "algorithmic_bytes_per_launch": alg,
         "roofline": rf,
@@ -321,8 +371,10 @@ def main():
         "roofline": h["roofline"],
         "roofline_note": "frac = algorithmic bytes (each weight once per pass + K/V rows read) over the "
                          "event-timed launch; dram_read_frac = the counted FETCH_SIZE bytes over the same time",
+        "generated_tok_per_s": h["generated_tok_per_s"],
         "decode_kernel_ms_per_launch": h["decode_kernel_ms_per_launch"],
         "us_per_token": h["us_per_token"],
+        "median_us_per_token": h["median_us_per_token"],
         "algorithmic_bytes_per_launch": h["algorithmic_bytes_per_launch"],
         "sync_step_tok_per_s": h["sync_step_tok_per_s"],
         "other_configs": {str(k): results[k] for k in others},
@@ -331,9 +383,16 @@ def main():
         print(f"[bench] prefill: {args.warmup} warm-up + {args.steps} timed calls of {PREFILL_N} ids",
               file=sys.stderr, flush=True)
         out["prefill"] = time_prefill(synth.CONFIGS[2], PREFILL_N, args.steps, args.warmup, torch, g2)
+    if not args.only:
+        print("[bench] streaming-read ceiling", file=sys.stderr, flush=True)
+        out["measured_stream_read_GBs"] = stream_read_ceiling(torch)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(head_cfg)
+        if not args.only:
+            # the other weight types' oracle rates (shorter samples: context only)
+            out["cpu_baseline_other"] = {str(k): cpu_baseline(synth.CONFIGS[k], seconds=4.0)
+                                         for k in (3, 4) if k != args.config}
     print(json.dumps(out), flush=True)
 
 
