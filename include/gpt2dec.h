@@ -104,7 +104,9 @@ GPT2DEC_API int gpt2_load(const gpt2_config *cfg, const gpt2_weights *w, gpt2_ct
  * do (model_type gpt2, activation_function gelu_new, scale_attn_weights true,
  * scale_attn_by_inverse_layer_idx, reorder_and_upcast_attn and
  * add_cross_attention false, each passing when absent; n_embd a multiple of
- * n_head; n_inner null or 4 * n_embd; layer_norm_epsilon 1e-5 when absent).
+ * n_head; n_inner null or 4 * n_embd; layer_norm_epsilon 1e-5 when absent;
+ * n_layer <= 1024, n_embd and n_head <= 65536, n_positions <= 2^20 and
+ * vocab_size <= 2^24, limits far above any GPT-2).
  * wdtype as gpt2_config; int4 groups of 32.  Every file and configuration check
  * runs before any device work: a rejected call is GPT2_E_INVAL with the reason
  * in gpt2_last_error(NULL).  Otherwise errors as gpt2_load. */

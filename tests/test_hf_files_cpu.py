@@ -59,6 +59,9 @@ def test_valid_files_reach_the_device_step(model, tmp_path, prefix):
     ({"n_inner": 1000}, "n_inner"),
     ({"n_layer": ...}, "n_layer"),
     ({"vocab_size": 2.5}, "vocab_size"),
+    # dimensions far beyond any GPT-2 (their tensors' sizes would leave 64-bit arithmetic)
+    ({"n_embd": 1 << 30, "n_head": 1}, "n_embd"),
+    ({"vocab_size": 1 << 25}, "vocab_size"),
     ({"layer_norm_epsilon": -1}, "layer_norm_epsilon"),
 ])
 def test_config_checks(model, tmp_path, override, needle):

@@ -128,12 +128,15 @@ bool read_config(const char *path, gpt2_config &cfg, std::string &err) {
       !need_bool("scale_attn_weights", true) || !need_bool("scale_attn_by_inverse_layer_idx", false) ||
       !need_bool("reorder_and_upcast_attn", false) || !need_bool("add_cross_attention", false))
     return false;
+  // (the upper limits, far above any GPT-2, keep every tensor's element count
+  // and byte range in 64-bit arithmetic)
   long long L, E, H, P, V;
   const char *names[5] = {"n_layer", "n_embd", "n_head", "n_positions", "vocab_size"};
+  const long long limit[5] = {1LL << 10, 1LL << 16, 1LL << 16, 1LL << 20, 1LL << 24};
   long long *dst[5] = {&L, &E, &H, &P, &V};
   for (int i = 0; i < 5; i++) {
-    if (!as_int(root.get(names[i]), *dst[i]) || *dst[i] < 1 || *dst[i] > (1LL << 30)) {
-      err = std::string("config ") + names[i] + " must be a positive integer";
+    if (!as_int(root.get(names[i]), *dst[i]) || *dst[i] < 1 || *dst[i] > limit[i]) {
+      err = std::string("config ") + names[i] + " must be an integer in [1, " + std::to_string(limit[i]) + "]";
       return false;
     }
   }
