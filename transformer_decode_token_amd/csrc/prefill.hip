@@ -58,6 +58,16 @@ __device__ __forceinline__ float pf_gelu_new(float x) {
 
 __device__ __forceinline__ float pf_half(unsigned bits) { return __half2float(__ushort_as_half((unsigned short)bits)); }
 
+// GEMM stages sit in LDS as rows of BK floats with no padding; the 16-byte
+// quads of row r are stored in the order q ^ s(r), so that the same quad of
+// 16 consecutive rows (a read) and the quads of one row (a write) fall in
+// distinct banks.  Returns the float offset of quad q in row r.
+template <int BK>
+__device__ __forceinline__ int pf_swz(int r, int q) {
+  constexpr int QR = BK / 4;  // quads per row: 8 or 16
+  return (q ^ ((r / (16 / QR)) & (QR - 1))) * 4;
+}
+
 // ---------------------------------------------------------------- row passes
 // One wave per row; lane l holds the row's float4 chunks l, l + 64, ... (at most
 // HEAD_XCH of them: E <= 2048) in registers.
@@ -166,7 +176,7 @@ struct GemmArgs {
 };
 
 // One stage of weights (64 rows x BK inputs, BK = 32 or 64) in flight, in its
-// storage type; store() writes it to LDS as fp32 rows of BK + 4 floats.
+// storage type; store() writes it to LDS as fp32 rows (quads swizzled).
 template <int WD, int BK>
 struct WStage;
 template <int BK>
@@ -181,11 +191,11 @@ struct WStage<WD_F32, BK> {
       v[i] = *reinterpret_cast<const pf_f4 *>(w + (size_t)(n0 + row) * g.K + k0 + c4 * 4);
     }
   }
-  __device__ void store(float (*ws)[BK + 4], int tid) const {
+  __device__ void store(float (*ws)[BK], int tid) const {
 #pragma unroll
     for (int i = 0; i < N; i++) {
       const int f = tid + i * 256, row = f / C4, c4 = f % C4;
-      *reinterpret_cast<pf_f4 *>(&ws[row][c4 * 4]) = v[i];
+      *reinterpret_cast<pf_f4 *>(&ws[row][pf_swz<BK>(row, c4)]) = v[i];
     }
   }
 };
@@ -201,15 +211,14 @@ struct WStage<WD_F16, BK> {
       v[i] = *reinterpret_cast<const uint4 *>(w + (size_t)(n0 + f / C8) * g.K + k0 + (f % C8) * 8);
     }
   }
-  __device__ void store(float (*ws)[BK + 4], int tid) const {
+  __device__ void store(float (*ws)[BK], int tid) const {
 #pragma unroll
     for (int i = 0; i < N; i++) {
-      const int f = tid + i * 256;
-      float *d = &ws[f / C8][(f % C8) * 8];
-      *reinterpret_cast<float4 *>(d) = make_float4(pf_half(v[i].x & 0xffffu), pf_half(v[i].x >> 16),
-                                                   pf_half(v[i].y & 0xffffu), pf_half(v[i].y >> 16));
-      *reinterpret_cast<float4 *>(d + 4) = make_float4(pf_half(v[i].z & 0xffffu), pf_half(v[i].z >> 16),
-                                                       pf_half(v[i].w & 0xffffu), pf_half(v[i].w >> 16));
+      const int f = tid + i * 256, row = f / C8, q = (f % C8) * 2;
+      *reinterpret_cast<pf_f4 *>(&ws[row][pf_swz<BK>(row, q)]) =
+          pf_f4{pf_half(v[i].x & 0xffffu), pf_half(v[i].x >> 16), pf_half(v[i].y & 0xffffu), pf_half(v[i].y >> 16)};
+      *reinterpret_cast<pf_f4 *>(&ws[row][pf_swz<BK>(row, q + 1)]) =
+          pf_f4{pf_half(v[i].z & 0xffffu), pf_half(v[i].z >> 16), pf_half(v[i].w & 0xffffu), pf_half(v[i].w >> 16)};
     }
   }
 };
@@ -227,29 +236,28 @@ struct WStage<WD_Q4, BK> {
     for (int i = 0; i < NW; i++) q[i] = src[i];
     s = g.sz[e0 / 32];
   }
-  __device__ void store(float (*ws)[BK + 4], int tid) const {
-    float *d = &ws[tid >> 2][(tid & 3) * (BK / 4)];
+  __device__ void store(float (*ws)[BK], int tid) const {
+    const int row = tid >> 2, q0 = (tid & 3) * (BK / 16);  // this thread's first quad of the row
 #pragma unroll
     for (int i = 0; i < NW; i++) {
       float f[8];
 #pragma unroll
       for (int j = 0; j < 8; j++) f[j] = __builtin_fmaf((float)((q[i] >> (4 * j)) & 15u), s.x, s.y);
-      *reinterpret_cast<float4 *>(d + 8 * i) = make_float4(f[0], f[1], f[2], f[3]);
-      *reinterpret_cast<float4 *>(d + 8 * i + 4) = make_float4(f[4], f[5], f[6], f[7]);
+      *reinterpret_cast<pf_f4 *>(&ws[row][pf_swz<BK>(row, q0 + 2 * i)]) = pf_f4{f[0], f[1], f[2], f[3]};
+      *reinterpret_cast<pf_f4 *>(&ws[row][pf_swz<BK>(row, q0 + 2 * i + 1)]) = pf_f4{f[4], f[5], f[6], f[7]};
     }
   }
 };
 
 template <int WD, int MODE, int BM, int BK>
 __global__ void __launch_bounds__(256) prefill_gemm(GemmArgs g) {
-  constexpr int LDK = BK + 4;  // padded stage row, floats
   // waves WM x WN over the tile; each wave owns TM x TN blocks of 16 x 16
   constexpr int WM = BM >= 32 ? 2 : 1, WN = 4 / WM;
   constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
   constexpr int AF4 = BM * BK / 4;                  // float4 of an A stage
   constexpr int AI = AF4 / 256;                     // per thread
-  __shared__ float as[2][BM][LDK];
-  __shared__ float ws[2][BN][LDK];
+  __shared__ float as[2][BM][BK];
+  __shared__ float ws[2][BN][BK];
   // XCD-aware tile order: workgroup id -> XCD id % 8; each XCD takes a run of
   // consecutive tiles, which walk the M tiles of one weight column block first
   const int per = gridDim.x / 8;
@@ -280,7 +288,7 @@ __global__ void __launch_bounds__(256) prefill_gemm(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < AI; i++) {
       const int f = tid + i * 256, row = f / AC4, c4 = f % AC4;
-      *reinterpret_cast<pf_f4 *>(&as[b][row][c4 * 4]) = av[i];
+      *reinterpret_cast<pf_f4 *>(&as[b][row][pf_swz<BK>(row, c4)]) = av[i];
     }
   };
 
@@ -308,12 +316,12 @@ __global__ void __launch_bounds__(256) prefill_gemm(GemmArgs g) {
     for (int i = 0; i < TM; i++)
 #pragma unroll
       for (int h = 0; h < RUN; h++)
-        ar[i][h] = *reinterpret_cast<const pf_f4 *>(&as[b][mw + i * 16 + r][gs * (BK / 4) + 4 * h]);
+        ar[i][h] = *reinterpret_cast<const pf_f4 *>(&as[b][mw + i * 16 + r][pf_swz<BK>(mw + i * 16 + r, gs * (BK / 16) + h)]);
 #pragma unroll
     for (int j = 0; j < TN; j++)
 #pragma unroll
       for (int h = 0; h < RUN; h++)
-        wr[j][h] = *reinterpret_cast<const pf_f4 *>(&ws[b][nw + j * 16 + r][gs * (BK / 4) + 4 * h]);
+        wr[j][h] = *reinterpret_cast<const pf_f4 *>(&ws[b][nw + j * 16 + r][pf_swz<BK>(nw + j * 16 + r, gs * (BK / 16) + h)]);
 #pragma unroll
     for (int h = 0; h < RUN; h++) {
 #pragma unroll
