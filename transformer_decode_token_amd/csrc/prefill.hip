@@ -31,6 +31,7 @@
 // order, so results do not depend on scheduling.
 #include <hip/hip_fp16.h>
 
+#include <type_traits>
 #include <utility>
 
 #include "lib_internal.h"
@@ -377,35 +378,47 @@ __global__ void __launch_bounds__(256) prefill_gemm(GemmArgs g) {
 // Scores are formed transposed, S^T = K Q^T (keys as the A rows, the rows'
 // queries as the B columns), so each lane holds the scores of one row (r) for
 // four keys per 16-key block, which is exactly the B operand of O^T = V^T P^T:
-// the weights never leave the registers.  The running maximum and sum belong
-// to row r in every lane that holds it; the row's maximum over a step is
-// combined over the four lanes of the row (lanes r, r+16, r+32, r+48).  Output
-// dims are spread as d = (D/16) r' + db over the D/16 result blocks db, so a
-// lane reads each value row as one run.
+// the weights never leave the registers.  Slot g of the score contraction
+// takes dims 16 i + 4 g + c (step 4 i + c), so the four lanes of a key row read
+// 64 contiguous bytes per load.  The queries are scaled by log2(e)/sqrt(D) as
+// they are read, so scores are in base-2 units and each weight is one exp2.
+// The running maximum and sum belong to row r in every lane that holds it; the
+// row's maximum over a step is combined over the four lanes of the row (lanes
+// r, r+16, r+32, r+48).  Output dims are spread as d = (D/16) r' + db over the
+// D/16 result blocks db, so a lane reads each value row as one run.  A step
+// wholly below every row's position (all but the last one or two of a block)
+// needs no masking and no clamping of row indices.
+//
+// Balance: a block's work grows with its position.  All workgroups are
+// resident at once, and workgroups i, i + 256, i + 512, ... share a CU (one
+// per CU in each round of 256), so the blocks are taken longest first and
+// every other round in reverse order: each CU gets long and short blocks.
 template <int D>
 __global__ void __launch_bounds__(256) prefill_attention(const float *qkv, const float *kc, const float *vc, int E,
                                                          int P, int p0, int n, float *out) {
-  constexpr int RQ = D / 4;   // a lane's run of dims in the score contraction
+  constexpr int RQ = D / 4;   // a lane's dims in the score contraction
   constexpr int DV = D / 16;  // value dims a lane reads per key (result blocks)
   __shared__ float sm[4][16], sl[4][16];
   __shared__ float so[4][D][17];
   const int wv = threadIdx.x / 64, l = threadIdx.x % 64, r = l & 15, gs = l >> 4;
-  const int nqb = gridDim.x, qb = nqb - 1 - (int)blockIdx.x;  // longest blocks first
-  const int h = blockIdx.y;
+  const int H = E / D, nqb = (n + 15) / 16, total = nqb * H;
+  const int wg = (int)blockIdx.x, round = wg / 256, pos = wg % 256, size = min(256, total - round * 256);
+  const int k = (round & 1) ? round * 256 + size - 1 - pos : wg;  // rank of this workgroup's block by length
+  const int qb = nqb - 1 - k / H, h = k % H;
   const int t0 = qb * 16, t = t0 + r;
   const int jmax = p0 + min(t0 + 15, n - 1);  // last cache row the block may read
   const int pq = min(p0 + t, jmax);           // last key of row r
-  const float scale = 1.0f / sqrtf((float)D);
+  const float qscale = 1.4426950408889634f / sqrtf((float)D);
   float q[RQ];
   {
-    const float *qr = qkv + (size_t)min(t, n - 1) * 3 * E + h * D + gs * RQ;
+    const float *qr = qkv + (size_t)min(t, n - 1) * 3 * E + h * D + 4 * gs;
 #pragma unroll
     for (int i = 0; i < RQ / 4; i++) {
-      const float4 v = *reinterpret_cast<const float4 *>(qr + 4 * i);
-      q[4 * i] = v.x;
-      q[4 * i + 1] = v.y;
-      q[4 * i + 2] = v.z;
-      q[4 * i + 3] = v.w;
+      const float4 v = *reinterpret_cast<const float4 *>(qr + 16 * i);
+      q[4 * i] = v.x * qscale;
+      q[4 * i + 1] = v.y * qscale;
+      q[4 * i + 2] = v.z * qscale;
+      q[4 * i + 3] = v.w * qscale;
     }
   }
   const float *Kh = kc + (size_t)h * P * D, *Vh = vc + (size_t)h * P * D;
@@ -414,16 +427,18 @@ __global__ void __launch_bounds__(256) prefill_attention(const float *qkv, const
 #pragma unroll
   for (int db = 0; db < DV; db++) o[db] = pf_f4{0.f, 0.f, 0.f, 0.f};
 
-  for (int j0 = 64 * wv; j0 <= jmax; j0 += 256) {
+  auto step = [&](int j0, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
     // scores: block kb, element e is key j0 + 16 kb + 4 gs + e of row r
     pf_f4 s[4];
     float kr[4][RQ];
 #pragma unroll
     for (int kb = 0; kb < 4; kb++) {
-      const float *kp = Kh + (size_t)min(j0 + kb * 16 + r, jmax) * D + gs * RQ;
+      const int row = MASKED ? min(j0 + kb * 16 + r, jmax) : j0 + kb * 16 + r;
+      const float *kp = Kh + (size_t)row * D + 4 * gs;
 #pragma unroll
       for (int i = 0; i < RQ / 4; i++) {
-        const float4 v = *reinterpret_cast<const float4 *>(kp + 4 * i);
+        const float4 v = *reinterpret_cast<const float4 *>(kp + 16 * i);
         kr[kb][4 * i] = v.x;
         kr[kb][4 * i + 1] = v.y;
         kr[kb][4 * i + 2] = v.z;
@@ -440,23 +455,24 @@ __global__ void __launch_bounds__(256) prefill_attention(const float *qkv, const
     for (int kb = 0; kb < 4; kb++)
 #pragma unroll
       for (int e = 0; e < 4; e++) {
-        const int j = j0 + kb * 16 + gs * 4 + e;
-        s[kb][e] = (j <= pq) ? s[kb][e] * scale : -INFINITY;
+        if constexpr (MASKED) s[kb][e] = (j0 + kb * 16 + gs * 4 + e <= pq) ? s[kb][e] : -INFINITY;
         mx = fmaxf(mx, s[kb][e]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // a row with no key in this step keeps its maximum (mx = -inf); one whose
-    // first key this is starts from m = -inf, where alpha is 0
+    // (masked: a row with no key in this step keeps its maximum, mx = -inf;
+    // one whose first key this is starts from m = -inf, where alpha is 0)
     const float mn = fmaxf(m, mx);
-    const float alpha = mn == -INFINITY ? 1.f : __expf(m - mn);
+    const float alpha = (MASKED && mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - mn);
     m = mn;
     float ps = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; kb++)
 #pragma unroll
       for (int e = 0; e < 4; e++) {
-        const float p = (j0 + kb * 16 + gs * 4 + e <= pq) ? __expf(s[kb][e] - mn) : 0.f;
+        float p;
+        if constexpr (MASKED) p = (j0 + kb * 16 + gs * 4 + e <= pq) ? __builtin_amdgcn_exp2f(s[kb][e] - mn) : 0.f;
+        else p = __builtin_amdgcn_exp2f(s[kb][e] - mn);
         s[kb][e] = p;
         ps += p;
       }
@@ -468,7 +484,8 @@ __global__ void __launch_bounds__(256) prefill_attention(const float *qkv, const
     for (int kb = 0; kb < 4; kb++)
 #pragma unroll
       for (int e = 0; e < 4; e++) {
-        const float *vp = Vh + (size_t)min(j0 + kb * 16 + gs * 4 + e, jmax) * D + r * DV;
+        const int key = j0 + kb * 16 + gs * 4 + e;
+        const float *vp = Vh + (size_t)(MASKED ? min(key, jmax) : key) * D + r * DV;
         float vv[DV];
         if constexpr (DV == 4) {
           const float4 v = *reinterpret_cast<const float4 *>(vp);
@@ -480,6 +497,10 @@ __global__ void __launch_bounds__(256) prefill_attention(const float *qkv, const
 #pragma unroll
         for (int db = 0; db < DV; db++) o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv[db], s[kb][e], o[db], 0, 0, 0);
       }
+  };
+  for (int j0 = 64 * wv; j0 <= jmax; j0 += 256) {
+    if (j0 + 63 <= p0 + t0) step(j0, std::false_type{});
+    else step(j0, std::true_type{});
   }
   // this wave's partials: row maximum and sum, and O^T (block db, element e:
   // dim DV (4 gs + e) + db of row r)
@@ -504,7 +525,7 @@ __global__ void __launch_bounds__(256) prefill_attention(const float *qkv, const
     float num = 0.f, den = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; w++) {
-      const float f = sm[w][rr] == -INFINITY ? 0.f : __expf(sm[w][rr] - mm);  // waves with no keys add nothing
+      const float f = sm[w][rr] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm[w][rr] - mm);  // waves with no keys add nothing
       num = __builtin_fmaf(f, so[w][d][rr], num);
       den = __builtin_fmaf(f, sl[w][rr], den);
     }
@@ -661,7 +682,7 @@ hipError_t launch_prefill(const PrefillArgs &p, hipStream_t s) {
     g.kc = a.kc + (size_t)l * H * p.P * D; g.vc = a.vc + (size_t)l * H * p.P * D;
     e = gemm_wd<PF_QKV>(p.wd, g, s);
     if (e != hipSuccess) break;
-    const dim3 ag((unsigned)((n + 15) / 16), (unsigned)H);
+    const dim3 ag((unsigned)((n + 15) / 16 * H));
     if (D == 64) prefill_attention<64><<<ag, 256, 0, s>>>(p.qkv, g.kc, g.vc, E, p.P, p.p0, n, p.att);
     else prefill_attention<32><<<ag, 256, 0, s>>>(p.qkv, g.kc, g.vc, E, p.P, p.p0, n, p.att);
     e = hipGetLastError();
