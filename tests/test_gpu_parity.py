@@ -416,15 +416,20 @@ def test_argmax_ties_124m(name):
         am, lg = g2.gpt2_step(ctx, 3, 0)
         assert lg[am0] == lg[partner], partner
         assert am == min(am0, partner), partner
+        # the prefill's head and its two-stage argmax (per-workgroup candidates)
+        g2.gpt2_reset(ctx)
+        am, lg = g2.gpt2_prefill(ctx, [3])
+        assert lg[am0] == lg[partner], partner
+        assert am == min(am0, partner), partner
         ctx.close()
 
 
 @pytest.mark.parametrize("name", ["tiny-rich", "gpt2-124m-fp32"])
 def test_nan_logits_are_an_error(name):
     """A final LayerNorm gain of NaN makes every logit NaN: no greedy id exists.
-    gpt2_step and the device-chained run both return GPT2_E_NUMERIC (the chained
-    run stops inside the kernel instead of feeding a made-up id) and poison the
-    context."""
+    gpt2_step, the device-chained run and gpt2_prefill all return
+    GPT2_E_NUMERIC (the chained run stops inside the kernel instead of feeding a
+    made-up id) and poison the context."""
     cfg = CASES[name]
     t = dict(synth.make_model(cfg).t)
     t["ln_f.weight"] = np.full_like(t["ln_f.weight"], np.nan)
@@ -442,6 +447,11 @@ def test_nan_logits_are_an_error(name):
         g2.gpt2_generate(ctx, np.array([1, 2, 3], np.int32), 5)
     assert e.value.code == g2.GPT2_E_NUMERIC
     assert "NaN" in g2.gpt2_last_error(ctx)
+    ctx.close()
+    ctx = load_gpu(model)
+    with pytest.raises(g2.Gpt2Error) as e:
+        g2.gpt2_prefill(ctx, [1, 2, 3])
+    assert e.value.code == g2.GPT2_E_NUMERIC
     ctx.close()
 
 

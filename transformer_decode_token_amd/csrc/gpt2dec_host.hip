@@ -84,6 +84,7 @@ struct gpt2_ctx {
   size_t tag_sizes[kTagBufs] = {};
   float *draws_d = nullptr, *draws_h = nullptr;  // uniform numbers of a sampled run
   float *pf_x = nullptr, *pf_qkv = nullptr, *pf_att = nullptr, *pf_act = nullptr;  // prefill work rows
+  float *pf_part = nullptr;  // prefill: the projections' K-split partial sums [4][P][E]
   // the no-allocation path: this device's static scratch, the word offsets of
   // the error word and of each tagged buffer in it, and the words one run needs
   uint64_t *scratch = nullptr;
@@ -410,7 +411,9 @@ int load_impl(gpt2_ctx *c, const gpt2_config *cfg, const gpt2_weights *w) {
   c->pf_qkv = c->dalloc<float>((size_t)P * 3 * E * 4);
   c->pf_att = c->dalloc<float>((size_t)P * E * 4);
   c->pf_act = c->dalloc<float>((size_t)P * F * 4);
-  if (!c->pf_x || !c->pf_qkv || !c->pf_att || !c->pf_act) return c->fail(GPT2_E_NOMEM, "allocation failed");
+  c->pf_part = c->dalloc<float>((size_t)4 * P * E * 4);
+  if (!c->pf_x || !c->pf_qkv || !c->pf_att || !c->pf_act || !c->pf_part)
+    return c->fail(GPT2_E_NOMEM, "allocation failed");
   c->draws_h = c->halloc<float>((size_t)P * 4);
   if (!c->draws_d || !c->draws_h) return c->fail(GPT2_E_NOMEM, "allocation failed");
   float *logits = c->dalloc<float>((size_t)V * 4);
@@ -667,7 +670,7 @@ int gpt2_prefill(gpt2_ctx *c, const int *tokens, int n, float *logits_out, int *
   p.n = n;
   p.p0 = c->filled;
   p.tok = c->feed_d;
-  p.x = c->pf_x; p.qkv = c->pf_qkv; p.att = c->pf_att; p.act = c->pf_act;
+  p.x = c->pf_x; p.qkv = c->pf_qkv; p.att = c->pf_att; p.act = c->pf_act; p.part = c->pf_part;
   p.argmax = c->ids_dev;
   c->ids_h[0] = -2;
   e = launch_prefill(p, c->stream);

@@ -20,6 +20,7 @@ struct PrefillArgs {
   int n, p0;
   const int *tok;            // [n] device
   float *x, *qkv, *att, *act;  // device work rows: [n][E], [n][3E], [n][E], [n][4E]
+  float *part;               // device: the projections' K-split partial sums, [4][n][E]
   int *argmax;               // the argmax (device-visible)
 };
 hipError_t launch_prefill(const PrefillArgs &p, hipStream_t s);

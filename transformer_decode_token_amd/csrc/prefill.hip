@@ -27,8 +27,9 @@
 // stage is written to LDS; products and sums are fp32.  Tiles are numbered so
 // that the workgroups on one XCD share weight columns (its L2 holds them).
 // The two projections (N = E) have few column tiles, so their K is split in up
-// to three parts that run as separate tiles; the row pass adds the parts in
-// order, so results do not depend on scheduling.
+// to four parts that run as separate tiles (at 1,024 rows: 768 tiles, three
+// per CU); the row pass adds the parts in order, so results do not depend on
+// scheduling.
 #include <hip/hip_fp16.h>
 
 #include <type_traits>
@@ -132,7 +133,8 @@ __global__ void __launch_bounds__(256) prefill_embed_ln(const int *tok, const fl
 
 // x[t] += (part_0[t] + part_1[t] + ...) + bias, then xn[t] = LN(x[t]).  The
 // parts are a projection's K-split partial sums [S][n][E], added in order.
-__global__ void __launch_bounds__(256) prefill_resid_ln(const float *part, int S, int n, int E, const float *bias,
+template <int S>
+__global__ void __launch_bounds__(256) prefill_resid_ln(const float *part, int n, int E, const float *bias,
                                                         const float *gamma, const float *beta, float eps, float *x,
                                                         float *xn) {
   const int t = blockIdx.x * 4 + threadIdx.x / 64, l = threadIdx.x % 64;
@@ -148,6 +150,7 @@ __global__ void __launch_bounds__(256) prefill_resid_ln(const float *part, int S
     xv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (c < nch) {
       float4 v = *reinterpret_cast<const float4 *>(pr + 4 * c);
+#pragma unroll
       for (int sp = 1; sp < S; sp++) {
         const float4 w = *reinterpret_cast<const float4 *>(pr + sp * ps + 4 * c);
         v = make_float4(v.x + w.x, v.y + w.y, v.z + w.z, v.w + w.w);
@@ -534,13 +537,25 @@ __global__ void __launch_bounds__(256) prefill_attention(const float *qkv, const
 }
 
 // ---------------------------------------------------------------- head
+// The better of two (logit, id) candidates for the argmax: a larger value, or
+// the lower id of equal values; NaN never wins and id -1 is no candidate.
+__device__ __forceinline__ void pf_better(float &v, int &i, float v2, int i2) {
+  if (i2 >= 0 && !__builtin_isnan(v2) && (i < 0 || v2 > v || (v2 == v && i2 < i))) {
+    v = v2;
+    i = i2;
+  }
+}
+
 // logits[v] = head row v . xn for the one normalised row xn; each wave takes
-// four rows at a time, a lane the float4 chunks l, l + 64, ...
+// four rows at a time, a lane the float4 chunks l, l + 64, ...  Each
+// workgroup (16 rows) also leaves its best (logit, id) in best[blockIdx.x].
 template <int HWD>
 __global__ void __launch_bounds__(256) prefill_head(const void *head, const float *xn, int E, int V,
-                                                    float *logits) {
-  const int l = threadIdx.x % 64, nch = E / 4;
-  const int row0 = (blockIdx.x * 4 + threadIdx.x / 64) * 4;
+                                                    float *logits, float2 *best) {
+  __shared__ float bv[4];
+  __shared__ int bi[4];
+  const int l = threadIdx.x % 64, wv = threadIdx.x / 64, nch = E / 4;
+  const int row0 = (blockIdx.x * 4 + wv) * 4;
   float4 xv[HEAD_XCH];
 #pragma unroll
   for (int j = 0; j < HEAD_XCH; j++) {
@@ -568,40 +583,51 @@ __global__ void __launch_bounds__(256) prefill_head(const void *head, const floa
       acc[i] = __builtin_fmaf(w.w, xv[j].w, acc[i]);
     }
   }
+  float mv = -INFINITY;
+  int mi = -1;
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const float v = pf_wave_sum(acc[i]);
-    if (l == 0 && row0 + i < V) logits[row0 + i] = v;
+    if (row0 + i < V) {
+      if (l == 0) logits[row0 + i] = v;
+      pf_better(mv, mi, v, row0 + i);
+    }
+  }
+  if (l == 0) {
+    bv[wv] = mv;
+    bi[wv] = mi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float v = bv[0];
+    int i = bi[0];
+    for (int w = 1; w < 4; w++) pf_better(v, i, bv[w], bi[w]);
+    best[blockIdx.x] = make_float2(v, __int_as_float(i));
   }
 }
 
 // The id of the largest logit, the lowest among equal ones (NaN never wins;
-// -1 when every logit is NaN), by one workgroup.
-__global__ void __launch_bounds__(1024) prefill_argmax(const float *logits, int V, int *out) {
+// -1 when every logit is NaN), from the head workgroups' candidates, by one
+// workgroup.
+__global__ void __launch_bounds__(1024) prefill_argmax(const float2 *best, int nb, int *out) {
   __shared__ float bv[1024];
   __shared__ int bi[1024];
   float v = -INFINITY;
   int idx = -1;
-  for (int i = threadIdx.x; i < V; i += 1024) {
-    const float x = logits[i];
-    if (x > v || (idx < 0 && x == v)) {
-      v = x;
-      idx = i;
-    }
+  for (int i = threadIdx.x; i < nb; i += 1024) {
+    const float2 c = best[i];
+    pf_better(v, idx, c.x, __float_as_int(c.y));
   }
   bv[threadIdx.x] = v;
   bi[threadIdx.x] = idx;
   __syncthreads();
   for (int s = 512; s > 0; s >>= 1) {
     if ((int)threadIdx.x < s) {
-      const float v2 = bv[threadIdx.x + s];
-      const int i2 = bi[threadIdx.x + s];
-      const float v1 = bv[threadIdx.x];
-      const int i1 = bi[threadIdx.x];
-      if (i2 >= 0 && (i1 < 0 || v2 > v1 || (v2 == v1 && i2 < i1))) {
-        bv[threadIdx.x] = v2;
-        bi[threadIdx.x] = i2;
-      }
+      float v1 = bv[threadIdx.x];
+      int i1 = bi[threadIdx.x];
+      pf_better(v1, i1, bv[threadIdx.x + s], bi[threadIdx.x + s]);
+      bv[threadIdx.x] = v1;
+      bi[threadIdx.x] = i1;
     }
     __syncthreads();
   }
@@ -638,11 +664,24 @@ hipError_t gemm_wd(int wd, const GemmArgs &g, hipStream_t s) {
   return gemm_bm<WD_Q4, MODE>(g, s);
 }
 
-// K parts of a projection: three where K's stages of 64 divide evenly (the
-// partials [3][n][E] fill the n x 3E work buffer at most), else two, else one.
+// K parts of a projection (at most four: the partials buffer holds [4][P][E]):
+// the most that divide K's stages of 64 evenly.
 int pick_splits(int K) {
   const int st = K / 64;
-  return st % 3 == 0 ? 3 : st % 2 == 0 ? 2 : 1;
+  return st % 4 == 0 ? 4 : st % 3 == 0 ? 3 : st % 2 == 0 ? 2 : 1;
+}
+
+// x += (the S partial sums in order) + bias; xn = LN(x): one wave per row.
+hipError_t resid_ln(const float *part, int S, int n, int E, const float *bias, const float *gamma, const float *beta,
+                    float eps, float *x, float *xn, hipStream_t s) {
+  const dim3 grid((unsigned)((n + 3) / 4));
+  switch (S) {
+  case 1: prefill_resid_ln<1><<<grid, 256, 0, s>>>(part, n, E, bias, gamma, beta, eps, x, xn); break;
+  case 2: prefill_resid_ln<2><<<grid, 256, 0, s>>>(part, n, E, bias, gamma, beta, eps, x, xn); break;
+  case 3: prefill_resid_ln<3><<<grid, 256, 0, s>>>(part, n, E, bias, gamma, beta, eps, x, xn); break;
+  default: prefill_resid_ln<4><<<grid, 256, 0, s>>>(part, n, E, bias, gamma, beta, eps, x, xn); break;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -651,11 +690,14 @@ hipError_t launch_prefill(const PrefillArgs &p, hipStream_t s) {
   const int E = p.E, F = 4 * p.E, D = p.D, H = p.E / p.D, n = p.n;
   // E % 64: whole GEMM column tiles (N = 3E, E, 4E) and stages of 64 (K = E, 4E);
   // E <= 2048: the head's input chunks fit its registers; D of 32 or 64
-  if (n < 1 || E % 64 != 0 || E > 4 * 64 * HEAD_XCH || (D != 32 && D != 64)) return hipErrorInvalidValue;
+  // the head's argmax candidates ((V + 15) / 16 pairs) reuse the partials buffer
+  if (n < 1 || E % 64 != 0 || E > 4 * 64 * HEAD_XCH || (D != 32 && D != 64) ||
+      (size_t)(p.V + 15) / 16 * sizeof(float2) > (size_t)4 * p.P * E * sizeof(float))
+    return hipErrorInvalidValue;
   const DecodeArgs &a = *p.dec;
   const dim3 rows((unsigned)((n + 3) / 4));
   // x_n lives in p.att (the attention output's buffer) whenever attention is not
-  // using it; the projections' partial sums in p.qkv once attention has read it
+  // using it; the projections' partial sums in p.part
   float *xn = p.att;
   prefill_embed_ln<<<rows, 256, 0, s>>>(p.tok, a.wte, a.wpe, E, p.p0, n, a.ln1w, a.ln1b, a.eps, p.x, xn);
   hipError_t e = hipGetLastError();
@@ -690,12 +732,11 @@ hipError_t launch_prefill(const PrefillArgs &p, hipStream_t s) {
     // attention projection (partials), then x += sum + b and x_n = LN2(x)
     auto ap = wptr(a.ap, wa, l);
     g.a = p.att; g.w = ap.first; g.sz = ap.second; g.bias = nullptr;
-    g.N = E; g.K = E; g.out = p.qkv; g.splits = pick_splits(E);
+    g.N = E; g.K = E; g.out = p.part; g.splits = pick_splits(E);
     e = gemm_wd<PF_PART>(p.wd, g, s);
     if (e != hipSuccess) break;
-    prefill_resid_ln<<<rows, 256, 0, s>>>(p.qkv, g.splits, n, E, a.bap + (size_t)l * E, a.ln2w + (size_t)l * E,
-                                          a.ln2b + (size_t)l * E, a.eps, p.x, xn);
-    e = hipGetLastError();
+    e = resid_ln(p.part, g.splits, n, E, a.bap + (size_t)l * E, a.ln2w + (size_t)l * E, a.ln2b + (size_t)l * E,
+                 a.eps, p.x, xn, s);
     if (e != hipSuccess) break;
     // fc + gelu_new
     auto fc = wptr(a.fc, wf, l);
@@ -706,24 +747,25 @@ hipError_t launch_prefill(const PrefillArgs &p, hipStream_t s) {
     // MLP projection (partials), then x += sum + b and x_n = the next LayerNorm
     auto pr = wptr(a.pr, wf, l);
     g.a = p.act; g.w = pr.first; g.sz = pr.second; g.bias = nullptr;
-    g.N = E; g.K = F; g.out = p.qkv; g.splits = pick_splits(F);
+    g.N = E; g.K = F; g.out = p.part; g.splits = pick_splits(F);
     e = gemm_wd<PF_PART>(p.wd, g, s);
     if (e != hipSuccess) break;
     const bool last = l + 1 == p.L;
     const float *gam = last ? a.lnfw : a.ln1w + (size_t)(l + 1) * E;
     const float *bet = last ? a.lnfb : a.ln1b + (size_t)(l + 1) * E;
-    prefill_resid_ln<<<rows, 256, 0, s>>>(p.qkv, g.splits, n, E, a.bpr + (size_t)l * E, gam, bet, a.eps, p.x, xn);
-    e = hipGetLastError();
+    e = resid_ln(p.part, g.splits, n, E, a.bpr + (size_t)l * E, gam, bet, a.eps, p.x, xn, s);
   }
   if (e != hipSuccess) return e;
   // the head on the last row of x_n (the final LayerNorm), the argmax
   const float *xl = xn + (size_t)(n - 1) * E;
-  const dim3 hg((unsigned)((p.V + 15) / 16));
-  if (p.head_wd == WD_F16) prefill_head<WD_F16><<<hg, 256, 0, s>>>(a.head, xl, E, p.V, a.logits);
-  else prefill_head<WD_F32><<<hg, 256, 0, s>>>(a.head, xl, E, p.V, a.logits);
+  // the head workgroups' argmax candidates go to the (now free) partials buffer
+  const int hb = (p.V + 15) / 16;
+  float2 *best = reinterpret_cast<float2 *>(p.part);
+  if (p.head_wd == WD_F16) prefill_head<WD_F16><<<hb, 256, 0, s>>>(a.head, xl, E, p.V, a.logits, best);
+  else prefill_head<WD_F32><<<hb, 256, 0, s>>>(a.head, xl, E, p.V, a.logits, best);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  prefill_argmax<<<1, 1024, 0, s>>>(a.logits, p.V, p.argmax);
+  prefill_argmax<<<1, 1024, 0, s>>>(best, hb, p.argmax);
   return hipGetLastError();
 }
 
