@@ -629,16 +629,17 @@ def test_load_from_published_files(name, prefix, tmp_path):
 @pytest.mark.parametrize("name,n_prompt", [("tiny-rich", 8), ("tiny-rich-fp16", 8), ("tiny-rich-int4", 8),
                                            ("tiny-long", 300), ("gpt2-124m-fp32", 10), ("gpt2-124m-fp16w", 10),
                                            ("gpt2-124m-int4w", 10), ("gpt2-124m-fp32", 100),
-                                           ("gpt2-124m-int4w", 200), ("gpt2-124m-fp32", 1000),
-                                           ("gpt2-124m-fp16w", 640)])
+                                           ("gpt2-124m-int4w", 200), ("gpt2-124m-int4w", 480),
+                                           ("gpt2-124m-fp32", 1000), ("gpt2-124m-fp16w", 640)])
 def test_prefill_matches_oracle(name, n_prompt):
     """gpt2_prefill (the prompt's positions through every layer together, the
     linears as GEMMs on the matrix cores) against the oracle fed the same prompt
     one position at a time: the last position's logits within the bar and its
     argmax; then decode steps that read the cache rows the prefill wrote, fed
-    the oracle's greedy ids.  The row counts reach every GEMM tile height (16,
-    32 and 64 rows) with a ragged last tile, and attention blocks whose rows
-    end inside a 64-key step."""
+    the oracle's greedy ids.  The row counts reach every GEMM tile shape (16,
+    32 and 64 rows; 48-column QKV tiles at 480, 640 and 1,000 rows) with a
+    ragged last tile, and attention blocks whose rows end inside a 64-key
+    step."""
     cfg = CASES[name]
     model = synth.make_model(cfg)
     rng = np.random.default_rng(n_prompt)

@@ -85,6 +85,7 @@ struct gpt2_ctx {
   float *draws_d = nullptr, *draws_h = nullptr;  // uniform numbers of a sampled run
   float *pf_x = nullptr, *pf_qkv = nullptr, *pf_att = nullptr, *pf_act = nullptr;  // prefill work rows
   float *pf_part = nullptr;  // prefill: the projections' K-split partial sums [4][P][E]
+  int cus = 0;               // the device's compute units
   // the no-allocation path: this device's static scratch, the word offsets of
   // the error word and of each tagged buffer in it, and the words one run needs
   uint64_t *scratch = nullptr;
@@ -341,6 +342,7 @@ int load_impl(gpt2_ctx *c, const gpt2_config *cfg, const gpt2_weights *w) {
   int blocks = 0;
   e = decode_occupancy(E, D, c->wd, &blocks);
   if (e != hipSuccess) return c->device_fail(e, "decode kernel occupancy");
+  c->cus = prop.multiProcessorCount;
   if (blocks < 1 || (long)blocks * prop.multiProcessorCount < G)
     return c->fail(GPT2_E_DEVICE, "device cannot hold %d co-resident workgroups (%d CUs x %d)", G,
                    prop.multiProcessorCount, blocks);
@@ -669,6 +671,7 @@ int gpt2_prefill(gpt2_ctx *c, const int *tokens, int n, float *logits_out, int *
   p.L = c->L; p.E = c->E; p.D = c->D; p.P = c->P; p.V = c->V;
   p.n = n;
   p.p0 = c->filled;
+  p.cus = c->cus;
   p.tok = c->feed_d;
   p.x = c->pf_x; p.qkv = c->pf_qkv; p.att = c->pf_att; p.act = c->pf_act; p.part = c->pf_part;
   p.argmax = c->ids_dev;

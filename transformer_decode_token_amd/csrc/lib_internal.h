@@ -18,6 +18,7 @@ struct PrefillArgs {
   int wd, head_wd;           // block-matrix and head storage
   int L, E, D, P, V;
   int n, p0;
+  int cus;                   // the device's compute units (tile balance)
   const int *tok;            // [n] device
   float *x, *qkv, *att, *act;  // device work rows: [n][E], [n][3E], [n][E], [n][4E]
   float *part;               // device: the projections' K-split partial sums, [4][n][E]

@@ -44,7 +44,6 @@ typedef float pf_f4 __attribute__((ext_vector_type(4)));
 
 enum { PF_QKV = 0, PF_PART = 1, PF_GELU = 2 };
 
-constexpr int BN = 64;        // output columns per GEMM tile
 constexpr int HEAD_XCH = 8;   // float4 chunks of a row a lane keeps (row passes, head): E <= 2048
 
 __device__ __forceinline__ float pf_wave_sum(float v) {
@@ -179,19 +178,23 @@ struct GemmArgs {
   int tiles_m, tiles_n, n_tiles;  // M tiles, N tiles, all tiles (x splits)
 };
 
-// One stage of weights (64 rows x BK inputs, BK = 32 or 64) in flight, in its
-// storage type; store() writes it to LDS as fp32 rows (quads swizzled).
-template <int WD, int BK>
+// One stage of weights (ROWS = 64 or 48 rows x BK = 32 or 64 inputs) in flight,
+// in its storage type, as PIECES loads spread over the 256 threads; store()
+// writes it to LDS as fp32 rows (quads swizzled).  Where the pieces do not
+// divide among the threads, the extra threads load a piece again (no load is
+// conditional) and only the first PIECES store.
+template <int WD, int BK, int ROWS>
 struct WStage;
-template <int BK>
-struct WStage<WD_F32, BK> {
-  static constexpr int C4 = BK / 4, N = 64 * C4 / 256;  // float4 per row; per thread
+template <int BK, int ROWS>
+struct WStage<WD_F32, BK, ROWS> {
+  static constexpr int C4 = BK / 4, PIECES = ROWS * C4;  // float4 per row; per stage
+  static constexpr int N = (PIECES + 255) / 256;
   pf_f4 v[N];
   __device__ void load(const GemmArgs &g, int n0, int k0, int tid) {
     const float *w = static_cast<const float *>(g.w);
 #pragma unroll
     for (int i = 0; i < N; i++) {
-      const int f = tid + i * 256, row = f / C4, c4 = f % C4;
+      const int f = (tid + i * 256) % PIECES, row = f / C4, c4 = f % C4;
       v[i] = *reinterpret_cast<const pf_f4 *>(w + (size_t)(n0 + row) * g.K + k0 + c4 * 4);
     }
   }
@@ -199,19 +202,20 @@ struct WStage<WD_F32, BK> {
 #pragma unroll
     for (int i = 0; i < N; i++) {
       const int f = tid + i * 256, row = f / C4, c4 = f % C4;
-      *reinterpret_cast<pf_f4 *>(&ws[row][pf_swz<BK>(row, c4)]) = v[i];
+      if (PIECES % 256 == 0 || f < PIECES) *reinterpret_cast<pf_f4 *>(&ws[row][pf_swz<BK>(row, c4)]) = v[i];
     }
   }
 };
-template <int BK>
-struct WStage<WD_F16, BK> {
-  static constexpr int C8 = BK / 8, N = 64 * C8 / 256;  // 8-half pieces per row; per thread
+template <int BK, int ROWS>
+struct WStage<WD_F16, BK, ROWS> {
+  static constexpr int C8 = BK / 8, PIECES = ROWS * C8;  // 8-half pieces per row; per stage
+  static constexpr int N = (PIECES + 255) / 256;
   uint4 v[N];
   __device__ void load(const GemmArgs &g, int n0, int k0, int tid) {
     const __half *w = static_cast<const __half *>(g.w);
 #pragma unroll
     for (int i = 0; i < N; i++) {
-      const int f = tid + i * 256;
+      const int f = (tid + i * 256) % PIECES;
       v[i] = *reinterpret_cast<const uint4 *>(w + (size_t)(n0 + f / C8) * g.K + k0 + (f % C8) * 8);
     }
   }
@@ -219,6 +223,7 @@ struct WStage<WD_F16, BK> {
 #pragma unroll
     for (int i = 0; i < N; i++) {
       const int f = tid + i * 256, row = f / C8, q = (f % C8) * 2;
+      if (PIECES % 256 != 0 && f >= PIECES) continue;
       *reinterpret_cast<pf_f4 *>(&ws[row][pf_swz<BK>(row, q)]) =
           pf_f4{pf_half(v[i].x & 0xffffu), pf_half(v[i].x >> 16), pf_half(v[i].y & 0xffffu), pf_half(v[i].y >> 16)};
       *reinterpret_cast<pf_f4 *>(&ws[row][pf_swz<BK>(row, q + 1)]) =
@@ -226,21 +231,24 @@ struct WStage<WD_F16, BK> {
     }
   }
 };
-template <int BK>
-struct WStage<WD_Q4, BK> {
-  // four threads per row, each BK/4 codes (even input in the low nibble) of
-  // one group of 32, and that group's (scale, zero)
-  static constexpr int NW = BK / 32;  // 32-bit words of codes per thread
+template <int BK, int ROWS>
+struct WStage<WD_Q4, BK, ROWS> {
+  // four pieces per row, each BK/4 codes (even input in the low nibble) of
+  // one group of 32, with that group's (scale, zero)
+  static constexpr int NW = BK / 32, PIECES = ROWS * 4;  // 32-bit words of codes per piece
+  static_assert(PIECES <= 256, "one piece per thread");
   uint32_t q[NW];
   float2 s;
   __device__ void load(const GemmArgs &g, int n0, int k0, int tid) {
-    const size_t e0 = (size_t)(n0 + (tid >> 2)) * g.K + k0 + (tid & 3) * (BK / 4);
+    const int f = tid % PIECES;
+    const size_t e0 = (size_t)(n0 + (f >> 2)) * g.K + k0 + (f & 3) * (BK / 4);
     const uint32_t *src = reinterpret_cast<const uint32_t *>(static_cast<const uint8_t *>(g.w) + e0 / 2);
 #pragma unroll
     for (int i = 0; i < NW; i++) q[i] = src[i];
     s = g.sz[e0 / 32];
   }
   __device__ void store(float (*ws)[BK], int tid) const {
+    if (PIECES < 256 && tid >= PIECES) return;
     const int row = tid >> 2, q0 = (tid & 3) * (BK / 16);  // this thread's first quad of the row
 #pragma unroll
     for (int i = 0; i < NW; i++) {
@@ -253,11 +261,13 @@ struct WStage<WD_Q4, BK> {
   }
 };
 
-template <int WD, int MODE, int BM, int BK>
+template <int WD, int MODE, int BM, int BK, int BN>
 __global__ void __launch_bounds__(256) prefill_gemm(GemmArgs g) {
   // waves WM x WN over the tile; each wave owns TM x TN blocks of 16 x 16
-  constexpr int WM = BM >= 32 ? 2 : 1, WN = 4 / WM;
+  // (48-column tiles: the four waves stacked, 16 x 48 each)
+  constexpr int WM = BN == 48 ? 4 : BM >= 32 ? 2 : 1, WN = 4 / WM;
   constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
+  static_assert(TM >= 1 && TN >= 1 && TM * WM * 16 == BM && TN * WN * 16 == BN, "whole 16 x 16 blocks");
   constexpr int AF4 = BM * BK / 4;                  // float4 of an A stage
   constexpr int AI = AF4 / 256;                     // per thread
   __shared__ float as[2][BM][BK];
@@ -275,7 +285,7 @@ __global__ void __launch_bounds__(256) prefill_gemm(GemmArgs g) {
 
   constexpr int AC4 = BK / 4;                       // float4 per A row
   pf_f4 av[AI];
-  WStage<WD, BK> wst;
+  WStage<WD, BK, BN> wst;
   // Rows past the last (a ragged last tile) load the last row again: they only
   // feed output rows that are never written.  The loads are unconditional so
   // that nothing waits for them before the stage's products.  (Staging values
@@ -393,20 +403,21 @@ __global__ void __launch_bounds__(256) prefill_gemm(GemmArgs g) {
 // needs no masking and no clamping of row indices.
 //
 // Balance: a block's work grows with its position.  All workgroups are
-// resident at once, and workgroups i, i + 256, i + 512, ... share a CU (one
-// per CU in each round of 256), so the blocks are taken longest first and
-// every other round in reverse order: each CU gets long and short blocks.
+// resident at once, and workgroups i, i + C, i + 2C, ... share a CU (one per
+// CU in each round of C = the CU count), so the blocks are taken longest
+// first and every other round in reverse order: each CU gets long and short
+// blocks.
 template <int D>
 __global__ void __launch_bounds__(256) prefill_attention(const float *qkv, const float *kc, const float *vc, int E,
-                                                         int P, int p0, int n, float *out) {
+                                                         int P, int p0, int n, int cus, float *out) {
   constexpr int RQ = D / 4;   // a lane's dims in the score contraction
   constexpr int DV = D / 16;  // value dims a lane reads per key (result blocks)
   __shared__ float sm[4][16], sl[4][16];
   __shared__ float so[4][D][17];
   const int wv = threadIdx.x / 64, l = threadIdx.x % 64, r = l & 15, gs = l >> 4;
   const int H = E / D, nqb = (n + 15) / 16, total = nqb * H;
-  const int wg = (int)blockIdx.x, round = wg / 256, pos = wg % 256, size = min(256, total - round * 256);
-  const int k = (round & 1) ? round * 256 + size - 1 - pos : wg;  // rank of this workgroup's block by length
+  const int wg = (int)blockIdx.x, round = wg / cus, pos = wg % cus, size = min(cus, total - round * cus);
+  const int k = (round & 1) ? round * cus + size - 1 - pos : wg;  // rank of this workgroup's block by length
   const int qb = nqb - 1 - k / H, h = k % H;
   const int t0 = qb * 16, t = t0 + r;
   const int jmax = p0 + min(t0 + 15, n - 1);  // last cache row the block may read
@@ -635,33 +646,41 @@ __global__ void __launch_bounds__(1024) prefill_argmax(const float2 *best, int n
 }
 
 // Rows per tile: the largest of 64, 32, 16 that still gives about one tile per
-// CU.  64-row tiles take K in stages of 32 (37 KB of LDS: four workgroups fit a
-// CU), the shorter ones in stages of 64 (half the barriers per input).
-int pick_bm(int n, int N, int splits) {
-  const int tn = N / BN * splits;
-  if (tn * ((n + 63) / 64) >= 240) return 64;
-  if (tn * ((n + 31) / 32) >= 240) return 32;
+// CU.  64-row tiles take K in stages of 32 (32 KB of LDS), the shorter ones
+// in stages of 64 (half the barriers per input).
+int pick_bm(int n, int N, int splits, int cus) {
+  const int tn = N / 64 * splits, enough = cus - cus / 16;
+  if (tn * ((n + 63) / 64) >= enough) return 64;
+  if (tn * ((n + 31) / 32) >= enough) return 32;
   return 16;
 }
 
 template <int WD, int MODE>
-hipError_t gemm_bm(GemmArgs g, hipStream_t s) {
-  const int bm = pick_bm(g.n_rows, g.N, g.splits);
+hipError_t gemm_bm(GemmArgs g, int cus, hipStream_t s) {
+  const int bm = pick_bm(g.n_rows, g.N, g.splits, cus);
   g.tiles_m = (g.n_rows + bm - 1) / bm;
-  g.tiles_n = g.N / BN;
+  // 64-row tiles: 48 columns instead of 64 where that leaves the busiest CU
+  // less work (tiles per CU rounded up, times the tile's width)
+  int bn = 64;
+  if (bm == 64 && g.N % 48 == 0) {
+    const long t64 = (long)g.tiles_m * (g.N / 64) * g.splits, t48 = (long)g.tiles_m * (g.N / 48) * g.splits;
+    if ((t48 + cus - 1) / cus * 48 < (t64 + cus - 1) / cus * 64) bn = 48;
+  }
+  g.tiles_n = g.N / bn;
   g.n_tiles = g.tiles_m * g.tiles_n * g.splits;
   const dim3 grid((unsigned)((g.n_tiles + 7) / 8 * 8));
-  if (bm == 64) prefill_gemm<WD, MODE, 64, 32><<<grid, 256, 0, s>>>(g);
-  else if (bm == 32) prefill_gemm<WD, MODE, 32, 64><<<grid, 256, 0, s>>>(g);
-  else prefill_gemm<WD, MODE, 16, 64><<<grid, 256, 0, s>>>(g);
+  if (bm == 64 && bn == 48) prefill_gemm<WD, MODE, 64, 32, 48><<<grid, 256, 0, s>>>(g);
+  else if (bm == 64) prefill_gemm<WD, MODE, 64, 32, 64><<<grid, 256, 0, s>>>(g);
+  else if (bm == 32) prefill_gemm<WD, MODE, 32, 64, 64><<<grid, 256, 0, s>>>(g);
+  else prefill_gemm<WD, MODE, 16, 64, 64><<<grid, 256, 0, s>>>(g);
   return hipGetLastError();
 }
 
 template <int MODE>
-hipError_t gemm_wd(int wd, const GemmArgs &g, hipStream_t s) {
-  if (wd == WD_F32) return gemm_bm<WD_F32, MODE>(g, s);
-  if (wd == WD_F16) return gemm_bm<WD_F16, MODE>(g, s);
-  return gemm_bm<WD_Q4, MODE>(g, s);
+hipError_t gemm_wd(int wd, const GemmArgs &g, int cus, hipStream_t s) {
+  if (wd == WD_F32) return gemm_bm<WD_F32, MODE>(g, cus, s);
+  if (wd == WD_F16) return gemm_bm<WD_F16, MODE>(g, cus, s);
+  return gemm_bm<WD_Q4, MODE>(g, cus, s);
 }
 
 // K parts of a projection (at most four: the partials buffer holds [4][P][E]):
@@ -691,7 +710,7 @@ hipError_t launch_prefill(const PrefillArgs &p, hipStream_t s) {
   // E % 64: whole GEMM column tiles (N = 3E, E, 4E) and stages of 64 (K = E, 4E);
   // E <= 2048: the head's input chunks fit its registers; D of 32 or 64
   // the head's argmax candidates ((V + 15) / 16 pairs) reuse the partials buffer
-  if (n < 1 || E % 64 != 0 || E > 4 * 64 * HEAD_XCH || (D != 32 && D != 64) ||
+  if (n < 1 || p.cus < 1 || E % 64 != 0 || E > 4 * 64 * HEAD_XCH || (D != 32 && D != 64) ||
       (size_t)(p.V + 15) / 16 * sizeof(float2) > (size_t)4 * p.P * E * sizeof(float))
     return hipErrorInvalidValue;
   const DecodeArgs &a = *p.dec;
@@ -722,18 +741,18 @@ hipError_t launch_prefill(const PrefillArgs &p, hipStream_t s) {
     g.a = xn; g.w = q.first; g.sz = q.second; g.bias = a.bqkv + (size_t)l * 3 * E;
     g.N = 3 * E; g.K = E; g.out = p.qkv;
     g.kc = a.kc + (size_t)l * H * p.P * D; g.vc = a.vc + (size_t)l * H * p.P * D;
-    e = gemm_wd<PF_QKV>(p.wd, g, s);
+    e = gemm_wd<PF_QKV>(p.wd, g, p.cus, s);
     if (e != hipSuccess) break;
     const dim3 ag((unsigned)((n + 15) / 16 * H));
-    if (D == 64) prefill_attention<64><<<ag, 256, 0, s>>>(p.qkv, g.kc, g.vc, E, p.P, p.p0, n, p.att);
-    else prefill_attention<32><<<ag, 256, 0, s>>>(p.qkv, g.kc, g.vc, E, p.P, p.p0, n, p.att);
+    if (D == 64) prefill_attention<64><<<ag, 256, 0, s>>>(p.qkv, g.kc, g.vc, E, p.P, p.p0, n, p.cus, p.att);
+    else prefill_attention<32><<<ag, 256, 0, s>>>(p.qkv, g.kc, g.vc, E, p.P, p.p0, n, p.cus, p.att);
     e = hipGetLastError();
     if (e != hipSuccess) break;
     // attention projection (partials), then x += sum + b and x_n = LN2(x)
     auto ap = wptr(a.ap, wa, l);
     g.a = p.att; g.w = ap.first; g.sz = ap.second; g.bias = nullptr;
     g.N = E; g.K = E; g.out = p.part; g.splits = pick_splits(E);
-    e = gemm_wd<PF_PART>(p.wd, g, s);
+    e = gemm_wd<PF_PART>(p.wd, g, p.cus, s);
     if (e != hipSuccess) break;
     e = resid_ln(p.part, g.splits, n, E, a.bap + (size_t)l * E, a.ln2w + (size_t)l * E, a.ln2b + (size_t)l * E,
                  a.eps, p.x, xn, s);
@@ -742,13 +761,13 @@ hipError_t launch_prefill(const PrefillArgs &p, hipStream_t s) {
     auto fc = wptr(a.fc, wf, l);
     g.a = xn; g.w = fc.first; g.sz = fc.second; g.bias = a.bfc + (size_t)l * F;
     g.N = F; g.K = E; g.out = p.act; g.splits = 1;
-    e = gemm_wd<PF_GELU>(p.wd, g, s);
+    e = gemm_wd<PF_GELU>(p.wd, g, p.cus, s);
     if (e != hipSuccess) break;
     // MLP projection (partials), then x += sum + b and x_n = the next LayerNorm
     auto pr = wptr(a.pr, wf, l);
     g.a = p.act; g.w = pr.first; g.sz = pr.second; g.bias = nullptr;
     g.N = E; g.K = F; g.out = p.part; g.splits = pick_splits(F);
-    e = gemm_wd<PF_PART>(p.wd, g, s);
+    e = gemm_wd<PF_PART>(p.wd, g, p.cus, s);
     if (e != hipSuccess) break;
     const bool last = l + 1 == p.L;
     const float *gam = last ? a.lnfw : a.ln1w + (size_t)(l + 1) * E;
