@@ -163,6 +163,102 @@ __global__ void __launch_bounds__(256) prefill_resid_ln(const float *part, int n
   pf_layernorm_row(xv, E, gamma, beta, eps, xn + (size_t)t * E, l);
 }
 
+// The same for many parts (a short prompt's projections, ns of them): one
+// workgroup per row, a thread per float4 chunk (two at most: E <= 2048), the
+// parts' loads eight at a time and their sums in order; the LayerNorm's two
+// sums are combined over the four waves through LDS.
+__global__ void __launch_bounds__(256) prefill_resid_ln_wg(const float *part, int ns, int n, int E,
+                                                           const float *bias, const float *gamma, const float *beta,
+                                                           float eps, float *x, float *xn) {
+  __shared__ float red[2][4];
+  const int t = blockIdx.x, tid = threadIdx.x, wv = tid / 64, l = tid % 64, nch = E / 4;
+  float *xr = x + (size_t)t * E;
+  const size_t ps = (size_t)n * E;
+  const float *pr = part + (size_t)t * E;
+  pf_f4 xv[2];
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    const int c = tid + 256 * j;
+    xv[j] = pf_f4{0.f, 0.f, 0.f, 0.f};
+    if (c >= nch) continue;
+    pf_f4 v = *reinterpret_cast<const pf_f4 *>(pr + 4 * c);
+    for (int s0 = 1; s0 < ns; s0 += 8) {
+      pf_f4 w[8];
+#pragma unroll
+      for (int u = 0; u < 8; u++) w[u] = *reinterpret_cast<const pf_f4 *>(pr + (size_t)min(s0 + u, ns - 1) * ps + 4 * c);
+#pragma unroll
+      for (int u = 0; u < 8; u++)
+        if (s0 + u < ns) v += w[u];
+    }
+    const pf_f4 b = *reinterpret_cast<const pf_f4 *>(bias + 4 * c);
+    const pf_f4 x0 = *reinterpret_cast<const pf_f4 *>(xr + 4 * c);
+    xv[j] = x0 + (v + b);
+    *reinterpret_cast<pf_f4 *>(xr + 4 * c) = xv[j];
+    sum += (xv[j][0] + xv[j][1]) + (xv[j][2] + xv[j][3]);
+  }
+  sum = pf_wave_sum(sum);
+  if (l == 0) red[0][wv] = sum;
+  __syncthreads();
+  const float mean = ((red[0][0] + red[0][1]) + (red[0][2] + red[0][3])) / (float)E;
+  float q = 0.f;
+#pragma unroll
+  for (int j = 0; j < 2; j++)
+    if (tid + 256 * j < nch)
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const float d = xv[j][e] - mean;
+        q = __builtin_fmaf(d, d, q);
+      }
+  q = pf_wave_sum(q);
+  if (l == 0) red[1][wv] = q;
+  __syncthreads();
+  const float rstd = __builtin_amdgcn_rsqf(((red[1][0] + red[1][1]) + (red[1][2] + red[1][3])) / (float)E + eps);
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    const int c = tid + 256 * j;
+    if (c >= nch) continue;
+    const pf_f4 g = *reinterpret_cast<const pf_f4 *>(gamma + 4 * c);
+    const pf_f4 b = *reinterpret_cast<const pf_f4 *>(beta + 4 * c);
+    pf_f4 o;
+#pragma unroll
+    for (int e = 0; e < 4; e++) o[e] = (xv[j][e] - mean) * rstd * g[e] + b[e];
+    *reinterpret_cast<pf_f4 *>(xn + (size_t)t * E + 4 * c) = o;
+  }
+}
+
+// A K-split QKV or fc: y = (part_0 + part_1 + ...) + bias over [n][N], then
+// QKV: the row, and its key / value part into the cache rows p0 + t;
+// fc: gelu_new of it.
+template <bool QKV>
+__global__ void __launch_bounds__(256) prefill_finish(const float *part, int S, int n, int N, const float *bias,
+                                                      float *out, float *kc, float *vc, int E, int D, int P, int p0) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x, total = (size_t)n * N;
+  if (idx >= total) return;
+  const int t = (int)(idx / N), o = (int)(idx % N);
+  float v = part[idx];
+  // eight parts' loads at a time, then their sums in order
+  for (int s0 = 1; s0 < S; s0 += 8) {
+    float w[8];
+#pragma unroll
+    for (int u = 0; u < 8; u++) w[u] = part[(size_t)min(s0 + u, S - 1) * total + idx];
+#pragma unroll
+    for (int u = 0; u < 8; u++)
+      if (s0 + u < S) v += w[u];
+  }
+  const float y = v + bias[o];
+  if constexpr (QKV) {
+    out[idx] = y;
+    if (o >= E) {
+      const int ev = (o - E) % E, hh = ev / D, d = ev % D;
+      float *cache = (o < 2 * E) ? kc : vc;
+      cache[((size_t)hh * P + p0 + t) * D + d] = y;
+    }
+  } else {
+    out[idx] = pf_gelu_new(y);
+  }
+}
+
 // ---------------------------------------------------------------- GEMM
 struct GemmArgs {
   const float *a;        // [n_rows][K] input rows
@@ -650,8 +746,8 @@ __global__ void __launch_bounds__(1024) prefill_argmax(const float2 *best, int n
 // in stages of 64 (half the barriers per input).
 int pick_bm(int n, int N, int splits, int cus) {
   const int tn = N / 64 * splits, enough = cus - cus / 16;
-  if (tn * ((n + 63) / 64) >= enough) return 64;
-  if (tn * ((n + 31) / 32) >= enough) return 32;
+  if (n > 32 && tn * ((n + 63) / 64) >= enough) return 64;
+  if (n > 16 && tn * ((n + 31) / 32) >= enough) return 32;
   return 16;
 }
 
@@ -683,14 +779,26 @@ hipError_t gemm_wd(int wd, const GemmArgs &g, int cus, hipStream_t s) {
   return gemm_bm<WD_Q4, MODE>(g, cus, s);
 }
 
-// K parts of a projection (at most four: the partials buffer holds [4][P][E]):
-// the most that divide K's stages of 64 evenly.
-int pick_splits(int K) {
-  const int st = K / 64;
+// K parts of a linear [n][K] x [K][N].  With few tiles (a short prompt): as
+// many as keep the tiles within two per CU, so that the weights stream on
+// every CU (their partial sums [d][n][N] must fit the partials buffer of
+// cap floats).  Otherwise a projection (N = E) takes up to four (the most
+// that divide K's stages of 64), the other linears none.
+int pick_splits(int n, int N, int K, bool projection, int cus, size_t cap) {
+  const int bm = pick_bm(n, N, 1, cus), st = K / 64;
+  const long tiles = (long)((n + bm - 1) / bm) * (N / 64);
+  if (tiles < cus / 2) {
+    int best = 1;
+    for (int d = 2; d <= st; d++)
+      if (st % d == 0 && tiles * d <= 2L * cus && (size_t)d * n * N <= cap) best = d;
+    return best;
+  }
+  if (!projection) return 1;
   return st % 4 == 0 ? 4 : st % 3 == 0 ? 3 : st % 2 == 0 ? 2 : 1;
 }
 
-// x += (the S partial sums in order) + bias; xn = LN(x): one wave per row.
+// x += (the S partial sums in order) + bias; xn = LN(x): one wave per row for
+// up to four parts, one workgroup per row for more.
 hipError_t resid_ln(const float *part, int S, int n, int E, const float *bias, const float *gamma, const float *beta,
                     float eps, float *x, float *xn, hipStream_t s) {
   const dim3 grid((unsigned)((n + 3) / 4));
@@ -698,8 +806,20 @@ hipError_t resid_ln(const float *part, int S, int n, int E, const float *bias, c
   case 1: prefill_resid_ln<1><<<grid, 256, 0, s>>>(part, n, E, bias, gamma, beta, eps, x, xn); break;
   case 2: prefill_resid_ln<2><<<grid, 256, 0, s>>>(part, n, E, bias, gamma, beta, eps, x, xn); break;
   case 3: prefill_resid_ln<3><<<grid, 256, 0, s>>>(part, n, E, bias, gamma, beta, eps, x, xn); break;
-  default: prefill_resid_ln<4><<<grid, 256, 0, s>>>(part, n, E, bias, gamma, beta, eps, x, xn); break;
+  case 4: prefill_resid_ln<4><<<grid, 256, 0, s>>>(part, n, E, bias, gamma, beta, eps, x, xn); break;
+  default:
+    prefill_resid_ln_wg<<<dim3((unsigned)n), 256, 0, s>>>(part, S, n, E, bias, gamma, beta, eps, x, xn);
+    break;
   }
+  return hipGetLastError();
+}
+
+template <bool QKV>
+hipError_t finish(const float *part, int S, int n, int N, const float *bias, float *out, float *kc, float *vc, int E,
+                  int D, int P, int p0, hipStream_t s) {
+  const size_t total = (size_t)n * N;
+  prefill_finish<QKV><<<dim3((unsigned)((total + 255) / 256)), 256, 0, s>>>(part, S, n, N, bias, out, kc, vc, E, D,
+                                                                             P, p0);
   return hipGetLastError();
 }
 
@@ -715,6 +835,7 @@ hipError_t launch_prefill(const PrefillArgs &p, hipStream_t s) {
     return hipErrorInvalidValue;
   const DecodeArgs &a = *p.dec;
   const dim3 rows((unsigned)((n + 3) / 4));
+  const size_t cap = (size_t)4 * p.P * E;  // floats of the partials buffer
   // x_n lives in p.att (the attention output's buffer) whenever attention is not
   // using it; the projections' partial sums in p.part
   float *xn = p.att;
@@ -741,7 +862,14 @@ hipError_t launch_prefill(const PrefillArgs &p, hipStream_t s) {
     g.a = xn; g.w = q.first; g.sz = q.second; g.bias = a.bqkv + (size_t)l * 3 * E;
     g.N = 3 * E; g.K = E; g.out = p.qkv;
     g.kc = a.kc + (size_t)l * H * p.P * D; g.vc = a.vc + (size_t)l * H * p.P * D;
-    e = gemm_wd<PF_QKV>(p.wd, g, p.cus, s);
+    g.splits = pick_splits(n, g.N, g.K, false, p.cus, cap);
+    if (g.splits == 1) {
+      e = gemm_wd<PF_QKV>(p.wd, g, p.cus, s);
+    } else {
+      g.out = p.part;
+      e = gemm_wd<PF_PART>(p.wd, g, p.cus, s);
+      if (e == hipSuccess) e = finish<true>(p.part, g.splits, n, g.N, g.bias, p.qkv, g.kc, g.vc, E, D, p.P, p.p0, s);
+    }
     if (e != hipSuccess) break;
     const dim3 ag((unsigned)((n + 15) / 16 * H));
     if (D == 64) prefill_attention<64><<<ag, 256, 0, s>>>(p.qkv, g.kc, g.vc, E, p.P, p.p0, n, p.cus, p.att);
@@ -751,7 +879,7 @@ hipError_t launch_prefill(const PrefillArgs &p, hipStream_t s) {
     // attention projection (partials), then x += sum + b and x_n = LN2(x)
     auto ap = wptr(a.ap, wa, l);
     g.a = p.att; g.w = ap.first; g.sz = ap.second; g.bias = nullptr;
-    g.N = E; g.K = E; g.out = p.part; g.splits = pick_splits(E);
+    g.N = E; g.K = E; g.out = p.part; g.splits = pick_splits(n, E, E, true, p.cus, cap);
     e = gemm_wd<PF_PART>(p.wd, g, p.cus, s);
     if (e != hipSuccess) break;
     e = resid_ln(p.part, g.splits, n, E, a.bap + (size_t)l * E, a.ln2w + (size_t)l * E, a.ln2b + (size_t)l * E,
@@ -760,13 +888,19 @@ hipError_t launch_prefill(const PrefillArgs &p, hipStream_t s) {
     // fc + gelu_new
     auto fc = wptr(a.fc, wf, l);
     g.a = xn; g.w = fc.first; g.sz = fc.second; g.bias = a.bfc + (size_t)l * F;
-    g.N = F; g.K = E; g.out = p.act; g.splits = 1;
-    e = gemm_wd<PF_GELU>(p.wd, g, p.cus, s);
+    g.N = F; g.K = E; g.out = p.act; g.splits = pick_splits(n, F, E, false, p.cus, cap);
+    if (g.splits == 1) {
+      e = gemm_wd<PF_GELU>(p.wd, g, p.cus, s);
+    } else {
+      g.out = p.part;
+      e = gemm_wd<PF_PART>(p.wd, g, p.cus, s);
+      if (e == hipSuccess) e = finish<false>(p.part, g.splits, n, F, g.bias, p.act, nullptr, nullptr, E, D, p.P, p.p0, s);
+    }
     if (e != hipSuccess) break;
     // MLP projection (partials), then x += sum + b and x_n = the next LayerNorm
     auto pr = wptr(a.pr, wf, l);
     g.a = p.act; g.w = pr.first; g.sz = pr.second; g.bias = nullptr;
-    g.N = E; g.K = F; g.out = p.part; g.splits = pick_splits(F);
+    g.N = E; g.K = F; g.out = p.part; g.splits = pick_splits(n, E, F, true, p.cus, cap);
     e = gemm_wd<PF_PART>(p.wd, g, p.cus, s);
     if (e != hipSuccess) break;
     const bool last = l + 1 == p.L;
