@@ -15,8 +15,11 @@ the other three 124M workloads are timed in the same run, each in
 them).  "prefill" times gpt2_prefill on the fp32 124M model: one call takes a
 1024-id prompt through every layer at once (GEMMs and attention on the matrix
 cores), so it is rated in tokens/s and against the fp32 matrix-core peak.
+"prefill_then_decode" runs the headline workload with its prompt prefilled.
 """
 import argparse
+import contextlib
+import gc
 import hashlib
 import json
 import os
@@ -31,6 +34,18 @@ import numpy as np  # noqa: E402
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
 MFMA_F32_PEAK_TFS = 157.3  # MI355X dense fp32 matrix-core peak, TFLOP/s
 PREFILL_N = 1024       # prompt ids per timed prefill call
+
+
+@contextlib.contextmanager
+def no_gc():
+    """Python's garbage collector off inside a timed loop (a collection pause
+    there would count as device time between the events around a launch)."""
+    gc.collect()
+    gc.disable()
+    try:
+        yield
+    finally:
+        gc.enable()
 
 
 def bytes_per_step(cfg, p):
@@ -170,15 +185,16 @@ def time_config(cfg, steps, warmup, sync_steps, torch, g2):
     # torch creates an event at its first record: do that outside the timed loop
     for ev in starts + ends:
         ev.record(stream)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        g2.gpt2_reset(ctx)
-        starts[i].record(stream)
-        g2.gpt2_generate(ctx, prompt, cfg.n_new)
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with no_gc():
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            g2.gpt2_reset(ctx)
+            starts[i].record(stream)
+            g2.gpt2_generate(ctx, prompt, cfg.n_new)
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     times = [a.elapsed_time(b) for a, b in zip(starts, ends)]
     ms_launch = float(np.mean(times))
     ms_median = float(np.median(times))
@@ -262,15 +278,16 @@ def time_prefill(cfg, n, steps, warmup, torch, g2):
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     for ev in starts + ends:
         ev.record(stream)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        g2.gpt2_reset(ctx)
-        starts[i].record(stream)
-        g2.gpt2_prefill(ctx, prompt, want_logits=False)
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with no_gc():
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            g2.gpt2_reset(ctx)
+            starts[i].record(stream)
+            g2.gpt2_prefill(ctx, prompt, want_logits=False)
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     ms = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)]))
     ctx.close()
     torch.cuda.synchronize()
@@ -288,6 +305,47 @@ def time_prefill(cfg, n, steps, warmup, torch, g2):
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_F32_PEAK_TFS, 4), "traffic": None},
         "roofline_note": "algorithmic flops of the whole call (linears, causal attention, head) over its "
                          "event-timed duration, against the dense fp32 matrix-core peak",
+    }
+
+
+def time_prefill_then_decode(cfg, steps, warmup, torch, g2):
+    """The headline workload as an application would run it: the prompt in one
+    gpt2_prefill call (its argmax is the first new id), then the other
+    n_new - 1 ids by gpt2_generate chained on the device: the same 69
+    positions.  Host clock around `steps` runs, each after a reset; also
+    whether the ids equal those of the one-pass-per-id run."""
+    import synth
+    model = synth.make_model(cfg)
+    prompt = synth.make_prompt(cfg)
+    ctx = g2.gpt2_load(cfg.n_layer, cfg.n_embd, cfg.n_head, cfg.n_positions, cfg.vocab, model.t,
+                       wdtype=cfg.wdtype, ln_eps=cfg.ln_eps, q4_group=cfg.q4_group)
+    del model
+
+    def run():
+        g2.gpt2_reset(ctx)
+        first, _ = g2.gpt2_prefill(ctx, prompt, want_logits=False)
+        rest = g2.gpt2_generate(ctx, np.array([first], np.int32), cfg.n_new - 1)
+        return [int(first)] + [int(i) for i in rest]
+
+    g2.gpt2_reset(ctx)
+    reference = [int(i) for i in g2.gpt2_generate(ctx, prompt, cfg.n_new)]
+    ids = None
+    for _ in range(warmup):
+        ids = run()
+    with no_gc():
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            ids = run()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    ctx.close()
+    return {
+        "workload": f"{cfg.name}: the {cfg.n_prompt}-id prompt in one gpt2_prefill call, then {cfg.n_new - 1} "
+                    f"greedy ids by gpt2_generate ({cfg.n_new} new ids, positions 0..{cfg.n_steps - 1}), batch 1",
+        "ms_per_run": round(wall * 1e3 / steps, 4),
+        "generated_tok_per_s": round(cfg.n_new * steps / wall, 2),
+        "same_ids_as_one_pass_per_id": ids == reference,
     }
 
 
@@ -383,6 +441,8 @@ def main():
         print(f"[bench] prefill: {args.warmup} warm-up + {args.steps} timed calls of {PREFILL_N} ids",
               file=sys.stderr, flush=True)
         out["prefill"] = time_prefill(synth.CONFIGS[2], PREFILL_N, args.steps, args.warmup, torch, g2)
+        print("[bench] prompt by prefill, then decode", file=sys.stderr, flush=True)
+        out["prefill_then_decode"] = time_prefill_then_decode(head_cfg, args.steps, args.warmup, torch, g2)
     if not args.only:
         print("[bench] streaming-read ceiling", file=sys.stderr, flush=True)
         out["measured_stream_read_GBs"] = stream_read_ceiling(torch)
