@@ -146,9 +146,11 @@ GPT2DEC_API int gpt2_generate(gpt2_ctx *c, const int *prompt, int n_prompt, int 
  * cores; their key and value rows are appended to the cache, as n gpt2_step
  * calls would append them ("Let's make GPT-2 in assembly", "What GPT-2 does":
  * the prompt, then the loop; gpt2.s docs: 10 prompt tokens before the 60
- * generated).  Returns the last position's logits (logits_out: NULL or host
- * float[V]) and argmax.  Afterwards filled += n.  The results agree with
- * per-position steps up to the order of the sums.  Errors: GPT2_E_INVAL (n < 1,
+ * generated).  tokens: host int[n].  Returns the last position's logits
+ * (logits_out: NULL or host float[V]) and argmax.  Afterwards filled += n.
+ * The work rows live in buffers gpt2_load allocated (n_positions rows): the
+ * call allocates nothing.  The results agree with per-position steps up to
+ * the order of the sums, and repeated calls are bitwise identical.  Errors: GPT2_E_INVAL (n < 1,
  * filled + n > n_positions, a token out of range), GPT2_E_DEVICE,
  * GPT2_E_NUMERIC, GPT2_E_STATE. */
 GPT2DEC_API int gpt2_prefill(gpt2_ctx *c, const int *tokens, int n, float *logits_out, int *argmax_out);

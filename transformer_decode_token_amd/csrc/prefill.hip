@@ -20,16 +20,17 @@
 // g-th run one input per step, so a lane reads its operands as float4 runs.
 //
 // GEMM: C[n][N] = A[n][K] W[N][K]^T with output-major weights, tiles of
-// BM x 64 outputs per workgroup of four waves, K in stages of 32 or 64 through LDS
-// (double-buffered: the next stage's loads are in flight while the current one
-// is multiplied).  fp16 weights are widened exactly and int4 weights become
-// zero + code * scale with one rounding (the quantised model's values) as a
-// stage is written to LDS; products and sums are fp32.  Tiles are numbered so
-// that the workgroups on one XCD share weight columns (its L2 holds them).
-// The two projections (N = E) have few column tiles, so their K is split in up
-// to four parts that run as separate tiles (at 1,024 rows: 768 tiles, three
-// per CU); the row pass adds the parts in order, so results do not depend on
-// scheduling.
+// BM x 64 (or 48) outputs per workgroup of four waves, K in stages of 32 or 64
+// through LDS (double-buffered: the next stage's loads are in flight while the
+// current one is multiplied).  fp16 weights are widened exactly and int4
+// weights become zero + code * scale with one rounding (the quantised model's
+// values) as a stage is written to LDS; products and sums are fp32.  Tiles are
+// numbered so that the workgroups on one XCD share weight columns (its L2
+// holds them).  The two projections (N = E) have few column tiles, so their K
+// is split in up to four parts that run as separate tiles (at 1,024 rows: 768
+// tiles, three per CU); a short prompt's linears all split K further, so that
+// the weights stream on every CU.  The parts are added in a fixed order, so
+// results do not depend on scheduling.
 #include <hip/hip_fp16.h>
 
 #include <type_traits>
