@@ -15,7 +15,8 @@ the other three 124M workloads are timed in the same run, each in
 them).  "prefill" times gpt2_prefill on the fp32 124M model: one call takes a
 1024-id prompt through every layer at once (GEMMs and attention on the matrix
 cores), so it is rated in tokens/s and against the fp32 matrix-core peak.
-"prefill_then_decode" runs the headline workload with its prompt prefilled.
+"prefill_then_decode" runs the headline workload with its prompt prefilled,
+"sampled" with temperature sampling instead of the greedy pick.
 """
 import argparse
 import contextlib
@@ -349,6 +350,47 @@ def time_prefill_then_decode(cfg, steps, warmup, torch, g2):
     }
 
 
+def time_sampled(cfg, steps, warmup, torch, g2, temperature=0.8, seed=20241):
+    """The headline workload with temperature sampling instead of the greedy
+    pick (gpt2_generate_sample: softmax(logits / T) and one xorshift64* draw
+    per id, chained on the device); event-timed like the greedy runs."""
+    import synth
+    model = synth.make_model(cfg)
+    prompt = synth.make_prompt(cfg)
+    ctx = g2.gpt2_load(cfg.n_layer, cfg.n_embd, cfg.n_head, cfg.n_positions, cfg.vocab, model.t,
+                       wdtype=cfg.wdtype, ln_eps=cfg.ln_eps, q4_group=cfg.q4_group)
+    del model
+    stream = torch.cuda.current_stream()
+    g2.gpt2_set_stream(ctx, stream.cuda_stream)
+    for _ in range(warmup):
+        g2.gpt2_reset(ctx)
+        g2.gpt2_generate_sample(ctx, prompt, cfg.n_new, temperature, seed)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for ev in starts + ends:
+        ev.record(stream)
+    with no_gc():
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            g2.gpt2_reset(ctx)
+            starts[i].record(stream)
+            g2.gpt2_generate_sample(ctx, prompt, cfg.n_new, temperature, seed + i)
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    ms = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)]))
+    ctx.close()
+    return {
+        "workload": f"{cfg.name}: {cfg.n_prompt} prompt ids + {cfg.n_new} ids drawn at temperature {temperature} "
+                    f"= {cfg.n_steps} one-token forward passes, batch 1",
+        "value": round(cfg.n_steps * steps / wall, 2),
+        "unit": "tok/s",
+        "ms_per_step": round(wall * 1e3 / steps, 4),
+        "us_per_token": round(ms * 1e3 / cfg.n_steps, 2),
+    }
+
+
 def workload_name(cfg):
     return (f"{cfg.name}: {cfg.n_prompt} prompt ids + {cfg.n_new} greedy ids = {cfg.n_steps} one-token "
             f"forward passes, batch 1")
@@ -443,6 +485,8 @@ def main():
         out["prefill"] = time_prefill(synth.CONFIGS[2], PREFILL_N, args.steps, args.warmup, torch, g2)
         print("[bench] prompt by prefill, then decode", file=sys.stderr, flush=True)
         out["prefill_then_decode"] = time_prefill_then_decode(head_cfg, args.steps, args.warmup, torch, g2)
+        print("[bench] sampled run", file=sys.stderr, flush=True)
+        out["sampled"] = time_sampled(head_cfg, args.steps, args.warmup, torch, g2)
     if not args.only:
         print("[bench] streaming-read ceiling", file=sys.stderr, flush=True)
         out["measured_stream_read_GBs"] = stream_read_ceiling(torch)

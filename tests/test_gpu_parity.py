@@ -692,3 +692,52 @@ def test_prefill_in_parts_and_then_generate():
     assert g2.gpt2_filled(ctx) == cfg.n_positions
     orc.close()
     ctx.close()
+
+
+def test_prefill_edges():
+    """gpt2_prefill at the edges of its contract, against the oracle: a one-id
+    prompt; a prompt after three decode steps (rows from position 3, mixing
+    the decode kernel's cache rows with the prefill's); a prompt that fills
+    every position in one call (tiny-long, 512 rows), after which one more id
+    is refused and changes nothing."""
+    cfg = CASES["tiny-rich"]
+    model = synth.make_model(cfg)
+    rng = np.random.default_rng(11)
+    toks = [int(t) for t in rng.integers(0, cfg.vocab, 40)]
+    orc = Oracle(model)
+    ctx = load_gpu(model)
+    am_o, lg_o = orc.step(toks[0], 0)
+    am, lg = g2.gpt2_prefill(ctx, toks[:1])
+    compare_step(lg, am, lg_o, "one-id prefill")
+    g2.gpt2_reset(ctx)
+    orc.reset()
+    for pos in range(3):
+        orc.step(toks[pos], pos)
+        g2.gpt2_step(ctx, toks[pos], pos, want_logits=False)
+    for pos in range(3, 23):
+        am_o, lg_o = orc.step(toks[pos], pos)
+    am, lg = g2.gpt2_prefill(ctx, toks[3:23])
+    compare_step(lg, am, lg_o, "prefill after three decode steps")
+    assert g2.gpt2_filled(ctx) == 23
+    am_o, lg_o = orc.step(toks[23], 23)
+    am, lg = g2.gpt2_step(ctx, toks[23], 23)
+    compare_step(lg, am, lg_o, "decode step after the prefill")
+    orc.close()
+    ctx.close()
+
+    cfg = CASES["tiny-long"]
+    model = synth.make_model(cfg)
+    P = cfg.n_positions
+    toks = [int(t) for t in np.random.default_rng(12).integers(0, cfg.vocab, P)]
+    orc = Oracle(model)
+    for pos, tok in enumerate(toks):
+        am_o, lg_o = orc.step(tok, pos)
+    orc.close()
+    ctx = load_gpu(model)
+    am, lg = g2.gpt2_prefill(ctx, toks)
+    compare_step(lg, am, lg_o, f"prefill of all {P} positions")
+    assert g2.gpt2_filled(ctx) == P
+    with pytest.raises(g2.Gpt2Error) as e:
+        g2.gpt2_prefill(ctx, toks[:1])
+    assert e.value.code == g2.GPT2_E_INVAL and g2.gpt2_filled(ctx) == P
+    ctx.close()
