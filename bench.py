@@ -7,7 +7,7 @@ second over the timed steps, with weights and prompt already resident on the
 GPU.  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--config 2..5] [--only] [--no-cpu-baseline]
-                  [--prefill-only]
+                  [--prefill-only] [--timeline CONFIG]
 
 The headline workload (--config, default 2) gives the line's value and roofline;
 the other three 124M workloads are timed in the same run, each in
@@ -391,6 +391,67 @@ def time_sampled(cfg, steps, warmup, torch, g2, temperature=0.8, seed=20241):
     }
 
 
+def timeline(cfg, torch, g2):
+    """Per-phase timeline of one traced greedy run (gpt2_debug_trace: a variant
+    of the kernel that stamps the device wall clock when each workgroup's
+    inputs are ready, passes its two barriers and has published; about 2 us
+    per pass slower than the untraced kernel).  Medians over the passes from
+    the 13th on, in us from the previous phase's last publish to the last
+    workgroup's event, per phase kind; the stamps' tick rate is taken from
+    the launch's event-timed duration."""
+    import synth
+    model = synth.make_model(cfg)
+    prompt = synth.make_prompt(cfg)
+    ctx = g2.gpt2_load(cfg.n_layer, cfg.n_embd, cfg.n_head, cfg.n_positions, cfg.vocab, model.t,
+                       wdtype=cfg.wdtype, ln_eps=cfg.ln_eps, q4_group=cfg.q4_group)
+    del model
+    stream = torch.cuda.current_stream()
+    g2.gpt2_set_stream(ctx, stream.cuda_stream)
+    L, ns = cfg.n_layer, cfg.n_steps
+    g2.gpt2_generate(ctx, prompt, cfg.n_new)
+    g2.gpt2_reset(ctx)
+    g2.gpt2_debug_trace(ctx, ns)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    g2.gpt2_generate(ctx, prompt, cfg.n_new)
+    b.record(stream)
+    torch.cuda.synchronize()
+    rec = g2.gpt2_debug_trace(ctx, 0, fetch=True).astype(np.float64)  # [ns][5L+1][G][4]
+    ctx.close()
+    launch_us = a.elapsed_time(b) * 1e3
+    stamps = rec[rec > 0]
+    # (the stamps span nearly the whole launch, so this overstates the tick by about 1%)
+    us_per_tick = launch_us / (stamps.max() - stamps.min())
+
+    def last(st, ph, k):
+        v = rec[st, ph, :, k]
+        v = v[v > 0]
+        return v.max() if v.size else np.nan
+
+    names = ["qkv", "attention", "attention_projection", "fc", "mlp_projection"]
+    rows = {nm: [] for nm in names}
+    per_layer, head, token = [], [], []
+    for st in range(12, ns):
+        for l in range(L):
+            for i, nm in enumerate(names):
+                ph = 5 * l + i
+                prev = last(st, ph - 1, 3) if ph > 0 else last(st - 1, 5 * L, 3)
+                rows[nm].append([(last(st, ph, k) - prev) * us_per_tick for k in range(4)])
+            if l > 0:
+                per_layer.append((last(st, 5 * l + 4, 3) - last(st, 5 * (l - 1) + 4, 3)) * us_per_tick)
+        head.append((last(st, 5 * L, 3) - last(st, 5 * L - 1, 3)) * us_per_tick)
+        token.append((last(st, 5 * L, 3) - last(st - 1, 5 * L, 3)) * us_per_tick)
+    return {
+        "workload": workload_name(cfg) + " (traced kernel)",
+        "us_per_tick": round(us_per_tick, 5),
+        "us_per_token": round(float(np.median(token)), 2),
+        "us_per_layer": round(float(np.median(per_layer)), 2),
+        "us_head": round(float(np.median(head)), 2),
+        "phases_us_ready_barrier1_barrier2_published": {
+            nm: [round(float(x), 2) for x in np.nanmedian(np.array(rows[nm]), axis=0)] for nm in names},
+    }
+
+
 def workload_name(cfg):
     return (f"{cfg.name}: {cfg.n_prompt} prompt ids + {cfg.n_new} greedy ids = {cfg.n_steps} one-token "
             f"forward passes, batch 1")
@@ -405,6 +466,8 @@ def main():
     ap.add_argument("--only", action="store_true",
                     help="time the headline workload alone (no per-config lines for the others)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--timeline", type=int, default=0, metavar="CONFIG",
+                    help="print the per-phase timeline of a traced greedy run of this workload (2..5)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only gpt2_prefill (fp32 124M, one 1024-id prompt per call) and print its line")
     ap.add_argument("--sync-steps", type=int, default=30,
@@ -433,6 +496,9 @@ def main():
     import transformer_decode_token_amd as g2
 
     torch.cuda.init()
+    if args.timeline:
+        print(json.dumps({"timeline": timeline(synth.CONFIGS[args.timeline], torch, g2)}), flush=True)
+        return
     if args.prefill_only:
         print(f"[bench] prefill: {args.warmup} warm-up + {args.steps} timed calls of {PREFILL_N} ids",
               file=sys.stderr, flush=True)
