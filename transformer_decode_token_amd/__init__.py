@@ -21,11 +21,10 @@ ERROR_NAMES = {GPT2_E_INVAL: "GPT2_E_INVAL", GPT2_E_NOMEM: "GPT2_E_NOMEM",
                GPT2_E_NUMERIC: "GPT2_E_NUMERIC"}
 
 # the symbols include/gpt2dec.h declares
-ABI_FUNCTIONS = ("gpt2_load", "gpt2_load_safetensors", "gpt2_get_config", "gpt2_set_stream", "gpt2_prefill", "gpt2_step", "gpt2_generate", "gpt2_generate_noalloc",
-                 "gpt2_generate_sample",
-                 "gpt2_reset",
-                 "gpt2_free", "gpt2_last_error", "gpt2_filled", "gpt2_debug_dequant",
-                 "gpt2_debug_fill_kv", "gpt2_debug_geometry", "gpt2_debug_trace",
+ABI_FUNCTIONS = ("gpt2_load", "gpt2_load_safetensors", "gpt2_get_config", "gpt2_set_stream",
+                 "gpt2_prefill", "gpt2_step", "gpt2_generate", "gpt2_generate_noalloc", "gpt2_generate_sample",
+                 "gpt2_reset", "gpt2_free", "gpt2_last_error", "gpt2_filled",
+                 "gpt2_debug_dequant", "gpt2_debug_fill_kv", "gpt2_debug_geometry", "gpt2_debug_trace",
                  "gpt2_tokenizer_load", "gpt2_tokenize", "gpt2_detokenize", "gpt2_tokenizer_free")
 
 
@@ -192,7 +191,8 @@ def gpt2_generate(ctx, prompt, n_new):
 
 
 def gpt2_prefill(ctx, tokens, want_logits=True):
-    """All tokens in one batched pass; returns (argmax of the last position, its logits or None)."""
+    """The ids at positions filled .. filled + len(tokens) - 1 through every layer in one call
+    (their cache rows appended); returns (argmax of the last position, its logits or None)."""
     t = np.ascontiguousarray(tokens, np.int32)
     logits = np.empty(ctx.cfg.vocab_size, np.float32) if want_logits else None
     am = C.c_int(-1)
