@@ -741,3 +741,28 @@ def test_prefill_edges():
         g2.gpt2_prefill(ctx, toks[:1])
     assert e.value.code == g2.GPT2_E_INVAL and g2.gpt2_filled(ctx) == P
     ctx.close()
+
+
+def test_stream_switch_between_runs():
+    """A run returns once its ids are in host memory, possibly before the
+    launch's workgroups have exited; gpt2_set_stream drains the old stream, so
+    a run on the new stream never overlaps the last one.  Runs alternate
+    between a torch stream and the library's own, back to back, each checked
+    against the oracle's greedy ids."""
+    import torch
+    cfg = CASES["tiny-rich"]
+    model = synth.make_model(cfg)
+    orc = Oracle(model)
+    prompt = [int(t) for t in synth.make_prompt(cfg)]
+    want, mg = _oracle_greedy(orc, prompt, 0, 12)
+    orc.close()
+    ctx = load_gpu(model)
+    side = torch.cuda.Stream()
+    for k in range(6):
+        g2.gpt2_set_stream(ctx, side.cuda_stream if k % 2 == 0 else None)
+        g2.gpt2_reset(ctx)
+        got = g2.gpt2_generate(ctx, np.array(prompt, np.int32), 12)
+        _assert_ids(got, want, mg, f"run {k} on the {'torch' if k % 2 == 0 else 'library'} stream")
+    g2.gpt2_set_stream(ctx, None)
+    ctx.close()
+    torch.cuda.synchronize()
