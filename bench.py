@@ -549,6 +549,16 @@ def main():
         print(f"[bench] prefill: {args.warmup} warm-up + {args.steps} timed calls of {PREFILL_N} ids",
               file=sys.stderr, flush=True)
         out["prefill"] = time_prefill(synth.CONFIGS[2], PREFILL_N, args.steps, args.warmup, torch, g2)
+        # the same prompt with fp16 and int4 block matrices (widened or decoded
+        # into the GEMM stages; products and sums in fp32, as for fp32 weights)
+        out["prefill_other_weights"] = {}
+        for k in (3, 4):
+            c = synth.CONFIGS[k]
+            print(f"[bench] prefill, {c.name}", file=sys.stderr, flush=True)
+            r = time_prefill(c, PREFILL_N, args.steps, args.warmup, torch, g2)
+            out["prefill_other_weights"][c.name] = {key: r[key] for key in
+                                                    ("value", "unit", "ms_per_call", "event_ms_per_call")}
+            out["prefill_other_weights"][c.name]["roofline_frac"] = r["roofline"]["frac"]
         print("[bench] prompt by prefill, then decode", file=sys.stderr, flush=True)
         out["prefill_then_decode"] = time_prefill_then_decode(head_cfg, args.steps, args.warmup, torch, g2)
         print("[bench] sampled run", file=sys.stderr, flush=True)
