@@ -769,26 +769,51 @@ __device__ __forceinline__ void head_range(int V, int w, int &hr0, int &hr1) {
 
 // The first head_lds_rows of this workgroup's output-head rows stay in LDS
 // for the whole launch (the head does not change between steps); they are
-// copied in once, during the first layer of the first step.
+// copied in once, during the first layer of the first step.  An fp16 head
+// (twice the rows) is copied by direct global-to-LDS loads: no registers, and
+// nothing waits for them until the compute waves' wait in the next layer
+// (wait_head_lds); a wave's load puts lane i's 16 bytes at its LDS base + 16 i,
+// so the waves copy the rows' bytes in runs of 1 KB.  (The same copy for the
+// fp32 head measured slower in whole runs of the fp32 and int4 kernels; it
+// shortened the fp16 kernel's one-pass launch by 4 us.)
 template <class S, int WD>
 __device__ void fill_head_lds(const DecodeArgs &a, float *lds, int lane) {
   constexpr int KC = S::E / 4, U = 4;
   constexpr int HWD = (WD == WD_F16) ? WD_F16 : WD_F32;
   int hr0, hr1;
   head_range<S, WD>(a.V, (int)blockIdx.x, hr0, hr1);
-  const int n = min(hr1 - hr0, a.head_lds_rows) * KC;
-  if (n <= 0) return;
-  const WSrc src = wsrc<HWD>(MatW{a.head, nullptr}, (size_t)hr0 * KC);
-  Chunk<HWD> *dst = reinterpret_cast<Chunk<HWD> *>(lds + S::L_HEAD);
-  for (int i0 = 0; i0 < n; i0 += U * S::NL) {
-    Chunk<HWD> c[U];
+  if constexpr (HWD == WD_F16) {
+    constexpr int RB16 = S::E * 2 / 16;  // 16-byte pieces per row
+    static_assert(S::E * 2 % 16 == 0, "whole 16-byte pieces per head row");
+    typedef __attribute__((address_space(1))) void g_void;
+    typedef __attribute__((address_space(3))) void l_void;
+    const int n = min(hr1 - hr0, a.head_lds_rows) * RB16;
+    const char *src = static_cast<const char *>(a.head) + (size_t)hr0 * RB16 * 16;
+    char *dst = reinterpret_cast<char *>(lds + S::L_HEAD);
+    const int wv = __builtin_amdgcn_readfirstlane(lane / 64), wl = lane % 64;
+    for (int i0 = 64 * wv; i0 < n; i0 += S::NL) {
+      if (i0 + wl < n)
+        __builtin_amdgcn_global_load_lds((g_void *)(src + (size_t)(i0 + wl) * 16),
+                                         (l_void *)(dst + (size_t)i0 * 16), 16, 0, 0);
+    }
+  } else {
+    const int n = min(hr1 - hr0, a.head_lds_rows) * KC;
+    if (n <= 0) return;
+    const WSrc src = wsrc<HWD>(MatW{a.head, nullptr}, (size_t)hr0 * KC);
+    Chunk<HWD> *dst = reinterpret_cast<Chunk<HWD> *>(lds + S::L_HEAD);
+    for (int i0 = 0; i0 < n; i0 += U * S::NL) {
+      Chunk<HWD> c[U];
 #pragma unroll
-    for (int u = 0; u < U; u++) c[u] = ld_chunk<HWD, HEAD_NT>(src, (uint32_t)min(i0 + u * S::NL + lane, n - 1));
+      for (int u = 0; u < U; u++) c[u] = ld_chunk<HWD, HEAD_NT>(src, (uint32_t)min(i0 + u * S::NL + lane, n - 1));
 #pragma unroll
-    for (int u = 0; u < U; u++)
-      if (i0 + u * S::NL + lane < n) dst[i0 + u * S::NL + lane] = c[u];
+      for (int u = 0; u < U; u++)
+        if (i0 + u * S::NL + lane < n) dst[i0 + u * S::NL + lane] = c[u];
+    }
   }
 }
+// This wave's direct copies into LDS are complete (the workgroup's next
+// barrier then makes every wave's copies visible to all).
+__device__ __forceinline__ void wait_head_lds() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Request head rows into registers, following the LDS-resident ones: NRB
 // batches into the idle slice registers b (late sets; once per step, after
@@ -981,6 +1006,9 @@ __device__ __attribute__((always_inline)) void compute_set(const DecodeArgs &a, 
       dot_set<ST, WD>(b, xs, part, lane);
       wg_barrier();
       wg_barrier();
+      if constexpr (WD == WD_F16) {
+        if (step == 0 && l == 1) wait_head_lds();  // (before the next slice request)
+      }
       if (l + 1 < a.L) {
         if (!defer) load_set<ST, WD>(b, m, l + 1, rank, lane);
       } else if (more && !LATE) {
@@ -993,6 +1021,7 @@ __device__ __attribute__((always_inline)) void compute_set(const DecodeArgs &a, 
         fill_head_lds<S, WD>(a, lds, lane);
         head_load_rows<S, WD, NRB, NX>(
             a, [&](int k, int i, const Chunk<HeadGeo<S, WD>::HWD> &c) { hx[k][i] = c; }, lane);
+        if (WD == WD_F16 && a.L == 1) wait_head_lds();
       }
     }
     if (!head_rows<S, WD, NRB, NX>(a, lds, lane, b, hx)) return;
