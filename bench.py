@@ -70,12 +70,30 @@ def bytes_per_step(cfg, p):
     return mats + head + small + kv
 
 
-def kernel_source_hash():
+def kernel_source_hash(files=("decode_kernel.hip", "dec_internal.h")):
     h = hashlib.sha256()
-    for f in ("decode_kernel.hip", "dec_internal.h"):
+    for f in files:
         with open(os.path.join(ROOT, "transformer_decode_token_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+PREFILL_SOURCES = ("prefill.hip", "lib_internal.h")
+
+
+def load_prefill_traffic(cfg_key, n):
+    """Memory-side bytes of one gpt2_prefill call (every kernel of the call),
+    measured with rocprofv3 counters for this exact prefill source
+    (profiles/prefill_traffic.json), else None."""
+    path = os.path.join(ROOT, "profiles", "prefill_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    e = d.get(f"{cfg_key}/{n}")
+    if not e or e.get("source_hash") != kernel_source_hash(PREFILL_SOURCES):
+        return None
+    return e
 
 
 def load_traffic(cfg_key):
@@ -294,6 +312,7 @@ def time_prefill(cfg, n, steps, warmup, torch, g2):
     torch.cuda.synchronize()
     flops = prefill_flops(cfg, n)
     achieved = flops / (ms * 1e-3) / 1e12
+    tr = load_prefill_traffic(cfg.key, n)
     return {
         "workload": f"{cfg.name}: one {n}-id prompt from position 0 through every layer in one gpt2_prefill "
                     f"call (then its last row's logits and argmax), batch 1",
@@ -303,7 +322,8 @@ def time_prefill(cfg, n, steps, warmup, torch, g2):
         "event_ms_per_call": round(ms, 4),
         "flops_per_call": flops,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F32_PEAK_TFS,
-                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_F32_PEAK_TFS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_F32_PEAK_TFS, 4),
+                     "traffic": tr["bytes_per_call"] if tr else None},
         "roofline_note": "algorithmic flops of the whole call (linears, causal attention, head) over its "
                          "event-timed duration, against the dense fp32 matrix-core peak",
     }
