@@ -29,6 +29,9 @@
  *    changes nothing.  After GPT2_E_DEVICE or GPT2_E_NUMERIC the context is
  *    poisoned: every later call except gpt2_last_error/gpt2_free returns
  *    GPT2_E_STATE.
+ *  - No C++ exception leaves the library: a host allocation that fails inside
+ *    a call returns GPT2_E_NOMEM (any other host-side failure GPT2_E_INVAL),
+ *    with its message in gpt2_last_error.
  *  - A context must not be used by two threads at once.
  */
 #ifndef GPT2DEC_H

@@ -97,6 +97,17 @@ def test_native_tokenizer_matches_oracle(files):
     tok.close()
 
 
+def test_host_allocation_failure_is_an_error_code(files, monkeypatch):
+    # an exception inside an exported call becomes its error code (here a failed host
+    # allocation, injected after the files are read), never an abort across the C ABI
+    monkeypatch.setenv("GPT2DEC_FAIL_HOST_ALLOC", "1")
+    with pytest.raises(g2.Gpt2Error) as e:
+        g2.gpt2_tokenizer_load(*files)
+    assert e.value.code == g2.GPT2_E_NOMEM and "host allocation" in str(e.value)
+    monkeypatch.delenv("GPT2DEC_FAIL_HOST_ALLOC")
+    g2.gpt2_tokenizer_load(*files).close()
+
+
 def test_native_tokenizer_errors(files, tmp_path):
     import ctypes as C
     tok = g2.gpt2_tokenizer_load(*files)

@@ -12,7 +12,10 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <memory>
 #include <mutex>
+#include <new>
+#include <stdexcept>
 #include <string>
 #include <vector>
 
@@ -550,6 +553,27 @@ int load_impl(gpt2_ctx *c, const gpt2_config *cfg, const gpt2_weights *w) {
 
 void gpt2dec::set_load_error(const std::string &msg) { g_load_error = msg; }
 
+int gpt2dec::exception_code(std::string *ctx_err) noexcept {
+  const char *msg = "host allocation failed";
+  int code = GPT2_E_NOMEM;
+  try {
+    throw;
+  } catch (const std::bad_alloc &) {
+  } catch (const std::length_error &) {
+    msg = "a size beyond the host library's limits";
+    code = GPT2_E_INVAL;
+  } catch (...) {
+    msg = "unexpected host error";
+    code = GPT2_E_INVAL;
+  }
+  try {
+    if (ctx_err) *ctx_err = msg;
+    else g_load_error = msg;
+  } catch (...) {
+  }
+  return code;
+}
+
 namespace {
 
 bool usable(gpt2_ctx *c, int *rc) {
@@ -566,7 +590,7 @@ bool usable(gpt2_ctx *c, int *rc) {
 
 extern "C" {
 
-int gpt2_load(const gpt2_config *cfg, const gpt2_weights *w, gpt2_ctx **out) {
+int gpt2_load(const gpt2_config *cfg, const gpt2_weights *w, gpt2_ctx **out) try {
   g_load_error.clear();
   if (!out) { g_load_error = "out is NULL"; return GPT2_E_INVAL; }
   *out = nullptr;
@@ -591,20 +615,21 @@ int gpt2_load(const gpt2_config *cfg, const gpt2_weights *w, gpt2_ctx **out) {
     g_load_error = "no HIP device available";
     return GPT2_E_DEVICE;
   }
-  gpt2_ctx *c = new (std::nothrow) gpt2_ctx();
+  std::unique_ptr<gpt2_ctx> c(new (std::nothrow) gpt2_ctx());
   if (!c) { g_load_error = "out of host memory"; return GPT2_E_NOMEM; }
   c->si = si;
-  rc = load_impl(c, cfg, w);
+  rc = load_impl(c.get(), cfg, w);
   if (rc != GPT2_OK) {
     g_load_error = c->err;
-    delete c;
     return rc;
   }
-  *out = c;
+  *out = c.release();
   return GPT2_OK;
+} catch (...) {
+  return gpt2dec::exception_code(nullptr);
 }
 
-int gpt2_set_stream(gpt2_ctx *c, void *hip_stream) {
+int gpt2_set_stream(gpt2_ctx *c, void *hip_stream) try {
   int rc;
   if (!usable(c, &rc)) return rc;
   // a launch may still be finishing on the old stream (its ids already
@@ -613,9 +638,11 @@ int gpt2_set_stream(gpt2_ctx *c, void *hip_stream) {
   if (e != hipSuccess) return c->device_fail(e, "draining the previous stream");
   c->stream = hip_stream ? static_cast<hipStream_t>(hip_stream) : c->own_stream;
   return GPT2_OK;
+} catch (...) {
+  return gpt2dec::exception_code(c ? &c->err : nullptr);
 }
 
-int gpt2_step(gpt2_ctx *c, int token_id, int position, float *logits_out, int *argmax_out) {
+int gpt2_step(gpt2_ctx *c, int token_id, int position, float *logits_out, int *argmax_out) try {
   int rc;
   if (!usable(c, &rc)) return rc;
   if (token_id < 0 || token_id >= c->V)
@@ -630,9 +657,11 @@ int gpt2_step(gpt2_ctx *c, int token_id, int position, float *logits_out, int *a
   c->filled = position + 1;
   if (argmax_out) *argmax_out = id;
   return GPT2_OK;
+} catch (...) {
+  return gpt2dec::exception_code(c ? &c->err : nullptr);
 }
 
-int gpt2_generate(gpt2_ctx *c, const int *prompt, int n_prompt, int n_new, int *out_ids) {
+int gpt2_generate(gpt2_ctx *c, const int *prompt, int n_prompt, int n_new, int *out_ids) try {
   int rc;
   if (!usable(c, &rc)) return rc;
   if (!prompt || !out_ids) return c->fail(GPT2_E_INVAL, "prompt or out_ids is NULL");
@@ -647,9 +676,11 @@ int gpt2_generate(gpt2_ctx *c, const int *prompt, int n_prompt, int n_new, int *
   if (rc != GPT2_OK) return rc;
   c->filled += (int)steps;
   return GPT2_OK;
+} catch (...) {
+  return gpt2dec::exception_code(c ? &c->err : nullptr);
 }
 
-int gpt2_prefill(gpt2_ctx *c, const int *tokens, int n, float *logits_out, int *argmax_out) {
+int gpt2_prefill(gpt2_ctx *c, const int *tokens, int n, float *logits_out, int *argmax_out) try {
   int rc;
   if (!usable(c, &rc)) return rc;
   if (!tokens) return c->fail(GPT2_E_INVAL, "tokens is NULL");
@@ -692,9 +723,11 @@ int gpt2_prefill(gpt2_ctx *c, const int *tokens, int n, float *logits_out, int *
   if (argmax_out) *argmax_out = id;
   if (logits_out) memcpy(logits_out, c->logits_h, sizeof(float) * (size_t)c->V);
   return GPT2_OK;
+} catch (...) {
+  return gpt2dec::exception_code(c ? &c->err : nullptr);
 }
 
-int gpt2_generate_noalloc(gpt2_ctx *c, const int *prompt, int n_prompt, int n_new, int *out_ids) {
+int gpt2_generate_noalloc(gpt2_ctx *c, const int *prompt, int n_prompt, int n_new, int *out_ids) try {
   int rc;
   if (!usable(c, &rc)) return rc;
   if (!prompt || !out_ids) return c->fail(GPT2_E_INVAL, "prompt or out_ids is NULL");
@@ -713,10 +746,12 @@ int gpt2_generate_noalloc(gpt2_ctx *c, const int *prompt, int n_prompt, int n_ne
   if (rc != GPT2_OK) return rc;
   c->filled += (int)steps;
   return GPT2_OK;
+} catch (...) {
+  return gpt2dec::exception_code(c ? &c->err : nullptr);
 }
 
 int gpt2_generate_sample(gpt2_ctx *c, const int *prompt, int n_prompt, int n_new, float temperature,
-                         unsigned long long seed, int *out_ids) {
+                         unsigned long long seed, int *out_ids) try {
   int rc;
   if (!usable(c, &rc)) return rc;
   if (!(temperature >= 0.0f) || !std::isfinite(temperature))
@@ -748,13 +783,17 @@ int gpt2_generate_sample(gpt2_ctx *c, const int *prompt, int n_prompt, int n_new
   if (rc != GPT2_OK) return rc;
   c->filled += (int)steps;
   return GPT2_OK;
+} catch (...) {
+  return gpt2dec::exception_code(c ? &c->err : nullptr);
 }
 
-int gpt2_reset(gpt2_ctx *c) {
+int gpt2_reset(gpt2_ctx *c) try {
   int rc;
   if (!usable(c, &rc)) return rc;
   c->filled = 0;
   return GPT2_OK;
+} catch (...) {
+  return gpt2dec::exception_code(c ? &c->err : nullptr);
 }
 
 void gpt2_free(gpt2_ctx *c) { delete c; }
@@ -772,7 +811,7 @@ int gpt2_get_config(const gpt2_ctx *c, gpt2_config *out) {
   return GPT2_OK;
 }
 
-int gpt2_debug_dequant(gpt2_ctx *c, int layer, int which, float *out) {
+int gpt2_debug_dequant(gpt2_ctx *c, int layer, int which, float *out) try {
   int rc;
   if (!usable(c, &rc)) return rc;
   if (!out) return c->fail(GPT2_E_INVAL, "out is NULL");
@@ -805,9 +844,11 @@ int gpt2_debug_dequant(gpt2_ctx *c, int layer, int which, float *out) {
   (void)hipFree(d);
   if (e != hipSuccess) return c->device_fail(e, "debug dequant");
   return GPT2_OK;
+} catch (...) {
+  return gpt2dec::exception_code(c ? &c->err : nullptr);
 }
 
-int gpt2_debug_fill_kv(gpt2_ctx *c, float value) {
+int gpt2_debug_fill_kv(gpt2_ctx *c, float value) try {
   int rc;
   if (!usable(c, &rc)) return rc;
   const size_t kv = (size_t)c->L * c->H * c->P * c->D;
@@ -816,9 +857,11 @@ int gpt2_debug_fill_kv(gpt2_ctx *c, float value) {
   if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
   if (e != hipSuccess) return c->device_fail(e, "fill kv");
   return GPT2_OK;
+} catch (...) {
+  return gpt2dec::exception_code(c ? &c->err : nullptr);
 }
 
-int gpt2_debug_trace(gpt2_ctx *c, int steps, long long *out, long long out_len, int *recorded_steps) {
+int gpt2_debug_trace(gpt2_ctx *c, int steps, long long *out, long long out_len, int *recorded_steps) try {
   int rc;
   if (!usable(c, &rc)) return rc;
   if (steps < -1) return c->fail(GPT2_E_INVAL, "steps must be >= -1");
@@ -849,6 +892,8 @@ int gpt2_debug_trace(gpt2_ctx *c, int steps, long long *out, long long out_len, 
     }
   }
   return GPT2_OK;
+} catch (...) {
+  return gpt2dec::exception_code(c ? &c->err : nullptr);
 }
 
 int gpt2_debug_geometry(const gpt2_ctx *c, int *workgroups, int *threads) {

@@ -16,6 +16,7 @@
 
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <memory>
 #include <new>
@@ -170,7 +171,7 @@ bool read_config(const char *path, gpt2_config &cfg, std::string &err) {
 }  // namespace
 
 extern "C" int gpt2_load_safetensors(const char *safetensors_path, const char *config_path, int wdtype,
-                                     gpt2_ctx **out) {
+                                     gpt2_ctx **out) try {
   auto reject = [](int code, const std::string &msg) {
     gpt2dec::set_load_error(msg);
     return code;
@@ -277,6 +278,8 @@ extern "C" int gpt2_load_safetensors(const char *safetensors_path, const char *c
   w.lnf_b = lnfb;
   // (gpt2_load copies everything before it returns; the mapping ends here)
   return gpt2_load(&cfg, &w, out);
+} catch (...) {
+  return gpt2dec::exception_code(nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -376,7 +379,7 @@ size_t chunk_end(const unsigned char *s, size_t n, size_t i) {
 
 extern "C" {
 
-int gpt2_tokenizer_load(const char *vocab_json_path, const char *merges_txt_path, gpt2_tokenizer **out) {
+int gpt2_tokenizer_load(const char *vocab_json_path, const char *merges_txt_path, gpt2_tokenizer **out) try {
   auto reject = [](const std::string &msg) {
     gpt2dec::set_load_error(msg);
     return GPT2_E_INVAL;
@@ -392,6 +395,9 @@ int gpt2_tokenizer_load(const char *vocab_json_path, const char *merges_txt_path
     return reject(std::string(vocab_json_path) + ": " + (jp.error().empty() ? "not a JSON object" : jp.error()));
   std::unique_ptr<gpt2_tokenizer> t(new (std::nothrow) gpt2_tokenizer());
   if (!t) return GPT2_E_NOMEM;
+  // (fault injection for the tests: a host allocation that fails here)
+  const char *inject = getenv("GPT2DEC_FAIL_HOST_ALLOC");
+  if (inject && atoi(inject) != 0) throw std::bad_alloc();
   for (int b = 0; b < 256; b++) t->byte_id[b] = -1;
   std::string bytes;
   for (const auto &kv : vocab.obj) {
@@ -433,9 +439,11 @@ int gpt2_tokenizer_load(const char *vocab_json_path, const char *merges_txt_path
   }
   *out = t.release();
   return GPT2_OK;
+} catch (...) {
+  return gpt2dec::exception_code(nullptr);
 }
 
-int gpt2_tokenize(const gpt2_tokenizer *t, const char *text, size_t len, int *ids, int cap, int *n_ids) {
+int gpt2_tokenize(const gpt2_tokenizer *t, const char *text, size_t len, int *ids, int cap, int *n_ids) try {
   if (!t || (!text && len) || !n_ids || cap < 0 || (!ids && cap > 0)) {
     gpt2dec::set_load_error("bad argument");
     return GPT2_E_INVAL;
@@ -479,9 +487,11 @@ int gpt2_tokenize(const gpt2_tokenizer *t, const char *text, size_t len, int *id
     return GPT2_E_INVAL;
   }
   return GPT2_OK;
+} catch (...) {
+  return gpt2dec::exception_code(nullptr);
 }
 
-int gpt2_detokenize(const gpt2_tokenizer *t, const int *ids, int n, char *buf, size_t cap, size_t *len) {
+int gpt2_detokenize(const gpt2_tokenizer *t, const int *ids, int n, char *buf, size_t cap, size_t *len) try {
   if (!t || n < 0 || (!ids && n) || !len || (!buf && cap)) {
     gpt2dec::set_load_error("bad argument");
     return GPT2_E_INVAL;
@@ -507,6 +517,8 @@ int gpt2_detokenize(const gpt2_tokenizer *t, const int *ids, int n, char *buf, s
     o += s.size();
   }
   return GPT2_OK;
+} catch (...) {
+  return gpt2dec::exception_code(nullptr);
 }
 
 void gpt2_tokenizer_free(gpt2_tokenizer *t) { delete t; }

@@ -10,6 +10,13 @@ namespace gpt2dec {
 // The message gpt2_last_error(NULL) returns for this thread (a failed load).
 void set_load_error(const std::string &msg);
 
+// Called from the handler of an exported call that an exception would leave
+// (a host allocation that failed, or a size the standard library refuses):
+// the call's error code (GPT2_E_NOMEM for a failed allocation, else
+// GPT2_E_INVAL), with the message in *ctx_err (the context's), or for this
+// thread's gpt2_last_error(NULL) when ctx_err is null.
+int exception_code(std::string *ctx_err) noexcept;
+
 // Batched prompt prefill (prefill.hip): n positions p0 .. p0+n-1 through every
 // layer together (their cache rows written), then the last row's logits and
 // argmax (-1 when all are NaN).
