@@ -78,7 +78,7 @@ def kernel_source_hash(files=("decode_kernel.hip", "dec_internal.h")):
     return h.hexdigest()[:16]
 
 
-PREFILL_SOURCES = ("prefill.hip", "lib_internal.h")
+PREFILL_SOURCES = ("prefill.hip",)
 
 
 def load_prefill_traffic(cfg_key, n):
