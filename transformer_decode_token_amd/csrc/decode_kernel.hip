@@ -26,7 +26,11 @@
 //     LDS (scaled by the LayerNorm gain where a LayerNorm comes first; the
 //     LayerNorm statistics are taken while the dot products run and applied
 //     to the row results), runs an attention chunk when it has one, and
-//     publishes.
+//     publishes;
+//   * with more than three compute waves (the fp32 kernel: two waves per
+//     SIMD, 256 registers each) the last compute wave takes no slice and runs
+//     the attention chunk in the control wave's place, with the chunk's value
+//     rows in LDS.
 // Each phase's inputs therefore come from, and go to, a few dozen workgroups
 // rather than all of them, which shortens every hand-over.
 // Batch 1 makes every linear a matrix-vector product (0.5 flop per fp32 byte),
@@ -72,7 +76,14 @@ struct Shape {
   // CD: the control wave takes a share of every block-matrix slice too (it
   // would otherwise idle through the dot products); NLD lanes share a slice.
   static constexpr bool CD = CD_ != 0;
-  static constexpr int NLD = NL + (CD_ ? 64 : 0);
+  // With more than three compute waves (two waves on some SIMDs, 256
+  // registers each), the attention items run on the last compute wave, which
+  // takes no share of the slices and keeps the chunk's value rows in LDS
+  // (att_item_cw): the control wave's registers would not hold an item.
+  static constexpr bool ITEM_CW = NCW_ > 3;
+  static constexpr int IW = NCW_ - 1;  // that compute wave
+  static constexpr int NLD = NL + (CD_ ? 64 : 0) - (ITEM_CW ? 64 : 0);  // lanes sharing a slice
+  static constexpr int NLH = NL - (ITEM_CW ? 64 : 0);  // compute lanes that take output-head rows
   static constexpr int MAXCH = MAXCH_;    // attention chunks per head at most
   static constexpr int LPRH = LPRH_;      // lanes per head row
   static constexpr int LPR = LPR_;        // lanes per row of a block matrix
@@ -101,26 +112,35 @@ struct Shape {
                 "equal row shares");
   static_assert(H * MAXCH <= G, "one attention chunk per workgroup at most");
   // LDS layout (floats)
-  static constexpr int L_XS = 0;                         // [F] phase input vector
-  static constexpr int L_PART = L_XS + F;                // [PSTRIDE] row results
+  // [F] phase input vector; with ITEM_CW also (at least [64][D]) the
+  // attention item's value rows, which are read before any input vector of
+  // the workgroup's next phase can be complete (that input depends on the
+  // item's output)
+  static constexpr int L_XS = 0;
+  static constexpr int XS_N = ITEM_CW && 64 * D_ > F ? 64 * D_ : F;
+  static constexpr int L_PART = L_XS + XS_N;             // [PSTRIDE] row results
   static constexpr int L_Q = L_PART + PSTRIDE;           // [D] query of the attention item
   static constexpr int L_KP = L_Q + D;                   // [D] key of this position
   static constexpr int L_VP = L_KP + D;                  // [D] value of this position
   static constexpr int L_SC = L_VP + D;                  // [64] attention weights (transposed)
+  static constexpr int L_V = L_XS;                       // [64][D] an item's value rows (ITEM_CW)
   static constexpr int L_FLAG = L_SC + 64;               // [4] flags: abort (control), abort (compute)
   static constexpr int L_TOTAL = L_FLAG + 4;
   static constexpr int L_HEAD = (L_TOTAL + 63) & ~63;    // output-head rows kept for the launch
 };
 
-// 124M shape: 256 workgroups x (3 compute + 1 control) waves.  fp32: sets of
-// 64 (QKV, 36 rows each), 32 (attention projection, 24 rows), 64 (fc, 48
-// rows) and 96 (MLP projection, 8 rows), so every workgroup reads 74 to 147
-// KB of weights per layer.  fp16 and int4, whose dot products cost more
-// vector instructions per weight: the control wave takes a share of every
-// slice too, in sets of 72 (32 rows), 24 (32 rows), 64 (48 rows) and 96 (8
-// rows), row counts that 16 (64 for K = 3072) rows per pass of 256 lanes
-// divide.  (Set sizes and the split chosen by measurement.)
-using ShapeS = Shape<768, 64, 3, 16, 16, 16, 64, 32, 64, 96>;
+// 124M shape.  fp32: 256 workgroups x (7 compute + 1 control) waves, two
+// waves on each SIMD: six waves take the dot products (32 lanes per row), the
+// seventh the attention item; sets of 64 (QKV, 36 rows each), 32 (attention
+// projection, 24 rows), 64 (fc, 48 rows) and 96 (MLP projection, 8 rows), so
+// every workgroup reads 74 to 147 KB of weights per layer.  fp16 and int4,
+// whose dot products cost more vector instructions per weight and more
+// registers: 256 workgroups x (3 compute + 1 control) waves, and the control
+// wave takes a share of every slice too, in sets of 72 (32 rows), 24 (32
+// rows), 64 (48 rows) and 96 (8 rows), row counts that 16 (64 for K = 3072)
+// rows per pass of 256 lanes divide.  (Set sizes and the split chosen by
+// measurement.)
+using ShapeS = Shape<768, 64, 7, 16, 32, 32, 64, 32, 64, 96, 0>;
 using ShapeSC = Shape<768, 64, 3, 16, 16, 16, 72, 24, 64, 96, 1>;
 // tiny shape: 32 workgroups x (2 compute + 1 control) waves, sets 8/4/16/4.
 using ShapeT = Shape<128, 32, 2, 8, 8, 8, 8, 4, 16, 4>;
@@ -705,10 +725,10 @@ __device__ __forceinline__ void dot_set(const Chunk<WD> (&b)[ST::NB], const floa
 
 template <class S, int WD>
 struct HeadGeo {
-  static constexpr int KC = S::E / 4, LPR = S::LPRH, NPH = KC / LPR, RB = S::NL / LPR;
+  static constexpr int KC = S::E / 4, LPR = S::LPRH, NPH = KC / LPR, RB = S::NLH / LPR;
   static constexpr int RBC = 64 / LPR, CTL_ROWS = S::HEAD_CTL_BATCHES * RBC;  // the control wave's rows
   static constexpr int HWD = (WD == WD_F16) ? WD_F16 : WD_F32;
-  static_assert(KC % LPR == 0 && S::NL % LPR == 0 && LPR % 8 == 0, "head geometry");
+  static_assert(KC % LPR == 0 && S::NLH % LPR == 0 && LPR % 8 == 0, "head geometry");
 };
 
 // Batches of output-head rows that a workgroup of set SET holds in registers
@@ -791,7 +811,7 @@ __device__ void fill_head_lds(const DecodeArgs &a, float *lds, int lane) {
     const char *src = static_cast<const char *>(a.head) + (size_t)hr0 * RB16 * 16;
     char *dst = reinterpret_cast<char *>(lds + S::L_HEAD);
     const int wv = __builtin_amdgcn_readfirstlane(lane / 64), wl = lane % 64;
-    for (int i0 = 64 * wv; i0 < n; i0 += S::NL) {
+    for (int i0 = 64 * wv; i0 < n; i0 += S::NLH) {
       if (i0 + wl < n)
         __builtin_amdgcn_global_load_lds((g_void *)(src + (size_t)(i0 + wl) * 16),
                                          (l_void *)(dst + (size_t)i0 * 16), 16, 0, 0);
@@ -801,13 +821,13 @@ __device__ void fill_head_lds(const DecodeArgs &a, float *lds, int lane) {
     if (n <= 0) return;
     const WSrc src = wsrc<HWD>(MatW{a.head, nullptr}, (size_t)hr0 * KC);
     Chunk<HWD> *dst = reinterpret_cast<Chunk<HWD> *>(lds + S::L_HEAD);
-    for (int i0 = 0; i0 < n; i0 += U * S::NL) {
+    for (int i0 = 0; i0 < n; i0 += U * S::NLH) {
       Chunk<HWD> c[U];
 #pragma unroll
-      for (int u = 0; u < U; u++) c[u] = ld_chunk<HWD, HEAD_NT>(src, (uint32_t)min(i0 + u * S::NL + lane, n - 1));
+      for (int u = 0; u < U; u++) c[u] = ld_chunk<HWD, HEAD_NT>(src, (uint32_t)min(i0 + u * S::NLH + lane, n - 1));
 #pragma unroll
       for (int u = 0; u < U; u++)
-        if (i0 + u * S::NL + lane < n) dst[i0 + u * S::NL + lane] = c[u];
+        if (i0 + u * S::NLH + lane < n) dst[i0 + u * S::NLH + lane] = c[u];
     }
   }
 }
@@ -885,7 +905,7 @@ __device__ bool head_rows(const DecodeArgs &a, float *lds, int lane, const Chunk
     for (int k = 0; k < HB; k++) fetch(hbuf[k], k * RB);
   }
   wg_barrier();
-  if (flag[0]) return false;
+  if (S::ITEM_CW ? (flag[0] | flag[1]) != 0 : flag[0] != 0) return false;
   float4 xv[NPH];
 #pragma unroll
   for (int i = 0; i < NPH; i++) xv[i] = reinterpret_cast<const float4 *>(xs)[i * LPR + q];
@@ -962,13 +982,301 @@ __device__ void poll_act_part(const DecodeArgs &a, int step, int l, float *lds, 
   }
 }
 
+// A workgroup's attention item at one position: head ih, chunk ic, over rows
+// t0..t1-1 (cache rows t0..tg-1; last: the chunk closes at the position itself).
+struct ItemOf {
+  int ih, ic, t0, t1, tg;
+  bool last;
+};
+// The attention item of workgroup w (of set SET) at position p, if it has one;
+// nch: the chunks per head at p.
+template <class S, int SET>
+__device__ __forceinline__ bool item_at(int p, int w, int &nch, ItemOf &it) {
+  int ch;
+  att_chunks<S>(p, nch, ch);
+  const int item = att_item_of<S>(w);
+  // (set Q's workgroups come first in blockIdx: they get items only when the
+  // other sets cannot hold them all)
+  constexpr bool MAY_ITEM = SET != SET_Q || S::H * S::MAXCH > S::G - S::NQ;
+  const bool has = MAY_ITEM && item < S::H * nch;
+  it.ih = has ? item / nch : 0;
+  it.ic = has ? item % nch : 0;
+  it.t0 = it.ic * ch;
+  it.t1 = min(it.t0 + ch, p + 1);
+  it.last = (it.t1 == p + 1);
+  it.tg = it.last ? p : it.t1;
+  return has;
+}
+
+template <bool TR>
+__device__ __forceinline__ void stamp_if(const DecodeArgs &a, int lane, int step, int ph, int which, int G) {
+  if constexpr (TR) {
+    if (lane == 0) stamp(a, step, ph, which, G);
+  }
+}
+
+// The attention item run by a compute wave (S::ITEM_CW; lane 0..63): the same
+// chunk as AttChunk on the control wave, but with the chunk's value rows copied
+// straight into LDS (direct global-to-LDS loads) instead of held in registers.
+// att_item_fetch requests the chunk's key rows (into k) and value rows (into
+// LDS, over the phase input vector; rows past the chunk's cache rows are
+// zeros) and waits for none of them.
+template <class S>
+__device__ __attribute__((always_inline)) void att_item_fetch(const DecodeArgs &a, float *lds, int l, const ItemOf &it,
+                                                              int lane, float4 (&k)[S::D / 4]) {
+  constexpr int D = S::D, H = S::H, D4 = D / 4;
+  static_assert(D == 64, "16 pieces of 16 bytes per value row, 4 rows per copy");
+  asm volatile("" : "+v"(lane));
+  const int ih = it.ih, it0 = it.t0, itg = it.tg;
+  const float *K = a.kc + ((size_t)(l * H + ih) * a.P) * D;
+  const float *V = a.vc + ((size_t)(l * H + ih) * a.P) * D;
+  const int nv = itg - it0;  // cache rows of the chunk
+  {
+    const int tk = it0 + lane;
+#pragma unroll
+    for (int i = 0; i < D4; i++) {
+      k[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (tk < itg) k[i] = reinterpret_cast<const float4 *>(K + (size_t)tk * D)[i];
+    }
+    typedef __attribute__((address_space(1))) void g_void;
+    typedef __attribute__((address_space(3))) void l_void;
+    const char *src = reinterpret_cast<const char *>(V + (size_t)it0 * D);
+    char *dst = reinterpret_cast<char *>(lds + S::L_V);
+    // rows past the chunk's cache rows: zeros, so the value loop needs no test
+    // (written before the copies are requested: an LDS write after them
+    // would first wait for all of them)
+#pragma unroll
+    for (int j = 0; j < D / 4; j++) {
+      const int f = 64 * j + lane;
+      if (f >= nv * (D / 4)) reinterpret_cast<float4 *>(dst)[f] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int j = 0; j < D / 4; j++) {  // copy j: rows 4j..4j+3, lane = one 16-byte piece
+      const int f = 64 * j + lane;
+      if (f < nv * (D / 4))
+        __builtin_amdgcn_global_load_lds((g_void *)(src + (size_t)f * 16), (l_void *)(dst + 64 * j * 16), 16, 0, 0);
+    }
+  }
+}
+
+// att_item_cw runs the item, with its rows fetched here unless `fetched` (k and
+// the LDS rows already hold them).  False when a wait failed (the error word is
+// set).
+template <class S, bool TR>
+__device__ __attribute__((always_inline)) bool att_item_cw(const DecodeArgs &a, float *lds, int step, int l, int p,
+                                                           int nch, const ItemOf &it, int lane, Waiter &wt,
+                                                           float4 (&k)[S::D / 4], bool fetched) {
+  constexpr int E = S::E, D = S::D, H = S::H, D4 = D / 4, RPL = 64 / D4, IT = 64 / RPL;
+  // (an opaque copy of the lane index: the item's per-lane addresses are
+  // computed where they are used instead of once for the whole launch, where
+  // they would hold registers through the head)
+  asm volatile("" : "+v"(lane));
+  const uint32_t epA = epoch_of(a, step, 5 * l + 0), epB = epA + 1;
+  const int ih = it.ih, ic = it.ic, it0 = it.t0, it1 = it.t1, itg = it.tg;
+  const bool ilast = it.last;
+  if (!fetched) att_item_fetch<S>(a, lds, l, it, lane, k);
+  wt.start(5 * l + 0);
+  const uint64_t *qk = a.qkv_t + ((size_t)l * NCOPY + my_copy()) * 3 * E + ih * D + (lane % D);
+  while (true) {
+    const uint64_t xq = tld(qk);
+    uint64_t xk = (uint64_t)epA << 32, xv = (uint64_t)epA << 32;
+    if (ilast) {
+      xk = tld(qk + E);
+      xv = tld(qk + 2 * E);
+    }
+    if (__all(tag_is(xq, epA) && tag_is(xk, epA) && tag_is(xv, epA))) {
+      if (lane < D) {
+        lds[S::L_Q + lane] = payload(xq);
+        lds[S::L_KP + lane] = payload(xk);
+        lds[S::L_VP + lane] = payload(xv);
+      }
+      break;
+    }
+    if (wt.expired()) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  stamp_if<TR>(a, lane, step, 5 * l + 1, 0, S::G);
+  // scores (lane = row it0 + lane), softmax weights, as AttChunk::run
+  float m, lsum;
+  float4 o;
+  {
+    const int g = lane / D4, d4 = lane % D4;
+    const float scale = 1.0f / sqrtf((float)D);
+    const float4 *q4 = reinterpret_cast<const float4 *>(lds + S::L_Q);
+    float sa = 0.f, sb = 0.f, sc = 0.f, sd = 0.f;
+#pragma unroll
+    for (int i = 0; i < D4; i += 4) {
+      sa = dot4(k[i], q4[i], sa);
+      sb = dot4(k[i + 1], q4[i + 1], sb);
+      sc = dot4(k[i + 2], q4[i + 2], sc);
+      sd = dot4(k[i + 3], q4[i + 3], sd);
+    }
+    const float sv = ((sa + sb) + (sc + sd)) * scale;
+    const bool has_p = itg < it1;
+    float sp = -INFINITY;
+    float4 vp = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (has_p) {
+      const float4 kp = reinterpret_cast<const float4 *>(lds + S::L_KP)[d4];
+      vp = reinterpret_cast<const float4 *>(lds + S::L_VP)[d4];
+      sp = seg_bcast_last<D4>(seg_sum_last<D4>(dot4(kp, q4[d4], 0.f)), lane) * scale;
+    }
+    const bool valid = it0 + lane < itg;
+    const bool isp = has_p && lane == p - it0;
+    const float sl = valid ? sv : (isp ? sp : -INFINITY);
+    m = wave_max_all(sl);
+    const float e = (valid || isp) ? __expf(sl - m) : 0.f;
+    lsum = wave_sum_all(e);
+    lds[S::L_SC + (lane % RPL) * IT + lane / RPL] = e;
+    float wgt[IT];
+#pragma unroll
+    for (int j = 0; j < IT; j += 4) {
+      const float4 x = reinterpret_cast<const float4 *>(lds + S::L_SC + g * IT)[j / 4];
+      wgt[j] = x.x;
+      wgt[j + 1] = x.y;
+      wgt[j + 2] = x.z;
+      wgt[j + 3] = x.w;
+    }
+    // the value rows are in LDS (this wave's own copies)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    float4 oo = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 *vl = reinterpret_cast<const float4 *>(lds + S::L_V);
+    float4 vv[IT];
+#pragma unroll
+    for (int i2 = 0; i2 < IT; i2++) vv[i2] = vl[(g + RPL * i2) * D4 + d4];
+#pragma unroll
+    for (int i2 = 0; i2 < IT; i2++) {
+      oo.x = __builtin_fmaf(wgt[i2], vv[i2].x, oo.x);
+      oo.y = __builtin_fmaf(wgt[i2], vv[i2].y, oo.y);
+      oo.z = __builtin_fmaf(wgt[i2], vv[i2].z, oo.z);
+      oo.w = __builtin_fmaf(wgt[i2], vv[i2].w, oo.w);
+    }
+    // all the row reads first, then the products (one LDS round trip, not IT)
+    __builtin_amdgcn_sched_group_barrier(0x100, IT, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 4 * IT, 0);
+    if (has_p && ((p - it0) % RPL) == g) {
+      const float ep = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), p - it0));
+      oo.x = __builtin_fmaf(ep, vp.x, oo.x);
+      oo.y = __builtin_fmaf(ep, vp.y, oo.y);
+      oo.z = __builtin_fmaf(ep, vp.z, oo.z);
+      oo.w = __builtin_fmaf(ep, vp.w, oo.w);
+    }
+#pragma unroll
+    for (int sh = D4; sh < 64; sh <<= 1) {
+      oo.x = xor_sum(oo.x, sh);
+      oo.y = xor_sum(oo.y, sh);
+      oo.z = xor_sum(oo.z, sh);
+      oo.w = xor_sum(oo.w, sh);
+    }
+    o = oo;
+  }
+  // the position's cache rows, stored after the value rows' wait above (which
+  // would otherwise wait for these stores too); they are complete before this
+  // wave reaches the next barrier (the caller's wait)
+  if (ilast && lane < D) {
+    const size_t row = ((size_t)(l * H + ih) * a.P + p) * D + lane;
+    st_agent(a.kc + row, lds[S::L_KP + lane]);
+    st_agent(a.vc + row, lds[S::L_VP + lane]);
+  }
+  stamp_if<TR>(a, lane, step, 5 * l + 1, 1, S::G);
+  const int g = lane / D4, d4 = lane % D4;
+  stamp_if<TR>(a, lane, step, 5 * l + 1, 2, S::G);
+  // every lane holds the head's output; row group g writes the copies c = g mod RPL
+  const auto attn_rs = __builtin_amdgcn_make_buffer_rsrc(a.attn_t + (size_t)l * NCOPY * E, (short)0,
+                                                         NCOPY * E * 8, 0x00020000);
+  auto publish_head = [&](const float4 &r) {
+    for (int c = g; c < NCOPY; c += RPL) {
+      const uint32_t off = (uint32_t)((c * E + ih * D + 4 * d4) * 8);
+      tst2(attn_rs, off, r.x, r.y, epB);
+      tst2(attn_rs, off + 16, r.z, r.w, epB);
+    }
+  };
+  if (nch == 1) {
+    const float rl = __builtin_amdgcn_rcpf(lsum);
+    publish_head(make_float4(o.x * rl, o.y * rl, o.z * rl, o.w * rl));
+  } else if (ic > 0) {
+    // this chunk's (o, m, l) for chunk 0 of the head, as word pairs
+    const auto prs = __builtin_amdgcn_make_buffer_rsrc(
+        a.att_t + ((size_t)(l * H + ih) * S::MAXCH + ic) * (D + 2), (short)0, (D + 2) * 8, 0x00020000);
+    if (g == 0) {
+      tst2(prs, (uint32_t)(4 * d4 * 8), o.x, o.y, epB);
+      tst2(prs, (uint32_t)((4 * d4 + 2) * 8), o.z, o.w, epB);
+    }
+    if (lane == 0) tst2(prs, (uint32_t)(D * 8), m, lsum, epB);
+  } else {
+    // chunk 0 merges the head.  The partials of chunks 1..nch-1 are polled as one
+    // flat array of word pairs spread over the lanes (a fixed number of 16-byte
+    // loads per lane, clamped, so the wait counts stay exact), staged in LDS (the
+    // phase-input area is free while the item runs), and combined: the largest
+    // chunk maximum, one rescale factor per chunk (lane c), then the sums in
+    // chunk order.
+    constexpr int PP = (D + 2) / 2;                       // word pairs per chunk slot
+    constexpr int PPL = ((S::MAXCH - 1) * PP + 63) / 64;  // pair loads per lane
+    constexpr int SP = D + 4;                             // staged slot stride (16-byte aligned)
+    const int npairs = (nch - 1) * PP;
+    const auto mrs = __builtin_amdgcn_make_buffer_rsrc(
+        a.att_t + ((size_t)(l * H + ih) * S::MAXCH + 1) * (D + 2), (short)0, (S::MAXCH - 1) * (D + 2) * 8,
+        0x00020000);
+    float va[PPL], vb[PPL];
+    wt.start(5 * l + 1);
+    while (true) {
+      bool ok = true;
+#pragma unroll
+      for (int k = 0; k < PPL; k++) {
+        const int f = min(lane + 64 * k, npairs - 1);
+        const auto x = __builtin_amdgcn_raw_buffer_load_b128(mrs, (uint32_t)(f * 16), 0, AUX_SC1);
+        va[k] = __uint_as_float(x[0]);
+        vb[k] = __uint_as_float(x[2]);
+        ok &= (lane + 64 * k >= npairs) || (x[1] == epB && x[3] == epB);
+      }
+      if (__all(ok)) break;
+      if (wt.expired()) return false;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    float *scr = lds + S::L_XS;
+#pragma unroll
+    for (int k = 0; k < PPL; k++) {
+      const int f = lane + 64 * k;
+      if (f < npairs) {
+        const int w2 = 2 * f, sl = w2 / (D + 2), wi = w2 % (D + 2);
+        scr[sl * SP + wi] = va[k];
+        scr[sl * SP + wi + 1] = vb[k];
+      }
+    }
+    float mcl = -INFINITY, lcl = 0.f;  // lane c < nch: chunk c's maximum and sum
+    if (lane == 0) {
+      mcl = m;
+      lcl = lsum;
+    } else if (lane < nch) {
+      mcl = scr[(lane - 1) * SP + D];
+      lcl = scr[(lane - 1) * SP + D + 1];
+    }
+    const float M = wave_max_all(mcl);
+    const float fl = lane < nch ? __expf(mcl - M) : 0.f;
+    const float Ls = wave_sum_all(lcl * fl);
+    const float f0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fl), 0));
+    float4 O = make_float4(o.x * f0, o.y * f0, o.z * f0, o.w * f0);
+    for (int c = 1; c < nch; c++) {
+      const float fc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fl), c));
+      const float4 oc = reinterpret_cast<const float4 *>(scr + (c - 1) * SP)[d4];
+      O.x = __builtin_fmaf(oc.x, fc, O.x);
+      O.y = __builtin_fmaf(oc.y, fc, O.y);
+      O.z = __builtin_fmaf(oc.z, fc, O.z);
+      O.w = __builtin_fmaf(oc.w, fc, O.w);
+    }
+    const float rl = __builtin_amdgcn_rcpf(Ls);
+    publish_head(make_float4(O.x * rl, O.y * rl, O.z * rl, O.w * rl));
+  }
+  stamp_if<TR>(a, lane, step, 5 * l + 1, 3, S::G);
+  return true;
+}
+
 // Compute waves of a workgroup of set SET.  Its slice of a layer sits in
 // registers from one layer to the next: right after the phase has consumed
 // it (and the control wave has issued the phase's stores, third barrier), the
 // next layer's slice is requested into the same registers, and has a whole
 // layer to arrive.  Sets whose phase comes late in the layer request the next
 // step's first slice only after the output head, whose loads it would delay.
-template <class S, int WD, int SET>
+template <class S, int WD, int SET, bool TR, bool DOTS>
 __device__ __attribute__((always_inline)) void compute_set(const DecodeArgs &a, const MatW &m, float *lds,
                                                            int lane) {
   using ST = Set<S, SET>;
@@ -977,11 +1285,34 @@ __device__ __attribute__((always_inline)) void compute_set(const DecodeArgs &a, 
   constexpr bool LATE = SET != SET_Q;
   constexpr int NRB = head_reg_batches<S, WD, SET>(), NX = head_extra_batches<S, WD, SET>();
   Chunk<HeadGeo<S, WD>::HWD> hx[NX > 0 ? NX : 1][HeadGeo<S, WD>::NPH];
-  const int *flag = reinterpret_cast<const int *>(lds + S::L_FLAG);
+  int *flag = reinterpret_cast<int *>(lds + S::L_FLAG);
   float *part = lds + S::L_PART;
   const float *xs = lds + S::L_XS;
   const int rank = (int)blockIdx.x - ST::FIRST;
   Chunk<WD> b[ST::NB];
+  // With S::ITEM_CW, compute wave IW (DOTS false: it holds no slice, takes no
+  // dot products and no output-head rows, but passes every barrier and polls
+  // its part of the MLP activation) runs the workgroup's attention item: sets
+  // A, F and M right before their own phase of the layer, set Q right after
+  // its phase (the item reads the QKV outputs).  Sets A and F request the next
+  // layer's rows of their item once their own phase is done; set M, whose
+  // phase closes the layer, requests them at the item.  A failed wait raises
+  // the compute-side abort flag, which every wave reads after the next
+  // barrier.
+  Waiter wt{&a, 0, 0, 0u};
+  float4 kpre[S::ITEM_CW && !DOTS ? S::D / 4 : 1];
+  bool pre = false;  // kpre and the LDS value rows hold this layer's chunk
+  auto run_item = [&](int step, int l, int nch, const ItemOf &it) {
+    if constexpr (S::ITEM_CW && !DOTS) {
+      const int wl = lane % 64;
+      if (!att_item_cw<S, TR>(a, lds, step, l, a.pos0 + step, nch, it, wl, wt, kpre, pre) && wl == 0) flag[1] = 1;
+      pre = false;
+      // its stores (the outputs, and the cache rows when the chunk closes at
+      // the position) are complete before this wave reaches the next barrier
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+  };
+  auto aborted = [&]() { return S::ITEM_CW ? (flag[0] | flag[1]) != 0 : flag[0] != 0; };
   // A workgroup of set M whose control wave runs an attention item in a step
   // requests each layer's slice only after that item (one more barrier): the
   // slice would otherwise still be streaming in, two phases after its request,
@@ -990,54 +1321,93 @@ __device__ __attribute__((always_inline)) void compute_set(const DecodeArgs &a, 
     return SET == SET_M && step < a.nsteps && has_att_item<S>(a.pos0 + step, (int)blockIdx.x);
   };
   bool defer = defers(0);
-  if (!defer) load_set<ST, WD>(b, m, 0, rank, lane);
+  if (DOTS && !defer) load_set<ST, WD>(b, m, 0, rank, lane);
   for (int step = 0; step < a.nsteps; step++) {
     const bool more = step + 1 < a.nsteps;
     const bool defer_next = defers(step + 1);
+    // (item wave: an opaque copy of the lane index per step, so that its
+    // per-lane addresses are not held in registers for the whole launch)
+    if constexpr (!DOTS) asm volatile("" : "+v"(lane));
+    int nch = 1;
+    ItemOf it{};
+    const bool my_item = !DOTS && item_at<S, SET>(a.pos0 + step, (int)blockIdx.x, nch, it);
     for (int l = 0; l < a.L; l++) {
+      if constexpr (!DOTS && SET != SET_Q) {
+        if (my_item) run_item(step, l, nch, it);
+      }
       if (defer) {
-        wg_barrier();  // the control wave has run its attention item
-        if (flag[0]) return;
-        load_set<ST, WD>(b, m, l, rank, lane);
+        wg_barrier();  // the attention item has run
+        if (aborted()) return;
+        if constexpr (DOTS) load_set<ST, WD>(b, m, l, rank, lane);
       }
       if constexpr (SET == SET_M && S::M_PARTS > 1) poll_act_part<S>(a, step, l, lds, lane);
       wg_barrier();
       if (flag[0] | flag[1]) return;
-      dot_set<ST, WD>(b, xs, part, lane);
+      if constexpr (DOTS) dot_set<ST, WD>(b, xs, part, lane);
       wg_barrier();
       wg_barrier();
+      if constexpr (S::ITEM_CW && !DOTS && (SET == SET_A || SET == SET_F)) {
+        // the next layer's key rows and value rows, requested once this set's
+        // phase is done (cache rows of earlier positions; not waited for until
+        // that item, this wave's next LDS access)
+        if (my_item && l + 1 < a.L) {
+          att_item_fetch<S>(a, lds, l + 1, it, lane % 64, kpre);
+          pre = true;
+        }
+      }
       if constexpr (WD == WD_F16) {
         if (step == 0 && l == 1) wait_head_lds();  // (before the next slice request)
       }
       if (l + 1 < a.L) {
-        if (!defer) load_set<ST, WD>(b, m, l + 1, rank, lane);
+        if (DOTS && !defer) load_set<ST, WD>(b, m, l + 1, rank, lane);
       } else if (more && !LATE) {
-        load_set<ST, WD>(b, m, 0, rank, lane);
-      } else {
+        if constexpr (DOTS) load_set<ST, WD>(b, m, 0, rank, lane);
+      } else if constexpr (DOTS) {
         head_prefetch_regs<S, WD, NRB>(a, b, lane);  // idle slice registers take head rows
       }
-      if (step == 0 && l == 0) {
+      if (DOTS && step == 0 && l == 0) {
         // output-head rows kept on chip for the launch: in LDS, and in hx
         fill_head_lds<S, WD>(a, lds, lane);
         head_load_rows<S, WD, NRB, NX>(
             a, [&](int k, int i, const Chunk<HeadGeo<S, WD>::HWD> &c) { hx[k][i] = c; }, lane);
         if (WD == WD_F16 && a.L == 1) wait_head_lds();
       }
+      if constexpr (!DOTS && SET == SET_Q) {
+        if (my_item) run_item(step, l, nch, it);
+      }
     }
-    if (!head_rows<S, WD, NRB, NX>(a, lds, lane, b, hx)) return;
+    if constexpr (DOTS) {
+      if (!head_rows<S, WD, NRB, NX>(a, lds, lane, b, hx)) return;
+    } else {
+      // (the item wave takes no head rows; it passes the head's two barriers)
+      wg_barrier();
+      if (aborted()) return;
+      wg_barrier();
+    }
     wg_barrier();  // the control wave has issued the logits and its argmax
-    if (more && LATE && !defer_next) load_set<ST, WD>(b, m, 0, rank, lane);
+    if (DOTS && more && LATE && !defer_next) load_set<ST, WD>(b, m, 0, rank, lane);
     defer = defer_next;
   }
 }
 
-template <class S, int WD>
+template <class S, int WD, bool TR>
 __device__ __attribute__((always_inline)) void compute_main(const DecodeArgs &a, float *lds, int lane) {
   const int w = (int)blockIdx.x;
-  if (w < Set<S, SET_A>::FIRST) compute_set<S, WD, SET_Q>(a, a.qkv, lds, lane);
-  else if (w < Set<S, SET_F>::FIRST) compute_set<S, WD, SET_A>(a, a.ap, lds, lane);
-  else if (w < Set<S, SET_M>::FIRST) compute_set<S, WD, SET_F>(a, a.fc, lds, lane);
-  else compute_set<S, WD, SET_M>(a, a.pr, lds, lane);
+  if constexpr (S::ITEM_CW) {
+    if (__builtin_amdgcn_readfirstlane(lane / 64) == S::IW) {
+      if (w < Set<S, SET_A>::FIRST) compute_set<S, WD, SET_Q, TR, false>(a, a.qkv, lds, lane);
+      else if (w < Set<S, SET_F>::FIRST) compute_set<S, WD, SET_A, TR, false>(a, a.ap, lds, lane);
+      else if (w < Set<S, SET_M>::FIRST) compute_set<S, WD, SET_F, TR, false>(a, a.fc, lds, lane);
+      else compute_set<S, WD, SET_M, TR, false>(a, a.pr, lds, lane);
+      // (on an abort the next layer's rows may still be in flight to LDS)
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      return;
+    }
+  }
+  if (w < Set<S, SET_A>::FIRST) compute_set<S, WD, SET_Q, TR, true>(a, a.qkv, lds, lane);
+  else if (w < Set<S, SET_F>::FIRST) compute_set<S, WD, SET_A, TR, true>(a, a.ap, lds, lane);
+  else if (w < Set<S, SET_M>::FIRST) compute_set<S, WD, SET_F, TR, true>(a, a.fc, lds, lane);
+  else compute_set<S, WD, SET_M, TR, true>(a, a.pr, lds, lane);
 }
 
 // ---- control wave ----------------------------------------------------------
@@ -1390,7 +1760,7 @@ __device__ __attribute__((always_inline)) void control_set(const DecodeArgs &a, 
   Chunk<WD> cb[CBN > SA::NB || !S::CD ? CBN : SA::NB];
   auto ctl_load = [&](int layer) {
     if constexpr (S::CD) {
-      const int cl = S::NL + lane;
+      const int cl = S::NLD - 64 + lane;
       if (set == SET_Q) load_set<SQ, WD>(*reinterpret_cast<Chunk<WD>(*)[SQ::NB]>(cb), a.qkv, layer, rank, cl);
       else if (set == SET_A) load_set<SA, WD>(*reinterpret_cast<Chunk<WD>(*)[SA::NB]>(cb), a.ap, layer, rank, cl);
       else if (set == SET_F) load_set<SF, WD>(*reinterpret_cast<Chunk<WD>(*)[SF::NB]>(cb), a.fc, layer, rank, cl);
@@ -1399,7 +1769,7 @@ __device__ __attribute__((always_inline)) void control_set(const DecodeArgs &a, 
   };
   auto ctl_dot = [&]() {
     if constexpr (S::CD) {
-      const int cl = S::NL + lane;
+      const int cl = S::NLD - 64 + lane;
       float *pt = lds + S::L_PART;
       if (set == SET_Q) dot_set<SQ, WD>(*reinterpret_cast<Chunk<WD>(*)[SQ::NB]>(cb), xs, pt, cl);
       else if (set == SET_A) dot_set<SA, WD>(*reinterpret_cast<Chunk<WD>(*)[SA::NB]>(cb), xs, pt, cl);
@@ -1516,6 +1886,7 @@ __device__ __attribute__((always_inline)) void control_set(const DecodeArgs &a, 
         st(step, 5 * l + 0, 0);
         if (lane == 0) flag[0] = 0;
         wg_barrier();
+        if (S::ITEM_CW && flag[1]) return;  // the attention item's wave failed (the error word is set)
         st(step, 5 * l + 0, 1);
         float mean, rstd;
         ln_stats<E>(x, a.eps, mean, rstd);  // (while the dot products run)
@@ -1530,8 +1901,8 @@ __device__ __attribute__((always_inline)) void control_set(const DecodeArgs &a, 
         fetch_params(lnext);
         ctl_after_phase(l);
       }
-      // ---------------- B: attention chunk (control wave only)
-      if (has_item) {
+      // ---------------- B: attention chunk (this wave; with S::ITEM_CW a compute wave)
+      if (has_item && !S::ITEM_CW) {
         AttChunk<S> at;
         at.fetch(a, l, ih, it0, itg, lane);  // cache rows: written at earlier steps
         wt.start(5 * l + 0);
@@ -1663,6 +2034,11 @@ __device__ __attribute__((always_inline)) void control_set(const DecodeArgs &a, 
           ctl_load(l);   // and so may this wave
         }
       }
+      if (S::ITEM_CW && has_item && set == SET_M) {
+        wg_barrier();  // a compute wave has run the item: the slices may now be requested
+        if (flag[1]) return;  // the item's wave failed (the error word is set)
+        ctl_load(l);
+      }
       // ---------------- C: attention projection + residual (set A)
       if (set == SET_A) {
         float xr = 0.f;  // residual stream row rank*R + lane
@@ -1687,6 +2063,7 @@ __device__ __attribute__((always_inline)) void control_set(const DecodeArgs &a, 
         st(step, 5 * l + 2, 0);
         if (lane == 0) flag[0] = 0;
         wg_barrier();
+        if (S::ITEM_CW && flag[1]) return;  // the attention item's wave failed (the error word is set)
         st(step, 5 * l + 2, 1);
         ctl_dot();
         wg_barrier();
@@ -1710,6 +2087,7 @@ __device__ __attribute__((always_inline)) void control_set(const DecodeArgs &a, 
         st(step, 5 * l + 3, 0);
         if (lane == 0) flag[0] = 0;
         wg_barrier();
+        if (S::ITEM_CW && flag[1]) return;  // the attention item's wave failed (the error word is set)
         st(step, 5 * l + 3, 1);
         float mean, rstd;
         ln_stats<E>(x, a.eps, mean, rstd);  // (while the dot products run)
@@ -1780,6 +2158,7 @@ __device__ __attribute__((always_inline)) void control_set(const DecodeArgs &a, 
       st(step, 5 * a.L, 0);
       if (lane == 0) flag[0] = 0;
       wg_barrier();
+      if (S::ITEM_CW && flag[1]) return;  // the attention item's wave failed
       st(step, 5 * a.L, 1);
       // while the head's dot products run: the statistics, and the folded
       // LayerNorm's constants of this workgroup's rows
@@ -1888,7 +2267,7 @@ __global__ void __launch_bounds__(S::NT, 1) decode_kernel(DecodeArgs a) {
   if (tid < 4) reinterpret_cast<int *>(lds + S::L_FLAG)[tid] = 0;
   __syncthreads();
   if (tid >= S::NL) control_main<S, WD, TR>(a, lds, tid - S::NL);
-  else compute_main<S, WD>(a, lds, tid);
+  else compute_main<S, WD, TR>(a, lds, tid);
 }
 
 // Dynamic LDS: the device's per-workgroup limit, at most 160 KB.  More than
@@ -1985,7 +2364,7 @@ void info_t(ShapeInfo *o) {
 }  // namespace
 
 bool shape_info(int E, int D, ShapeInfo *out) {
-  static_assert(ShapeS::G == ShapeSC::G && ShapeS::NT == ShapeSC::NT && ShapeS::MAXCH == ShapeSC::MAXCH,
+  static_assert(ShapeS::G == ShapeSC::G && ShapeS::MAXCH == ShapeSC::MAXCH,
                 "the two 124M variants share their launch geometry");
   if (E == ShapeS::E && D == ShapeS::D) { info_t<ShapeS>(out); return true; }
   if (E == ShapeT::E && D == ShapeT::D) { info_t<ShapeT>(out); return true; }
