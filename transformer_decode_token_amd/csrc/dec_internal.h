@@ -91,7 +91,9 @@ struct ShapeInfo {
   size_t lds_bytes;
   int maxch;                         // maximum attention chunks per head
 };
-bool shape_info(int E, int D, ShapeInfo *out);
+// The shape the decode kernel runs for an E/D model with weight type wd
+// (the 124M shape has one variant for fp32 and one for fp16 and int4).
+bool shape_info(int E, int D, int wd, ShapeInfo *out);
 
 // Launch the decode kernel (all its workgroups are resident at once: one per CU).
 hipError_t launch_decode(int E, int D, int wd, const DecodeArgs &a, hipStream_t s);

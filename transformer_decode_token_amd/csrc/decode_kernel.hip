@@ -2363,10 +2363,14 @@ void info_t(ShapeInfo *o) {
 
 }  // namespace
 
-bool shape_info(int E, int D, ShapeInfo *out) {
+bool shape_info(int E, int D, int wd, ShapeInfo *out) {
   static_assert(ShapeS::G == ShapeSC::G && ShapeS::MAXCH == ShapeSC::MAXCH,
-                "the two 124M variants share their launch geometry");
-  if (E == ShapeS::E && D == ShapeS::D) { info_t<ShapeS>(out); return true; }
+                "the two 124M variants share their grid and chunk limits");
+  if (E == ShapeS::E && D == ShapeS::D) {
+    if (wd == WD_F32) info_t<ShapeS>(out);
+    else info_t<ShapeSC>(out);
+    return true;
+  }
   if (E == ShapeT::E && D == ShapeT::D) { info_t<ShapeT>(out); return true; }
   return false;
 }

@@ -175,7 +175,7 @@ int validate_config(const gpt2_config *c, ShapeInfo *si, std::string &msg) {
     return GPT2_E_INVAL;
   }
   const int D = c->n_embd / c->n_head;
-  if (!shape_info(c->n_embd, D, si)) {
+  if (!shape_info(c->n_embd, D, c->wdtype, si)) {
     snprintf(buf, sizeof buf, "unsupported shape n_embd=%d head_dim=%d (built: 768/64, 128/32)", c->n_embd, D);
     msg = buf;
     return GPT2_E_INVAL;
