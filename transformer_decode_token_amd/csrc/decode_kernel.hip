@@ -124,6 +124,7 @@ struct Shape {
   static constexpr int L_VP = L_KP + D;                  // [D] value of this position
   static constexpr int L_SC = L_VP + D;                  // [64] attention weights (transposed)
   static constexpr int L_V = L_XS;                       // [64][D] an item's value rows (ITEM_CW)
+  static constexpr int L_XRAW = L_XS + E;                // [E] a LayerNorm input before its gain (ITEM_CW)
   static constexpr int L_FLAG = L_SC + 64;               // [4] flags: abort (control), abort (compute)
   static constexpr int L_TOTAL = L_FLAG + 4;
   static constexpr int L_HEAD = (L_TOTAL + 63) & ~63;    // output-head rows kept for the launch
@@ -964,6 +965,55 @@ __device__ bool head_rows(const DecodeArgs &a, float *lds, int lane, const Chunk
 // failed wait raises the compute-side abort flag, which every wave reads
 // after the next barrier.
 template <class S>
+__device__ void poll_act_part(const DecodeArgs &a, int step, int l, float *lds, int lane);
+// With S::ITEM_CW the six dot waves poll the 768-word input of sets Q, A and
+// F at once (set F: in a workgroup without an attention item, else its
+// control wave polls it), 128 words each, one pair load per lane per round.
+// The part, times the LayerNorm gain where one comes first, goes into the dot
+// products' input, and (gain given) the part itself to L_XRAW, from which the
+// control wave takes the LayerNorm statistics after the first barrier.
+// The input region also holds the workgroup's attention item's value rows
+// until the item has read them.  Every element of set Q's and set F's input
+// depends on every attention output, so none is complete before that; a part
+// of set A's input (two heads) can be, and is written only after the item's
+// release word (`release`: that layer's attention epoch; 0: no item).  src:
+// the input vector's copy of this XCD; prod: the producing phase.
+template <class S>
+__device__ void poll_in_part(const DecodeArgs &a, const uint64_t *src, uint32_t ep, int prod, const float *gain,
+                             float *lds, int lane, uint32_t release = 0) {
+  static_assert(6 * 128 == S::E, "six parts of 128 words");
+  const int wv = __builtin_amdgcn_readfirstlane(lane / 64), wl = lane % 64;
+  const int e0 = wv * 128 + 2 * wl;
+  float g0 = 1.f, g1 = 1.f;
+  if (gain) {
+    g0 = gain[e0];
+    g1 = gain[e0 + 1];
+  }
+  Waiter wt{&a, 0, 0, 0u};
+  wt.start(prod);
+  float v[2];
+  if (poll_vec<2>(src + wv * 128, ep, v, wl, wt)) {
+    // (a bounded wait; it ends early when a wave of the workgroup has failed)
+    int *fl = reinterpret_cast<int *>(lds + S::L_FLAG);
+    while (release &&
+           __hip_atomic_load(fl + 2, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != (int)release) {
+      if (__hip_atomic_load(fl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0 || wt.expired()) {
+        if (wl == 0) fl[1] = 1;
+        return;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    lds[S::L_XS + e0] = v[0] * g0;
+    lds[S::L_XS + e0 + 1] = v[1] * g1;
+    if (gain) {
+      lds[S::L_XRAW + e0] = v[0];
+      lds[S::L_XRAW + e0 + 1] = v[1];
+    }
+  } else if (wl == 0) {
+    reinterpret_cast<int *>(lds + S::L_FLAG)[1] = 1;
+  }
+}
+template <class S>
 __device__ void poll_act_part(const DecodeArgs &a, int step, int l, float *lds, int lane) {
   constexpr int PW = S::F / S::M_PARTS, PER = PW / 64;
   // the wave index is uniform: in a scalar register, the part's buffer
@@ -1190,10 +1240,20 @@ __device__ __attribute__((always_inline)) bool att_item_cw(const DecodeArgs &a, 
       tst2(attn_rs, off + 16, r.z, r.w, epB);
     }
   };
+  // The item's last read of the LDS under the phase input: the workgroup's
+  // dot waves of set A may write their part of the phase input from here on
+  // (a part is complete once two heads are in, maybe before this one).
+  auto release_input = [&]() {
+    if (lane == 0)
+      __hip_atomic_store(reinterpret_cast<int *>(lds + S::L_FLAG) + 2, (int)epB, __ATOMIC_RELEASE,
+                         __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
   if (nch == 1) {
     const float rl = __builtin_amdgcn_rcpf(lsum);
+    release_input();
     publish_head(make_float4(o.x * rl, o.y * rl, o.z * rl, o.w * rl));
   } else if (ic > 0) {
+    release_input();
     // this chunk's (o, m, l) for chunk 0 of the head, as word pairs
     const auto prs = __builtin_amdgcn_make_buffer_rsrc(
         a.att_t + ((size_t)(l * H + ih) * S::MAXCH + ic) * (D + 2), (short)0, (D + 2) * 8, 0x00020000);
@@ -1264,6 +1324,7 @@ __device__ __attribute__((always_inline)) bool att_item_cw(const DecodeArgs &a, 
       O.w = __builtin_fmaf(oc.w, fc, O.w);
     }
     const float rl = __builtin_amdgcn_rcpf(Ls);
+    release_input();
     publish_head(make_float4(O.x * rl, O.y * rl, O.z * rl, O.w * rl));
   }
   stamp_if<TR>(a, lane, step, 5 * l + 1, 3, S::G);
@@ -1331,6 +1392,8 @@ __device__ __attribute__((always_inline)) void compute_set(const DecodeArgs &a, 
     int nch = 1;
     ItemOf it{};
     const bool my_item = !DOTS && item_at<S, SET>(a.pos0 + step, (int)blockIdx.x, nch, it);
+    // (the dot waves of sets A and F: whether the workgroup's attention wave runs an item)
+    const bool wg_item = (SET == SET_A || SET == SET_F) && DOTS && has_att_item<S>(a.pos0 + step, (int)blockIdx.x);
     for (int l = 0; l < a.L; l++) {
       if constexpr (!DOTS && SET != SET_Q) {
         if (my_item) run_item(step, l, nch, it);
@@ -1341,6 +1404,24 @@ __device__ __attribute__((always_inline)) void compute_set(const DecodeArgs &a, 
         if constexpr (DOTS) load_set<ST, WD>(b, m, l, rank, lane);
       }
       if constexpr (SET == SET_M && S::M_PARTS > 1) poll_act_part<S>(a, step, l, lds, lane);
+      if constexpr (S::ITEM_CW && DOTS) {
+        // this wave's part of the phase input (sets Q from the second layer on,
+        // A, and F without an item; poll_in_part)
+        const uint32_t ep0 = epoch_of(a, step, 5 * l + 0);
+        const size_t cp = (size_t)my_copy() * S::E;
+        if constexpr (SET == SET_Q) {
+          if (l > 0)
+            poll_in_part<S>(a, a.xb_t + (size_t)(l - 1) * NCOPY * S::E + cp, ep0 - 1, 5 * (l - 1) + 4,
+                            a.ln1w + (size_t)l * S::E, lds, lane);
+        } else if constexpr (SET == SET_A) {
+          poll_in_part<S>(a, a.attn_t + (size_t)l * NCOPY * S::E + cp, ep0 + 1, 5 * l + 1, nullptr, lds, lane,
+                          wg_item ? ep0 + 1 : 0u);
+        } else if constexpr (SET == SET_F) {
+          if (!wg_item)
+            poll_in_part<S>(a, a.xa_t + (size_t)l * NCOPY * S::E + cp, ep0 + 2, 5 * l + 2,
+                            a.ln2w + (size_t)l * S::E, lds, lane);
+        }
+      }
       wg_barrier();
       if (flag[0] | flag[1]) return;
       if constexpr (DOTS) dot_set<ST, WD>(b, xs, part, lane);
@@ -1875,19 +1956,25 @@ __device__ __attribute__((always_inline)) void control_set(const DecodeArgs &a, 
 #pragma unroll
           for (int j = 0; j < PE; j++)
             x[j] = a.wte[(size_t)tok * E + vidx(lane, j)] + a.wpe[(size_t)p * E + vidx(lane, j)];
-        } else {
+        } else if constexpr (!S::ITEM_CW) {
           wt.start(5 * (l - 1) + 4);
           if (!poll_vec<PE>(a.xb_t + ((size_t)(l - 1) * NCOPY + my_copy()) * E, epA - 1, x, lane, wt)) {
             abort_all();
             return;
           }
         }
-        gain_to_lds<E>(x, g, xs, lane);
+        if (!S::ITEM_CW || l == 0) gain_to_lds<E>(x, g, xs, lane);  // (else the dot waves poll it)
         st(step, 5 * l + 0, 0);
         if (lane == 0) flag[0] = 0;
         wg_barrier();
-        if (S::ITEM_CW && flag[1]) return;  // the attention item's wave failed (the error word is set)
+        if (S::ITEM_CW && flag[1]) return;  // a compute wave's wait failed (the error word is set)
         st(step, 5 * l + 0, 1);
+        if constexpr (S::ITEM_CW) {
+          if (l > 0) {
+#pragma unroll
+            for (int j = 0; j < PE; j++) x[j] = lds[S::L_XRAW + vidx(lane, j)];
+          }
+        }
         float mean, rstd;
         ln_stats<E>(x, a.eps, mean, rstd);  // (while the dot products run)
         ctl_dot();
@@ -2055,15 +2142,20 @@ __device__ __attribute__((always_inline)) void control_set(const DecodeArgs &a, 
             return;
           }
         }
-        float x[PE];
-        wt.start(5 * l + 1);
-        if (!poll_vec<PE>(a.attn_t + ((size_t)l * NCOPY + my_copy()) * E, epB, x, lane, wt)) { abort_all(); return; }
+        if constexpr (!S::ITEM_CW) {  // (else the dot waves poll it)
+          float x[PE];
+          wt.start(5 * l + 1);
+          if (!poll_vec<PE>(a.attn_t + ((size_t)l * NCOPY + my_copy()) * E, epB, x, lane, wt)) {
+            abort_all();
+            return;
+          }
 #pragma unroll
-        for (int j = 0; j < PE; j++) xs[vidx(lane, j)] = x[j];
+          for (int j = 0; j < PE; j++) xs[vidx(lane, j)] = x[j];
+        }
         st(step, 5 * l + 2, 0);
         if (lane == 0) flag[0] = 0;
         wg_barrier();
-        if (S::ITEM_CW && flag[1]) return;  // the attention item's wave failed (the error word is set)
+        if (S::ITEM_CW && flag[1]) return;  // a compute wave's wait failed (the error word is set)
         st(step, 5 * l + 2, 1);
         ctl_dot();
         wg_barrier();
@@ -2081,14 +2173,23 @@ __device__ __attribute__((always_inline)) void control_set(const DecodeArgs &a, 
       if (set == SET_F) {
         if constexpr (S::CD) fetch_gain(g, a.ln2w + l * E);  // (arrives during the poll)
         float x[PE];
-        wt.start(5 * l + 2);
-        if (!poll_vec<PE>(a.xa_t + ((size_t)l * NCOPY + my_copy()) * E, epC, x, lane, wt)) { abort_all(); return; }
-        gain_to_lds<E>(x, g, xs, lane);
+        if (!S::ITEM_CW || has_item) {  // (else the dot waves poll it)
+          wt.start(5 * l + 2);
+          if (!poll_vec<PE>(a.xa_t + ((size_t)l * NCOPY + my_copy()) * E, epC, x, lane, wt)) {
+            abort_all();
+            return;
+          }
+          gain_to_lds<E>(x, g, xs, lane);
+        }
         st(step, 5 * l + 3, 0);
         if (lane == 0) flag[0] = 0;
         wg_barrier();
-        if (S::ITEM_CW && flag[1]) return;  // the attention item's wave failed (the error word is set)
+        if (S::ITEM_CW && flag[1]) return;  // a compute wave's wait failed (the error word is set)
         st(step, 5 * l + 3, 1);
+        if (S::ITEM_CW && !has_item) {
+#pragma unroll
+          for (int j = 0; j < PE; j++) x[j] = lds[S::L_XRAW + vidx(lane, j)];
+        }
         float mean, rstd;
         ln_stats<E>(x, a.eps, mean, rstd);  // (while the dot products run)
         ctl_dot();
