@@ -383,8 +383,8 @@ def test_rewind_deep_124m(name):
     model = synth.make_model(cfg)
     ctx = load_gpu(model)
     # the launch geometry of this weight type's kernel: 256 workgroups of
-    # eight waves (fp32) or four (fp16, int4)
-    assert g2.gpt2_debug_geometry(ctx) == (256, 512 if cfg.wdtype == "fp32" else 256)
+    # eight waves (fp32, fp16) or four (int4)
+    assert g2.gpt2_debug_geometry(ctx) == (256, 256 if cfg.wdtype == "int4" else 512)
     prompt = synth.make_prompt(cfg)
     ids = g2.gpt2_generate(ctx, prompt, 1000 - len(prompt) + 1)
     assert g2.gpt2_filled(ctx) == 1000

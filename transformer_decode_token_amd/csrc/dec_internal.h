@@ -92,7 +92,7 @@ struct ShapeInfo {
   int maxch;                         // maximum attention chunks per head
 };
 // The shape the decode kernel runs for an E/D model with weight type wd
-// (the 124M shape has one variant for fp32 and one for fp16 and int4).
+// (the 124M shape has one variant for fp32 and fp16 and one for int4).
 bool shape_info(int E, int D, int wd, ShapeInfo *out);
 
 // Launch the decode kernel (all its workgroups are resident at once: one per CU).

@@ -27,10 +27,10 @@
 //     LayerNorm statistics are taken while the dot products run and applied
 //     to the row results), runs an attention chunk when it has one, and
 //     publishes;
-//   * with more than three compute waves (the fp32 kernel: two waves per
-//     SIMD, 256 registers each) the last compute wave takes no slice and runs
-//     the attention chunk in the control wave's place, with the chunk's value
-//     rows in LDS.
+//   * with more than three compute waves (the fp32 and fp16 kernels: two
+//     waves per SIMD, 256 registers each) the last compute wave takes no slice
+//     and runs the attention chunk in the control wave's place, with the
+//     chunk's value rows in LDS.
 // Each phase's inputs therefore come from, and go to, a few dozen workgroups
 // rather than all of them, which shortens every hand-over.
 // Batch 1 makes every linear a matrix-vector product (0.5 flop per fp32 byte),
@@ -130,16 +130,16 @@ struct Shape {
   static constexpr int L_HEAD = (L_TOTAL + 63) & ~63;    // output-head rows kept for the launch
 };
 
-// 124M shape.  fp32: 256 workgroups x (7 compute + 1 control) waves, two
-// waves on each SIMD: six waves take the dot products (32 lanes per row), the
-// seventh the attention item; sets of 64 (QKV, 36 rows each), 32 (attention
-// projection, 24 rows), 64 (fc, 48 rows) and 96 (MLP projection, 8 rows), so
-// every workgroup reads 74 to 147 KB of weights per layer.  fp16 and int4,
-// whose dot products cost more vector instructions per weight and more
-// registers: 256 workgroups x (3 compute + 1 control) waves, and the control
-// wave takes a share of every slice too, in sets of 72 (32 rows), 24 (32
-// rows), 64 (48 rows) and 96 (8 rows), row counts that 16 (64 for K = 3072)
-// rows per pass of 256 lanes divide.  (Set sizes and the split chosen by
+// 124M shape.  fp32 and fp16: 256 workgroups x (7 compute + 1 control) waves,
+// two waves on each SIMD: six waves take the dot products (32 lanes per row),
+// the seventh the attention item; sets of 64 (QKV, 36 rows each), 32
+// (attention projection, 24 rows), 64 (fc, 48 rows) and 96 (MLP projection, 8
+// rows), so every fp32 workgroup reads 74 to 147 KB of weights per layer.
+// int4, whose dot products cost about two vector instructions per weight and
+// more registers: 256 workgroups x (3 compute + 1 control) waves, and the
+// control wave takes a share of every slice too, in sets of 72 (32 rows), 24
+// (32 rows), 64 (48 rows) and 96 (8 rows), row counts that 16 (64 for K =
+// 3072) rows per pass of 256 lanes divide.  (Set sizes and the split chosen by
 // measurement.)
 using ShapeS = Shape<768, 64, 7, 16, 32, 32, 64, 32, 64, 96, 0>;
 using ShapeSC = Shape<768, 64, 3, 16, 16, 16, 72, 24, 64, 96, 1>;
@@ -2389,10 +2389,10 @@ int head_lds_rows_for(int wd, size_t lds) {
 }
 
 // The weight types a shape is built for: the 124M shape in two variants
-// (fp32; fp16 and int4), the tiny shape for all three.
+// (eight waves: fp32 and fp16; four waves: int4), the tiny shape for all three.
 template <class S>
 constexpr bool shape_has(int wd) {
-  return std::is_same<S, ShapeS>::value ? wd == WD_F32 : std::is_same<S, ShapeSC>::value ? wd != WD_F32 : true;
+  return std::is_same<S, ShapeS>::value ? wd != WD_Q4 : std::is_same<S, ShapeSC>::value ? wd == WD_Q4 : true;
 }
 template <class S, bool TR>
 const void *kernel_for_tr(int wd) {
@@ -2468,7 +2468,7 @@ bool shape_info(int E, int D, int wd, ShapeInfo *out) {
   static_assert(ShapeS::G == ShapeSC::G && ShapeS::MAXCH == ShapeSC::MAXCH,
                 "the two 124M variants share their grid and chunk limits");
   if (E == ShapeS::E && D == ShapeS::D) {
-    if (wd == WD_F32) info_t<ShapeS>(out);
+    if (wd != WD_Q4) info_t<ShapeS>(out);
     else info_t<ShapeSC>(out);
     return true;
   }
@@ -2477,14 +2477,14 @@ bool shape_info(int E, int D, int wd, ShapeInfo *out) {
 }
 
 hipError_t launch_decode(int E, int D, int wd, const DecodeArgs &a, hipStream_t s) {
-  if (E == ShapeS::E && D == ShapeS::D) return wd == WD_F32 ? launch_t<ShapeS>(wd, a, s) : launch_t<ShapeSC>(wd, a, s);
+  if (E == ShapeS::E && D == ShapeS::D) return wd != WD_Q4 ? launch_t<ShapeS>(wd, a, s) : launch_t<ShapeSC>(wd, a, s);
   if (E == ShapeT::E && D == ShapeT::D) return launch_t<ShapeT>(wd, a, s);
   return hipErrorInvalidValue;
 }
 
 hipError_t decode_occupancy(int E, int D, int wd, int *blocks) {
   if (E == ShapeS::E && D == ShapeS::D)
-    return wd == WD_F32 ? occupancy_t<ShapeS>(wd, blocks) : occupancy_t<ShapeSC>(wd, blocks);
+    return wd != WD_Q4 ? occupancy_t<ShapeS>(wd, blocks) : occupancy_t<ShapeSC>(wd, blocks);
   if (E == ShapeT::E && D == ShapeT::D) return occupancy_t<ShapeT>(wd, blocks);
   return hipErrorInvalidValue;
 }
