@@ -1,12 +1,12 @@
 /*
  * gpt2dec.h -- C ABI of the MI355X (gfx950) batch-1 GPT-2 decode library.
  *
- * One call of gpt2_step runs the one-token forward pass that the "model.fir"
- * page (gpt2-125m model file) describes node by node: token + positional
- * embedding, per layer LayerNorm -> QKV linear + bias -> attn_decode (append
- * this position's K/V, causal softmax over positions 0..position, weighted sum
- * of values) -> attention linear + bias + residual -> LayerNorm -> fc linear +
- * bias -> gelu_new -> projection linear + bias + residual, then the final
+ * One call of gpt2_step runs the one-token GPT-2 forward pass (the gpt2-125m
+ * "model.fir" page's network): token + positional embedding, per layer
+ * LayerNorm -> QKV linear + bias -> attn_decode (append this position's K/V,
+ * causal softmax over positions 0..position, weighted sum of values) ->
+ * attention linear + bias + residual -> LayerNorm -> fc linear + bias ->
+ * gelu_new -> projection linear + bias + residual, then the final
  * LayerNorm and the output head tied to wte, with greedy choice = argmax
  * ("Let's make GPT-2 in assembly", Step 7).  Weights arrive in the Hugging Face
  * checkpoint layout (Conv1D matrices as [input][output], as both pages note)

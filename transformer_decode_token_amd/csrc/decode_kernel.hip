@@ -1,8 +1,8 @@
 // decode_kernel.hip -- the persistent batch-1 GPT-2 decode kernel for gfx950.
 //
 // One launch runs `nsteps` whole forward passes (one token each).
-// The per-token work follows the node order of the gpt2-125m "model.fir" file:
-// embedding add, then per layer
+// The per-token work is the GPT-2 forward pass (the gpt2-125m "model.fir"
+// page's network): embedding add, then per layer
 //   A: LayerNorm 1 + QKV linear + bias
 //   B: attn_decode: this position's K/V are appended, causal softmax over
 //      positions 0..position, weighted sum of values (split in position chunks
