@@ -113,9 +113,9 @@ struct Shape {
   static_assert(H * MAXCH <= G, "one attention chunk per workgroup at most");
   // LDS layout (floats)
   // [F] phase input vector; with ITEM_CW also (at least [64][D]) the
-  // attention item's value rows, which are read before any input vector of
-  // the workgroup's next phase can be complete (that input depends on the
-  // item's output)
+  // attention item's value rows, read before the workgroup's next phase input
+  // can be complete (it depends on the item's output; a dot wave's part of set
+  // A's input waits for the item's release word, poll_in_part)
   static constexpr int L_XS = 0;
   static constexpr int XS_N = ITEM_CW && 64 * D_ > F ? 64 * D_ : F;
   static constexpr int L_PART = L_XS + XS_N;             // [PSTRIDE] row results
@@ -960,12 +960,29 @@ __device__ bool head_rows(const DecodeArgs &a, float *lds, int lane, const Chunk
 
 // Compute wave lane/64 (< M_PARTS - 1) of a set-M workgroup polls its part of
 // the MLP activation into the phase input (right after requesting its slice);
-// the control wave polls the last part.  Each wave's poll round is a quarter
-// of the whole vector, so the last part is seen sooner after it lands.  A
+// the control wave polls the last part.  Each wave's poll round covers one
+// of the M_PARTS parts (four in the int4 kernel, eight in the eight-wave one),
+// so the last part is seen sooner after it lands.  A
 // failed wait raises the compute-side abort flag, which every wave reads
 // after the next barrier.
 template <class S>
-__device__ void poll_act_part(const DecodeArgs &a, int step, int l, float *lds, int lane);
+__device__ void poll_act_part(const DecodeArgs &a, int step, int l, float *lds, int lane) {
+  constexpr int PW = S::F / S::M_PARTS, PER = PW / 64;
+  // the wave index is uniform: in a scalar register, the part's buffer
+  // resource is too (a per-lane resource would serialise the loads)
+  const int wv = __builtin_amdgcn_readfirstlane(lane / 64), wl = lane % 64;
+  if (wv >= S::M_PARTS - 1) return;
+  Waiter wt{&a, 0, 0, 0u};
+  wt.start(5 * l + 3);
+  float v[PER];
+  const uint64_t *src = a.act_t + ((size_t)l * NCOPY + my_copy()) * S::F + wv * PW;
+  if (poll_vec<PER>(src, epoch_of(a, step, 5 * l + 3), v, wl, wt)) {
+#pragma unroll
+    for (int j = 0; j < PER; j++) lds[S::L_XS + wv * PW + vidx(wl, j)] = v[j];
+  } else if (wl == 0) {
+    reinterpret_cast<int *>(lds + S::L_FLAG)[1] = 1;
+  }
+}
 // With S::ITEM_CW the six dot waves poll the 768-word input of sets Q, A and
 // F at once (set F: in a workgroup without an attention item, else its
 // control wave polls it), 128 words each, one pair load per lane per round.
@@ -1009,24 +1026,6 @@ __device__ void poll_in_part(const DecodeArgs &a, const uint64_t *src, uint32_t 
       lds[S::L_XRAW + e0] = v[0];
       lds[S::L_XRAW + e0 + 1] = v[1];
     }
-  } else if (wl == 0) {
-    reinterpret_cast<int *>(lds + S::L_FLAG)[1] = 1;
-  }
-}
-template <class S>
-__device__ void poll_act_part(const DecodeArgs &a, int step, int l, float *lds, int lane) {
-  constexpr int PW = S::F / S::M_PARTS, PER = PW / 64;
-  // the wave index is uniform: in a scalar register, the part's buffer
-  // resource is too (a per-lane resource would serialise the loads)
-  const int wv = __builtin_amdgcn_readfirstlane(lane / 64), wl = lane % 64;
-  if (wv >= S::M_PARTS - 1) return;
-  Waiter wt{&a, 0, 0, 0u};
-  wt.start(5 * l + 3);
-  float v[PER];
-  const uint64_t *src = a.act_t + ((size_t)l * NCOPY + my_copy()) * S::F + wv * PW;
-  if (poll_vec<PER>(src, epoch_of(a, step, 5 * l + 3), v, wl, wt)) {
-#pragma unroll
-    for (int j = 0; j < PER; j++) lds[S::L_XS + wv * PW + vidx(wl, j)] = v[j];
   } else if (wl == 0) {
     reinterpret_cast<int *>(lds + S::L_FLAG)[1] = 1;
   }
