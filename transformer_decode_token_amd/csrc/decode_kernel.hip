@@ -94,6 +94,9 @@ struct Shape {
   static constexpr int HEAD_BATCHES = 3;
   static constexpr int HEAD_REGS_Q = 2, HEAD_REGS_LATE = 3;
   static constexpr int HEAD_REGS_Q4_Q = 2, HEAD_REGS_Q4_LATE = 3;  // int4 (its head is fp32)
+  // fp16 with two waves per SIMD: a batch of fp16 head rows takes half the
+  // registers of an fp32 one, and the fp16 slices leave them free
+  static constexpr int HEAD_REGS_F16_Q = 5, HEAD_REGS_F16_LATE = 8;
   // Batches (of 64/LPRH rows) of output-head rows the control wave keeps in its
   // own registers for the launch and takes during the head (none with a slice
   // share, whose registers it needs).
@@ -737,10 +740,11 @@ struct HeadGeo {
 // sets, when the register chunk type is the head's: not for int4), requested
 // after the set's last phase of each step, and head_extra_batches in registers
 // of their own, requested once and kept for the launch, up to a total per
-// weight type (the same batch counts for fp32 and fp16 heads: more fp16
-// batches, though half the registers each, measured slower).
+// weight type and shape (fp16 with four waves: the fp32 counts, more measured
+// slower; fp16 with eight waves: 5 and 8, measured faster than 2 and 3).
 template <class S, int WD, int SET>
 constexpr int head_reg_want() {
+  if constexpr (WD == WD_F16 && S::ITEM_CW) return SET == SET_Q ? S::HEAD_REGS_F16_Q : S::HEAD_REGS_F16_LATE;
   return WD == WD_Q4 ? (SET == SET_Q ? S::HEAD_REGS_Q4_Q : S::HEAD_REGS_Q4_LATE)
                      : (SET == SET_Q ? S::HEAD_REGS_Q : S::HEAD_REGS_LATE);
 }
