@@ -1076,7 +1076,8 @@ __device__ __forceinline__ void stamp_if(const DecodeArgs &a, int lane, int step
 // zeros) and waits for none of them.
 template <class S>
 __device__ __attribute__((always_inline)) void att_item_fetch(const DecodeArgs &a, float *lds, int l, const ItemOf &it,
-                                                              int lane, float4 (&k)[S::D / 4]) {
+                                                              int lane, float4 (&k)[S::D / 4], bool keys = true,
+                                                              bool values = true) {
   constexpr int D = S::D, H = S::H, D4 = D / 4;
   static_assert(D == 64, "16 pieces of 16 bytes per value row, 4 rows per copy");
   asm volatile("" : "+v"(lane));
@@ -1086,11 +1087,14 @@ __device__ __attribute__((always_inline)) void att_item_fetch(const DecodeArgs &
   const int nv = itg - it0;  // cache rows of the chunk
   {
     const int tk = it0 + lane;
+    if (keys) {
 #pragma unroll
-    for (int i = 0; i < D4; i++) {
-      k[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (tk < itg) k[i] = reinterpret_cast<const float4 *>(K + (size_t)tk * D)[i];
+      for (int i = 0; i < D4; i++) {
+        k[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (tk < itg) k[i] = reinterpret_cast<const float4 *>(K + (size_t)tk * D)[i];
+      }
     }
+    if (!values) return;
     typedef __attribute__((address_space(1))) void g_void;
     typedef __attribute__((address_space(3))) void l_void;
     const char *src = reinterpret_cast<const char *>(V + (size_t)it0 * D);
@@ -1118,7 +1122,7 @@ __device__ __attribute__((always_inline)) void att_item_fetch(const DecodeArgs &
 template <class S, bool TR>
 __device__ __attribute__((always_inline)) bool att_item_cw(const DecodeArgs &a, float *lds, int step, int l, int p,
                                                            int nch, const ItemOf &it, int lane, Waiter &wt,
-                                                           float4 (&k)[S::D / 4], bool fetched) {
+                                                           float4 (&k)[S::D / 4], int have) {
   constexpr int E = S::E, D = S::D, H = S::H, D4 = D / 4, RPL = 64 / D4, IT = 64 / RPL;
   // (an opaque copy of the lane index: the item's per-lane addresses are
   // computed where they are used instead of once for the whole launch, where
@@ -1127,7 +1131,7 @@ __device__ __attribute__((always_inline)) bool att_item_cw(const DecodeArgs &a, 
   const uint32_t epA = epoch_of(a, step, 5 * l + 0), epB = epA + 1;
   const int ih = it.ih, ic = it.ic, it0 = it.t0, it1 = it.t1, itg = it.tg;
   const bool ilast = it.last;
-  if (!fetched) att_item_fetch<S>(a, lds, l, it, lane, k);
+  if (have != 3) att_item_fetch<S>(a, lds, l, it, lane, k, !(have & 1), !(have & 2));
   wt.start(5 * l + 0);
   const uint64_t *qk = a.qkv_t + ((size_t)l * NCOPY + my_copy()) * 3 * E + ih * D + (lane % D);
   while (true) {
@@ -1360,20 +1364,29 @@ __device__ __attribute__((always_inline)) void compute_set(const DecodeArgs &a, 
   // A, F and M right before their own phase of the layer, set Q right after
   // its phase (the item reads the QKV outputs).  Sets A and F request the next
   // layer's rows of their item once their own phase is done; set M, whose
-  // phase closes the layer, requests them at the item.  A failed wait raises
+  // phase closes the layer and uses that LDS, requests the next layer's key
+  // rows right after its item and the value rows at the item.  A failed wait raises
   // the compute-side abort flag, which every wave reads after the next
   // barrier.
   Waiter wt{&a, 0, 0, 0u};
   float4 kpre[S::ITEM_CW && !DOTS ? S::D / 4 : 1];
-  bool pre = false;  // kpre and the LDS value rows hold this layer's chunk
+  int pre = 0;  // this layer's chunk already requested: key rows in kpre (1), value rows in LDS (2)
   auto run_item = [&](int step, int l, int nch, const ItemOf &it) {
     if constexpr (S::ITEM_CW && !DOTS) {
       const int wl = lane % 64;
       if (!att_item_cw<S, TR>(a, lds, step, l, a.pos0 + step, nch, it, wl, wt, kpre, pre) && wl == 0) flag[1] = 1;
-      pre = false;
+      pre = 0;
       // its stores (the outputs, and the cache rows when the chunk closes at
       // the position) are complete before this wave reaches the next barrier
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if constexpr (SET == SET_M) {
+        // the next layer's key rows now (registers; its value rows must wait
+        // for the end of this set's phase, which uses their LDS)
+        if (l + 1 < a.L) {
+          att_item_fetch<S>(a, lds, l + 1, it, wl, kpre, true, false);
+          pre = 1;
+        }
+      }
     }
   };
   auto aborted = [&]() { return S::ITEM_CW ? (flag[0] | flag[1]) != 0 : flag[0] != 0; };
@@ -1436,7 +1449,7 @@ __device__ __attribute__((always_inline)) void compute_set(const DecodeArgs &a, 
         // that item, this wave's next LDS access)
         if (my_item && l + 1 < a.L) {
           att_item_fetch<S>(a, lds, l + 1, it, lane % 64, kpre);
-          pre = true;
+          pre = 3;
         }
       }
       if constexpr (WD == WD_F16) {
