@@ -467,8 +467,12 @@ def timeline(cfg, torch, g2):
         "us_per_token": round(float(np.median(token)), 2),
         "us_per_layer": round(float(np.median(per_layer)), 2),
         "us_head": round(float(np.median(head)), 2),
+        # (a negative 'inputs ready' is a stamp taken before the inputs were in:
+        # in the eight-wave kernels the dot waves poll the inputs of sets Q, A
+        # and F, and barrier 1 marks their arrival; reported as null)
         "phases_us_ready_barrier1_barrier2_published": {
-            nm: [round(float(x), 2) for x in np.nanmedian(np.array(rows[nm]), axis=0)] for nm in names},
+            nm: [None if (k == 0 and x < 0) else round(float(x), 2)
+                 for k, x in enumerate(np.nanmedian(np.array(rows[nm]), axis=0))] for nm in names},
     }
 
 
